@@ -1,0 +1,221 @@
+"""Pins for the oracle's INT8 / NVFP4 activation quantizers and weight prep.
+
+Pinned against: exact round trips of tensors built on the quantization grid
+(scale a power of two for INT8; g = 1 and every block amax = 6 * scale for
+NVFP4), zero and spike special cases, RNE error bounds, row-permutation
+equivariance, the Hadamard composed from its closed form, and X W^T
+invariance of the rotation.
+"""
+import numpy as np
+import pytest
+
+import workloads
+from workloads import bf16_bits_to_f32, to_bf16_bits
+
+
+def _sylvester16():
+    i = np.arange(16)
+    pc = np.vectorize(lambda v: bin(v).count("1"))(i[:, None] & i[None, :])
+    return np.where(pc % 2 == 0, 1.0, -1.0)
+
+
+def _rotate_exact(x):
+    """Block Hadamard via the dense closed form (exact for small integers)."""
+    M, K = x.shape
+    H = _sylvester16() / 4
+    return (x.reshape(M, K // 16, 16) @ H.T).reshape(M, K)
+
+
+# ---- INT8 -----------------------------------------------------------------
+
+def test_int8_roundtrip_on_grid(orc):
+    rng = np.random.default_rng(3)
+    M, K = 37, 96
+    q = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    q[np.arange(M), rng.integers(0, K, M)] = rng.choice([-127, 127], M)
+    s = np.ldexp(1.0, -rng.integers(0, 12, M)).astype(np.float32)
+    x = to_bf16_bits(q.astype(np.float32) * s[:, None])
+    q2, s2 = orc.quant_int8(x, flags=orc.NO_HADAMARD)
+    # s = amax/127 with amax = 127 * 2^-k: exact
+    assert np.array_equal(s2, s)
+    assert np.array_equal(q2, q)
+
+
+def test_int8_zero_row_and_spike(orc):
+    K = 48
+    x = np.zeros((3, K), np.float32)
+    x[1, 7] = -3.5
+    x[2, :] = 0.25
+    q, s = orc.quant_int8(to_bf16_bits(x), flags=orc.NO_HADAMARD)
+    assert s[0] == 0 and not q[0].any()
+    assert q[1, 7] == -127 and np.count_nonzero(q[1]) == 1
+    assert s[1] == np.float32(3.5) / np.float32(127)
+    assert np.all(q[2] == 127)
+
+
+def test_int8_rne_error_bound(orc):
+    rng = np.random.default_rng(4)
+    x = workloads.activations(rng, 64, 256)
+    q, s = orc.quant_int8(x)
+    xt = np.stack([np.concatenate([orc.fwht16(r[j:j + 16]) for j in range(0, 256, 16)])
+                   for r in bf16_bits_to_f32(x)]).astype(np.float64)
+    amax = np.abs(xt).max(axis=1)
+    assert np.allclose(s, amax / 127, rtol=2e-7, atol=0)
+    err = np.abs(q.astype(np.float64) * s[:, None] - xt)
+    assert np.all(err <= 0.5 * s[:, None] * (1 + 1e-5) + 1e-6 * amax[:, None])
+    assert np.all(np.abs(q).max(axis=1) == 127)
+
+
+def test_int8_rows_permute(orc):
+    rng = np.random.default_rng(5)
+    x = workloads.activations(rng, 50, 128)
+    perm = rng.permutation(50)
+    q, s = orc.quant_int8(x)
+    qp, sp = orc.quant_int8(np.ascontiguousarray(x[perm]))
+    assert np.array_equal(qp, q[perm]) and np.array_equal(sp, s[perm])
+
+
+def test_int8_hadamard_is_block_rotation(orc):
+    rng = np.random.default_rng(6)
+    x = rng.integers(-7, 8, (20, 64)).astype(np.float32)
+    xt = _rotate_exact(x.astype(np.float64)).astype(np.float32)
+    a = orc.quant_int8(to_bf16_bits(x))
+    b = orc.quant_int8(to_bf16_bits(xt), flags=orc.NO_HADAMARD)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ---- NVFP4 ----------------------------------------------------------------
+
+def _nvfp4_grid_tensor(orc, rng, M, K):
+    """Tensor with g = 1: values val(c) * dec(e_b), every block holding a +-6."""
+    nb = K // 16
+    codes = rng.integers(0, 16, (M, K)).astype(np.uint8)
+    pos = rng.integers(0, 16, (M, nb))
+    for m in range(M):
+        for b in range(nb):
+            codes[m, 16 * b + pos[m, b]] = rng.choice([7, 15])
+    e = rng.integers(1, 0x7F, (M, nb)).astype(np.uint8)
+    e[0, 0] = 0x7E  # tensor amax = 6 * 448 = 2688 -> g = 1
+    val = np.vectorize(orc.e2m1_value)(codes).astype(np.float64)
+    dec = np.vectorize(orc.e4m3_value)(e).astype(np.float64)
+    x = val * np.repeat(dec, 16, axis=1)
+    xb = to_bf16_bits(x.astype(np.float32))
+    assert np.array_equal(bf16_bits_to_f32(xb).astype(np.float64), x)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return xb, packed, e
+
+
+def test_nvfp4_roundtrip_on_grid(orc):
+    rng = np.random.default_rng(7)
+    xb, codes, e = _nvfp4_grid_tensor(orc, rng, 9, 80)
+    c2, s2, g = orc.quant_nvfp4(xb, flags=orc.NO_HADAMARD)
+    assert g == 1.0
+    assert np.array_equal(s2, e)
+    assert np.array_equal(c2, codes)
+
+
+def test_nvfp4_all_zero(orc):
+    c, s, g = orc.quant_nvfp4(np.zeros((4, 32), np.uint16))
+    assert g == 0.0 and not c.any() and not s.any()
+
+
+def test_nvfp4_properties_random(orc):
+    rng = np.random.default_rng(8)
+    M, K = 48, 256
+    x = workloads.activations(rng, M, K)
+    c, s, g = orc.quant_nvfp4(x)
+    xt = np.stack([np.concatenate([orc.fwht16(r[j:j + 16]) for j in range(0, K, 16)])
+                   for r in bf16_bits_to_f32(x)]).astype(np.float64)
+    A = np.abs(xt).max()
+    assert g == np.float32(np.float32(A) / np.float32(2688.0))
+    assert np.all(s <= 0x7E)                       # non-negative, finite, <= 448
+    codes = orc.nibbles(c)
+    val = np.vectorize(orc.e2m1_value)(codes).astype(np.float64)
+    S = np.vectorize(orc.e4m3_value)(s).astype(np.float64) * g
+    S16 = np.repeat(S, 16, axis=1)
+    # block amax maps to the top code (scale ~ amax/6 up to E4M3 rounding)
+    blk_max = np.abs(val).reshape(M, K // 16, 16).max(axis=2)
+    normal = S >= 2.0 ** -6 * g
+    assert np.all(blk_max[normal] == 6.0)
+    # dequantization error: at most half the largest E2M1 gap (1.0) times S,
+    # plus whatever saturation clipped
+    err = np.abs(val * S16 - xt)
+    clip = np.maximum(np.abs(xt) - 6 * S16, 0)
+    assert np.all(err <= 1.0 * S16 * (1 + 1e-6) + clip)
+
+
+def test_nvfp4_hadamard_is_block_rotation(orc):
+    rng = np.random.default_rng(9)
+    x = rng.integers(-7, 8, (12, 64)).astype(np.float32)
+    xt = _rotate_exact(x.astype(np.float64)).astype(np.float32)
+    a = orc.quant_nvfp4(to_bf16_bits(x))
+    b = orc.quant_nvfp4(to_bf16_bits(xt), flags=orc.NO_HADAMARD)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2]
+
+
+def test_quant_rejects_bad_k(orc):
+    with pytest.raises(ValueError):
+        orc.quant_int8(np.zeros((2, 24), np.uint16))
+    with pytest.raises(ValueError):
+        orc.quant_nvfp4(np.zeros((2, 40), np.uint16))
+
+
+# ---- weight preparation ---------------------------------------------------
+
+def test_prep_weight_nvfp4_part_is_quantizer(orc):
+    rng = np.random.default_rng(10)
+    w = workloads.weight(rng, 40, 64)
+    p = orc.prep_weight(w)
+    c, s, g = orc.quant_nvfp4(w)
+    assert np.array_equal(p["cw"], c) and np.array_equal(p["sw"], s) and p["gw"] == g
+
+
+def test_prep_weight_int8_from_nvfp4(orc):
+    rng = np.random.default_rng(11)
+    N, K = 40, 64
+    p = orc.prep_weight(workloads.weight(rng, N, K))
+    val = np.vectorize(orc.e2m1_value)(orc.nibbles(p["cw"])).astype(np.float32)
+    dec = np.repeat(np.vectorize(orc.e4m3_value)(p["sw"]).astype(np.float32), 16, axis=1)
+    wd = (val * dec) * np.float32(p["gw"])
+    amax = np.abs(wd).max(axis=1).astype(np.float64)
+    assert np.allclose(p["sw_row"], amax / 127, rtol=2e-7, atol=0)
+    err = np.abs(p["qw"] * p["sw_row"][:, None].astype(np.float64) - wd)
+    assert np.all(err <= 0.5 * p["sw_row"][:, None] * (1 + 1e-5) + 1e-6 * amax[:, None])
+    # the requantized weight keeps the NVFP4 weight's zero pattern and signs
+    assert np.array_equal(np.sign(p["qw"]), np.sign(np.round(wd / p["sw_row"][:, None])))
+
+
+def test_prep_weight_direct_is_int8_quant(orc):
+    rng = np.random.default_rng(12)
+    w = workloads.weight(rng, 24, 48)
+    p = orc.prep_weight(w, orc.W8_DIRECT)
+    q, s = orc.quant_int8(w)
+    assert np.array_equal(p["qw"], q) and np.array_equal(p["sw_row"], s)
+
+
+def test_rotation_preserves_xwt_exactly(orc):
+    # (X H)(W H)^T = X W^T: exact for small integers without quantization
+    rng = np.random.default_rng(13)
+    x = rng.integers(-6, 7, (8, 64)).astype(np.float64)
+    w = rng.integers(-6, 7, (5, 64)).astype(np.float64)
+    xr = np.stack([np.concatenate([orc.fwht16(r[j:j + 16]) for j in range(0, 64, 16)]) for r in x])
+    wr = np.stack([np.concatenate([orc.fwht16(r[j:j + 16]) for j in range(0, 64, 16)]) for r in w])
+    assert np.array_equal(xr.astype(np.float64) @ wr.T.astype(np.float64), x @ w.T)
+
+
+def test_rotated_quantized_linear_tracks_float(orc):
+    rng = np.random.default_rng(14)
+    M, N, K = 64, 48, 256
+    x = workloads.activations(rng, M, K)
+    w = workloads.weight(rng, N, K)
+    ref = bf16_bits_to_f32(x).astype(np.float64) @ bf16_bits_to_f32(w).astype(np.float64).T
+    p = orc.prep_weight(w)
+    qa, sa = orc.quant_int8(x)
+    _, y8 = orc.gemm_int8(qa, sa, p["qw"], p["sw_row"])
+    ca, sca, ga = orc.quant_nvfp4(x)
+    y4, _ = orc.gemm_nvfp4(ca, sca, ga, p["cw"], p["sw"], p["gw"])
+    rel8 = np.linalg.norm(y8 - ref) / np.linalg.norm(ref)
+    rel4 = np.linalg.norm(y4 - ref) / np.linalg.norm(ref)
+    assert rel8 < 0.12 and rel4 < 0.2
+    # INT8 activations over the NVFP4-derived weight beat all-NVFP4
+    assert rel8 < rel4
