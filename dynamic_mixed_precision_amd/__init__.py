@@ -1,0 +1,215 @@
+"""Python binding of libdmpq, the gfx950 hot path of 6Bit-Diffusion's dynamic
+mixed-precision quantized linear layer.
+
+Argument marshalling only: each function passes torch tensors' device
+pointers, sizes and the current HIP stream to the C entry point of the same
+name (``dmpq_<name>``) and raises :class:`DmpqError` on a non-OK status.  All
+arithmetic runs in the library's HIP kernels; there is no fallback.  Output
+tensors are allocated by the caller, as the C ABI requires.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdmpq.so")
+
+OK = 0
+ROUTE_NVFP4, ROUTE_INT8 = 0, 1
+OUT_F32, OUT_BF16, OUT_I32 = 0, 1, 2
+NO_HADAMARD = 1
+W8_FROM_NVFP4, W8_DIRECT = 0, 1
+TDC_SKIP, TDC_REFRESH = 0, 1
+FP4_BF16_DEQUANT = 0
+OP_GAMMA, OP_QUANT_NVFP4, OP_TDC, OP_PREP_WEIGHT = 0, 1, 2, 3
+
+EXPORTS = ("dmpq_last_error", "dmpq_version", "dmpq_workspace_bytes", "dmpq_gamma_sums",
+           "dmpq_gate_and_route", "dmpq_hadamard_quant_int8", "dmpq_hadamard_quant_nvfp4",
+           "dmpq_qgemm_int8", "dmpq_qgemm_nvfp4", "dmpq_tdc_init", "dmpq_tdc_decide",
+           "dmpq_tdc_step", "dmpq_tdc_commit", "dmpq_prep_weight")
+
+
+class DmpqError(RuntimeError):
+    def __init__(self, status: int, fn: str, msg: str):
+        super().__init__(f"{fn} -> status {status}: {msg}")
+        self.status = status
+
+
+class TdcState(C.Structure):
+    """Mirror of dmpq_tdc_state."""
+    _fields_ = [("n_refresh", C.c_int64), ("d", C.c_double), ("acc", C.c_double),
+                ("delta_valid", C.c_int32), ("gamma_valid", C.c_int32), ("gamma", C.c_double)]
+
+
+class TdcParams(C.Structure):
+    """Mirror of dmpq_tdc_params."""
+    _fields_ = [("eps_sim", C.c_double), ("delta_acc", C.c_double)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libdmpq.so (built in-tree by dynamic_mixed_precision_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run python -m "
+                              "dynamic_mixed_precision_amd.build (needs hipcc)")
+        _lib = _declare(C.CDLL(LIB_PATH))
+    return _lib
+
+
+def _declare(L):
+    vp, i64, i32, f64 = C.c_void_p, C.c_int64, C.c_int, C.c_double
+    pd = C.POINTER(C.c_double)
+    sig = {
+        "dmpq_last_error": (C.c_char_p, []),
+        "dmpq_version": (C.c_char_p, []),
+        "dmpq_workspace_bytes": (C.c_size_t, [i32, i64, i64]),
+        "dmpq_gamma_sums": (i32, [vp, vp, vp, i64, vp, vp, C.c_size_t]),
+        "dmpq_gate_and_route": (i32, [pd, i32, pd, pd, f64, pd, pd, C.POINTER(C.c_uint8)]),
+        "dmpq_hadamard_quant_int8": (i32, [vp, vp, i64, i64, i32, vp, vp]),
+        "dmpq_hadamard_quant_nvfp4": (i32, [vp, vp, i64, i64, i32, vp, vp, vp, vp, C.c_size_t]),
+        "dmpq_qgemm_int8": (i32, [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]),
+        "dmpq_qgemm_nvfp4": (i32, [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, i32]),
+        "dmpq_tdc_init": (i32, [C.POINTER(TdcState)]),
+        "dmpq_tdc_decide": (i32, [C.POINTER(TdcState), C.POINTER(TdcParams), C.POINTER(C.c_int)]),
+        "dmpq_tdc_step": (i32, [vp, i32, vp, vp, vp, i64, i32, vp, vp, C.c_size_t]),
+        "dmpq_tdc_commit": (i32, [C.POINTER(TdcState), i32, pd]),
+        "dmpq_prep_weight": (i32, [vp, vp, i64, i64, i32, vp, vp, vp, vp, vp, vp, C.c_size_t]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    return L
+
+
+def _check(status: int, fn: str) -> None:
+    if status != OK:
+        raise DmpqError(status, fn, lib().dmpq_last_error().decode())
+
+
+def _stream(stream=None) -> int:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libdmpq device arguments must be GPU tensors")
+    if not t.is_contiguous():
+        raise ValueError("libdmpq tensors must be contiguous")
+    return t.data_ptr()
+
+
+def last_error() -> str:
+    return lib().dmpq_last_error().decode()
+
+
+def version() -> str:
+    return lib().dmpq_version().decode()
+
+
+def workspace_bytes(op: int, M: int = 0, K: int = 0) -> int:
+    return int(lib().dmpq_workspace_bytes(op, M, K))
+
+
+def new_workspace(op: int, device="cuda"):
+    """Zero-filled workspace tensor for ``op`` (the C ABI's first-use rule)."""
+    import torch
+    return torch.zeros(workspace_bytes(op), dtype=torch.uint8, device=device)
+
+
+def gamma_sums(x_in, x_out, sums, ws, stream=None) -> None:
+    _check(lib().dmpq_gamma_sums(_stream(stream), _ptr(x_in), _ptr(x_out), x_in.numel(),
+                                 _ptr(sums), _ptr(ws), ws.numel()), "dmpq_gamma_sums")
+
+
+def gate_and_route(sums2, alpha, beta, tau: float):
+    """Host router.  sums2: 2 floats or None (Gamma missing).
+    Returns (gamma, errors[n_lin], routes[n_lin])."""
+    a = np.ascontiguousarray(alpha, np.float64)
+    b = np.ascontiguousarray(beta, np.float64)
+    n = len(a)
+    s = None if sums2 is None else np.ascontiguousarray(sums2, np.float64)
+    g = np.zeros(1, np.float64)
+    e = np.zeros(n, np.float64)
+    r = np.zeros(n, np.uint8)
+    pd = C.POINTER(C.c_double)
+    _check(lib().dmpq_gate_and_route(
+        None if s is None else s.ctypes.data_as(pd), n, a.ctypes.data_as(pd),
+        b.ctypes.data_as(pd), tau, g.ctypes.data_as(pd), e.ctypes.data_as(pd),
+        r.ctypes.data_as(C.POINTER(C.c_uint8))), "dmpq_gate_and_route")
+    return float(g[0]), e, r
+
+
+def hadamard_quant_int8(x, q, s_row, flags: int = 0, stream=None) -> None:
+    M, K = x.shape
+    _check(lib().dmpq_hadamard_quant_int8(_stream(stream), _ptr(x), M, K, flags, _ptr(q),
+                                          _ptr(s_row)), "dmpq_hadamard_quant_int8")
+
+
+def hadamard_quant_nvfp4(x, codes, scales, g, ws, flags: int = 0, stream=None) -> None:
+    M, K = x.shape
+    _check(lib().dmpq_hadamard_quant_nvfp4(_stream(stream), _ptr(x), M, K, flags, _ptr(codes),
+                                           _ptr(scales), _ptr(g), _ptr(ws), ws.numel()),
+           "dmpq_hadamard_quant_nvfp4")
+
+
+def qgemm_int8(qa, sa, qw, sw, y, out_dtype: int = OUT_F32, stream=None) -> None:
+    M, K = qa.shape
+    N = qw.shape[0]
+    _check(lib().dmpq_qgemm_int8(_stream(stream), _ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), M, N, K,
+                                 out_dtype, _ptr(y)), "dmpq_qgemm_int8")
+
+
+def qgemm_nvfp4(ca, sa, ga, cw, sw, gw, y, out_dtype: int = OUT_F32,
+                variant: int = FP4_BF16_DEQUANT, stream=None) -> None:
+    M, K = ca.shape[0], 2 * ca.shape[1]
+    N = cw.shape[0]
+    _check(lib().dmpq_qgemm_nvfp4(_stream(stream), _ptr(ca), _ptr(sa), _ptr(ga), _ptr(cw),
+                                  _ptr(sw), _ptr(gw), M, N, K, out_dtype, _ptr(y), variant),
+           "dmpq_qgemm_nvfp4")
+
+
+def tdc_init() -> TdcState:
+    st = TdcState()
+    _check(lib().dmpq_tdc_init(C.byref(st)), "dmpq_tdc_init")
+    return st
+
+
+def tdc_decide(st: TdcState, eps_sim: float, delta_acc: float) -> bool:
+    p = TdcParams(eps_sim, delta_acc)
+    out = C.c_int(0)
+    _check(lib().dmpq_tdc_decide(C.byref(st), C.byref(p), C.byref(out)), "dmpq_tdc_decide")
+    return bool(out.value)
+
+
+def tdc_step(mode: int, x_in, x_out, delta, delta_valid: bool, sums=None, ws=None,
+             stream=None) -> None:
+    _check(lib().dmpq_tdc_step(_stream(stream), mode, _ptr(x_in), _ptr(x_out), _ptr(delta),
+                               x_in.numel(), int(delta_valid), _ptr(sums), _ptr(ws),
+                               0 if ws is None else ws.numel()), "dmpq_tdc_step")
+
+
+def tdc_commit(st: TdcState, mode: int, sums4=None) -> None:
+    s = None if sums4 is None else np.ascontiguousarray(sums4, np.float64)
+    _check(lib().dmpq_tdc_commit(C.byref(st), mode,
+                                 None if s is None else s.ctypes.data_as(C.POINTER(C.c_double))),
+           "dmpq_tdc_commit")
+
+
+def prep_weight(w, cw, sw, gw, qw, sw_row, ws, int8_mode: int = W8_FROM_NVFP4,
+                stream=None) -> None:
+    N, K = w.shape
+    _check(lib().dmpq_prep_weight(_stream(stream), _ptr(w), N, K, int8_mode, _ptr(cw), _ptr(sw),
+                                  _ptr(gw), _ptr(qw), _ptr(sw_row), _ptr(ws), ws.numel()),
+           "dmpq_prep_weight")

@@ -1,0 +1,284 @@
+// api.hip -- the C ABI of libdmpq (declared in include/dmpq.h): argument
+// validation, per-thread error messages, the host-side router and TDC
+// bookkeeping, and dispatch to the gfx950 kernels.
+#include "dmpq.h"
+#include "internal.hpp"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+using namespace dmpq;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+dmpq_status fail(dmpq_status code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+dmpq_status ok() {
+    g_err[0] = '\0';
+    return DMPQ_OK;
+}
+
+dmpq_status hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ok();
+    return fail(DMPQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE_PTR(p)                                                                  \
+    do {                                                                                \
+        if (!(p)) return fail(DMPQ_ERR_INVALID_ARG, "%s: %s is NULL", __func__, #p);    \
+        if (!aligned16(p))                                                              \
+            return fail(DMPQ_ERR_MISALIGNED, "%s: %s is not 16-byte aligned", __func__, #p); \
+    } while (0)
+
+#define REQUIRE_HOST(p)                                                                 \
+    do {                                                                                \
+        if (!(p)) return fail(DMPQ_ERR_INVALID_ARG, "%s: %s is NULL", __func__, #p);    \
+    } while (0)
+
+dmpq_status check_k(const char *fn, int64_t K) {
+    if (K <= 0 || K % 16 != 0)
+        return fail(DMPQ_ERR_BAD_SHAPE, "%s: K = %lld must be a positive multiple of 16", fn,
+                    (long long)K);
+    return DMPQ_OK;
+}
+
+dmpq_status check_ws(const char *fn, const void *ws, size_t bytes) {
+    if (!ws) return fail(DMPQ_ERR_WORKSPACE, "%s: workspace is NULL", fn);
+    if (!aligned16(ws)) return fail(DMPQ_ERR_MISALIGNED, "%s: workspace is not 16-byte aligned", fn);
+    if (bytes < kWsBytes)
+        return fail(DMPQ_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, bytes,
+                    kWsBytes);
+    return DMPQ_OK;
+}
+
+double rel_ratio(double num, double den) {
+    if (den == 0.0) return num == 0.0 ? 0.0 : INFINITY;
+    return num / den;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dmpq_last_error(void) { return g_err; }
+
+const char *dmpq_version(void) { return "dmpq 0.1 gfx950"; }
+
+size_t dmpq_workspace_bytes(int op, int64_t M, int64_t K) {
+    (void)M;
+    (void)K;
+    switch (op) {
+        case DMPQ_OP_GAMMA:
+        case DMPQ_OP_QUANT_NVFP4:
+        case DMPQ_OP_TDC:
+        case DMPQ_OP_PREP_WEIGHT: return kWsBytes;
+    }
+    return 0;
+}
+
+dmpq_status dmpq_gamma_sums(hipStream_t stream, const uint16_t *x_in, const uint16_t *x_out,
+                            int64_t n, double *d_sums2, void *ws, size_t ws_bytes) {
+    REQUIRE_PTR(x_in);
+    REQUIRE_PTR(x_out);
+    REQUIRE_PTR(d_sums2);
+    if (n < 0) return fail(DMPQ_ERR_BAD_SHAPE, "%s: n = %lld < 0", __func__, (long long)n);
+    if (dmpq_status s = check_ws(__func__, ws, ws_bytes)) return s;
+    return hip_status(launch_gamma(stream, x_in, x_out, n, d_sums2, Workspace(ws)), __func__);
+}
+
+dmpq_status dmpq_gate_and_route(const double *h_sums2, int n_lin, const double *h_alpha,
+                                const double *h_beta, double tau, double *h_gamma_out,
+                                double *h_err_out, uint8_t *h_route_out) {
+    if (n_lin < 0) return fail(DMPQ_ERR_BAD_SHAPE, "%s: n_lin = %d < 0", __func__, n_lin);
+    REQUIRE_HOST(h_route_out);
+    if (!h_sums2) {  // Gamma missing: INT8 for every linear
+        if (h_gamma_out) *h_gamma_out = NAN;
+        for (int l = 0; l < n_lin; l++) {
+            if (h_err_out) h_err_out[l] = NAN;
+            h_route_out[l] = DMPQ_ROUTE_INT8;
+        }
+        return ok();
+    }
+    REQUIRE_HOST(h_alpha);
+    REQUIRE_HOST(h_beta);
+    const double gamma = rel_ratio(h_sums2[0], h_sums2[1]);
+    if (h_gamma_out) *h_gamma_out = gamma;
+    for (int l = 0; l < n_lin; l++) {
+        const double e = h_alpha[l] * gamma + h_beta[l];
+        if (h_err_out) h_err_out[l] = e;
+        h_route_out[l] = e > tau ? DMPQ_ROUTE_INT8 : DMPQ_ROUTE_NVFP4;
+    }
+    return ok();
+}
+
+dmpq_status dmpq_hadamard_quant_int8(hipStream_t stream, const uint16_t *x, int64_t M,
+                                     int64_t K, int flags, int8_t *q, float *s_row) {
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(s_row);
+    if (M < 0) return fail(DMPQ_ERR_BAD_SHAPE, "%s: M = %lld < 0", __func__, (long long)M);
+    if (dmpq_status s = check_k(__func__, K)) return s;
+    if (flags & ~DMPQ_NO_HADAMARD) return fail(DMPQ_ERR_INVALID_ARG, "%s: unknown flags %d", __func__, flags);
+    if (!hq_int8_supported(K))
+        return fail(DMPQ_ERR_UNSUPPORTED, "%s: K = %lld exceeds 32768", __func__, (long long)K);
+    return hip_status(launch_hq_int8(stream, x, M, K, flags, q, s_row), __func__);
+}
+
+dmpq_status dmpq_hadamard_quant_nvfp4(hipStream_t stream, const uint16_t *x, int64_t M,
+                                      int64_t K, int flags, uint8_t *codes, uint8_t *scales,
+                                      float *d_g, void *ws, size_t ws_bytes) {
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(codes);
+    REQUIRE_PTR(scales);
+    REQUIRE_PTR(d_g);
+    if (M < 0) return fail(DMPQ_ERR_BAD_SHAPE, "%s: M = %lld < 0", __func__, (long long)M);
+    if (dmpq_status s = check_k(__func__, K)) return s;
+    if (flags & ~DMPQ_NO_HADAMARD) return fail(DMPQ_ERR_INVALID_ARG, "%s: unknown flags %d", __func__, flags);
+    if (dmpq_status s = check_ws(__func__, ws, ws_bytes)) return s;
+    return hip_status(launch_hq_nvfp4(stream, x, M, K, flags, codes, scales, d_g, Workspace(ws)),
+                      __func__);
+}
+
+static dmpq_status check_gemm(const char *fn, int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0)
+        return fail(DMPQ_ERR_BAD_SHAPE, "%s: M = %lld, N = %lld must be >= 0", fn, (long long)M,
+                    (long long)N);
+    if (M > (int64_t)INT32_MAX * 128 || N > (int64_t)INT32_MAX)
+        return fail(DMPQ_ERR_UNSUPPORTED, "%s: M or N too large", fn);
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    if (tiles > (int64_t)UINT32_MAX) return fail(DMPQ_ERR_UNSUPPORTED, "%s: too many tiles", fn);
+    return check_k(fn, K);
+}
+
+dmpq_status dmpq_qgemm_int8(hipStream_t stream, const int8_t *qa, const float *sa,
+                            const int8_t *qw, const float *sw, int64_t M, int64_t N, int64_t K,
+                            int out_dtype, void *y) {
+    REQUIRE_PTR(qa);
+    REQUIRE_PTR(sa);
+    REQUIRE_PTR(qw);
+    REQUIRE_PTR(sw);
+    REQUIRE_PTR(y);
+    if (dmpq_status s = check_gemm(__func__, M, N, K)) return s;
+    if (out_dtype != DMPQ_OUT_F32 && out_dtype != DMPQ_OUT_BF16 && out_dtype != DMPQ_OUT_I32)
+        return fail(DMPQ_ERR_INVALID_ARG, "%s: unknown out_dtype %d", __func__, out_dtype);
+    return hip_status(launch_gemm_int8(stream, qa, sa, qw, sw, M, N, K, out_dtype, y), __func__);
+}
+
+dmpq_status dmpq_qgemm_nvfp4(hipStream_t stream, const uint8_t *ca, const uint8_t *sa,
+                             const float *d_ga, const uint8_t *cw, const uint8_t *sw,
+                             const float *d_gw, int64_t M, int64_t N, int64_t K, int out_dtype,
+                             void *y, int variant) {
+    REQUIRE_PTR(ca);
+    REQUIRE_PTR(sa);
+    REQUIRE_PTR(d_ga);
+    REQUIRE_PTR(cw);
+    REQUIRE_PTR(sw);
+    REQUIRE_PTR(d_gw);
+    REQUIRE_PTR(y);
+    if (dmpq_status s = check_gemm(__func__, M, N, K)) return s;
+    if (out_dtype != DMPQ_OUT_F32 && out_dtype != DMPQ_OUT_BF16)
+        return fail(DMPQ_ERR_INVALID_ARG, "%s: unknown out_dtype %d", __func__, out_dtype);
+    if (variant != DMPQ_FP4_BF16_DEQUANT)
+        return fail(DMPQ_ERR_INVALID_ARG, "%s: unknown variant %d", __func__, variant);
+    return hip_status(launch_gemm_nvfp4(stream, ca, sa, d_ga, cw, sw, d_gw, M, N, K, out_dtype,
+                                        y, variant),
+                      __func__);
+}
+
+dmpq_status dmpq_tdc_init(dmpq_tdc_state *h_st) {
+    REQUIRE_HOST(h_st);
+    memset(h_st, 0, sizeof *h_st);
+    h_st->d = INFINITY;
+    h_st->gamma = NAN;
+    return ok();
+}
+
+dmpq_status dmpq_tdc_decide(const dmpq_tdc_state *h_st, const dmpq_tdc_params *h_p,
+                            int *h_skip) {
+    REQUIRE_HOST(h_st);
+    REQUIRE_HOST(h_p);
+    REQUIRE_HOST(h_skip);
+    *h_skip = h_st->n_refresh >= 2 && h_st->delta_valid && h_st->d < h_p->eps_sim &&
+              h_st->acc + h_st->d <= h_p->delta_acc;
+    return ok();
+}
+
+dmpq_status dmpq_tdc_step(hipStream_t stream, int mode, const uint16_t *x_in, uint16_t *x_out,
+                          uint16_t *delta, int64_t n, int delta_valid, double *d_sums4,
+                          void *ws, size_t ws_bytes) {
+    REQUIRE_PTR(x_in);
+    REQUIRE_PTR(x_out);
+    REQUIRE_PTR(delta);
+    if (n < 0) return fail(DMPQ_ERR_BAD_SHAPE, "%s: n = %lld < 0", __func__, (long long)n);
+    if (mode == DMPQ_TDC_SKIP) {
+        if (!delta_valid)
+            return fail(DMPQ_ERR_INVALID_ARG, "%s: SKIP needs a cached delta", __func__);
+        if (n == 0) return ok();
+        return hip_status(launch_tdc_skip(stream, x_in, delta, n, x_out), __func__);
+    }
+    if (mode != DMPQ_TDC_REFRESH)
+        return fail(DMPQ_ERR_INVALID_ARG, "%s: unknown mode %d", __func__, mode);
+    REQUIRE_PTR(d_sums4);
+    if (dmpq_status s = check_ws(__func__, ws, ws_bytes)) return s;
+    return hip_status(launch_tdc_refresh(stream, x_in, x_out, delta, n, delta_valid, d_sums4,
+                                         Workspace(ws)),
+                      __func__);
+}
+
+dmpq_status dmpq_tdc_commit(dmpq_tdc_state *h_st, int mode, const double *h_sums4) {
+    REQUIRE_HOST(h_st);
+    if (mode == DMPQ_TDC_SKIP) {
+        h_st->acc += h_st->d;
+        h_st->gamma_valid = 0;
+        return ok();
+    }
+    if (mode != DMPQ_TDC_REFRESH)
+        return fail(DMPQ_ERR_INVALID_ARG, "%s: unknown mode %d", __func__, mode);
+    REQUIRE_HOST(h_sums4);
+    h_st->d = h_st->delta_valid ? rel_ratio(h_sums4[2], h_sums4[3]) : INFINITY;
+    h_st->acc = 0.0;
+    h_st->n_refresh += 1;
+    h_st->delta_valid = 1;
+    h_st->gamma = rel_ratio(h_sums4[0], h_sums4[1]);
+    h_st->gamma_valid = 1;
+    return ok();
+}
+
+dmpq_status dmpq_prep_weight(hipStream_t stream, const uint16_t *w, int64_t N, int64_t K,
+                             int int8_mode, uint8_t *cw, uint8_t *sw, float *d_gw, int8_t *qw,
+                             float *sw_row, void *ws, size_t ws_bytes) {
+    REQUIRE_PTR(w);
+    REQUIRE_PTR(cw);
+    REQUIRE_PTR(sw);
+    REQUIRE_PTR(d_gw);
+    REQUIRE_PTR(qw);
+    REQUIRE_PTR(sw_row);
+    if (N < 0) return fail(DMPQ_ERR_BAD_SHAPE, "%s: N = %lld < 0", __func__, (long long)N);
+    if (dmpq_status s = check_k(__func__, K)) return s;
+    if (int8_mode != DMPQ_W8_FROM_NVFP4 && int8_mode != DMPQ_W8_DIRECT)
+        return fail(DMPQ_ERR_INVALID_ARG, "%s: unknown int8_mode %d", __func__, int8_mode);
+    if (!hq_int8_supported(K))
+        return fail(DMPQ_ERR_UNSUPPORTED, "%s: K = %lld exceeds 32768", __func__, (long long)K);
+    if (dmpq_status s = check_ws(__func__, ws, ws_bytes)) return s;
+    hipError_t e = launch_hq_nvfp4(stream, w, N, K, 0, cw, sw, d_gw, Workspace(ws));
+    if (e != hipSuccess) return hip_status(e, __func__);
+    if (int8_mode == DMPQ_W8_DIRECT)
+        e = launch_hq_int8(stream, w, N, K, 0, qw, sw_row);
+    else
+        e = launch_w8_from_nvfp4(stream, cw, sw, d_gw, N, K, qw, sw_row);
+    return hip_status(e, __func__);
+}
+
+}  // extern "C"

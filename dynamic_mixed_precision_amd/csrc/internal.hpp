@@ -1,0 +1,63 @@
+// internal.hpp -- launchers shared between the translation units of libdmpq.
+// Each launcher assumes its arguments were validated by the C-ABI layer
+// (api.hip) and returns the hipError_t of its launch(es).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dmpq {
+
+// Fixed workspace layout for the deterministic two-stage reductions: up to
+// kMaxPartials per-workgroup partials, then a ticket counter and a scratch
+// slot.  All grids that use a workspace are capped at kMaxPartials groups.
+constexpr int kMaxPartials = 2048;
+constexpr int kMaxSums = 4;
+constexpr size_t kWsPartialBytes = sizeof(double) * kMaxSums * kMaxPartials;
+constexpr size_t kWsBytes = kWsPartialBytes + 256;
+
+struct Workspace {
+    double *partial;   // kMaxSums * kMaxPartials doubles (also viewed as floats)
+    unsigned *ticket;  // self-resetting arrival counter
+    float *amax;       // NVFP4 tensor amax handed from pass 1 to pass 2
+    explicit Workspace(void *ws)
+        : partial(static_cast<double *>(ws)),
+          ticket(reinterpret_cast<unsigned *>(static_cast<char *>(ws) + kWsPartialBytes)),
+          amax(reinterpret_cast<float *>(static_cast<char *>(ws) + kWsPartialBytes + 64)) {}
+};
+
+hipError_t launch_hq_int8(hipStream_t s, const uint16_t *x, int64_t M, int64_t K, int flags,
+                          int8_t *q, float *s_row);
+hipError_t launch_hq_nvfp4(hipStream_t s, const uint16_t *x, int64_t M, int64_t K, int flags,
+                           uint8_t *codes, uint8_t *scales, float *g, const Workspace &ws);
+hipError_t launch_w8_from_nvfp4(hipStream_t s, const uint8_t *cw, const uint8_t *sw,
+                                const float *gw, int64_t N, int64_t K, int8_t *qw,
+                                float *sw_row);
+bool hq_int8_supported(int64_t K);
+
+hipError_t launch_gamma(hipStream_t s, const uint16_t *x_in, const uint16_t *x_out, int64_t n,
+                        double *sums, const Workspace &ws);
+hipError_t launch_tdc_skip(hipStream_t s, const uint16_t *x_in, const uint16_t *delta,
+                           int64_t n, uint16_t *x_out);
+hipError_t launch_tdc_refresh(hipStream_t s, const uint16_t *x_in, const uint16_t *x_out,
+                              uint16_t *delta, int64_t n, int delta_valid, double *sums,
+                              const Workspace &ws);
+
+hipError_t launch_gemm_int8(hipStream_t s, const int8_t *qa, const float *sa, const int8_t *qw,
+                            const float *sw, int64_t M, int64_t N, int64_t K, int out_dtype,
+                            void *y);
+hipError_t launch_gemm_nvfp4(hipStream_t s, const uint8_t *ca, const uint8_t *sa,
+                             const float *ga, const uint8_t *cw, const uint8_t *sw,
+                             const float *gw, int64_t M, int64_t N, int64_t K, int out_dtype,
+                             void *y, int variant);
+
+// Grid for a grid-stride loop over `work` items with 256 threads per group.
+inline unsigned stride_grid(int64_t work, int64_t per_group, unsigned cap) {
+    int64_t g = (work + per_group - 1) / per_group;
+    if (g < 1) g = 1;
+    if (g > (int64_t)cap) g = cap;
+    return (unsigned)g;
+}
+
+}  // namespace dmpq

@@ -1,0 +1,310 @@
+// quant.hip -- online block Hadamard fused with dynamic activation
+// quantization (per-token INT8, two-level NVFP4), and the INT8 requant of an
+// NVFP4 weight.  Method: 6Bit-Diffusion, DMPQ (gist.science summaries, §2.A:
+// Hadamard on local activation blocks, then INT8 or NVFP4 by route; the
+// Chinese summary's §2.A adds that weights are NVFP4 offline and converted
+// when an INT8 GEMM needs them).
+//
+// Layout of the work: every lane owns whole 16-element blocks, so the
+// Hadamard butterflies run entirely in registers with no lane exchange.  A
+// block is 32 contiguous bytes of bf16; consecutive lanes own consecutive
+// blocks, so a wave streams a contiguous 2 KB span per load pair.
+#include "device.hpp"
+#include "internal.hpp"
+
+#include <float.h>
+
+namespace dmpq {
+
+// ---------------------------------------------------------------------------
+// Row-wise INT8 quantization.  LPR lanes cooperate on one row; each lane holds
+// BPL blocks (16*BPL fp32 values) in registers between the absmax reduction
+// and the code write, so the row is read from memory exactly once.
+// ---------------------------------------------------------------------------
+
+// Source of a row's 16-blocks: bf16 activations, rotated unless flagged off.
+struct Bf16Rows {
+    const uint16_t *x;
+    int flags;
+    __device__ __forceinline__ void load(int64_t row, int64_t K, int b, float v[16]) const {
+        const uint4 *p = reinterpret_cast<const uint4 *>(x + row * K + 16 * (int64_t)b);
+        uint4 a0 = load_nt16(p);
+        uint4 a1 = load_nt16(p + 1);
+        unpack16(a0, a1, v);
+        if (!(flags & 1)) fwht16(v);
+    }
+};
+
+// Source of a row's 16-blocks: an NVFP4 weight dequantized to
+// (E2M1 value * E4M3 value) * g in fp32.
+struct Nvfp4Rows {
+    const uint8_t *codes;
+    const uint8_t *scales;
+    const float *g;
+    __device__ __forceinline__ void load(int64_t row, int64_t K, int b, float v[16]) const {
+        const uint2 c = *reinterpret_cast<const uint2 *>(codes + row * (K / 2) + 8 * (int64_t)b);
+        const float s = e4m3_value(scales[row * (K / 16) + b]);
+        const float gg = *g;
+        const uint32_t w[2] = {c.x, c.y};
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            uint32_t code = (w[i >> 3] >> (4 * (i & 7))) & 15u;
+            uint32_t mag = code & 7u;
+            // E2M1 magnitude as fp32 bits: 0, 0.5, then 2^(e-1) * (1 + m/2)
+            uint32_t bits = mag >= 2u ? ((((mag >> 1) + 126u) << 23) | ((mag & 1u) << 22))
+                                      : (mag ? 0x3F000000u : 0u);
+            float val = __uint_as_float(bits | ((code & 8u) << 28));
+            v[i] = (val * s) * gg;
+        }
+    }
+};
+
+template <int LPR, int BPL, class Src>
+__global__ __launch_bounds__(256) void row_quant_int8_kernel(Src src, int64_t M, int64_t K,
+                                                             int8_t *__restrict__ q,
+                                                             float *__restrict__ s_row) {
+    static_assert(LPR >= 16 && LPR <= 256 && 256 % LPR == 0, "lanes per row");
+    constexpr int ROWS = 256 / LPR;
+    __shared__ float red[4];
+    const int tid = threadIdx.x;
+    const int lr = tid % LPR;
+    const int64_t row = (int64_t)blockIdx.x * ROWS + tid / LPR;
+    const int nblk = (int)(K / 16);
+    const bool row_ok = row < M;
+
+    float v[BPL][16];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < BPL; i++) {
+        const int b = lr + i * LPR;
+        if (row_ok && b < nblk) {
+            src.load(row, K, b, v[i]);
+#pragma unroll
+            for (int j = 0; j < 16; j++) amax = fmaxf(amax, __builtin_fabsf(v[i][j]));
+        }
+    }
+    if constexpr (LPR <= kWave) {
+        amax = group_max<LPR>(amax);
+    } else {
+        amax = wave_max(amax);
+        if ((tid & (kWave - 1)) == 0) red[tid / kWave] = amax;
+        __syncthreads();
+        constexpr int WPR = LPR / kWave;
+        const int w0 = (tid / LPR) * WPR;
+        amax = red[w0];
+#pragma unroll
+        for (int w = 1; w < WPR; w++) amax = fmaxf(amax, red[w0 + w]);
+    }
+    if (!row_ok) return;
+
+    float inv = 0.0f;
+    if (amax > 0.0f) inv = 127.0f / amax;
+    if (lr == 0) s_row[row] = amax > 0.0f ? amax / 127.0f : 0.0f;
+    int8_t *qr = q + row * K;
+#pragma unroll
+    for (int i = 0; i < BPL; i++) {
+        const int b = lr + i * LPR;
+        if (b >= nblk) continue;
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+            float r = __builtin_rintf(v[i][j] * inv);
+            r = fminf(fmaxf(r, -127.0f), 127.0f);
+            w[j >> 2] |= ((uint32_t)(int)r & 0xFFu) << (8 * (j & 3));
+        }
+        *reinterpret_cast<uint4 *>(qr + 16 * (int64_t)b) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+// Pick lanes-per-row and blocks-per-lane for a row of nblk 16-blocks: the
+// least idle lanes, then the most blocks per lane (fewer lanes to reduce).
+struct RowPlan {
+    int lpr, bpl;
+};
+static const int kBplChoices[] = {1, 2, 3, 4, 6, 8};
+
+static bool plan_rows(int64_t K, RowPlan *out) {
+    const int64_t nblk = K / 16;
+    bool found = false;
+    int64_t best_waste = 0;
+    for (int lpr = 16; lpr <= 256; lpr *= 2) {
+        for (int bpl : kBplChoices) {
+            if ((int64_t)lpr * bpl < nblk) continue;
+            const int64_t waste = (int64_t)lpr * bpl - nblk;
+            // only the smallest bpl that covers the row for this lpr
+            bool smaller_fits = false;
+            for (int b2 : kBplChoices)
+                if (b2 < bpl && (int64_t)lpr * b2 >= nblk) smaller_fits = true;
+            if (smaller_fits) continue;
+            if (!found || waste < best_waste || (waste == best_waste && bpl > out->bpl)) {
+                found = true;
+                best_waste = waste;
+                out->lpr = lpr;
+                out->bpl = bpl;
+            }
+        }
+    }
+    return found;
+}
+
+bool hq_int8_supported(int64_t K) {
+    RowPlan p;
+    return K > 0 && K % 16 == 0 && plan_rows(K, &p);
+}
+
+template <class Src, int LPR>
+static hipError_t launch_rows_lpr(hipStream_t s, int bpl, const Src &src, int64_t M,
+                                  int64_t K, int8_t *q, float *s_row) {
+    const int64_t rows_per_group = 256 / LPR;
+    const dim3 grid((unsigned)((M + rows_per_group - 1) / rows_per_group));
+    switch (bpl) {
+#define DMPQ_BPL(B)                                                                      \
+    case B:                                                                              \
+        hipLaunchKernelGGL((row_quant_int8_kernel<LPR, B, Src>), grid, dim3(256), 0, s, src, \
+                           M, K, q, s_row);                                              \
+        break;
+        DMPQ_BPL(1) DMPQ_BPL(2) DMPQ_BPL(3) DMPQ_BPL(4) DMPQ_BPL(6) DMPQ_BPL(8)
+#undef DMPQ_BPL
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <class Src>
+static hipError_t launch_rows(hipStream_t s, const Src &src, int64_t M, int64_t K, int8_t *q,
+                              float *s_row) {
+    RowPlan p;
+    if (!plan_rows(K, &p)) return hipErrorInvalidValue;
+    if (M == 0) return hipSuccess;
+    switch (p.lpr) {
+        case 16: return launch_rows_lpr<Src, 16>(s, p.bpl, src, M, K, q, s_row);
+        case 32: return launch_rows_lpr<Src, 32>(s, p.bpl, src, M, K, q, s_row);
+        case 64: return launch_rows_lpr<Src, 64>(s, p.bpl, src, M, K, q, s_row);
+        case 128: return launch_rows_lpr<Src, 128>(s, p.bpl, src, M, K, q, s_row);
+        case 256: return launch_rows_lpr<Src, 256>(s, p.bpl, src, M, K, q, s_row);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_hq_int8(hipStream_t s, const uint16_t *x, int64_t M, int64_t K, int flags,
+                          int8_t *q, float *s_row) {
+    return launch_rows(s, Bf16Rows{x, flags}, M, K, q, s_row);
+}
+
+hipError_t launch_w8_from_nvfp4(hipStream_t s, const uint8_t *cw, const uint8_t *sw,
+                                const float *gw, int64_t N, int64_t K, int8_t *qw,
+                                float *sw_row) {
+    return launch_rows(s, Nvfp4Rows{cw, sw, gw}, N, K, qw, sw_row);
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4, pass 1: absmax of the rotated tensor.  Each workgroup reduces its
+// share to one float; the last workgroup to arrive (ticket counter) reduces
+// the partials, publishes A and g = A/2688, and resets the ticket.  Max is
+// order independent, so the result does not depend on arrival order.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void nvfp4_amax_kernel(const uint16_t *__restrict__ x,
+                                                         int64_t nblocks, int flags,
+                                                         float *__restrict__ partial,
+                                                         unsigned *ticket, float *amax_out,
+                                                         float *g_out) {
+    __shared__ float red[4];
+    __shared__ bool last;
+    const int tid = threadIdx.x;
+    float m = 0.0f;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t b = (int64_t)blockIdx.x * 256 + tid; b < nblocks; b += stride) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(x + 16 * b);
+        uint4 a0 = load_nt16(p);
+        uint4 a1 = load_nt16(p + 1);
+        float v[16];
+        unpack16(a0, a1, v);
+        if (!(flags & 1)) fwht16(v);
+#pragma unroll
+        for (int j = 0; j < 16; j++) m = fmaxf(m, __builtin_fabsf(v[j]));
+    }
+    m = wave_max(m);
+    if ((tid & (kWave - 1)) == 0) red[tid / kWave] = m;
+    __syncthreads();
+    if (tid == 0) {
+        float w = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        partial[blockIdx.x] = w;
+        __threadfence();
+        last = atomicAdd(ticket, 1u) == gridDim.x - 1;
+    }
+    __syncthreads();
+    if (!last) return;
+    __threadfence();
+    float a = 0.0f;
+    for (unsigned i = tid; i < gridDim.x; i += 256)
+        a = fmaxf(a, __hip_atomic_load(&partial[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    a = wave_max(a);
+    __syncthreads();
+    if ((tid & (kWave - 1)) == 0) red[tid / kWave] = a;
+    __syncthreads();
+    if (tid == 0) {
+        const float A = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        *amax_out = A;
+        *g_out = A / 2688.0f;
+        __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4, pass 2: per 16-block E4M3 scale and E2M1 codes.  The flat block index
+// b addresses codes (8 bytes per block) and scales (1 byte per block)
+// directly, because K is a multiple of 16.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t *__restrict__ x,
+                                                          int64_t nblocks, int flags,
+                                                          const float *__restrict__ amax_in,
+                                                          uint8_t *__restrict__ codes,
+                                                          uint8_t *__restrict__ scales) {
+    const float A = *amax_in;
+    const float g = A / 2688.0f;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < nblocks; b += stride) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(x + 16 * b);
+        uint4 a0 = load_nt16(p);
+        uint4 a1 = load_nt16(p + 1);
+        float v[16];
+        unpack16(a0, a1, v);
+        if (!(flags & 1)) fwht16(v);
+        float ab = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 16; j++) ab = fmaxf(ab, __builtin_fabsf(v[j]));
+        uint32_t e = 0u;
+        float S = 0.0f;
+        if (A > 0.0f) {
+            const float r = ab / A;
+            e = e4m3_encode_nonneg(r * 448.0f);
+            S = e4m3_value(e) * g;
+        }
+        uint32_t w0 = 0u, w1 = 0u;
+        if (S >= FLT_MIN) {
+            const float inv = 1.0f / S;
+#pragma unroll
+            for (int j = 0; j < 8; j++) w0 |= e2m1_encode(v[j] * inv) << (4 * j);
+#pragma unroll
+            for (int j = 0; j < 8; j++) w1 |= e2m1_encode(v[8 + j] * inv) << (4 * j);
+        }
+        *reinterpret_cast<uint2 *>(codes + 8 * b) = make_uint2(w0, w1);
+        scales[b] = (uint8_t)e;
+    }
+}
+
+hipError_t launch_hq_nvfp4(hipStream_t s, const uint16_t *x, int64_t M, int64_t K, int flags,
+                           uint8_t *codes, uint8_t *scales, float *g, const Workspace &ws) {
+    const int64_t nblocks = M * (K / 16);
+    const unsigned ga = stride_grid(nblocks, 256 * 4, kMaxPartials);
+    hipLaunchKernelGGL(nvfp4_amax_kernel, dim3(ga), dim3(256), 0, s, x, nblocks, flags,
+                       reinterpret_cast<float *>(ws.partial), ws.ticket, ws.amax, g);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || nblocks == 0) return e;
+    const unsigned gb = stride_grid(nblocks, 256 * 2, 8192);
+    hipLaunchKernelGGL(nvfp4_quant_kernel, dim3(gb), dim3(256), 0, s, x, nblocks, flags,
+                       ws.amax, codes, scales);
+    return hipGetLastError();
+}
+
+}  // namespace dmpq

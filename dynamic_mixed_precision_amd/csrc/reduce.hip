@@ -1,0 +1,280 @@
+// reduce.hip -- Gamma predictor sums and the Temporal Delta Cache step.
+// Method: 6Bit-Diffusion (gist.science summaries): Gamma is the relative L1
+// distance between a block's output and input at the previous step (§2.A,
+// "Mechanism"); TDC caches the residual delta out - in, compares the last two
+// deltas, and either reuses the cached delta or recomputes (§2.B).
+//
+// All kernels stream bf16 in 16-byte vectors (8 elements).  Sums: each lane
+// adds 8 non-negative fp32 terms (relative error <= 7 ulp of fp32, below
+// 4.2e-7), then accumulates in fp64; workgroups reduce in a fixed tree and
+// the last workgroup to arrive adds the per-group partials in index order,
+// so results are bit-identical from run to run.
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace dmpq {
+
+namespace {
+
+constexpr int kUnroll = 4;
+
+__device__ __forceinline__ uint4 ld16(const uint16_t *p) {
+    return load_nt16(p);
+}
+
+__device__ __forceinline__ void to8(const uint4 &a, float v[8]) {
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        v[2 * i] = bf16_lo(w[i]);
+        v[2 * i + 1] = bf16_hi(w[i]);
+    }
+}
+
+// Reduce NS per-lane fp64 sums over the grid into out[0..NS).  Must be called
+// by every thread of every workgroup.
+template <int NS>
+__device__ void grid_sum(double (&s)[NS], double *partial, unsigned *ticket, double *out) {
+    __shared__ double red[NS][4];
+    __shared__ bool last;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < NS; j++) s[j] = wave_sum(s[j]);
+    if ((tid & (kWave - 1)) == 0) {
+#pragma unroll
+        for (int j = 0; j < NS; j++) red[j][tid / kWave] = s[j];
+    }
+    __syncthreads();
+    if (tid == 0) {
+#pragma unroll
+        for (int j = 0; j < NS; j++)
+            partial[(size_t)blockIdx.x * NS + j] = (red[j][0] + red[j][1]) + (red[j][2] + red[j][3]);
+        __threadfence();
+        last = atomicAdd(ticket, 1u) == gridDim.x - 1;
+    }
+    __syncthreads();
+    if (!last) return;
+    __threadfence();
+    double t[NS];
+#pragma unroll
+    for (int j = 0; j < NS; j++) t[j] = 0.0;
+    for (unsigned i = tid; i < gridDim.x; i += 256) {
+#pragma unroll
+        for (int j = 0; j < NS; j++)
+            t[j] += __hip_atomic_load(&partial[(size_t)i * NS + j], __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int j = 0; j < NS; j++) t[j] = wave_sum(t[j]);
+    __syncthreads();
+    if ((tid & (kWave - 1)) == 0) {
+#pragma unroll
+        for (int j = 0; j < NS; j++) red[j][tid / kWave] = t[j];
+    }
+    __syncthreads();
+    if (tid == 0) {
+#pragma unroll
+        for (int j = 0; j < NS; j++) out[j] = (red[j][0] + red[j][1]) + (red[j][2] + red[j][3]);
+        __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Gamma sums: S1 = sum |out - in|, S2 = sum |in|.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gamma_kernel(const uint16_t *__restrict__ xin,
+                                                    const uint16_t *__restrict__ xout,
+                                                    int64_t n, double *partial, unsigned *ticket,
+                                                    double *out) {
+    double s[2] = {0.0, 0.0};
+    const int64_t nch = n / 8;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    for (; c + (kUnroll - 1) * stride < nch; c += kUnroll * stride) {
+        uint4 a[kUnroll], b[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; u++) {
+            a[u] = ld16(xin + 8 * (c + u * stride));
+            b[u] = ld16(xout + 8 * (c + u * stride));
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; u++) {
+            float va[8], vb[8];
+            to8(a[u], va);
+            to8(b[u], vb);
+            float f1 = 0.0f, f2 = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                f1 += __builtin_fabsf(vb[i] - va[i]);
+                f2 += __builtin_fabsf(va[i]);
+            }
+            s[0] += (double)f1;
+            s[1] += (double)f2;
+        }
+    }
+    for (; c < nch; c += stride) {
+        float va[8], vb[8];
+        to8(ld16(xin + 8 * c), va);
+        to8(ld16(xout + 8 * c), vb);
+        float f1 = 0.0f, f2 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            f1 += __builtin_fabsf(vb[i] - va[i]);
+            f2 += __builtin_fabsf(va[i]);
+        }
+        s[0] += (double)f1;
+        s[1] += (double)f2;
+    }
+    if (blockIdx.x == 0 && threadIdx.x < n - 8 * nch) {  // ragged tail, < 8 elements
+        const int64_t i = 8 * nch + threadIdx.x;
+        const float a = __uint_as_float((uint32_t)xin[i] << 16);
+        const float b = __uint_as_float((uint32_t)xout[i] << 16);
+        s[0] += (double)__builtin_fabsf(b - a);
+        s[1] += (double)__builtin_fabsf(a);
+    }
+    grid_sum<2>(s, partial, ticket, out);
+}
+
+hipError_t launch_gamma(hipStream_t st, const uint16_t *x_in, const uint16_t *x_out, int64_t n,
+                        double *sums, const Workspace &ws) {
+    const unsigned g = stride_grid(n / 8, 256 * kUnroll * 2, kMaxPartials);
+    hipLaunchKernelGGL(gamma_kernel, dim3(g), dim3(256), 0, st, x_in, x_out, n, ws.partial,
+                       ws.ticket, sums);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// TDC skip: x_out = bf16(float(x_in) + float(delta)).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void tdc_skip_kernel(const uint16_t *__restrict__ xin,
+                                                       const uint16_t *__restrict__ delta,
+                                                       int64_t n, uint16_t *__restrict__ xout) {
+    const int64_t nch = n / 8;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < nch; c += stride) {
+        float a[8], d[8];
+        to8(ld16(xin + 8 * c), a);
+        to8(ld16(delta + 8 * c), d);
+        uint4 o;
+        o.x = pack_bf16x2(a[0] + d[0], a[1] + d[1]);
+        o.y = pack_bf16x2(a[2] + d[2], a[3] + d[3]);
+        o.z = pack_bf16x2(a[4] + d[4], a[5] + d[5]);
+        o.w = pack_bf16x2(a[6] + d[6], a[7] + d[7]);
+        store_nt16(xout + 8 * c, o);
+    }
+    if (blockIdx.x == 0 && threadIdx.x < n - 8 * nch) {
+        const int64_t i = 8 * nch + threadIdx.x;
+        const float a = __uint_as_float((uint32_t)xin[i] << 16);
+        const float d = __uint_as_float((uint32_t)delta[i] << 16);
+        xout[i] = (uint16_t)f32_to_bf16(a + d);
+    }
+}
+
+hipError_t launch_tdc_skip(hipStream_t st, const uint16_t *x_in, const uint16_t *delta,
+                           int64_t n, uint16_t *x_out) {
+    const unsigned g = stride_grid(n / 8, 256 * 4, 8192);
+    hipLaunchKernelGGL(tdc_skip_kernel, dim3(g), dim3(256), 0, st, x_in, delta, n, x_out);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// TDC refresh: new = bf16(out - in); S1 = sum |out - in| (fp32 difference),
+// S2 = sum |in|, S3 = sum |new - delta|, S4 = sum |delta| (only when a delta
+// is cached), then delta <- new.
+// ---------------------------------------------------------------------------
+template <bool DV>
+__device__ __forceinline__ void refresh8(const uint4 &ia, const uint4 &oa, const uint4 &da,
+                                         double s[4], uint4 &nd) {
+    float a[8], b[8], d[8];
+    to8(ia, a);
+    to8(oa, b);
+    if (DV) to8(da, d);
+    float f1 = 0.0f, f2 = 0.0f, f3 = 0.0f, f4 = 0.0f;
+    uint32_t nb[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const float dn = b[i] - a[i];
+        nb[i] = f32_to_bf16(dn);
+        f1 += __builtin_fabsf(dn);
+        f2 += __builtin_fabsf(a[i]);
+        if (DV) {
+            f3 += __builtin_fabsf(__uint_as_float(nb[i] << 16) - d[i]);
+            f4 += __builtin_fabsf(d[i]);
+        }
+    }
+    nd = make_uint4(nb[0] | (nb[1] << 16), nb[2] | (nb[3] << 16), nb[4] | (nb[5] << 16),
+                    nb[6] | (nb[7] << 16));
+    s[0] += (double)f1;
+    s[1] += (double)f2;
+    if (DV) {
+        s[2] += (double)f3;
+        s[3] += (double)f4;
+    }
+}
+
+template <bool DV>
+__global__ __launch_bounds__(256) void tdc_refresh_kernel(const uint16_t *__restrict__ xin,
+                                                          const uint16_t *__restrict__ xout,
+                                                          uint16_t *__restrict__ delta,
+                                                          int64_t n, double *partial,
+                                                          unsigned *ticket, double *out) {
+    double s[4] = {0.0, 0.0, 0.0, 0.0};
+    const int64_t nch = n / 8;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+    for (; c + (kUnroll - 1) * stride < nch; c += kUnroll * stride) {
+        uint4 ia[kUnroll], oa[kUnroll], da[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; u++) {
+            ia[u] = ld16(xin + 8 * (c + u * stride));
+            oa[u] = ld16(xout + 8 * (c + u * stride));
+            da[u] = DV ? ld16(delta + 8 * (c + u * stride)) : zero;
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; u++) {
+            uint4 nd;
+            refresh8<DV>(ia[u], oa[u], da[u], s, nd);
+            store_nt16(delta + 8 * (c + u * stride), nd);
+        }
+    }
+    for (; c < nch; c += stride) {
+        uint4 nd;
+        refresh8<DV>(ld16(xin + 8 * c), ld16(xout + 8 * c), DV ? ld16(delta + 8 * c) : zero, s,
+                     nd);
+        store_nt16(delta + 8 * c, nd);
+    }
+    if (blockIdx.x == 0 && threadIdx.x < n - 8 * nch) {
+        const int64_t i = 8 * nch + threadIdx.x;
+        const float a = __uint_as_float((uint32_t)xin[i] << 16);
+        const float b = __uint_as_float((uint32_t)xout[i] << 16);
+        const float dn = b - a;
+        const uint32_t nb = f32_to_bf16(dn);
+        s[0] += (double)__builtin_fabsf(dn);
+        s[1] += (double)__builtin_fabsf(a);
+        if (DV) {
+            const float d = __uint_as_float((uint32_t)delta[i] << 16);
+            s[2] += (double)__builtin_fabsf(__uint_as_float(nb << 16) - d);
+            s[3] += (double)__builtin_fabsf(d);
+        }
+        delta[i] = (uint16_t)nb;
+    }
+    grid_sum<4>(s, partial, ticket, out);
+}
+
+hipError_t launch_tdc_refresh(hipStream_t st, const uint16_t *x_in, const uint16_t *x_out,
+                              uint16_t *delta, int64_t n, int delta_valid, double *sums,
+                              const Workspace &ws) {
+    const unsigned g = stride_grid(n / 8, 256 * kUnroll * 2, kMaxPartials);
+    if (delta_valid)
+        hipLaunchKernelGGL(tdc_refresh_kernel<true>, dim3(g), dim3(256), 0, st, x_in, x_out,
+                           delta, n, ws.partial, ws.ticket, sums);
+    else
+        hipLaunchKernelGGL(tdc_refresh_kernel<false>, dim3(g), dim3(256), 0, st, x_in, x_out,
+                           delta, n, ws.partial, ws.ticket, sums);
+    return hipGetLastError();
+}
+
+}  // namespace dmpq

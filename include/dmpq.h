@@ -1,0 +1,225 @@
+/*
+ * dmpq.h -- C ABI of libdmpq, the MI355X (gfx950) hot path of 6Bit-Diffusion's
+ * dynamic mixed-precision quantized linear layer (arXiv 2603.18742).
+ *
+ * Page citations name the web pages that describe the method:
+ *   [gist-en]  gist.science/paper/2603.18742 (English summary)
+ *   [gist-it]  gist.science/it/paper/2603.18742 (Italian summary)
+ *   [gist-zh]  gist.science/zh/paper/2603.18742 (Chinese technical summary)
+ *   [abstract] the paper's English abstract (chatpaper.ai page)
+ *
+ * Conventions shared by every entry point
+ *   - Return value: DMPQ_OK, or an error code; dmpq_last_error() then holds a
+ *     message for the calling thread.  No C++ exception crosses this ABI.
+ *   - Argument errors are detected and returned before anything is launched.
+ *     DMPQ_ERR_HIP means a launch failed; the stream state is then whatever
+ *     the HIP runtime reports.
+ *   - Pointers prefixed d_ or without prefix are device pointers (GPU memory
+ *     of the current device); pointers prefixed h_ are host pointers.  The
+ *     caller owns every buffer; the library allocates nothing.
+ *   - Device calls are asynchronous and ordered on the given stream (NULL =
+ *     the null stream).  Host calls (gate_and_route, tdc_decide, tdc_commit,
+ *     tdc_init) are pure functions of their arguments and never touch a GPU.
+ *   - Tensors are dense row-major.  bf16 values are passed as uint16_t bit
+ *     patterns.  Activations X are [M x K] (row = token, K contiguous);
+ *     weights W are [N x K] (row = output channel, K contiguous); Y = X W^T
+ *     is [M x N].
+ *   - Every device tensor pointer must be 16-byte aligned.  K must be a
+ *     positive multiple of 16 (the Hadamard block and the NVFP4 scale group).
+ *     M, N >= 0 (0 is an empty no-op).
+ *   - Non-finite inputs (NaN, Inf) are outside the contract: results are
+ *     unspecified, but every kernel still terminates.
+ *   - Workspaces (ws) come from dmpq_workspace_bytes().  A workspace must be
+ *     zero-filled once before its first use; every call leaves it ready for
+ *     the next.  Calls that run concurrently must not share a workspace.
+ */
+#ifndef DMPQ_H
+#define DMPQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dmpq_status {
+    DMPQ_OK = 0,
+    DMPQ_ERR_INVALID_ARG = 1, /* null pointer, unknown enum value */
+    DMPQ_ERR_BAD_SHAPE = 2,   /* negative size, K not a multiple of 16, ... */
+    DMPQ_ERR_MISALIGNED = 3,  /* a device pointer is not 16-byte aligned */
+    DMPQ_ERR_UNSUPPORTED = 4, /* valid but outside what the kernels handle */
+    DMPQ_ERR_HIP = 5,         /* the HIP runtime reported an error */
+    DMPQ_ERR_WORKSPACE = 6    /* workspace missing or too small */
+} dmpq_status;
+
+/* Routes of a linear layer (DMPQ assigns NVFP4 to temporally stable layers,
+ * INT8 to volatile ones: [gist-en] §2.A, [abstract]). */
+enum { DMPQ_ROUTE_NVFP4 = 0, DMPQ_ROUTE_INT8 = 1 };
+/* GEMM output types: fp32 (the contract), bf16 (RNE of the fp32 value), and
+ * the raw int32 accumulators of the INT8 GEMM (test mode). */
+enum { DMPQ_OUT_F32 = 0, DMPQ_OUT_BF16 = 1, DMPQ_OUT_I32 = 2 };
+/* Quantizer flags: bit 0 skips the block Hadamard (test hook). */
+enum { DMPQ_NO_HADAMARD = 1 };
+/* INT8 weight derivation in dmpq_prep_weight. */
+enum { DMPQ_W8_FROM_NVFP4 = 0, DMPQ_W8_DIRECT = 1 };
+/* TDC step modes. */
+enum { DMPQ_TDC_SKIP = 0, DMPQ_TDC_REFRESH = 1 };
+/* NVFP4 GEMM variants: 0 = exact E2M1 x E4M3 -> bf16 dequant in LDS feeding
+ * bf16 MFMA. */
+enum { DMPQ_FP4_BF16_DEQUANT = 0 };
+/* Workspace users. */
+enum { DMPQ_OP_GAMMA = 0, DMPQ_OP_QUANT_NVFP4 = 1, DMPQ_OP_TDC = 2, DMPQ_OP_PREP_WEIGHT = 3 };
+
+/* Message describing the calling thread's last error ("" if none). */
+const char *dmpq_last_error(void);
+/* Library version string. */
+const char *dmpq_version(void);
+/* Bytes of workspace the op needs (sizes M, K are accepted for future use;
+ * the current kernels need a fixed amount). 0 for an unknown op. */
+size_t dmpq_workspace_bytes(int op, int64_t M, int64_t K);
+
+/* ---------------------------------------------------------------------------
+ * Gamma predictor sums ([gist-en] §2.A "Mechanism" item 1; [gist-it] §2.A
+ * "Meccanismo"): the relative L1 distance between a block's output and input
+ * at the previous step.  Writes d_sums2[0] = sum |float(out) - float(in)|
+ * (fp32 difference per element) and d_sums2[1] = sum |float(in)|, as fp64,
+ * over the n elements of x_in and x_out (bf16).  Gamma = S1/S2 is formed on
+ * the host by dmpq_gate_and_route.  Deterministic: the same inputs give the
+ * same bits on every call.
+ * ------------------------------------------------------------------------- */
+dmpq_status dmpq_gamma_sums(hipStream_t stream, const uint16_t *x_in, const uint16_t *x_out,
+                            int64_t n, double *d_sums2, void *ws, size_t ws_bytes);
+
+/* ---------------------------------------------------------------------------
+ * Router ([gist-en] §2.A "Mechanism" items 2-3; [gist-zh] §2.A; missing
+ * metric fallback: [gist-en] §2.C "Solution").  Host, pure.
+ * h_sums2 = {S1, S2} of the block at the previous step, or NULL when Gamma is
+ * missing (first step, or the block was skipped at the previous step).
+ * Gamma = S1/S2 (0 if both are 0, +inf if only S2 is 0).  For each of the
+ * n_lin linears, E_l = h_alpha[l] * Gamma + h_beta[l] (fp64); route INT8 if
+ * E_l > tau, else NVFP4.  Missing Gamma routes every linear to INT8 and
+ * writes NaN to h_gamma_out and h_err_out.  h_gamma_out and h_err_out may be
+ * NULL; h_route_out has n_lin entries.
+ * ------------------------------------------------------------------------- */
+dmpq_status dmpq_gate_and_route(const double *h_sums2, int n_lin, const double *h_alpha,
+                                const double *h_beta, double tau, double *h_gamma_out,
+                                double *h_err_out, uint8_t *h_route_out);
+
+/* ---------------------------------------------------------------------------
+ * Online block Hadamard + dynamic per-token INT8 quantization ([gist-en]
+ * §2.A "Outlier Smoothing" and "Routing"; [gist-zh] §2.A).  For each row of
+ * x [M x K] bf16: every 16-element block is rotated by H16/4 (Sylvester
+ * order, fp32 butterflies in stages 1, 2, 4, 8, then x0.25); a = max |rotated
+ * row|; s_row[m] = a/127; q = RNE(rotated * (127/a)) clamped to +-127; a zero
+ * row gives s = 0 and q = 0.  Outputs q [M x K] int8, s_row [M] fp32.
+ * flags: DMPQ_NO_HADAMARD skips the rotation.  K <= 32768.
+ * ------------------------------------------------------------------------- */
+dmpq_status dmpq_hadamard_quant_int8(hipStream_t stream, const uint16_t *x, int64_t M,
+                                     int64_t K, int flags, int8_t *q, float *s_row);
+
+/* ---------------------------------------------------------------------------
+ * Online block Hadamard + dynamic NVFP4 quantization ([gist-en] §1 "Hardware
+ * Gap" and §2.A; [gist-it] §3 item 4; [gist-zh] §2.A).  Rotation as above.
+ * A = max |rotated tensor| (current tensor, computed on the device);
+ * d_g[0] = A/2688 (fp32 tensor scale; 2688 = 6 * 448).  Per 16-block b of a
+ * row: scales[m][b] = E4M3(448 * a_b / A) (OCP E4M3FN, RNE, saturating);
+ * S = E4M3value * g; codes = E2M1 RNE of rotated * (1/S), sign kept, or +0
+ * when S is zero or below FLT_MIN.  codes [M x K/2]: element 2i in the low
+ * nibble of byte i; scales [M x K/16] uint8.  A zero tensor gives g = 0 and
+ * all-zero outputs.  Two passes over x (tensor amax, then codes).
+ * ws: dmpq_workspace_bytes(DMPQ_OP_QUANT_NVFP4, M, K) bytes.
+ * ------------------------------------------------------------------------- */
+dmpq_status dmpq_hadamard_quant_nvfp4(hipStream_t stream, const uint16_t *x, int64_t M,
+                                      int64_t K, int flags, uint8_t *codes, uint8_t *scales,
+                                      float *d_g, void *ws, size_t ws_bytes);
+
+/* ---------------------------------------------------------------------------
+ * INT8 quantized linear ([gist-en] §2.A "Routing"; [gist-zh] §2.A weight
+ * handling).  acc[m][n] = sum_k qa[m][k] * qw[n][k] (exact int32), then
+ * out_dtype F32: y = (float(acc) * sa[m]) * sw[n]; BF16: RNE of that value;
+ * I32: the accumulator.  qa [M x K] int8 with per-row scales sa [M];
+ * qw [N x K] int8 with per-output-channel scales sw [N]; y [M x N].
+ * ------------------------------------------------------------------------- */
+dmpq_status dmpq_qgemm_int8(hipStream_t stream, const int8_t *qa, const float *sa,
+                            const int8_t *qw, const float *sw, int64_t M, int64_t N, int64_t K,
+                            int out_dtype, void *y);
+
+/* ---------------------------------------------------------------------------
+ * NVFP4 quantized linear ([gist-en] §1 and §3 item 4; [gist-zh] §2.A).
+ * y[m][n] = ga * gw * sum_b eA[m][b] eW[n][b] sum_{k in b} vA[m][k] vW[n][k],
+ * accumulated in fp32 (every product E2M1 x E4M3 is exact; only the fp32
+ * accumulation rounds).  ca/sa/d_ga: activation codes [M x K/2], E4M3
+ * scales [M x K/16], tensor scale (device fp32); cw/sw/d_gw likewise for the
+ * weight [N x K].  out_dtype F32 or BF16.  variant: DMPQ_FP4_BF16_DEQUANT.
+ * ------------------------------------------------------------------------- */
+dmpq_status dmpq_qgemm_nvfp4(hipStream_t stream, const uint8_t *ca, const uint8_t *sa,
+                             const float *d_ga, const uint8_t *cw, const uint8_t *sw,
+                             const float *d_gw, int64_t M, int64_t N, int64_t K,
+                             int out_dtype, void *y, int variant);
+
+/* ---------------------------------------------------------------------------
+ * Temporal Delta Cache ([gist-en] §2.B; [gist-it] §2.B; [gist-zh] §2.B).
+ * Host state of one block; the cached delta itself is a caller-owned device
+ * bf16 buffer of the block's activation size.
+ * ------------------------------------------------------------------------- */
+typedef struct dmpq_tdc_state {
+    int64_t n_refresh;   /* computed (refreshed) steps so far */
+    double d;            /* relative L1 distance of the last two deltas (+inf until two exist) */
+    double acc;          /* accumulated error of the current run of skips */
+    int32_t delta_valid; /* the device delta buffer holds a delta */
+    int32_t gamma_valid; /* gamma holds the Gamma of the last step (0 after a skip) */
+    double gamma;        /* S1/S2 of the last computed step */
+} dmpq_tdc_state;
+
+typedef struct dmpq_tdc_params {
+    double eps_sim;   /* skip only if d < eps_sim (deltas similar enough) */
+    double delta_acc; /* ... and acc + d <= delta_acc (accumulated-error gate) */
+} dmpq_tdc_params;
+
+/* Fresh state: no delta, d = +inf, acc = 0, Gamma missing.  Host. */
+dmpq_status dmpq_tdc_init(dmpq_tdc_state *h_st);
+
+/* Skip decision, host, pure: *h_skip = 1 iff n_refresh >= 2 and a delta is
+ * cached and d < eps_sim and acc + d <= delta_acc. */
+dmpq_status dmpq_tdc_decide(const dmpq_tdc_state *h_st, const dmpq_tdc_params *h_p,
+                            int *h_skip);
+
+/* Device step over n bf16 elements.
+ * SKIP: x_out = bf16(float(x_in) + float(delta)) (the cached delta is reused;
+ *   d_sums4, ws unused and may be NULL).
+ * REFRESH (x_out = the block's computed output): new = bf16(out - in);
+ *   d_sums4 = {S1 = sum |out - in| (fp32 difference), S2 = sum |in|,
+ *   S3 = sum |new - delta|, S4 = sum |delta|} in fp64, S3 = S4 = 0 when
+ *   delta_valid is 0; then delta <- new.  ws: DMPQ_OP_TDC workspace. */
+dmpq_status dmpq_tdc_step(hipStream_t stream, int mode, const uint16_t *x_in, uint16_t *x_out,
+                          uint16_t *delta, int64_t n, int delta_valid, double *d_sums4,
+                          void *ws, size_t ws_bytes);
+
+/* Host bookkeeping after a step.  SKIP: acc += d, Gamma becomes missing.
+ * REFRESH (h_sums4 = the step's sums, copied to the host): d = S3/S4 if a
+ * delta was cached before (0 if both 0, +inf if only S4 is 0), else +inf;
+ * acc = 0; n_refresh += 1; delta_valid = 1; gamma = S1/S2, gamma_valid = 1. */
+dmpq_status dmpq_tdc_commit(dmpq_tdc_state *h_st, int mode, const double *h_sums4);
+
+/* ---------------------------------------------------------------------------
+ * Offline weight preparation ([gist-zh] §2.A weight-handling bullet: weights
+ * are quantized to NVFP4 offline and converted when an INT8 GEMM needs
+ * them).  w [N x K] bf16 is block-rotated like the activations, then
+ * quantized to NVFP4 exactly as dmpq_hadamard_quant_nvfp4 (cw, sw, d_gw).
+ * INT8 weight qw [N x K] with per-row scales sw_row [N]:
+ *   DMPQ_W8_FROM_NVFP4: wd = (E2M1value * E4M3value) * gw, then per row
+ *     s = amax/127, q = RNE(wd * (127/amax)) clamped to +-127;
+ *   DMPQ_W8_DIRECT: dmpq_hadamard_quant_int8 of w.
+ * ws: DMPQ_OP_PREP_WEIGHT workspace.  Runs once per weight, off the hot path.
+ * ------------------------------------------------------------------------- */
+dmpq_status dmpq_prep_weight(hipStream_t stream, const uint16_t *w, int64_t N, int64_t K,
+                             int int8_mode, uint8_t *cw, uint8_t *sw, float *d_gw, int8_t *qw,
+                             float *sw_row, void *ws, size_t ws_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DMPQ_H */

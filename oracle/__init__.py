@@ -65,6 +65,7 @@ def _declare(L):
     u8, u16, i8, i32, i64 = C.c_uint8, C.c_uint16, C.c_int8, C.c_int32, C.c_int64
     f32, f64 = C.c_float, C.c_double
     sig = {
+        "orc_max_threads": (C.c_int, []),
         "orc_bf16_round": (u16, [f32]),
         "orc_bf16_value": (f32, [u16]),
         "orc_e2m1_value": (f32, [u8]),
@@ -108,6 +109,10 @@ def _u16(x) -> np.ndarray:
     x = np.ascontiguousarray(x)
     assert x.dtype == np.uint16, "bf16 tensors travel as uint16 bit patterns"
     return x
+
+
+def max_threads() -> int:
+    return int(lib().orc_max_threads())
 
 
 # ---- codecs -------------------------------------------------------------

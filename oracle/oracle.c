@@ -12,8 +12,14 @@
 
 #include <float.h>
 #include <math.h>
+#include <omp.h>
 #include <stdlib.h>
 #include <string.h>
+
+int orc_max_threads(void)
+{
+    return omp_get_max_threads();
+}
 
 /* ======================================================================
  * Codecs.  The pages name the formats only: NVFP4 is a micro-scaling block

@@ -40,6 +40,9 @@ extern "C" {
 /* flags for the quantizers: bit0 set = skip the block Hadamard (test hook) */
 #define ORC_NO_HADAMARD 1
 
+/* OpenMP threads the oracle's parallel loops use (for reporting). */
+int orc_max_threads(void);
+
 /* ---- codecs ---------------------------------------------------------- */
 uint16_t orc_bf16_round(float f);        /* fp32 -> bf16 bits, RNE; NaN -> 0x7FC0 */
 float    orc_bf16_value(uint16_t b);     /* bf16 bits -> fp32 (exact) */

@@ -1,0 +1,134 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+include/dmpq.h declares, its host-side functions (router, TDC decide/commit)
+agree with the oracle, and argument errors are reported before any launch.
+"""
+import ctypes as C
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import dynamic_mixed_precision_amd as dm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "dmpq.h")).read()
+    return sorted(set(re.findall(r"\b(dmpq_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    L = dm.lib()
+    names = _declared()
+    assert len(names) >= 14
+    for name in names:
+        assert hasattr(L, name), name
+    assert sorted(dm.EXPORTS) == names
+
+
+def test_version_and_workspace():
+    assert "gfx950" in dm.version()
+    for op in (dm.OP_GAMMA, dm.OP_QUANT_NVFP4, dm.OP_TDC, dm.OP_PREP_WEIGHT):
+        assert dm.workspace_bytes(op, 17776, 3072) >= 2048 * 4 * 8
+    assert dm.workspace_bytes(99) == 0
+
+
+def test_router_matches_oracle(orc):
+    rng = np.random.default_rng(50)
+    for _ in range(300):
+        n = int(rng.integers(1, 8))
+        alpha = rng.uniform(-2, 3, n)
+        beta = rng.uniform(-0.5, 0.5, n)
+        tau = float(rng.uniform(-0.2, 0.8))
+        sums = rng.uniform(0, 10, 2)
+        if rng.random() < 0.1:
+            sums[1] = 0.0
+        g0, e0, r0 = orc.route(sums, alpha, beta, tau)
+        g1, e1, r1 = dm.gate_and_route(sums, alpha, beta, tau)
+        assert (g0 == g1) or (math.isinf(g0) and math.isinf(g1))
+        assert np.array_equal(np.nan_to_num(e0), np.nan_to_num(e1))
+        assert np.array_equal(r0, r1)
+    g, e, r = dm.gate_and_route(None, [1.0, 2.0], [0.0, 0.0], 0.1)
+    assert math.isnan(g) and np.all(r == dm.ROUTE_INT8)
+    # exact tie -> NVFP4
+    _, _, r = dm.gate_and_route([1.0, 4.0], [1.0], [0.0], 0.25)
+    assert r[0] == dm.ROUTE_NVFP4
+
+
+def test_tdc_bookkeeping_matches_oracle(orc):
+    rng = np.random.default_rng(51)
+    eps, dacc = 0.3, 0.7
+    so, sl = orc.tdc_new(), dm.tdc_init()
+    for t in range(200):
+        skip_o = orc.tdc_decide(so, eps, dacc)
+        skip_l = dm.tdc_decide(sl, eps, dacc)
+        assert skip_o == skip_l, t
+        if skip_o:
+            orc.tdc_commit_skip(so)
+            dm.tdc_commit(sl, dm.TDC_SKIP)
+        else:
+            sums = rng.uniform(0, 1, 4)
+            sums[2] *= rng.choice([0.1, 1.0])
+            orc.tdc_commit_refresh(so, sums)
+            dm.tdc_commit(sl, dm.TDC_REFRESH, sums)
+        for f in ("n_refresh", "d", "acc", "delta_valid", "gamma_valid"):
+            assert getattr(so, f) == getattr(sl, f), (t, f)
+
+
+class _Fake:
+    """Stands in for a device tensor in calls that must fail validation."""
+
+    def __init__(self, shape, addr=0x10000, numel=None):
+        self.shape = shape
+        self._addr = addr
+        self._n = numel if numel is not None else int(np.prod(shape))
+        self.is_cuda = True
+
+    def is_contiguous(self):
+        return True
+
+    def data_ptr(self):
+        return self._addr
+
+    def numel(self):
+        return self._n
+
+
+def _expect(status, fn, *args, **kw):
+    with pytest.raises(dm.DmpqError) as ei:
+        fn(*args, **kw)
+    assert ei.value.status == status
+    assert dm.last_error()
+
+
+def test_validation_before_launch(monkeypatch):
+    monkeypatch.setattr(dm, "_stream", lambda s=None: 0)
+    x = _Fake((4, 24))
+    _expect(2, dm.hadamard_quant_int8, x, _Fake((4, 24)), _Fake((4,)))           # K % 16
+    _expect(3, dm.hadamard_quant_int8, _Fake((4, 32), addr=0x10008), _Fake((4, 32)), _Fake((4,)))
+    _expect(1, dm.hadamard_quant_int8, _Fake((4, 32)), _Fake((4, 32)), _Fake((4,)), flags=6)
+    _expect(4, dm.hadamard_quant_int8, _Fake((4, 65536)), _Fake((4, 65536)), _Fake((4,)))
+    ws_small = _Fake((16,), numel=16)
+    _expect(6, dm.hadamard_quant_nvfp4, _Fake((4, 32)), _Fake((4, 16)), _Fake((4, 2)), _Fake((1,)),
+            ws_small)
+    _expect(2, dm.qgemm_int8, _Fake((4, 40)), _Fake((4,)), _Fake((8, 40)), _Fake((8,)), _Fake((4, 8)))
+    _expect(1, dm.qgemm_int8, _Fake((4, 64)), _Fake((4,)), _Fake((8, 64)), _Fake((8,)),
+            _Fake((4, 8)), out_dtype=7)
+    _expect(1, dm.qgemm_nvfp4, _Fake((4, 32)), _Fake((4, 4)), _Fake((1,)), _Fake((8, 32)),
+            _Fake((8, 4)), _Fake((1,)), _Fake((4, 8)), variant=5)
+    _expect(1, dm.tdc_step, 9, _Fake((64,)), _Fake((64,)), _Fake((64,)), True)
+    _expect(1, dm.tdc_step, dm.TDC_SKIP, _Fake((64,)), _Fake((64,)), _Fake((64,)), False)
+    _expect(6, dm.tdc_step, dm.TDC_REFRESH, _Fake((64,)), _Fake((64,)), _Fake((64,)), True,
+            sums=_Fake((4,)), ws=None)
+    _expect(1, dm.prep_weight, _Fake((8, 32)), _Fake((8, 16)), _Fake((8, 2)), _Fake((1,)),
+            _Fake((8, 32)), _Fake((8,)), _Fake((65792,)), int8_mode=3)
+
+
+def test_null_pointer_rejected():
+    L = dm.lib()
+    st = L.dmpq_hadamard_quant_int8(None, None, 4, 32, 0, None, None)
+    assert st == 1 and "NULL" in dm.last_error()
+    assert L.dmpq_tdc_decide(None, None, None) == 1

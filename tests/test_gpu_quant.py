@@ -1,0 +1,159 @@
+"""GPU parity: Hadamard + INT8 / NVFP4 activation quantization and weight prep
+against the oracle, bit for bit (codes, scales, tensor scale)."""
+import numpy as np
+import pytest
+import torch
+
+import dynamic_mixed_precision_amd as dm
+import workloads
+from gpu_util import dev, empty, host, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(1, 16), (37, 16), (37, 48), (5, 256), (256, 256), (37, 1920), (19, 3072),
+          (11, 7680), (9, 12288), (3, 16400), (2, 32768)]
+
+
+def _gpu_int8(x, flags=0):
+    M, K = x.shape
+    q, s = empty((M, K), np.int8), empty((M,), np.float32)
+    dm.hadamard_quant_int8(dev(x).view(M, K), q, s, flags=flags)
+    torch.cuda.synchronize()
+    return host(q), host(s)
+
+
+def _gpu_nvfp4(x, flags=0):
+    M, K = x.shape
+    c, s = empty((M, K // 2), np.uint8), empty((M, K // 16), np.uint8)
+    g = torch.full((1,), -1.0, device="cuda")
+    ws = dm.new_workspace(dm.OP_QUANT_NVFP4)
+    dm.hadamard_quant_nvfp4(dev(x).view(M, K), c, s, g, ws, flags=flags)
+    torch.cuda.synchronize()
+    return host(c), host(s), float(host(g)[0])
+
+
+def _check_int8(orc, x, flags=0):
+    q0, s0 = orc.quant_int8(x, flags)
+    q1, s1 = _gpu_int8(x, flags)
+    assert np.array_equal(s1.view(np.uint32), s0.view(np.uint32))
+    assert np.array_equal(q1, q0)
+
+
+def _check_nvfp4(orc, x, flags=0):
+    c0, s0, g0 = orc.quant_nvfp4(x, flags)
+    c1, s1, g1 = _gpu_nvfp4(x, flags)
+    assert np.float32(g1).view(np.uint32) == np.float32(g0).view(np.uint32)
+    assert np.array_equal(s1, s0)
+    assert np.array_equal(c1, c0)
+
+
+@pytest.mark.parametrize("M,K", SHAPES)
+def test_int8_quant_parity(orc, M, K):
+    require_gpu()
+    say(f"hadamard_quant_int8 M={M} K={K}")
+    x = workloads.activations(np.random.default_rng(M * 7 + K), M, K)
+    _check_int8(orc, x)
+    _check_int8(orc, x, dm.NO_HADAMARD)
+
+
+@pytest.mark.parametrize("M,K", SHAPES)
+def test_nvfp4_quant_parity(orc, M, K):
+    require_gpu()
+    say(f"hadamard_quant_nvfp4 M={M} K={K}")
+    x = workloads.activations(np.random.default_rng(M * 11 + K), M, K)
+    _check_nvfp4(orc, x)
+    _check_nvfp4(orc, x, dm.NO_HADAMARD)
+
+
+def test_quant_edge_cases(orc):
+    require_gpu()
+    say("quant edge cases: zero rows, zero tensor, tiny and huge values, M=0")
+    rng = np.random.default_rng(60)
+    x = workloads.activations(rng, 40, 256)
+    x[3] = 0
+    x[17, 5:40] = 0
+    _check_int8(orc, x)
+    _check_nvfp4(orc, x)
+    z = np.zeros((9, 64), np.uint16)
+    _check_int8(orc, z)
+    _check_nvfp4(orc, z)
+    # wide dynamic range: tiny blocks next to huge ones (scale underflow to 0)
+    f = rng.standard_normal((16, 128)).astype(np.float32)
+    f[:, :16] *= np.float32(1e30)
+    f[:, 16:32] *= np.float32(1e-30)
+    xr = workloads.to_bf16_bits(f)
+    _check_int8(orc, xr)
+    _check_nvfp4(orc, xr)
+    # empty input is a no-op
+    q, s = empty((0, 64), np.int8), empty((0,), np.float32)
+    dm.hadamard_quant_int8(empty((0, 64), np.uint16), q, s)
+    c, sc = empty((0, 32), np.uint8), empty((0, 4), np.uint8)
+    g = torch.zeros(1, device="cuda")
+    dm.hadamard_quant_nvfp4(empty((0, 64), np.uint16), c, sc, g, dm.new_workspace(1))
+    torch.cuda.synchronize()
+    assert float(g[0]) == 0.0
+
+
+def test_nvfp4_grid_roundtrip_gpu(orc):
+    # tensor on the NVFP4 grid with g = 1 (see the oracle pins): GPU recovers it
+    require_gpu()
+    say("nvfp4 grid round trip")
+    from test_oracle_quant import _nvfp4_grid_tensor
+    xb, codes, e = _nvfp4_grid_tensor(orc, np.random.default_rng(61), 12, 96)
+    c, s, g = _gpu_nvfp4(xb, dm.NO_HADAMARD)
+    assert g == 1.0 and np.array_equal(s, e) and np.array_equal(c, codes)
+
+
+@pytest.mark.parametrize("K", [1920, 3072, 7680, 12288])
+def test_quant_full_token_count(orc, K):
+    # every row of a CogVideoX-like 17776-token activation
+    require_gpu()
+    M = workloads.M_480P
+    say(f"full-size quant M={M} K={K}")
+    x = workloads.activations(np.random.default_rng(K), M, K)
+    _check_int8(orc, x)
+    _check_nvfp4(orc, x)
+
+
+def test_quant_1080p_tokens(orc):
+    require_gpu()
+    M, K = workloads.M_1080P, 3072
+    say(f"full-size quant M={M} K={K}")
+    x = workloads.activations(np.random.default_rng(1080), M, K)
+    _check_int8(orc, x)
+    _check_nvfp4(orc, x)
+
+
+@pytest.mark.parametrize("mode", [dm.W8_FROM_NVFP4, dm.W8_DIRECT])
+@pytest.mark.parametrize("N,K", [(256, 256), (5760, 1920), (48, 12288), (33, 80)])
+def test_prep_weight_parity(orc, mode, N, K):
+    require_gpu()
+    say(f"prep_weight mode={mode} N={N} K={K}")
+    w = workloads.weight(np.random.default_rng(N + K), N, K)
+    ref = orc.prep_weight(w, mode)
+    cw, sw = empty((N, K // 2), np.uint8), empty((N, K // 16), np.uint8)
+    gw = torch.zeros(1, device="cuda")
+    qw, swr = empty((N, K), np.int8), empty((N,), np.float32)
+    dm.prep_weight(dev(w).view(N, K), cw, sw, gw, qw, swr, dm.new_workspace(dm.OP_PREP_WEIGHT),
+                   int8_mode=mode)
+    torch.cuda.synchronize()
+    assert np.float32(host(gw)[0]).view(np.uint32) == np.float32(ref["gw"]).view(np.uint32)
+    assert np.array_equal(host(cw), ref["cw"]) and np.array_equal(host(sw), ref["sw"])
+    assert np.array_equal(host(swr).view(np.uint32), ref["sw_row"].view(np.uint32))
+    assert np.array_equal(host(qw), ref["qw"])
+
+
+def test_quant_subnormal_inputs(orc):
+    # bf16 subnormals (below 2^-126) must be kept, not flushed, through the
+    # Hadamard and both quantizers
+    require_gpu()
+    say("quant with subnormal inputs")
+    rng = np.random.default_rng(62)
+    f = rng.standard_normal((8, 64)).astype(np.float32) * np.float32(1e-39)
+    f[:, :16] = rng.standard_normal((8, 16)).astype(np.float32)
+    x = workloads.to_bf16_bits(f)
+    _check_int8(orc, x)
+    _check_nvfp4(orc, x)
+    xs = workloads.to_bf16_bits(rng.standard_normal((8, 64)).astype(np.float32) * np.float32(1e-39))
+    _check_int8(orc, xs)
+    _check_nvfp4(orc, xs)

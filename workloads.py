@@ -105,3 +105,36 @@ VIDEO_1080P = Config("1080p-like", M_1080P, 3072, linears_for(3072, 12288), (11,
 # tau=0.2 two blocks route to INT8 and two to NVFP4 (about 6 bits average).
 GAMMA_TARGETS_5B = (0.05, 0.40, 0.05, 0.40)
 ROUTER_5B = dict(alpha=1.0, beta=0.0, tau=0.2)
+
+
+# ---- device-side generators (same recipes, torch's seeded GPU generator) ----
+# Used where the inputs are too large to draw on the host quickly (benchmark
+# steps); parity tests use the host generators above.
+
+def device_generator(seed: int, device="cuda") -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def activations_device(gen: torch.Generator, M: int, K: int, outlier_scale: float = 50.0,
+                       device="cuda") -> torch.Tensor:
+    """bf16 [M, K] activations: N(0,1) with round(0.01*K) channels scaled by 50."""
+    x = torch.randn((M, K), generator=gen, device=device, dtype=torch.float32)
+    n = n_outlier_channels(K)
+    ch = torch.randperm(K, generator=gen, device=device)[:n]
+    x[:, ch] *= outlier_scale
+    return x.to(torch.bfloat16)
+
+
+def weight_device(gen: torch.Generator, N: int, K: int, device="cuda") -> torch.Tensor:
+    w = torch.randn((N, K), generator=gen, device=device, dtype=torch.float32)
+    return (w * (1.0 / math.sqrt(K))).to(torch.bfloat16)
+
+
+def perturbed_output_device(gen: torch.Generator, x_in: torch.Tensor,
+                            gamma_target: float) -> torch.Tensor:
+    x = x_in.float()
+    c = gamma_target * float(x.abs().mean(dtype=torch.float64)) / math.sqrt(2.0 / math.pi)
+    noise = torch.randn(x.shape, generator=gen, device=x.device, dtype=torch.float32)
+    return (x + c * noise).to(torch.bfloat16)
