@@ -146,7 +146,9 @@ static int bad_shape(int64_t M, int64_t K)
  * Dynamic INT8 activation quantization, per token (row), symmetric, on the
  * rotated row.  INT8 is the route for volatile layers ([gist-en] §2.A
  * "Routing"; [gist-it] §2.A "Routing Dinamico").  Range +-127, scale =
- * amax/127, codes = RNE(x * (127/amax)).  An all-zero row gets scale 0.
+ * amax/127, codes = RNE(x * (127/amax)).  A row whose 127/amax is not a
+ * finite fp32 (amax zero, or below about 3.7e-37) gets scale 0 and zero
+ * codes.
  * ==================================================================== */
 
 int orc_quant_int8(const uint16_t *x, int64_t M, int64_t K, int flags,
@@ -164,13 +166,13 @@ int orc_quant_int8(const uint16_t *x, int64_t M, int64_t K, int flags,
             for (int64_t k = 0; k < K; k++)
                 if (fabsf(row[k]) > a)
                     a = fabsf(row[k]);
-            if (a == 0.0f) {
+            float inv = 127.0f / a;
+            if (a == 0.0f || isinf(inv)) { /* no finite reciprocal: a zero row */
                 s_row[m] = 0.0f;
                 for (int64_t k = 0; k < K; k++)
                     q[m * K + k] = 0;
                 continue;
             }
-            float inv = 127.0f / a;
             s_row[m] = a / 127.0f;
             for (int64_t k = 0; k < K; k++) {
                 float r = rintf(row[k] * inv);
@@ -305,13 +307,13 @@ int orc_prep_weight(const uint16_t *w, int64_t N, int64_t K, int int8_mode,
                 if (fabsf(wd[k]) > a)
                     a = fabsf(wd[k]);
             }
-            if (a == 0.0f) {
+            float inv = 127.0f / a;
+            if (a == 0.0f || isinf(inv)) {
                 sw_row[n] = 0.0f;
                 for (int64_t k = 0; k < K; k++)
                     qw[n * K + k] = 0;
                 continue;
             }
-            float inv = 127.0f / a;
             sw_row[n] = a / 127.0f;
             for (int64_t k = 0; k < K; k++) {
                 float r = rintf(wd[k] * inv);

@@ -219,3 +219,17 @@ def test_rotated_quantized_linear_tracks_float(orc):
     assert rel8 < 0.12 and rel4 < 0.2
     # INT8 activations over the NVFP4-derived weight beat all-NVFP4
     assert rel8 < rel4
+
+
+def test_int8_row_without_finite_reciprocal(orc):
+    # 127/amax must be a finite fp32: amax at or below 127/FLT_MAX (~3.7e-37)
+    # quantizes as a zero row; just above, the row spans +-127 as usual
+    K = 32
+    x = np.zeros((3, K), np.float32)
+    x[0, 3] = 1e-38                      # bf16 subnormal-range value: 127/a overflows
+    x[1, 5] = -2e-37                     # 127/a = 6.35e38 > FLT_MAX: overflows
+    x[2, 7] = 4e-37                      # 127/a = 3.2e38: finite
+    q, s = orc.quant_int8(to_bf16_bits(x), flags=orc.NO_HADAMARD)
+    assert s[0] == 0 and not q[0].any()
+    assert s[1] == 0 and not q[1].any()
+    assert s[2] > 0 and q[2, 7] == 127 and np.count_nonzero(q[2]) == 1
