@@ -35,12 +35,16 @@ dmpq_status hip_status(hipError_t e, const char *what) {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-#define REQUIRE_PTR(p)                                                                  \
-    do {                                                                                \
-        if (!(p)) return fail(DMPQ_ERR_INVALID_ARG, "%s: %s is NULL", __func__, #p);    \
-        if (!aligned16(p))                                                              \
+// A device pointer must be non-NULL and 16-byte aligned, except that a buffer
+// of zero elements may be NULL (torch hands out NULL for empty tensors).
+#define REQUIRE_PTR_N(p, count)                                                          \
+    do {                                                                                 \
+        if ((count) > 0 && !(p))                                                         \
+            return fail(DMPQ_ERR_INVALID_ARG, "%s: %s is NULL", __func__, #p);           \
+        if ((p) && !aligned16(p))                                                        \
             return fail(DMPQ_ERR_MISALIGNED, "%s: %s is not 16-byte aligned", __func__, #p); \
     } while (0)
+#define REQUIRE_PTR(p) REQUIRE_PTR_N(p, 1)
 
 #define REQUIRE_HOST(p)                                                                 \
     do {                                                                                \
@@ -90,10 +94,10 @@ size_t dmpq_workspace_bytes(int op, int64_t M, int64_t K) {
 
 dmpq_status dmpq_gamma_sums(hipStream_t stream, const uint16_t *x_in, const uint16_t *x_out,
                             int64_t n, double *d_sums2, void *ws, size_t ws_bytes) {
-    REQUIRE_PTR(x_in);
-    REQUIRE_PTR(x_out);
-    REQUIRE_PTR(d_sums2);
     if (n < 0) return fail(DMPQ_ERR_BAD_SHAPE, "%s: n = %lld < 0", __func__, (long long)n);
+    REQUIRE_PTR_N(x_in, n);
+    REQUIRE_PTR_N(x_out, n);
+    REQUIRE_PTR(d_sums2);
     if (dmpq_status s = check_ws(__func__, ws, ws_bytes)) return s;
     return hip_status(launch_gamma(stream, x_in, x_out, n, d_sums2, Workspace(ws)), __func__);
 }
@@ -125,11 +129,11 @@ dmpq_status dmpq_gate_and_route(const double *h_sums2, int n_lin, const double *
 
 dmpq_status dmpq_hadamard_quant_int8(hipStream_t stream, const uint16_t *x, int64_t M,
                                      int64_t K, int flags, int8_t *q, float *s_row) {
-    REQUIRE_PTR(x);
-    REQUIRE_PTR(q);
-    REQUIRE_PTR(s_row);
     if (M < 0) return fail(DMPQ_ERR_BAD_SHAPE, "%s: M = %lld < 0", __func__, (long long)M);
     if (dmpq_status s = check_k(__func__, K)) return s;
+    REQUIRE_PTR_N(x, M);
+    REQUIRE_PTR_N(q, M);
+    REQUIRE_PTR_N(s_row, M);
     if (flags & ~DMPQ_NO_HADAMARD) return fail(DMPQ_ERR_INVALID_ARG, "%s: unknown flags %d", __func__, flags);
     if (!hq_int8_supported(K))
         return fail(DMPQ_ERR_UNSUPPORTED, "%s: K = %lld exceeds 32768", __func__, (long long)K);
@@ -139,12 +143,12 @@ dmpq_status dmpq_hadamard_quant_int8(hipStream_t stream, const uint16_t *x, int6
 dmpq_status dmpq_hadamard_quant_nvfp4(hipStream_t stream, const uint16_t *x, int64_t M,
                                       int64_t K, int flags, uint8_t *codes, uint8_t *scales,
                                       float *d_g, void *ws, size_t ws_bytes) {
-    REQUIRE_PTR(x);
-    REQUIRE_PTR(codes);
-    REQUIRE_PTR(scales);
-    REQUIRE_PTR(d_g);
     if (M < 0) return fail(DMPQ_ERR_BAD_SHAPE, "%s: M = %lld < 0", __func__, (long long)M);
     if (dmpq_status s = check_k(__func__, K)) return s;
+    REQUIRE_PTR_N(x, M);
+    REQUIRE_PTR_N(codes, M);
+    REQUIRE_PTR_N(scales, M);
+    REQUIRE_PTR(d_g);
     if (flags & ~DMPQ_NO_HADAMARD) return fail(DMPQ_ERR_INVALID_ARG, "%s: unknown flags %d", __func__, flags);
     if (dmpq_status s = check_ws(__func__, ws, ws_bytes)) return s;
     return hip_status(launch_hq_nvfp4(stream, x, M, K, flags, codes, scales, d_g, Workspace(ws)),
@@ -165,12 +169,12 @@ static dmpq_status check_gemm(const char *fn, int64_t M, int64_t N, int64_t K) {
 dmpq_status dmpq_qgemm_int8(hipStream_t stream, const int8_t *qa, const float *sa,
                             const int8_t *qw, const float *sw, int64_t M, int64_t N, int64_t K,
                             int out_dtype, void *y) {
-    REQUIRE_PTR(qa);
-    REQUIRE_PTR(sa);
-    REQUIRE_PTR(qw);
-    REQUIRE_PTR(sw);
-    REQUIRE_PTR(y);
     if (dmpq_status s = check_gemm(__func__, M, N, K)) return s;
+    REQUIRE_PTR_N(qa, M);
+    REQUIRE_PTR_N(sa, M);
+    REQUIRE_PTR_N(qw, N);
+    REQUIRE_PTR_N(sw, N);
+    REQUIRE_PTR_N(y, M * N);
     if (out_dtype != DMPQ_OUT_F32 && out_dtype != DMPQ_OUT_BF16 && out_dtype != DMPQ_OUT_I32)
         return fail(DMPQ_ERR_INVALID_ARG, "%s: unknown out_dtype %d", __func__, out_dtype);
     return hip_status(launch_gemm_int8(stream, qa, sa, qw, sw, M, N, K, out_dtype, y), __func__);
@@ -180,14 +184,14 @@ dmpq_status dmpq_qgemm_nvfp4(hipStream_t stream, const uint8_t *ca, const uint8_
                              const float *d_ga, const uint8_t *cw, const uint8_t *sw,
                              const float *d_gw, int64_t M, int64_t N, int64_t K, int out_dtype,
                              void *y, int variant) {
-    REQUIRE_PTR(ca);
-    REQUIRE_PTR(sa);
-    REQUIRE_PTR(d_ga);
-    REQUIRE_PTR(cw);
-    REQUIRE_PTR(sw);
-    REQUIRE_PTR(d_gw);
-    REQUIRE_PTR(y);
     if (dmpq_status s = check_gemm(__func__, M, N, K)) return s;
+    REQUIRE_PTR_N(ca, M);
+    REQUIRE_PTR_N(sa, M);
+    REQUIRE_PTR_N(d_ga, M * N);
+    REQUIRE_PTR_N(cw, N);
+    REQUIRE_PTR_N(sw, N);
+    REQUIRE_PTR_N(d_gw, M * N);
+    REQUIRE_PTR_N(y, M * N);
     if (out_dtype != DMPQ_OUT_F32 && out_dtype != DMPQ_OUT_BF16)
         return fail(DMPQ_ERR_INVALID_ARG, "%s: unknown out_dtype %d", __func__, out_dtype);
     if (variant != DMPQ_FP4_BF16_DEQUANT)
@@ -218,10 +222,10 @@ dmpq_status dmpq_tdc_decide(const dmpq_tdc_state *h_st, const dmpq_tdc_params *h
 dmpq_status dmpq_tdc_step(hipStream_t stream, int mode, const uint16_t *x_in, uint16_t *x_out,
                           uint16_t *delta, int64_t n, int delta_valid, double *d_sums4,
                           void *ws, size_t ws_bytes) {
-    REQUIRE_PTR(x_in);
-    REQUIRE_PTR(x_out);
-    REQUIRE_PTR(delta);
     if (n < 0) return fail(DMPQ_ERR_BAD_SHAPE, "%s: n = %lld < 0", __func__, (long long)n);
+    REQUIRE_PTR_N(x_in, n);
+    REQUIRE_PTR_N(x_out, n);
+    REQUIRE_PTR_N(delta, n);
     if (mode == DMPQ_TDC_SKIP) {
         if (!delta_valid)
             return fail(DMPQ_ERR_INVALID_ARG, "%s: SKIP needs a cached delta", __func__);
@@ -259,14 +263,14 @@ dmpq_status dmpq_tdc_commit(dmpq_tdc_state *h_st, int mode, const double *h_sums
 dmpq_status dmpq_prep_weight(hipStream_t stream, const uint16_t *w, int64_t N, int64_t K,
                              int int8_mode, uint8_t *cw, uint8_t *sw, float *d_gw, int8_t *qw,
                              float *sw_row, void *ws, size_t ws_bytes) {
-    REQUIRE_PTR(w);
-    REQUIRE_PTR(cw);
-    REQUIRE_PTR(sw);
-    REQUIRE_PTR(d_gw);
-    REQUIRE_PTR(qw);
-    REQUIRE_PTR(sw_row);
     if (N < 0) return fail(DMPQ_ERR_BAD_SHAPE, "%s: N = %lld < 0", __func__, (long long)N);
     if (dmpq_status s = check_k(__func__, K)) return s;
+    REQUIRE_PTR_N(w, N);
+    REQUIRE_PTR_N(cw, N);
+    REQUIRE_PTR_N(sw, N);
+    REQUIRE_PTR(d_gw);
+    REQUIRE_PTR_N(qw, N);
+    REQUIRE_PTR_N(sw_row, N);
     if (int8_mode != DMPQ_W8_FROM_NVFP4 && int8_mode != DMPQ_W8_DIRECT)
         return fail(DMPQ_ERR_INVALID_ARG, "%s: unknown int8_mode %d", __func__, int8_mode);
     if (!hq_int8_supported(K))

@@ -9,22 +9,17 @@
 
 namespace dmpq {
 
-// Fixed workspace layout for the deterministic two-stage reductions: up to
-// kMaxPartials per-workgroup partials, then a ticket counter and a scratch
-// slot.  All grids that use a workspace are capped at kMaxPartials groups.
+// Workspace layout: per-workgroup partial results handed from the first
+// kernel of a call to the second (partial fp64 sums, or partial float maxima
+// for the NVFP4 amax).  Grids that use it are capped at kMaxPartials groups.
+// Its contents need no initialization: every call writes before it reads.
 constexpr int kMaxPartials = 2048;
 constexpr int kMaxSums = 4;
-constexpr size_t kWsPartialBytes = sizeof(double) * kMaxSums * kMaxPartials;
-constexpr size_t kWsBytes = kWsPartialBytes + 256;
+constexpr size_t kWsBytes = sizeof(double) * kMaxSums * kMaxPartials;
 
 struct Workspace {
-    double *partial;   // kMaxSums * kMaxPartials doubles (also viewed as floats)
-    unsigned *ticket;  // self-resetting arrival counter
-    float *amax;       // NVFP4 tensor amax handed from pass 1 to pass 2
-    explicit Workspace(void *ws)
-        : partial(static_cast<double *>(ws)),
-          ticket(reinterpret_cast<unsigned *>(static_cast<char *>(ws) + kWsPartialBytes)),
-          amax(reinterpret_cast<float *>(static_cast<char *>(ws) + kWsPartialBytes + 64)) {}
+    double *partial;  // kMaxSums * kMaxPartials doubles (also viewed as floats)
+    explicit Workspace(void *ws) : partial(static_cast<double *>(ws)) {}
 };
 
 hipError_t launch_hq_int8(hipStream_t s, const uint16_t *x, int64_t M, int64_t K, int flags,

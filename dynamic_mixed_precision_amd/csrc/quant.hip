@@ -97,9 +97,12 @@ __global__ __launch_bounds__(256) void row_quant_int8_kernel(Src src, int64_t M,
     }
     if (!row_ok) return;
 
-    float inv = 0.0f;
-    if (amax > 0.0f) inv = 127.0f / amax;
-    if (lr == 0) s_row[row] = amax > 0.0f ? amax / 127.0f : 0.0f;
+    // A row whose reciprocal 127/amax is not finite (amax zero, or below about
+    // 3.7e-37) quantizes as a zero row: scale 0, codes 0.
+    float inv = 127.0f / amax;
+    const bool zero_row = !(inv <= FLT_MAX);
+    if (zero_row) inv = 0.0f;
+    if (lr == 0) s_row[row] = zero_row ? 0.0f : amax / 127.0f;
     int8_t *qr = q + row * K;
 #pragma unroll
     for (int i = 0; i < BPL; i++) {
@@ -198,27 +201,40 @@ hipError_t launch_w8_from_nvfp4(hipStream_t s, const uint8_t *cw, const uint8_t 
 }
 
 // ---------------------------------------------------------------------------
-// NVFP4, pass 1: absmax of the rotated tensor.  Each workgroup reduces its
-// share to one float; the last workgroup to arrive (ticket counter) reduces
-// the partials, publishes A and g = A/2688, and resets the ticket.  Max is
-// order independent, so the result does not depend on arrival order.
+// NVFP4, pass 1: absmax of the rotated tensor.  Each workgroup writes the max
+// of its share to partial[blockIdx.x]; pass 2 reduces the partials itself
+// (max is order independent).  No cross-workgroup fence is needed: the kernel
+// boundary orders the two passes.
 // ---------------------------------------------------------------------------
+constexpr int kAmaxGroups = 1024;
+
 __global__ __launch_bounds__(256) void nvfp4_amax_kernel(const uint16_t *__restrict__ x,
                                                          int64_t nblocks, int flags,
-                                                         float *__restrict__ partial,
-                                                         unsigned *ticket, float *amax_out,
-                                                         float *g_out) {
+                                                         float *__restrict__ partial) {
     __shared__ float red[4];
-    __shared__ bool last;
     const int tid = threadIdx.x;
     float m = 0.0f;
     const int64_t stride = (int64_t)gridDim.x * 256;
-    for (int64_t b = (int64_t)blockIdx.x * 256 + tid; b < nblocks; b += stride) {
-        const uint4 *p = reinterpret_cast<const uint4 *>(x + 16 * b);
-        uint4 a0 = load_nt16(p);
-        uint4 a1 = load_nt16(p + 1);
-        float v[16];
+    int64_t b = (int64_t)blockIdx.x * 256 + tid;
+    for (; b + stride < nblocks; b += 2 * stride) {  // two blocks in flight per lane
+        const uint4 *p0 = reinterpret_cast<const uint4 *>(x + 16 * b);
+        const uint4 *p1 = reinterpret_cast<const uint4 *>(x + 16 * (b + stride));
+        uint4 a0 = load_nt16(p0), a1 = load_nt16(p0 + 1);
+        uint4 c0 = load_nt16(p1), c1 = load_nt16(p1 + 1);
+        float v[16], w[16];
         unpack16(a0, a1, v);
+        unpack16(c0, c1, w);
+        if (!(flags & 1)) {
+            fwht16(v);
+            fwht16(w);
+        }
+#pragma unroll
+        for (int j = 0; j < 16; j++) m = fmaxf(m, fmaxf(__builtin_fabsf(v[j]), __builtin_fabsf(w[j])));
+    }
+    if (b < nblocks) {
+        const uint4 *p0 = reinterpret_cast<const uint4 *>(x + 16 * b);
+        float v[16];
+        unpack16(load_nt16(p0), load_nt16(p0 + 1), v);
         if (!(flags & 1)) fwht16(v);
 #pragma unroll
         for (int j = 0; j < 16; j++) m = fmaxf(m, __builtin_fabsf(v[j]));
@@ -226,44 +242,46 @@ __global__ __launch_bounds__(256) void nvfp4_amax_kernel(const uint16_t *__restr
     m = wave_max(m);
     if ((tid & (kWave - 1)) == 0) red[tid / kWave] = m;
     __syncthreads();
-    if (tid == 0) {
-        float w = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-        partial[blockIdx.x] = w;
-        __threadfence();
-        last = atomicAdd(ticket, 1u) == gridDim.x - 1;
-    }
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
-    float a = 0.0f;
-    for (unsigned i = tid; i < gridDim.x; i += 256)
-        a = fmaxf(a, __hip_atomic_load(&partial[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    a = wave_max(a);
-    __syncthreads();
-    if ((tid & (kWave - 1)) == 0) red[tid / kWave] = a;
-    __syncthreads();
-    if (tid == 0) {
-        const float A = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-        *amax_out = A;
-        *g_out = A / 2688.0f;
-        __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (tid == 0) partial[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
 // ---------------------------------------------------------------------------
-// NVFP4, pass 2: per 16-block E4M3 scale and E2M1 codes.  The flat block index
-// b addresses codes (8 bytes per block) and scales (1 byte per block)
-// directly, because K is a multiple of 16.
+// NVFP4, pass 2: reduce the pass-1 partials to the tensor amax A, then per
+// 16-block the E4M3 scale and the E2M1 codes.  The flat block index b
+// addresses codes (8 bytes per block) and scales (1 byte per block) directly
+// because K is a multiple of 16.  Codes use the gfx950 converter
+// v_cvt_scalef32_pk_fp4_f32 with scale 1.0 (round to nearest even,
+// saturating at 6, sign kept), which matches the E2M1 rule for every finite
+// fp32 input.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e2m1x8(const float *y) {
+    uint32_t w = 0u;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], 1.0f, 3);
+    return w;
+}
+
 __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t *__restrict__ x,
                                                           int64_t nblocks, int flags,
-                                                          const float *__restrict__ amax_in,
-                                                          uint8_t *__restrict__ codes,
-                                                          uint8_t *__restrict__ scales) {
-    const float A = *amax_in;
+                                                          const float *__restrict__ partial,
+                                                          int nparts, uint8_t *__restrict__ codes,
+                                                          uint8_t *__restrict__ scales,
+                                                          float *__restrict__ g_out) {
+    __shared__ float red[4];
+    const int tid = threadIdx.x;
+    float a = 0.0f;
+    for (int i = tid; i < nparts; i += 256) a = fmaxf(a, partial[i]);
+    a = wave_max(a);
+    if ((tid & (kWave - 1)) == 0) red[tid / kWave] = a;
+    __syncthreads();
+    const float A = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const float g = A / 2688.0f;
+    if (blockIdx.x == 0 && tid == 0) *g_out = g;
+
     const int64_t stride = (int64_t)gridDim.x * 256;
-    for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < nblocks; b += stride) {
+    for (int64_t b = (int64_t)blockIdx.x * 256 + tid; b < nblocks; b += stride) {
         const uint4 *p = reinterpret_cast<const uint4 *>(x + 16 * b);
         uint4 a0 = load_nt16(p);
         uint4 a1 = load_nt16(p + 1);
@@ -284,9 +302,9 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t *__rest
         if (S >= FLT_MIN) {
             const float inv = 1.0f / S;
 #pragma unroll
-            for (int j = 0; j < 8; j++) w0 |= e2m1_encode(v[j] * inv) << (4 * j);
-#pragma unroll
-            for (int j = 0; j < 8; j++) w1 |= e2m1_encode(v[8 + j] * inv) << (4 * j);
+            for (int j = 0; j < 16; j++) v[j] = v[j] * inv;
+            w0 = e2m1x8(v);
+            w1 = e2m1x8(v + 8);
         }
         *reinterpret_cast<uint2 *>(codes + 8 * b) = make_uint2(w0, w1);
         scales[b] = (uint8_t)e;
@@ -296,14 +314,14 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t *__rest
 hipError_t launch_hq_nvfp4(hipStream_t s, const uint16_t *x, int64_t M, int64_t K, int flags,
                            uint8_t *codes, uint8_t *scales, float *g, const Workspace &ws) {
     const int64_t nblocks = M * (K / 16);
-    const unsigned ga = stride_grid(nblocks, 256 * 4, kMaxPartials);
-    hipLaunchKernelGGL(nvfp4_amax_kernel, dim3(ga), dim3(256), 0, s, x, nblocks, flags,
-                       reinterpret_cast<float *>(ws.partial), ws.ticket, ws.amax, g);
+    float *partial = reinterpret_cast<float *>(ws.partial);
+    const unsigned ga = stride_grid(nblocks, 256 * 4, kAmaxGroups);
+    hipLaunchKernelGGL(nvfp4_amax_kernel, dim3(ga), dim3(256), 0, s, x, nblocks, flags, partial);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || nblocks == 0) return e;
+    if (e != hipSuccess) return e;
     const unsigned gb = stride_grid(nblocks, 256 * 2, 8192);
-    hipLaunchKernelGGL(nvfp4_quant_kernel, dim3(gb), dim3(256), 0, s, x, nblocks, flags,
-                       ws.amax, codes, scales);
+    hipLaunchKernelGGL(nvfp4_quant_kernel, dim3(gb), dim3(256), 0, s, x, nblocks, flags, partial,
+                       (int)ga, codes, scales, g);
     return hipGetLastError();
 }
 

@@ -7,8 +7,9 @@
 // All kernels stream bf16 in 16-byte vectors (8 elements).  Sums: each lane
 // adds 8 non-negative fp32 terms (relative error <= 7 ulp of fp32, below
 // 4.2e-7), then accumulates in fp64; workgroups reduce in a fixed tree and
-// the last workgroup to arrive adds the per-group partials in index order,
-// so results are bit-identical from run to run.
+// a second one-workgroup kernel adds the per-group partials in index order,
+// so results are bit-identical from run to run (and no cross-workgroup fence
+// is needed).
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -31,12 +32,11 @@ __device__ __forceinline__ void to8(const uint4 &a, float v[8]) {
     }
 }
 
-// Reduce NS per-lane fp64 sums over the grid into out[0..NS).  Must be called
-// by every thread of every workgroup.
+// Reduce NS per-lane fp64 sums of one workgroup (fixed tree) and write them
+// to partial[blockIdx.x * NS + j].  Must be called by every thread.
 template <int NS>
-__device__ void grid_sum(double (&s)[NS], double *partial, unsigned *ticket, double *out) {
+__device__ void block_partials(double (&s)[NS], double *partial) {
     __shared__ double red[NS][4];
-    __shared__ bool last;
     const int tid = threadIdx.x;
 #pragma unroll
     for (int j = 0; j < NS; j++) s[j] = wave_sum(s[j]);
@@ -45,49 +45,53 @@ __device__ void grid_sum(double (&s)[NS], double *partial, unsigned *ticket, dou
         for (int j = 0; j < NS; j++) red[j][tid / kWave] = s[j];
     }
     __syncthreads();
-    if (tid == 0) {
-#pragma unroll
-        for (int j = 0; j < NS; j++)
-            partial[(size_t)blockIdx.x * NS + j] = (red[j][0] + red[j][1]) + (red[j][2] + red[j][3]);
-        __threadfence();
-        last = atomicAdd(ticket, 1u) == gridDim.x - 1;
-    }
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
+    if (tid < NS)
+        partial[(size_t)blockIdx.x * NS + tid] = (red[tid][0] + red[tid][1]) + (red[tid][2] + red[tid][3]);
+}
+
+// bf16 RNE of two fp32 values packed low/high, with the gfx950 converter
+// (v_cvt_pk_bf16_f32), which matches round-to-nearest-even on every finite
+// input.
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+    typedef float v2f __attribute__((ext_vector_type(2)));
+    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+    const v2bf r = __builtin_convertvector((v2f){lo, hi}, v2bf);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+}  // namespace
+
+// Second stage of every sum: one workgroup adds the per-group partials in a
+// fixed order (thread t takes partials t, t+256, ..., then a fixed tree), so
+// the result does not depend on scheduling.
+template <int NS>
+__global__ __launch_bounds__(256) void finalize_sums_kernel(const double *__restrict__ partial,
+                                                            int nparts, double *__restrict__ out) {
+    __shared__ double red[NS][4];
+    const int tid = threadIdx.x;
     double t[NS];
 #pragma unroll
     for (int j = 0; j < NS; j++) t[j] = 0.0;
-    for (unsigned i = tid; i < gridDim.x; i += 256) {
+    for (int i = tid; i < nparts; i += 256) {
 #pragma unroll
-        for (int j = 0; j < NS; j++)
-            t[j] += __hip_atomic_load(&partial[(size_t)i * NS + j], __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
+        for (int j = 0; j < NS; j++) t[j] += partial[(size_t)i * NS + j];
     }
 #pragma unroll
     for (int j = 0; j < NS; j++) t[j] = wave_sum(t[j]);
-    __syncthreads();
     if ((tid & (kWave - 1)) == 0) {
 #pragma unroll
         for (int j = 0; j < NS; j++) red[j][tid / kWave] = t[j];
     }
     __syncthreads();
-    if (tid == 0) {
-#pragma unroll
-        for (int j = 0; j < NS; j++) out[j] = (red[j][0] + red[j][1]) + (red[j][2] + red[j][3]);
-        __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (tid < NS) out[tid] = (red[tid][0] + red[tid][1]) + (red[tid][2] + red[tid][3]);
 }
-
-}  // namespace
 
 // ---------------------------------------------------------------------------
 // Gamma sums: S1 = sum |out - in|, S2 = sum |in|.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void gamma_kernel(const uint16_t *__restrict__ xin,
                                                     const uint16_t *__restrict__ xout,
-                                                    int64_t n, double *partial, unsigned *ticket,
-                                                    double *out) {
+                                                    int64_t n, double *partial) {
     double s[2] = {0.0, 0.0};
     const int64_t nch = n / 8;
     const int64_t stride = (int64_t)gridDim.x * 256;
@@ -134,14 +138,14 @@ __global__ __launch_bounds__(256) void gamma_kernel(const uint16_t *__restrict__
         s[0] += (double)__builtin_fabsf(b - a);
         s[1] += (double)__builtin_fabsf(a);
     }
-    grid_sum<2>(s, partial, ticket, out);
+    block_partials<2>(s, partial);
 }
 
 hipError_t launch_gamma(hipStream_t st, const uint16_t *x_in, const uint16_t *x_out, int64_t n,
                         double *sums, const Workspace &ws) {
     const unsigned g = stride_grid(n / 8, 256 * kUnroll * 2, kMaxPartials);
-    hipLaunchKernelGGL(gamma_kernel, dim3(g), dim3(256), 0, st, x_in, x_out, n, ws.partial,
-                       ws.ticket, sums);
+    hipLaunchKernelGGL(gamma_kernel, dim3(g), dim3(256), 0, st, x_in, x_out, n, ws.partial);
+    hipLaunchKernelGGL(finalize_sums_kernel<2>, dim3(1), dim3(256), 0, st, ws.partial, (int)g, sums);
     return hipGetLastError();
 }
 
@@ -158,10 +162,10 @@ __global__ __launch_bounds__(256) void tdc_skip_kernel(const uint16_t *__restric
         to8(ld16(xin + 8 * c), a);
         to8(ld16(delta + 8 * c), d);
         uint4 o;
-        o.x = pack_bf16x2(a[0] + d[0], a[1] + d[1]);
-        o.y = pack_bf16x2(a[2] + d[2], a[3] + d[3]);
-        o.z = pack_bf16x2(a[4] + d[4], a[5] + d[5]);
-        o.w = pack_bf16x2(a[6] + d[6], a[7] + d[7]);
+        o.x = cvt_bf16x2(a[0] + d[0], a[1] + d[1]);
+        o.y = cvt_bf16x2(a[2] + d[2], a[3] + d[3]);
+        o.z = cvt_bf16x2(a[4] + d[4], a[5] + d[5]);
+        o.w = cvt_bf16x2(a[6] + d[6], a[7] + d[7]);
         store_nt16(xout + 8 * c, o);
     }
     if (blockIdx.x == 0 && threadIdx.x < n - 8 * nch) {
@@ -192,20 +196,23 @@ __device__ __forceinline__ void refresh8(const uint4 &ia, const uint4 &oa, const
     to8(oa, b);
     if (DV) to8(da, d);
     float f1 = 0.0f, f2 = 0.0f, f3 = 0.0f, f4 = 0.0f;
-    uint32_t nb[8];
+    float dn[8];
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 8; i++) dn[i] = b[i] - a[i];
+#pragma unroll
+    for (int i = 0; i < 4; i++) w[i] = cvt_bf16x2(dn[2 * i], dn[2 * i + 1]);
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-        const float dn = b[i] - a[i];
-        nb[i] = f32_to_bf16(dn);
-        f1 += __builtin_fabsf(dn);
+        f1 += __builtin_fabsf(dn[i]);
         f2 += __builtin_fabsf(a[i]);
         if (DV) {
-            f3 += __builtin_fabsf(__uint_as_float(nb[i] << 16) - d[i]);
+            const float nbf = (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]);
+            f3 += __builtin_fabsf(nbf - d[i]);
             f4 += __builtin_fabsf(d[i]);
         }
     }
-    nd = make_uint4(nb[0] | (nb[1] << 16), nb[2] | (nb[3] << 16), nb[4] | (nb[5] << 16),
-                    nb[6] | (nb[7] << 16));
+    nd = make_uint4(w[0], w[1], w[2], w[3]);
     s[0] += (double)f1;
     s[1] += (double)f2;
     if (DV) {
@@ -218,8 +225,7 @@ template <bool DV>
 __global__ __launch_bounds__(256) void tdc_refresh_kernel(const uint16_t *__restrict__ xin,
                                                           const uint16_t *__restrict__ xout,
                                                           uint16_t *__restrict__ delta,
-                                                          int64_t n, double *partial,
-                                                          unsigned *ticket, double *out) {
+                                                          int64_t n, double *partial) {
     double s[4] = {0.0, 0.0, 0.0, 0.0};
     const int64_t nch = n / 8;
     const int64_t stride = (int64_t)gridDim.x * 256;
@@ -261,7 +267,7 @@ __global__ __launch_bounds__(256) void tdc_refresh_kernel(const uint16_t *__rest
         }
         delta[i] = (uint16_t)nb;
     }
-    grid_sum<4>(s, partial, ticket, out);
+    block_partials<4>(s, partial);
 }
 
 hipError_t launch_tdc_refresh(hipStream_t st, const uint16_t *x_in, const uint16_t *x_out,
@@ -270,10 +276,11 @@ hipError_t launch_tdc_refresh(hipStream_t st, const uint16_t *x_in, const uint16
     const unsigned g = stride_grid(n / 8, 256 * kUnroll * 2, kMaxPartials);
     if (delta_valid)
         hipLaunchKernelGGL(tdc_refresh_kernel<true>, dim3(g), dim3(256), 0, st, x_in, x_out,
-                           delta, n, ws.partial, ws.ticket, sums);
+                           delta, n, ws.partial);
     else
         hipLaunchKernelGGL(tdc_refresh_kernel<false>, dim3(g), dim3(256), 0, st, x_in, x_out,
-                           delta, n, ws.partial, ws.ticket, sums);
+                           delta, n, ws.partial);
+    hipLaunchKernelGGL(finalize_sums_kernel<4>, dim3(1), dim3(256), 0, st, ws.partial, (int)g, sums);
     return hipGetLastError();
 }
 

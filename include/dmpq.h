@@ -26,12 +26,13 @@
  *     is [M x N].
  *   - Every device tensor pointer must be 16-byte aligned.  K must be a
  *     positive multiple of 16 (the Hadamard block and the NVFP4 scale group).
- *     M, N >= 0 (0 is an empty no-op).
+ *     M, N >= 0 (0 is an empty no-op); a buffer of zero elements may be NULL.
  *   - Non-finite inputs (NaN, Inf) are outside the contract: results are
  *     unspecified, but every kernel still terminates.
- *   - Workspaces (ws) come from dmpq_workspace_bytes().  A workspace must be
- *     zero-filled once before its first use; every call leaves it ready for
- *     the next.  Calls that run concurrently must not share a workspace.
+ *   - Workspaces (ws) come from dmpq_workspace_bytes().  They carry
+ *     per-workgroup partial results between the kernels of one call and need
+ *     no initialization.  Calls that may run concurrently (different streams)
+ *     must not share a workspace; calls on one stream may.
  */
 #ifndef DMPQ_H
 #define DMPQ_H
