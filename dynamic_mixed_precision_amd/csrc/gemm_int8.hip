@@ -5,7 +5,9 @@
 // Both operands are K-contiguous, the natural MFMA layout: one lane's
 // 16-byte LDS read is a 16-value k-slice of one A row (or W row).  The k
 // order inside an MFMA does not matter for the result: A and W fragments use
-// the same k mapping and int32 addition is exact.
+// the same k mapping and int32 addition is exact.  The W fragment is the
+// MFMA's first operand, so the accumulators come out transposed and each lane
+// stores 4 consecutive output columns at once.
 //
 // Tiling: 256 threads = 4 waves in a 2 x 2 grid.  Workgroup tile 256 x 256,
 // wave tile 128 x 128 = 4 x 4 MFMA 32x32x32 tiles (256 int32 accumulators per
@@ -26,6 +28,7 @@ namespace i8gemm {
 constexpr int BM = 256, BN = 256, BK = 128;
 constexpr int ROW = BK + 16;                  // padded LDS row, bytes
 constexpr int STAGE = (BM + BN) * ROW;        // bytes per LDS stage
+static_assert(4 * EpiBand<4>::BYTES <= 2 * STAGE, "epilogue bands fit in the stage buffers");
 constexpr int LOADS = BM * BK / 16 / 256;     // 16-byte chunks per thread per operand
 constexpr unsigned GROUP_M = 8;
 }  // namespace i8gemm
@@ -51,33 +54,39 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0;
 
-    // global -> register staging: chunk c = tid + 256*j covers row c/8, bytes (c%8)*16
+    // global -> register staging: chunk c = tid + 256*j covers row c/8, bytes
+    // (c%8)*16.  Out-of-range chunks (ragged M, N or K) load from a clamped
+    // in-range address; bit j of oka/okw records whether chunk j is real, and
+    // the zeroing is applied only when the chunk is written to LDS, so the
+    // loads stay in flight across the MFMAs.
     uint4 ra[LOADS], rw[LOADS];
+    uint32_t oka = 0u, okw = 0u;
     const int nk = (int)((K + BK - 1) / BK);
 
-    // Out-of-range chunks (ragged M, N or K) load from a clamped in-range
-    // address and are then replaced by zeros (a select on values, so no
-    // pointer to a local zero is ever formed).
 #define DMPQ_I8_GLOAD(k0)                                                                    \
+    oka = 0u;                                                                                \
+    okw = 0u;                                                                                \
     _Pragma("unroll") for (int j = 0; j < LOADS; j++) {                                      \
         const int c = tid + 256 * j;                                                         \
         const int r = c >> 3;                                                                \
         const int64_t gk = (k0) + (c & 7) * 16;                                              \
         const int64_t gm = m0 + r, gn = n0 + r;                                              \
         const int64_t gkc = gk < K ? gk : K - 16;                                            \
-        const uint4 va = *reinterpret_cast<const uint4 *>(A + (gm < M ? gm : M - 1) * K + gkc); \
-        const uint4 vw = *reinterpret_cast<const uint4 *>(W + (gn < N ? gn : N - 1) * K + gkc); \
-        const bool oka = gm < M && gk < K, okw = gn < N && gk < K;                           \
-        ra[j] = make_uint4(oka ? va.x : 0u, oka ? va.y : 0u, oka ? va.z : 0u, oka ? va.w : 0u); \
-        rw[j] = make_uint4(okw ? vw.x : 0u, okw ? vw.y : 0u, okw ? vw.z : 0u, okw ? vw.w : 0u); \
+        ra[j] = *reinterpret_cast<const uint4 *>(A + (gm < M ? gm : M - 1) * K + gkc);      \
+        rw[j] = *reinterpret_cast<const uint4 *>(W + (gn < N ? gn : N - 1) * K + gkc);      \
+        oka |= (uint32_t)(gm < M && gk < K) << j;                                            \
+        okw |= (uint32_t)(gn < N && gk < K) << j;                                            \
     }
 #define DMPQ_I8_SSTORE(buf)                                                                  \
     _Pragma("unroll") for (int j = 0; j < LOADS; j++) {                                      \
         const int c = tid + 256 * j;                                                         \
         const int r = c >> 3, kc = (c & 7) * 16;                                             \
         int8_t *base = lds + (buf) * STAGE;                                                  \
-        *reinterpret_cast<uint4 *>(base + r * ROW + kc) = ra[j];                             \
-        *reinterpret_cast<uint4 *>(base + (BM + r) * ROW + kc) = rw[j];                      \
+        const bool ia = (oka >> j) & 1u, iw = (okw >> j) & 1u;                               \
+        *reinterpret_cast<uint4 *>(base + r * ROW + kc) =                                    \
+            make_uint4(ia ? ra[j].x : 0u, ia ? ra[j].y : 0u, ia ? ra[j].z : 0u, ia ? ra[j].w : 0u); \
+        *reinterpret_cast<uint4 *>(base + (BM + r) * ROW + kc) =                             \
+            make_uint4(iw ? rw[j].x : 0u, iw ? rw[j].y : 0u, iw ? rw[j].z : 0u, iw ? rw[j].w : 0u); \
     }
 
     DMPQ_I8_GLOAD(0)
@@ -104,7 +113,7 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(
             for (int i = 0; i < 4; i++)
 #pragma unroll
                 for (int j = 0; j < 4; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[j], a[i], acc[i][j], 0, 0, 0);
         }
         if (more) {
             DMPQ_I8_SSTORE(cur ^ 1)
@@ -114,68 +123,246 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(
 #undef DMPQ_I8_GLOAD
 #undef DMPQ_I8_SSTORE
 
-    // Epilogue.  32x32 accumulator layout: lane l holds column l % 32 and rows
-    // 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.
+    // Epilogue.  The MFMA runs with the W fragment as its first operand, so
+    // acc[i][j] holds the transposed block: lane l owns activation row
+    // m = l % 32 of A-subtile i and, for register group g = r / 4, the four
+    // consecutive output columns 8g + 4*(l/32) + 0..3 of W-subtile j.  Values
+    // are scaled here, staged per wave through LDS in two 64-row bands, and
+    // stored row-contiguous (the last loop iteration ended with a barrier, so
+    // the stage buffers are free).
+    constexpr int ES = OUT == 1 ? 2 : 4;
+    using Band = EpiBand<ES>;
+    const int lm = lane & 31, lh = lane >> 5;
+    float swv[4][4][4];
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int64_t col = n0 + wn * 128 + j * 32 + (lane & 31);
-        if (col >= N) continue;
-        const float swc = sw[col];
+    for (int j = 0; j < 4; j++)
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
+        for (int g = 0; g < 4; g++)
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int64_t row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (row >= M) continue;
-                const int a = acc[i][j][r];
-                const int64_t o = row * N + col;
-                if constexpr (OUT == 2) {
-                    static_cast<int32_t *>(y)[o] = a;
-                } else {
-                    const float v = ((float)a * sa[row]) * swc;
-                    if constexpr (OUT == 0)
-                        static_cast<float *>(y)[o] = v;
-                    else
-                        static_cast<uint16_t *>(y)[o] = (uint16_t)f32_to_bf16(v);
+            for (int e = 0; e < 4; e++) {
+                const int64_t col = n0 + wn * 128 + j * 32 + 8 * g + 4 * lh + e;
+                swv[j][g][e] = col < N ? sw[col] : 0.0f;
+            }
+    uint8_t *band = reinterpret_cast<uint8_t *>(lds) + wave * Band::BYTES;
+    const bool vec = ((N * ES) & 15) == 0;
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ii++) {
+            const int i = 2 * h + ii;
+            const int64_t row = m0 + wm * 128 + i * 32 + lm;
+            const float sar = row < M ? sa[row] : 0.0f;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+#pragma unroll
+                for (int g = 0; g < 4; g++) {
+                    uint8_t *dst = band + (ii * 32 + lm) * Band::STRIDE + (j * 32 + 8 * g + 4 * lh) * ES;
+                    if constexpr (OUT == 2) {
+                        *reinterpret_cast<int4 *>(dst) = make_int4(acc[i][j][4 * g], acc[i][j][4 * g + 1],
+                                                                   acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+                    } else {
+                        float v4[4];
+#pragma unroll
+                        for (int e = 0; e < 4; e++) v4[e] = ((float)acc[i][j][4 * g + e] * sar) * swv[j][g][e];
+                        if constexpr (OUT == 0)
+                            *reinterpret_cast<float4 *>(dst) = make_float4(v4[0], v4[1], v4[2], v4[3]);
+                        else
+                            *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3]));
+                    }
                 }
             }
         }
+        epi_band_to_global<ES>(band, y, M, N, m0 + wm * 128 + h * 64, n0 + wn * 128, lane, vec);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Fast path for K % 128 == 0: operand tiles go from global memory straight into
+// LDS with gfx950's global_load_lds_dwordx4 (each lane's 16 bytes land at
+// base + 16 * lane of a wave's 1 KB block), so no staging registers and no
+// LDS write instructions are needed.  Rows are 128 bytes; the 16-byte chunk
+// kc of row r is stored at slot kc ^ ((r >> 1) & 7), which makes the 32-row
+// fragment reads conflict-free on the 64-bank LDS.  Per stage: wait for the
+// stage's loads and barrier, read every fragment of the stage into registers,
+// issue the next stage's loads into the other buffer, then 64 MFMAs per wave.
+// Out-of-range rows (ragged M, N) load a clamped row; their outputs are never
+// stored.
+// ---------------------------------------------------------------------------
+namespace i8dma {
+constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int TILE = BM * BK;        // bytes per operand per stage
+constexpr int STAGE = 2 * TILE;      // A tile + W tile
+constexpr int NBUF = 2;
+constexpr int BLOCKS = TILE / 1024 / 4;  // 1 KB load blocks per wave per operand
+constexpr size_t LDS_BYTES = NBUF * STAGE > 4 * EpiBand<4>::BYTES ? NBUF * STAGE : 4 * EpiBand<4>::BYTES;
+}  // namespace i8dma
+
+__device__ __forceinline__ int swz128(int row, int kc) { return kc ^ ((row >> 1) & 7); }
+
+template <int OUT>
+__global__ __launch_bounds__(256, 1) void gemm_i8_dma_kernel(
+    const int8_t *__restrict__ A, const float *__restrict__ sa, const int8_t *__restrict__ W,
+    const float *__restrict__ sw, int64_t M, int64_t N, int64_t K, void *__restrict__ y,
+    unsigned tiles_m, unsigned tiles_n) {
+    using namespace i8dma;
+    extern __shared__ __attribute__((aligned(16))) int8_t lds[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const TileCoord tc = tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, i8gemm::GROUP_M);
+    const int64_t m0 = (int64_t)tc.m * BM, n0 = (int64_t)tc.n * BN;
+
+    v16i acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0;
+
+    // Per-lane source offsets of this wave's load blocks: block b = wave + 4q
+    // covers tile rows 8b .. 8b+7; lane L fills row 8b + L/8, slot L%8.
+    const int8_t *srcA[BLOCKS], *srcW[BLOCKS];
+#pragma unroll
+    for (int q = 0; q < BLOCKS; q++) {
+        const int b = wave + 4 * q;
+        const int row = 8 * b + (lane >> 3);
+        const int kc = swz128(row, lane & 7);
+        const int64_t gm = m0 + row < M ? m0 + row : M - 1;
+        const int64_t gn = n0 + row < N ? n0 + row : N - 1;
+        srcA[q] = A + gm * K + kc * 16;
+        srcW[q] = W + gn * K + kc * 16;
+    }
+    typedef __attribute__((address_space(3))) void lds_void;
+#define DMPQ_I8_DMA(buf, k0)                                                                   \
+    _Pragma("unroll") for (int q = 0; q < BLOCKS; q++) {                                       \
+        const int b = wave + 4 * q;                                                            \
+        __builtin_amdgcn_global_load_lds((const void *)(srcA[q] + (k0)),                       \
+                                         (lds_void *)(lds + (buf) * STAGE + b * 1024), 16, 0, 0); \
+        __builtin_amdgcn_global_load_lds((const void *)(srcW[q] + (k0)),                       \
+                                         (lds_void *)(lds + (buf) * STAGE + TILE + b * 1024), 16, 0, 0); \
+    }
+
+    const int nk = (int)(K / BK);
+    DMPQ_I8_DMA(0, 0)
+    for (int kt = 0; kt < nk; kt++) {
+        const int cur = kt & 1;
+        __builtin_amdgcn_s_waitcnt(0xC07F & ~0xC00F);  // vmcnt(0): this wave's loads of stage kt
+        __syncthreads();                               // ... and every other wave's
+        v4i a[4][4], b[4][4];
+        const int8_t *base = lds + cur * STAGE;
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+            const int kc = 2 * s + (lane >> 5);
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int ra = wm * 128 + i * 32 + (lane & 31);
+                const int rb = wn * 128 + i * 32 + (lane & 31);
+                a[s][i] = *reinterpret_cast<const v4i *>(base + ra * BK + swz128(ra, kc) * 16);
+                b[s][i] = *reinterpret_cast<const v4i *>(base + TILE + rb * BK + swz128(rb, kc) * 16);
+            }
+        }
+        if (kt + 1 < nk) {
+            DMPQ_I8_DMA(cur ^ 1, (int64_t)(kt + 1) * BK)
+        }
+#pragma unroll
+        for (int s = 0; s < 4; s++)
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[s][j], a[s][i], acc[i][j], 0, 0, 0);
+    }
+#undef DMPQ_I8_DMA
+    __syncthreads();  // every wave is done reading the stage buffers before they hold bands
+
+    constexpr int ES = OUT == 1 ? 2 : 4;
+    using Band = EpiBand<ES>;
+    const int lm = lane & 31, lh = lane >> 5;
+    float swv[4][4][4];
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+        for (int g = 0; g < 4; g++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int64_t col = n0 + wn * 128 + j * 32 + 8 * g + 4 * lh + e;
+                swv[j][g][e] = col < N ? sw[col] : 0.0f;
+            }
+    uint8_t *band = reinterpret_cast<uint8_t *>(lds) + wave * Band::BYTES;
+    const bool vec = ((N * ES) & 15) == 0;
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ii++) {
+            const int i = 2 * h + ii;
+            const int64_t row = m0 + wm * 128 + i * 32 + lm;
+            const float sar = row < M ? sa[row] : 0.0f;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+#pragma unroll
+                for (int g = 0; g < 4; g++) {
+                    uint8_t *dst = band + (ii * 32 + lm) * Band::STRIDE + (j * 32 + 8 * g + 4 * lh) * ES;
+                    if constexpr (OUT == 2) {
+                        *reinterpret_cast<int4 *>(dst) = make_int4(acc[i][j][4 * g], acc[i][j][4 * g + 1],
+                                                                   acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+                    } else {
+                        float v4[4];
+#pragma unroll
+                        for (int e = 0; e < 4; e++) v4[e] = ((float)acc[i][j][4 * g + e] * sar) * swv[j][g][e];
+                        if constexpr (OUT == 0)
+                            *reinterpret_cast<float4 *>(dst) = make_float4(v4[0], v4[1], v4[2], v4[3]);
+                        else
+                            *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3]));
+                    }
+                }
+            }
+        }
+        epi_band_to_global<ES>(band, y, M, N, m0 + wm * 128 + h * 64, n0 + wn * 128, lane, vec);
     }
 }
 
 hipError_t launch_gemm_int8(hipStream_t s, const int8_t *qa, const float *sa, const int8_t *qw,
                             const float *sw, int64_t M, int64_t N, int64_t K, int out_dtype,
                             void *y) {
-    using namespace i8gemm;
     if (M == 0 || N == 0) return hipSuccess;
-    const int64_t tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
-    const dim3 grid((unsigned)(tm * tn)), block(256);
-    const size_t lds = 2 * STAGE;  // above the default dynamic-LDS limit: opt in once
+    // Kernels need more dynamic LDS than the default limit: opt in once.
     static const hipError_t attr = [] {
-        const void *fns[3] = {reinterpret_cast<const void *>(gemm_i8_kernel<0>),
+        const void *fns[6] = {reinterpret_cast<const void *>(gemm_i8_kernel<0>),
                               reinterpret_cast<const void *>(gemm_i8_kernel<1>),
-                              reinterpret_cast<const void *>(gemm_i8_kernel<2>)};
-        for (const void *f : fns) {
-            hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (int)(2 * STAGE));
+                              reinterpret_cast<const void *>(gemm_i8_kernel<2>),
+                              reinterpret_cast<const void *>(gemm_i8_dma_kernel<0>),
+                              reinterpret_cast<const void *>(gemm_i8_dma_kernel<1>),
+                              reinterpret_cast<const void *>(gemm_i8_dma_kernel<2>)};
+        const size_t bytes[6] = {2 * i8gemm::STAGE, 2 * i8gemm::STAGE, 2 * i8gemm::STAGE,
+                                 i8dma::LDS_BYTES, i8dma::LDS_BYTES, i8dma::LDS_BYTES};
+        for (int f = 0; f < 6; f++) {
+            hipError_t e = hipFuncSetAttribute(fns[f], hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)bytes[f]);
             if (e != hipSuccess) return e;
         }
         return hipSuccess;
     }();
     if (attr != hipSuccess) return attr;
-    switch (out_dtype) {
-        case 0:
-            hipLaunchKernelGGL(gemm_i8_kernel<0>, grid, block, lds, s, qa, sa, qw, sw, M, N, K, y,
-                               (unsigned)tm, (unsigned)tn);
-            break;
-        case 1:
-            hipLaunchKernelGGL(gemm_i8_kernel<1>, grid, block, lds, s, qa, sa, qw, sw, M, N, K, y,
-                               (unsigned)tm, (unsigned)tn);
-            break;
-        default:
-            hipLaunchKernelGGL(gemm_i8_kernel<2>, grid, block, lds, s, qa, sa, qw, sw, M, N, K, y,
-                               (unsigned)tm, (unsigned)tn);
-            break;
+    const int64_t tm = (M + 255) / 256, tn = (N + 255) / 256;
+    const dim3 grid((unsigned)(tm * tn)), block(256);
+    const unsigned utm = (unsigned)tm, utn = (unsigned)tn;
+    if (K % i8dma::BK == 0) {
+        const size_t lds = i8dma::LDS_BYTES;
+        if (out_dtype == 0)
+            hipLaunchKernelGGL(gemm_i8_dma_kernel<0>, grid, block, lds, s, qa, sa, qw, sw, M, N, K, y, utm, utn);
+        else if (out_dtype == 1)
+            hipLaunchKernelGGL(gemm_i8_dma_kernel<1>, grid, block, lds, s, qa, sa, qw, sw, M, N, K, y, utm, utn);
+        else
+            hipLaunchKernelGGL(gemm_i8_dma_kernel<2>, grid, block, lds, s, qa, sa, qw, sw, M, N, K, y, utm, utn);
+    } else {
+        const size_t lds = 2 * i8gemm::STAGE;
+        if (out_dtype == 0)
+            hipLaunchKernelGGL(gemm_i8_kernel<0>, grid, block, lds, s, qa, sa, qw, sw, M, N, K, y, utm, utn);
+        else if (out_dtype == 1)
+            hipLaunchKernelGGL(gemm_i8_kernel<1>, grid, block, lds, s, qa, sa, qw, sw, M, N, K, y, utm, utn);
+        else
+            hipLaunchKernelGGL(gemm_i8_kernel<2>, grid, block, lds, s, qa, sa, qw, sw, M, N, K, y, utm, utn);
     }
     return hipGetLastError();
 }

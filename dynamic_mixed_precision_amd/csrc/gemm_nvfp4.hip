@@ -35,6 +35,7 @@ namespace fp4gemm {
 constexpr int BM = 256, BN = 256, BKE = 64;  // BKE: k elements per stage
 constexpr int ROW = BKE * 2 + 16;            // padded LDS row, bytes (fp16)
 constexpr int STAGE = (BM + BN) * ROW;
+static_assert(4 * EpiBand<4>::BYTES <= 2 * STAGE, "epilogue bands fit in the stage buffers");
 constexpr unsigned GROUP_M = 8;
 }  // namespace fp4gemm
 
@@ -81,34 +82,32 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_f16_kernel(
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
     // staging: chunk c = tid + 256*h (h = 0, 1) is row c/2, k-half c%2 of the
-    // stage (16 code bytes = 32 elements = 2 scale groups)
-    uint4 rca[2], rcw[2];
-    uint32_t rsa[2], rsw[2];
+    // stage (16 code bytes = 32 elements = 2 scale groups).  Out-of-range
+    // groups read a clamped in-range address; bits of `ok` record which groups
+    // are real and the zeroing is applied when the chunk is dequantized into
+    // LDS, after the stage's MFMAs have been issued.
+    uint2 rca[2][2], rcw[2][2];
+    uint32_t rsa[2][2], rsw[2][2];
+    uint32_t ok = 0u;  // bit 4h+q: A group q (0,1), W group q (2,3) of chunk h
     const int nk = (int)((nb + 3) / 4);
 
-    // Out-of-range chunks read a clamped in-range address and are replaced by
-    // zero codes / zero scales (a value select; no pointer to a local).
 #define DMPQ_F4_GLOAD(g0)                                                                     \
+    ok = 0u;                                                                                  \
     _Pragma("unroll") for (int h = 0; h < 2; h++) {                                           \
         const int c = tid + 256 * h;                                                          \
         const int r = c >> 1;                                                                 \
-        const int64_t gi = (g0) + 2 * (c & 1); /* first scale group of the chunk */           \
-        const int64_t gic = gi < nb ? gi : nb - 1;                                            \
         const int64_t gm = m0 + r, gn = n0 + r;                                               \
         const int64_t gmc = gm < M ? gm : M - 1, gnc = gn < N ? gn : N - 1;                   \
-        const uint2 a0 = *reinterpret_cast<const uint2 *>(ca + gmc * rb + 8 * gic);           \
-        const uint2 w0 = *reinterpret_cast<const uint2 *>(cw + gnc * rb + 8 * gic);           \
-        const int64_t gic1 = gi + 1 < nb ? gi + 1 : nb - 1;                                   \
-        const uint2 a1 = *reinterpret_cast<const uint2 *>(ca + gmc * rb + 8 * gic1);          \
-        const uint2 w1 = *reinterpret_cast<const uint2 *>(cw + gnc * rb + 8 * gic1);          \
-        const uint32_t sa0 = sa[gmc * nb + gic], sa1 = sa[gmc * nb + gic1];                   \
-        const uint32_t sw0 = sw[gnc * nb + gic], sw1 = sw[gnc * nb + gic1];                   \
-        const bool a_ok0 = gm < M && gi < nb, a_ok1 = gm < M && gi + 1 < nb;                  \
-        const bool w_ok0 = gn < N && gi < nb, w_ok1 = gn < N && gi + 1 < nb;                  \
-        rca[h] = make_uint4(a_ok0 ? a0.x : 0u, a_ok0 ? a0.y : 0u, a_ok1 ? a1.x : 0u, a_ok1 ? a1.y : 0u); \
-        rcw[h] = make_uint4(w_ok0 ? w0.x : 0u, w_ok0 ? w0.y : 0u, w_ok1 ? w1.x : 0u, w_ok1 ? w1.y : 0u); \
-        rsa[h] = (a_ok0 ? sa0 : 0u) | ((a_ok1 ? sa1 : 0u) << 8);                              \
-        rsw[h] = (w_ok0 ? sw0 : 0u) | ((w_ok1 ? sw1 : 0u) << 8);                              \
+        _Pragma("unroll") for (int q = 0; q < 2; q++) {                                       \
+            const int64_t gi = (g0) + 2 * (c & 1) + q;                                        \
+            const int64_t gic = gi < nb ? gi : nb - 1;                                        \
+            rca[h][q] = *reinterpret_cast<const uint2 *>(ca + gmc * rb + 8 * gic);            \
+            rcw[h][q] = *reinterpret_cast<const uint2 *>(cw + gnc * rb + 8 * gic);            \
+            rsa[h][q] = sa[gmc * nb + gic];                                                   \
+            rsw[h][q] = sw[gnc * nb + gic];                                                   \
+            ok |= (uint32_t)(gm < M && gi < nb) << (4 * h + q);                               \
+            ok |= (uint32_t)(gn < N && gi < nb) << (4 * h + 2 + q);                           \
+        }                                                                                     \
     }
 #define DMPQ_F4_SSTORE(buf)                                                                   \
     _Pragma("unroll") for (int h = 0; h < 2; h++) {                                           \
@@ -116,11 +115,17 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_f16_kernel(
         const int r = c >> 1;                                                                 \
         uint8_t *pa = lds + (buf) * STAGE + r * ROW + (c & 1) * 64;                           \
         uint8_t *pw = lds + (buf) * STAGE + (BM + r) * ROW + (c & 1) * 64;                    \
+        const bool a0 = (ok >> (4 * h)) & 1u, a1 = (ok >> (4 * h + 1)) & 1u;                  \
+        const bool w0 = (ok >> (4 * h + 2)) & 1u, w1 = (ok >> (4 * h + 3)) & 1u;              \
         uint32_t d[16];                                                                       \
-        dequant32(rca[h], rsa[h], d);                                                         \
+        dequant32(make_uint4(a0 ? rca[h][0].x : 0u, a0 ? rca[h][0].y : 0u,                    \
+                             a1 ? rca[h][1].x : 0u, a1 ? rca[h][1].y : 0u),                   \
+                  (a0 ? rsa[h][0] : 0u) | ((a1 ? rsa[h][1] : 0u) << 8), d);                   \
         _Pragma("unroll") for (int q = 0; q < 4; q++)                                         \
             *reinterpret_cast<uint4 *>(pa + 16 * q) = make_uint4(d[4 * q], d[4 * q + 1], d[4 * q + 2], d[4 * q + 3]); \
-        dequant32(rcw[h], rsw[h], d);                                                         \
+        dequant32(make_uint4(w0 ? rcw[h][0].x : 0u, w0 ? rcw[h][0].y : 0u,                    \
+                             w1 ? rcw[h][1].x : 0u, w1 ? rcw[h][1].y : 0u),                   \
+                  (w0 ? rsw[h][0] : 0u) | ((w1 ? rsw[h][1] : 0u) << 8), d);                   \
         _Pragma("unroll") for (int q = 0; q < 4; q++)                                         \
             *reinterpret_cast<uint4 *>(pw + 16 * q) = make_uint4(d[4 * q], d[4 * q + 1], d[4 * q + 2], d[4 * q + 3]); \
     }
@@ -149,7 +154,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_f16_kernel(
             for (int i = 0; i < 4; i++)
 #pragma unroll
                 for (int j = 0; j < 4; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[j], a[i], acc[i][j], 0, 0, 0);
         }
         if (more) {
             DMPQ_F4_SSTORE(cur ^ 1)
@@ -159,25 +164,37 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_f16_kernel(
 #undef DMPQ_F4_GLOAD
 #undef DMPQ_F4_SSTORE
 
+    // Epilogue (operands swapped as in the INT8 GEMM): lane l owns activation
+    // row m = l % 32 of A-subtile i and four consecutive output columns
+    // 8g + 4*(l/32) + 0..3 of W-subtile j per register group g.  Staged per
+    // wave through LDS in two 64-row bands and stored row-contiguous.
+    constexpr int ES = OUT == 1 ? 2 : 4;
+    using Band = EpiBand<ES>;
     const float gA = *ga, gW = *gw;
+    const int lm = lane & 31, lh = lane >> 5;
+    uint8_t *band = lds + wave * Band::BYTES;
+    const bool vec = ((N * ES) & 15) == 0;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int64_t col = n0 + wn * 128 + j * 32 + (lane & 31);
-        if (col >= N) continue;
+    for (int h = 0; h < 2; h++) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
+        for (int ii = 0; ii < 2; ii++) {
+            const int i = 2 * h + ii;
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int64_t row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (row >= M) continue;
-                const float v = (acc[i][j][r] * gA) * gW;
-                const int64_t o = row * N + col;
-                if constexpr (OUT == 0)
-                    static_cast<float *>(y)[o] = v;
-                else
-                    static_cast<uint16_t *>(y)[o] = (uint16_t)f32_to_bf16(v);
+            for (int j = 0; j < 4; j++) {
+#pragma unroll
+                for (int g = 0; g < 4; g++) {
+                    uint8_t *dst = band + (ii * 32 + lm) * Band::STRIDE + (j * 32 + 8 * g + 4 * lh) * ES;
+                    float v4[4];
+#pragma unroll
+                    for (int e = 0; e < 4; e++) v4[e] = (acc[i][j][4 * g + e] * gA) * gW;
+                    if constexpr (OUT == 0)
+                        *reinterpret_cast<float4 *>(dst) = make_float4(v4[0], v4[1], v4[2], v4[3]);
+                    else
+                        *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3]));
+                }
             }
         }
+        epi_band_to_global<ES>(band, y, M, N, m0 + wm * 128 + h * 64, n0 + wn * 128, lane, vec);
     }
 }
 
