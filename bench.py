@@ -40,7 +40,7 @@ def parse():
     p.add_argument("--out-dtype", choices=["bf16", "f32"], default="bf16",
                    help="GEMM output type (bf16 feeds the next layer; f32 is the parity contract)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=96,
+    p.add_argument("--cpu-rows", type=int, default=512,
                    help="rows of the qkv linear the oracle runs for the CPU baseline")
     return p.parse_args()
 

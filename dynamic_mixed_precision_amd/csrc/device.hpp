@@ -42,6 +42,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }
 
+// Same result as pack_bf16x2 for every non-NaN input, in one instruction
+// (gfx950 v_cvt_pk_bf16_f32, round to nearest even; checked against
+// f32_to_bf16 on all finite and infinite fp32 patterns).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+    typedef float v2f __attribute__((ext_vector_type(2)));
+    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+    const v2bf r = __builtin_convertvector((v2f){lo, hi}, v2bf);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
 // Unpack 16 bf16 (two 16-byte words) into fp32.
 __device__ __forceinline__ void unpack16(const uint4 &a, const uint4 &b, float v[16]) {
     const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};

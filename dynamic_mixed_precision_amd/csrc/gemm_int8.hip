@@ -167,7 +167,7 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(
                         if constexpr (OUT == 0)
                             *reinterpret_cast<float4 *>(dst) = make_float4(v4[0], v4[1], v4[2], v4[3]);
                         else
-                            *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3]));
+                            *reinterpret_cast<uint2 *>(dst) = make_uint2(cvt_pk_bf16(v4[0], v4[1]), cvt_pk_bf16(v4[2], v4[3]));
                     }
                 }
             }
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_dma_kernel(
                         if constexpr (OUT == 0)
                             *reinterpret_cast<float4 *>(dst) = make_float4(v4[0], v4[1], v4[2], v4[3]);
                         else
-                            *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3]));
+                            *reinterpret_cast<uint2 *>(dst) = make_uint2(cvt_pk_bf16(v4[0], v4[1]), cvt_pk_bf16(v4[2], v4[3]));
                     }
                 }
             }

@@ -19,8 +19,9 @@
 // Tiling: 256 threads = 2 x 2 waves, workgroup tile 256 x 256, wave tile
 // 128 x 128 = 4 x 4 MFMA 32x32x16 tiles.  K advances 64 elements (4 scale
 // groups) per stage through a double-buffered LDS (fp16 rows of 128 bytes
-// padded to 144); the next stage's codes and scales are in flight during the
-// current stage's MFMAs.
+// padded to 144).  While the MFMAs of stage kt run, the next stage is
+// dequantized into the other LDS buffer in four parts placed between the
+// four k-steps, and the codes of stage kt+2 are loaded into registers.
 #include "device.hpp"
 #include "gemm_common.hpp"
 #include "internal.hpp"
@@ -58,6 +59,65 @@ __device__ __forceinline__ void dequant32(const uint4 c, uint32_t s01, uint32_t 
     }
 }
 
+// As dequant32, with the two E4M3 scale codes in the low 16 bits of s01
+// decoded by v_cvt_scalef32_pk_f16_fp8 (scale 1.0; every finite OCP E4M3
+// value is exact in fp16).
+__device__ __forceinline__ void dequant32_fast(const uint4 c, uint32_t s01, uint32_t out[16]) {
+    const v2h s = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s01, 1.0f, false);
+    const v2h s0 = __builtin_shufflevector(s, s, 0, 0);
+    const v2h s1 = __builtin_shufflevector(s, s, 1, 1);
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const v2h sc = i < 2 ? s0 : s1;
+        out[4 * i + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 0) * sc);
+        out[4 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 1) * sc);
+        out[4 * i + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 2) * sc);
+        out[4 * i + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 3) * sc);
+    }
+}
+
+// Epilogue shared by the NVFP4 kernels (operands swapped as in the INT8
+// GEMM): lane l owns activation row m = l % 32 of A-subtile i and four
+// consecutive output columns 8g + 4*(l/32) + 0..3 of W-subtile j per register
+// group g.  y = (acc * gA) * gW, staged per wave through LDS in two 64-row
+// bands and stored row-contiguous.  Callers end their main loop with a
+// barrier, so the stage buffers are free.
+template <int OUT>
+__device__ __forceinline__ void fp4_epilogue(v16f (&acc)[4][4], uint8_t *lds, const float *ga,
+                                             const float *gw, int64_t M, int64_t N, int64_t m0,
+                                             int64_t n0, int wave, int wm, int wn, int lane,
+                                             void *y) {
+    constexpr int ES = OUT == 1 ? 2 : 4;
+    using Band = EpiBand<ES>;
+    const float gA = *ga, gW = *gw;
+    const int lm = lane & 31, lh = lane >> 5;
+    uint8_t *band = lds + wave * Band::BYTES;
+    const bool vec = ((N * ES) & 15) == 0;
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ii++) {
+            const int i = 2 * h + ii;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+#pragma unroll
+                for (int g = 0; g < 4; g++) {
+                    uint8_t *dst = band + (ii * 32 + lm) * Band::STRIDE + (j * 32 + 8 * g + 4 * lh) * ES;
+                    float v4[4];
+#pragma unroll
+                    for (int e = 0; e < 4; e++) v4[e] = (acc[i][j][4 * g + e] * gA) * gW;
+                    if constexpr (OUT == 0)
+                        *reinterpret_cast<float4 *>(dst) = make_float4(v4[0], v4[1], v4[2], v4[3]);
+                    else
+                        *reinterpret_cast<uint2 *>(dst) = make_uint2(cvt_pk_bf16(v4[0], v4[1]), cvt_pk_bf16(v4[2], v4[3]));
+                }
+            }
+        }
+        epi_band_to_global<ES>(band, y, M, N, m0 + wm * 128 + h * 64, n0 + wn * 128, lane, vec);
+    }
+}
+
 template <int OUT>
 __global__ __launch_bounds__(256, 1) void gemm_fp4_f16_kernel(
     const uint8_t *__restrict__ ca, const uint8_t *__restrict__ sa, const float *__restrict__ ga,
@@ -81,18 +141,18 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_f16_kernel(
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
-    // staging: chunk c = tid + 256*h (h = 0, 1) is row c/2, k-half c%2 of the
-    // stage (16 code bytes = 32 elements = 2 scale groups).  Out-of-range
-    // groups read a clamped in-range address; bits of `ok` record which groups
-    // are real and the zeroing is applied when the chunk is dequantized into
-    // LDS, after the stage's MFMAs have been issued.
-    uint2 rca[2][2], rcw[2][2];
-    uint32_t rsa[2][2], rsw[2][2];
-    uint32_t ok = 0u;  // bit 4h+q: A group q (0,1), W group q (2,3) of chunk h
+    // Staging: chunk c = tid + 256*h (h = 0, 1) is row c/2, k-half c%2 of a
+    // stage (16 code bytes = 32 elements = 2 scale groups).  Two register sets
+    // (stage s lives in set s & 1) keep the global loads one full stage ahead.
+    // Out-of-range groups read a clamped in-range address and a bit of `ok`
+    // records whether they are real; zeroing happens at dequant time.
+    uint2 rca0[2][2], rcw0[2][2], rca1[2][2], rcw1[2][2];
+    uint32_t rsa0[2][2], rsw0[2][2], rsa1[2][2], rsw1[2][2];
+    uint32_t ok0 = 0u, ok1 = 0u;  // bit 4h+q: A group q, bit 4h+2+q: W group q
     const int nk = (int)((nb + 3) / 4);
 
-#define DMPQ_F4_GLOAD(g0)                                                                     \
-    ok = 0u;                                                                                  \
+#define DMPQ_F4_GLOAD(SET, g0)                                                                \
+    ok##SET = 0u;                                                                             \
     _Pragma("unroll") for (int h = 0; h < 2; h++) {                                           \
         const int c = tid + 256 * h;                                                          \
         const int r = c >> 1;                                                                 \
@@ -101,101 +161,224 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_f16_kernel(
         _Pragma("unroll") for (int q = 0; q < 2; q++) {                                       \
             const int64_t gi = (g0) + 2 * (c & 1) + q;                                        \
             const int64_t gic = gi < nb ? gi : nb - 1;                                        \
-            rca[h][q] = *reinterpret_cast<const uint2 *>(ca + gmc * rb + 8 * gic);            \
-            rcw[h][q] = *reinterpret_cast<const uint2 *>(cw + gnc * rb + 8 * gic);            \
-            rsa[h][q] = sa[gmc * nb + gic];                                                   \
-            rsw[h][q] = sw[gnc * nb + gic];                                                   \
-            ok |= (uint32_t)(gm < M && gi < nb) << (4 * h + q);                               \
-            ok |= (uint32_t)(gn < N && gi < nb) << (4 * h + 2 + q);                           \
+            rca##SET[h][q] = *reinterpret_cast<const uint2 *>(ca + gmc * rb + 8 * gic);       \
+            rcw##SET[h][q] = *reinterpret_cast<const uint2 *>(cw + gnc * rb + 8 * gic);       \
+            rsa##SET[h][q] = sa[gmc * nb + gic];                                              \
+            rsw##SET[h][q] = sw[gnc * nb + gic];                                              \
+            ok##SET |= (uint32_t)(gm < M && gi < nb) << (4 * h + q);                          \
+            ok##SET |= (uint32_t)(gn < N && gi < nb) << (4 * h + 2 + q);                      \
         }                                                                                     \
     }
-#define DMPQ_F4_SSTORE(buf)                                                                   \
-    _Pragma("unroll") for (int h = 0; h < 2; h++) {                                           \
+    // Dequantize one quarter of a staged stage (part p: A/W of chunk h = p/2)
+    // into LDS buffer buf.
+#define DMPQ_F4_DQ(SET, buf, p)                                                               \
+    {                                                                                         \
+        const int h = (p) >> 1, isw = (p) & 1;                                                \
         const int c = tid + 256 * h;                                                          \
         const int r = c >> 1;                                                                 \
-        uint8_t *pa = lds + (buf) * STAGE + r * ROW + (c & 1) * 64;                           \
-        uint8_t *pw = lds + (buf) * STAGE + (BM + r) * ROW + (c & 1) * 64;                    \
-        const bool a0 = (ok >> (4 * h)) & 1u, a1 = (ok >> (4 * h + 1)) & 1u;                  \
-        const bool w0 = (ok >> (4 * h + 2)) & 1u, w1 = (ok >> (4 * h + 3)) & 1u;              \
+        uint8_t *dst = lds + (buf) * STAGE + ((isw ? BM : 0) + r) * ROW + (c & 1) * 64;       \
+        const uint2 *cc = isw ? rcw##SET[h] : rca##SET[h];                                    \
+        const uint32_t *ss = isw ? rsw##SET[h] : rsa##SET[h];                                 \
+        const bool k0 = (ok##SET >> (4 * h + 2 * isw)) & 1u;                                  \
+        const bool k1 = (ok##SET >> (4 * h + 2 * isw + 1)) & 1u;                              \
         uint32_t d[16];                                                                       \
-        dequant32(make_uint4(a0 ? rca[h][0].x : 0u, a0 ? rca[h][0].y : 0u,                    \
-                             a1 ? rca[h][1].x : 0u, a1 ? rca[h][1].y : 0u),                   \
-                  (a0 ? rsa[h][0] : 0u) | ((a1 ? rsa[h][1] : 0u) << 8), d);                   \
+        dequant32(make_uint4(k0 ? cc[0].x : 0u, k0 ? cc[0].y : 0u, k1 ? cc[1].x : 0u,         \
+                             k1 ? cc[1].y : 0u),                                              \
+                  (k0 ? ss[0] : 0u) | ((k1 ? ss[1] : 0u) << 8), d);                           \
         _Pragma("unroll") for (int q = 0; q < 4; q++)                                         \
-            *reinterpret_cast<uint4 *>(pa + 16 * q) = make_uint4(d[4 * q], d[4 * q + 1], d[4 * q + 2], d[4 * q + 3]); \
-        dequant32(make_uint4(w0 ? rcw[h][0].x : 0u, w0 ? rcw[h][0].y : 0u,                    \
-                             w1 ? rcw[h][1].x : 0u, w1 ? rcw[h][1].y : 0u),                   \
-                  (w0 ? rsw[h][0] : 0u) | ((w1 ? rsw[h][1] : 0u) << 8), d);                   \
-        _Pragma("unroll") for (int q = 0; q < 4; q++)                                         \
-            *reinterpret_cast<uint4 *>(pw + 16 * q) = make_uint4(d[4 * q], d[4 * q + 1], d[4 * q + 2], d[4 * q + 3]); \
+            *reinterpret_cast<uint4 *>(dst + 16 * q) =                                        \
+                make_uint4(d[4 * q], d[4 * q + 1], d[4 * q + 2], d[4 * q + 3]);               \
+    }
+    // Fragments of k-step s (16 k-elements = 32 bytes) of LDS buffer buf.
+#define DMPQ_F4_FRAG(dsta, dstb, buf, s)                                                      \
+    {                                                                                         \
+        const uint8_t *As = lds + (buf) * STAGE + (wm * 128 + (lane & 31)) * ROW + (lane >> 5) * 16 + 32 * (s); \
+        const uint8_t *Ws = lds + (buf) * STAGE + (BM + wn * 128 + (lane & 31)) * ROW + (lane >> 5) * 16 + 32 * (s); \
+        _Pragma("unroll") for (int i = 0; i < 4; i++) {                                       \
+            dsta[i] = *reinterpret_cast<const v8h *>(As + i * 32 * ROW);                      \
+            dstb[i] = *reinterpret_cast<const v8h *>(Ws + i * 32 * ROW);                      \
+        }                                                                                     \
+    }
+#define DMPQ_F4_MFMA(fa, fb)                                                                  \
+    _Pragma("unroll") for (int i = 0; i < 4; i++)                                             \
+        _Pragma("unroll") for (int j = 0; j < 4; j++)                                         \
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+    // One stage kt (parity P): first the global loads of stage kt+2 into
+    // register set P (its stage kt was dequantized during stage kt-1), then the
+    // MFMAs on LDS buffer P interleaved with the dequant of stage kt+1
+    // (register set 1-P) into LDS buffer 1-P.
+#define DMPQ_F4_ITER(P, Q)                                                                    \
+    {                                                                                         \
+        v8h fa0[4], fb0[4], fa1[4], fb1[4];                                                   \
+        const bool more = kt + 1 < nk;                                                        \
+        if (kt + 2 < nk) {                                                                    \
+            DMPQ_F4_GLOAD(P, (int64_t)(kt + 2) * 4)                                           \
+        }                                                                                     \
+        DMPQ_F4_FRAG(fa0, fb0, P, 0)                                                          \
+        DMPQ_F4_FRAG(fa1, fb1, P, 1)                                                          \
+        DMPQ_F4_MFMA(fa0, fb0)                                                                \
+        if (more) DMPQ_F4_DQ(Q, Q, 0)                                                         \
+        DMPQ_F4_FRAG(fa0, fb0, P, 2)                                                          \
+        DMPQ_F4_MFMA(fa1, fb1)                                                                \
+        if (more) DMPQ_F4_DQ(Q, Q, 1)                                                         \
+        DMPQ_F4_FRAG(fa1, fb1, P, 3)                                                          \
+        DMPQ_F4_MFMA(fa0, fb0)                                                                \
+        if (more) DMPQ_F4_DQ(Q, Q, 2)                                                         \
+        DMPQ_F4_MFMA(fa1, fb1)                                                                \
+        if (more) DMPQ_F4_DQ(Q, Q, 3)                                                         \
+        __syncthreads();                                                                      \
     }
 
-    DMPQ_F4_GLOAD(0)
-    DMPQ_F4_SSTORE(0)
+    DMPQ_F4_GLOAD(0, 0)
+    if (nk > 1) {
+        DMPQ_F4_GLOAD(1, 4)
+    }
+    DMPQ_F4_DQ(0, 0, 0)
+    DMPQ_F4_DQ(0, 0, 1)
+    DMPQ_F4_DQ(0, 0, 2)
+    DMPQ_F4_DQ(0, 0, 3)
     __syncthreads();
-
-    for (int kt = 0; kt < nk; kt++) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            DMPQ_F4_GLOAD((int64_t)(kt + 1) * 4)
-        }
-        const uint8_t *As = lds + cur * STAGE + (wm * 128 + (lane & 31)) * ROW + (lane >> 5) * 16;
-        const uint8_t *Ws = lds + cur * STAGE + (BM + wn * 128 + (lane & 31)) * ROW + (lane >> 5) * 16;
-#pragma unroll
-        for (int ks = 0; ks < BKE * 2; ks += 32) {  // 16 k-elements = 32 bytes per step
-            v8h a[4], b[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                a[i] = *reinterpret_cast<const v8h *>(As + i * 32 * ROW + ks);
-                b[i] = *reinterpret_cast<const v8h *>(Ws + i * 32 * ROW + ks);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-#pragma unroll
-                for (int j = 0; j < 4; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[j], a[i], acc[i][j], 0, 0, 0);
-        }
-        if (more) {
-            DMPQ_F4_SSTORE(cur ^ 1)
-        }
-        __syncthreads();
+    // Stage kt uses LDS buffer kt & 1; stage kt+1 is dequantized from register
+    // set (kt+1) & 1; stage kt+2 is loaded into set kt & 1 (already consumed).
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        DMPQ_F4_ITER(0, 1)
+        kt++;
+        DMPQ_F4_ITER(1, 0)
+        kt--;
     }
+    if (kt < nk) DMPQ_F4_ITER(0, 1)
 #undef DMPQ_F4_GLOAD
-#undef DMPQ_F4_SSTORE
+#undef DMPQ_F4_DQ
+#undef DMPQ_F4_FRAG
+#undef DMPQ_F4_MFMA
+#undef DMPQ_F4_ITER
 
-    // Epilogue (operands swapped as in the INT8 GEMM): lane l owns activation
-    // row m = l % 32 of A-subtile i and four consecutive output columns
-    // 8g + 4*(l/32) + 0..3 of W-subtile j per register group g.  Staged per
-    // wave through LDS in two 64-row bands and stored row-contiguous.
-    constexpr int ES = OUT == 1 ? 2 : 4;
-    using Band = EpiBand<ES>;
-    const float gA = *ga, gW = *gw;
-    const int lm = lane & 31, lh = lane >> 5;
-    uint8_t *band = lds + wave * Band::BYTES;
-    const bool vec = ((N * ES) & 15) == 0;
+    fp4_epilogue<OUT>(acc, lds, ga, gw, M, N, m0, n0, wave, wm, wn, lane, y);
+}
+
+// ---------------------------------------------------------------------------
+// Fast path for K % 64 == 0 (every stage is full): no K tail to zero, and
+// rows past M or N only feed outputs that are never stored, so operands load
+// from clamped rows without any masking.  Each staged chunk is one 16-byte
+// code load and one 2-byte scale load from per-lane pointers fixed for the
+// whole K loop; scales are decoded by the hardware fp8 converter.
+// ---------------------------------------------------------------------------
+template <int OUT>
+__global__ __launch_bounds__(256, 1) void gemm_fp4_fast_kernel(
+    const uint8_t *__restrict__ ca, const uint8_t *__restrict__ sa, const float *__restrict__ ga,
+    const uint8_t *__restrict__ cw, const uint8_t *__restrict__ sw, const float *__restrict__ gw,
+    int64_t M, int64_t N, int64_t K, void *__restrict__ y, unsigned tiles_m, unsigned tiles_n) {
+    using namespace fp4gemm;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const TileCoord tc = tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, GROUP_M);
+    const int64_t m0 = (int64_t)tc.m * BM, n0 = (int64_t)tc.n * BN;
+    const int64_t nb = K / 16, rb = K / 2;
+    const int nk = (int)(nb / 4);
+
+    v16f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
+
+    // chunk h (h = 0, 1) of this thread: row (tid + 256h) / 2, k-half tid % 2
+    const uint8_t *pa[2], *pw[2], *qa[2], *qw[2];
 #pragma unroll
     for (int h = 0; h < 2; h++) {
-#pragma unroll
-        for (int ii = 0; ii < 2; ii++) {
-            const int i = 2 * h + ii;
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-#pragma unroll
-                for (int g = 0; g < 4; g++) {
-                    uint8_t *dst = band + (ii * 32 + lm) * Band::STRIDE + (j * 32 + 8 * g + 4 * lh) * ES;
-                    float v4[4];
-#pragma unroll
-                    for (int e = 0; e < 4; e++) v4[e] = (acc[i][j][4 * g + e] * gA) * gW;
-                    if constexpr (OUT == 0)
-                        *reinterpret_cast<float4 *>(dst) = make_float4(v4[0], v4[1], v4[2], v4[3]);
-                    else
-                        *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3]));
-                }
-            }
-        }
-        epi_band_to_global<ES>(band, y, M, N, m0 + wm * 128 + h * 64, n0 + wn * 128, lane, vec);
+        const int c = tid + 256 * h, r = c >> 1;
+        const int64_t gm = m0 + r < M ? m0 + r : M - 1;
+        const int64_t gn = n0 + r < N ? n0 + r : N - 1;
+        pa[h] = ca + gm * rb + 16 * (c & 1);
+        pw[h] = cw + gn * rb + 16 * (c & 1);
+        qa[h] = sa + gm * nb + 2 * (c & 1);
+        qw[h] = sw + gn * nb + 2 * (c & 1);
     }
+    uint4 xa0[2], xw0[2], xa1[2], xw1[2];
+    uint32_t ya0[2], yw0[2], ya1[2], yw1[2];
+
+#define DMPQ_F4F_GLOAD(SET, st)                                                                \
+    _Pragma("unroll") for (int h = 0; h < 2; h++) {                                            \
+        xa##SET[h] = *reinterpret_cast<const uint4 *>(pa[h] + 32 * (int64_t)(st));             \
+        xw##SET[h] = *reinterpret_cast<const uint4 *>(pw[h] + 32 * (int64_t)(st));             \
+        ya##SET[h] = *reinterpret_cast<const uint16_t *>(qa[h] + 4 * (int64_t)(st));           \
+        yw##SET[h] = *reinterpret_cast<const uint16_t *>(qw[h] + 4 * (int64_t)(st));           \
+    }
+#define DMPQ_F4F_DQ(SET, buf, p)                                                               \
+    {                                                                                          \
+        const int h = (p) >> 1, isw = (p) & 1;                                                 \
+        const int c = tid + 256 * h;                                                           \
+        uint8_t *dst = lds + (buf) * STAGE + ((isw ? BM : 0) + (c >> 1)) * ROW + (c & 1) * 64; \
+        uint32_t d[16];                                                                        \
+        dequant32_fast(isw ? xw##SET[h] : xa##SET[h], isw ? yw##SET[h] : ya##SET[h], d);       \
+        _Pragma("unroll") for (int q = 0; q < 4; q++)                                          \
+            *reinterpret_cast<uint4 *>(dst + 16 * q) =                                         \
+                make_uint4(d[4 * q], d[4 * q + 1], d[4 * q + 2], d[4 * q + 3]);                \
+    }
+#define DMPQ_F4F_FRAG(dsta, dstb, buf, s)                                                      \
+    {                                                                                          \
+        const uint8_t *As = lds + (buf) * STAGE + (wm * 128 + (lane & 31)) * ROW + (lane >> 5) * 16 + 32 * (s); \
+        const uint8_t *Ws = lds + (buf) * STAGE + (BM + wn * 128 + (lane & 31)) * ROW + (lane >> 5) * 16 + 32 * (s); \
+        _Pragma("unroll") for (int i = 0; i < 4; i++) {                                        \
+            dsta[i] = *reinterpret_cast<const v8h *>(As + i * 32 * ROW);                       \
+            dstb[i] = *reinterpret_cast<const v8h *>(Ws + i * 32 * ROW);                       \
+        }                                                                                      \
+    }
+#define DMPQ_F4F_MFMA(fa, fb)                                                                  \
+    _Pragma("unroll") for (int i = 0; i < 4; i++)                                              \
+        _Pragma("unroll") for (int j = 0; j < 4; j++)                                          \
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+#define DMPQ_F4F_ITER(P, Q)                                                                    \
+    {                                                                                          \
+        v8h fa0[4], fb0[4], fa1[4], fb1[4];                                                    \
+        const bool more = kt + 1 < nk;                                                         \
+        if (kt + 2 < nk) {                                                                     \
+            DMPQ_F4F_GLOAD(P, kt + 2)                                                          \
+        }                                                                                      \
+        DMPQ_F4F_FRAG(fa0, fb0, P, 0)                                                          \
+        DMPQ_F4F_FRAG(fa1, fb1, P, 1)                                                          \
+        DMPQ_F4F_MFMA(fa0, fb0)                                                                \
+        if (more) DMPQ_F4F_DQ(Q, Q, 0)                                                         \
+        DMPQ_F4F_FRAG(fa0, fb0, P, 2)                                                          \
+        DMPQ_F4F_MFMA(fa1, fb1)                                                                \
+        if (more) DMPQ_F4F_DQ(Q, Q, 1)                                                         \
+        DMPQ_F4F_FRAG(fa1, fb1, P, 3)                                                          \
+        DMPQ_F4F_MFMA(fa0, fb0)                                                                \
+        if (more) DMPQ_F4F_DQ(Q, Q, 2)                                                         \
+        DMPQ_F4F_MFMA(fa1, fb1)                                                                \
+        if (more) DMPQ_F4F_DQ(Q, Q, 3)                                                         \
+        __syncthreads();                                                                       \
+    }
+
+    DMPQ_F4F_GLOAD(0, 0)
+    if (nk > 1) {
+        DMPQ_F4F_GLOAD(1, 1)
+    }
+    DMPQ_F4F_DQ(0, 0, 0)
+    DMPQ_F4F_DQ(0, 0, 1)
+    DMPQ_F4F_DQ(0, 0, 2)
+    DMPQ_F4F_DQ(0, 0, 3)
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        DMPQ_F4F_ITER(0, 1)
+        kt++;
+        DMPQ_F4F_ITER(1, 0)
+        kt--;
+    }
+    if (kt < nk) DMPQ_F4F_ITER(0, 1)
+#undef DMPQ_F4F_GLOAD
+#undef DMPQ_F4F_DQ
+#undef DMPQ_F4F_FRAG
+#undef DMPQ_F4F_MFMA
+#undef DMPQ_F4F_ITER
+
+    fp4_epilogue<OUT>(acc, lds, ga, gw, M, N, m0, n0, wave, wm, wn, lane, y);
 }
 
 template <class KernelFn>
@@ -213,17 +396,24 @@ hipError_t launch_gemm_nvfp4(hipStream_t s, const uint8_t *ca, const uint8_t *sa
     if (M == 0 || N == 0) return hipSuccess;
     static const hipError_t attr = [] {
         hipError_t e = allow_lds(gemm_fp4_f16_kernel<0>, 2 * STAGE);
-        return e != hipSuccess ? e : allow_lds(gemm_fp4_f16_kernel<1>, 2 * STAGE);
+        if (e == hipSuccess) e = allow_lds(gemm_fp4_f16_kernel<1>, 2 * STAGE);
+        if (e == hipSuccess) e = allow_lds(gemm_fp4_fast_kernel<0>, 2 * STAGE);
+        if (e == hipSuccess) e = allow_lds(gemm_fp4_fast_kernel<1>, 2 * STAGE);
+        return e;
     }();
     if (attr != hipSuccess) return attr;
     const int64_t tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
     const dim3 grid((unsigned)(tm * tn)), block(256);
-    if (out_dtype == 0)
-        hipLaunchKernelGGL(gemm_fp4_f16_kernel<0>, grid, block, 2 * STAGE, s, ca, sa, ga, cw, sw,
-                           gw, M, N, K, y, (unsigned)tm, (unsigned)tn);
+    const unsigned utm = (unsigned)tm, utn = (unsigned)tn;
+    const bool fast = K % (4 * 16) == 0;
+    if (fast && out_dtype == 0)
+        hipLaunchKernelGGL(gemm_fp4_fast_kernel<0>, grid, block, 2 * STAGE, s, ca, sa, ga, cw, sw, gw, M, N, K, y, utm, utn);
+    else if (fast)
+        hipLaunchKernelGGL(gemm_fp4_fast_kernel<1>, grid, block, 2 * STAGE, s, ca, sa, ga, cw, sw, gw, M, N, K, y, utm, utn);
+    else if (out_dtype == 0)
+        hipLaunchKernelGGL(gemm_fp4_f16_kernel<0>, grid, block, 2 * STAGE, s, ca, sa, ga, cw, sw, gw, M, N, K, y, utm, utn);
     else
-        hipLaunchKernelGGL(gemm_fp4_f16_kernel<1>, grid, block, 2 * STAGE, s, ca, sa, ga, cw, sw,
-                           gw, M, N, K, y, (unsigned)tm, (unsigned)tn);
+        hipLaunchKernelGGL(gemm_fp4_f16_kernel<1>, grid, block, 2 * STAGE, s, ca, sa, ga, cw, sw, gw, M, N, K, y, utm, utn);
     return hipGetLastError();
 }
 

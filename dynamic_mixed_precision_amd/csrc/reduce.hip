@@ -49,15 +49,6 @@ __device__ void block_partials(double (&s)[NS], double *partial) {
         partial[(size_t)blockIdx.x * NS + tid] = (red[tid][0] + red[tid][1]) + (red[tid][2] + red[tid][3]);
 }
 
-// bf16 RNE of two fp32 values packed low/high, with the gfx950 converter
-// (v_cvt_pk_bf16_f32), which matches round-to-nearest-even on every finite
-// input.
-__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
-    typedef float v2f __attribute__((ext_vector_type(2)));
-    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-    const v2bf r = __builtin_convertvector((v2f){lo, hi}, v2bf);
-    return __builtin_bit_cast(uint32_t, r);
-}
 
 }  // namespace
 
@@ -162,10 +153,10 @@ __global__ __launch_bounds__(256) void tdc_skip_kernel(const uint16_t *__restric
         to8(ld16(xin + 8 * c), a);
         to8(ld16(delta + 8 * c), d);
         uint4 o;
-        o.x = cvt_bf16x2(a[0] + d[0], a[1] + d[1]);
-        o.y = cvt_bf16x2(a[2] + d[2], a[3] + d[3]);
-        o.z = cvt_bf16x2(a[4] + d[4], a[5] + d[5]);
-        o.w = cvt_bf16x2(a[6] + d[6], a[7] + d[7]);
+        o.x = cvt_pk_bf16(a[0] + d[0], a[1] + d[1]);
+        o.y = cvt_pk_bf16(a[2] + d[2], a[3] + d[3]);
+        o.z = cvt_pk_bf16(a[4] + d[4], a[5] + d[5]);
+        o.w = cvt_pk_bf16(a[6] + d[6], a[7] + d[7]);
         store_nt16(xout + 8 * c, o);
     }
     if (blockIdx.x == 0 && threadIdx.x < n - 8 * nch) {
@@ -201,7 +192,7 @@ __device__ __forceinline__ void refresh8(const uint4 &ia, const uint4 &oa, const
 #pragma unroll
     for (int i = 0; i < 8; i++) dn[i] = b[i] - a[i];
 #pragma unroll
-    for (int i = 0; i < 4; i++) w[i] = cvt_bf16x2(dn[2 * i], dn[2 * i + 1]);
+    for (int i = 0; i < 4; i++) w[i] = cvt_pk_bf16(dn[2 * i], dn[2 * i + 1]);
 #pragma unroll
     for (int i = 0; i < 8; i++) {
         f1 += __builtin_fabsf(dn[i]);
