@@ -1,0 +1,92 @@
+"""GPU parity of the routed hot path on the CogVideoX-like configurations.
+
+5B-like (17776 tokens, hidden 3072): four synthetic blocks with Gamma about
+0.05, 0.40, 0.05, 0.40 route (alpha = 1, beta = 0, tau = 0.2) to NVFP4, INT8,
+NVFP4, INT8; the Gamma sums, routes, activation quantization (every row) and
+the GEMM (row sample) of each block's linears match the oracle.
+1080p-like (106306 tokens): the FFN-up linear (12288 x 3072) on both routes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dynamic_mixed_precision_amd as dm
+import workloads as wl
+from gpu_util import dev, empty, host, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _rows(M, step):
+    return np.unique(np.concatenate([np.arange(0, M, step), np.arange(M - 3, M)]))
+
+
+def _linear_parity(orc, rng, M, N, K, route, rows):
+    x = wl.activations(rng, M, K)
+    w = wl.weight(rng, N, K)
+    p = orc.prep_weight(w)
+    ws = dm.new_workspace(dm.OP_QUANT_NVFP4)
+    cw, sw = dev(p["cw"]), dev(p["sw"])
+    gw = dev(np.array([p["gw"]], np.float32))
+    y = empty((M, N), np.float32)
+    xd = dev(x)
+    sel = torch.from_numpy(rows).cuda()
+    if route == dm.ROUTE_INT8:
+        q, s = empty((M, K), np.int8), empty((M,), np.float32)
+        dm.hadamard_quant_int8(xd, q, s)
+        dm.qgemm_int8(q, s, dev(p["qw"]), dev(p["sw_row"]), y)
+        torch.cuda.synchronize()
+        q0, s0 = orc.quant_int8(x)
+        assert np.array_equal(host(q), q0) and np.array_equal(host(s).view(np.uint32), s0.view(np.uint32))
+        _, y0 = orc.gemm_int8(q0, s0, p["qw"], p["sw_row"], rows=rows)
+        assert np.array_equal(host(y[sel]).view(np.uint32), y0.view(np.uint32))
+    else:
+        c, sc, g = empty((M, K // 2), np.uint8), empty((M, K // 16), np.uint8), torch.zeros(1, device="cuda")
+        dm.hadamard_quant_nvfp4(xd, c, sc, g, ws)
+        dm.qgemm_nvfp4(c, sc, g, cw, sw, gw, y)
+        torch.cuda.synchronize()
+        c0, sc0, g0 = orc.quant_nvfp4(x)
+        assert np.array_equal(host(c), c0) and np.array_equal(host(sc), sc0) and float(host(g)[0]) == g0
+        y0, b0 = orc.gemm_nvfp4(c0, sc0, g0, p["cw"], p["sw"], p["gw"], rows=rows)
+        assert np.all(np.abs(host(y[sel]).astype(np.float64) - y0) <= 1e-5 * b0)
+
+
+def test_cogvideox5b_routing_and_linears(orc):
+    require_gpu()
+    cfg = wl.COGVIDEOX_5B
+    M, H = cfg.M, cfg.hidden
+    alpha = np.full(4, wl.ROUTER_5B["alpha"])
+    beta = np.full(4, wl.ROUTER_5B["beta"])
+    tau = wl.ROUTER_5B["tau"]
+    ws = dm.new_workspace(dm.OP_GAMMA)
+    routes = []
+    for b, seed in enumerate(cfg.seeds):
+        say(f"5B-like block {b}: gamma + route")
+        rng = np.random.default_rng(seed)
+        x_in = wl.activations(rng, M, H)
+        x_out = wl.perturbed_output(rng, x_in, wl.GAMMA_TARGETS_5B[b])
+        s = torch.zeros(2, dtype=torch.float64, device="cuda")
+        dm.gamma_sums(dev(x_in), dev(x_out), s, ws)
+        torch.cuda.synchronize()
+        s0 = orc.gamma_sums(x_in, x_out)
+        assert np.all(np.abs(host(s) - s0) <= 1e-6 * s0)
+        g, e, r = dm.gate_and_route(host(s), alpha, beta, tau)
+        _, e0, r0 = orc.route(s0, alpha, beta, tau)
+        assert np.array_equal(r, r0)
+        assert abs(g - wl.GAMMA_TARGETS_5B[b]) < 0.01       # the synthetic Gamma hits its target
+        routes.append(int(r[0]))
+    assert routes == [dm.ROUTE_NVFP4, dm.ROUTE_INT8, dm.ROUTE_NVFP4, dm.ROUTE_INT8]
+    # each route on every 5B linear shape, full token count, sampled GEMM rows
+    for li, lin in enumerate(cfg.linears):
+        for route in (dm.ROUTE_NVFP4, dm.ROUTE_INT8):
+            say(f"5B-like linear {lin.name} N={lin.N} K={lin.K} route={route}")
+            _linear_parity(orc, np.random.default_rng(100 + 10 * li + route), M, lin.N, lin.K,
+                           route, _rows(M, 1481))
+
+
+@pytest.mark.parametrize("route", [0, 1])
+def test_1080p_ffn_up_linear(orc, route):
+    require_gpu()
+    M, N, K = wl.M_1080P, 12288, 3072
+    say(f"1080p-like ffn_up M={M} N={N} K={K} route={route}")
+    _linear_parity(orc, np.random.default_rng(1080 + route), M, N, K, route, _rows(M, 8861))
