@@ -24,6 +24,7 @@ NO_HADAMARD = 1
 W8_FROM_NVFP4, W8_DIRECT = 0, 1
 TDC_SKIP, TDC_REFRESH = 0, 1
 FP4_BF16_DEQUANT = 0
+FP4_SCALED_MFMA = 1
 OP_GAMMA, OP_QUANT_NVFP4, OP_TDC, OP_PREP_WEIGHT = 0, 1, 2, 3
 
 EXPORTS = ("dmpq_last_error", "dmpq_version", "dmpq_workspace_bytes", "dmpq_gamma_sums",

@@ -185,6 +185,8 @@ dmpq_status dmpq_qgemm_nvfp4(hipStream_t stream, const uint8_t *ca, const uint8_
                              const float *d_gw, int64_t M, int64_t N, int64_t K, int out_dtype,
                              void *y, int variant) {
     if (dmpq_status s = check_gemm(__func__, M, N, K)) return s;
+    if (variant == DMPQ_FP4_SCALED_MFMA && ((M + 127) / 128) * ((N + 127) / 128) > (int64_t)UINT32_MAX)
+        return fail(DMPQ_ERR_UNSUPPORTED, "%s: too many tiles", __func__);
     REQUIRE_PTR_N(ca, M);
     REQUIRE_PTR_N(sa, M);
     REQUIRE_PTR_N(d_ga, M * N);
@@ -194,7 +196,7 @@ dmpq_status dmpq_qgemm_nvfp4(hipStream_t stream, const uint8_t *ca, const uint8_
     REQUIRE_PTR_N(y, M * N);
     if (out_dtype != DMPQ_OUT_F32 && out_dtype != DMPQ_OUT_BF16)
         return fail(DMPQ_ERR_INVALID_ARG, "%s: unknown out_dtype %d", __func__, out_dtype);
-    if (variant != DMPQ_FP4_BF16_DEQUANT)
+    if (variant != DMPQ_FP4_BF16_DEQUANT && variant != DMPQ_FP4_SCALED_MFMA)
         return fail(DMPQ_ERR_INVALID_ARG, "%s: unknown variant %d", __func__, variant);
     return hip_status(launch_gemm_nvfp4(stream, ca, sa, d_ga, cw, sw, d_gw, M, N, K, out_dtype,
                                         y, variant),

@@ -381,6 +381,137 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_fast_kernel(
     fp4_epilogue<OUT>(acc, lds, ga, gw, M, N, m0, n0, wave, wm, wn, lane, y);
 }
 
+// ---------------------------------------------------------------------------
+// Variant DMPQ_FP4_SCALED_MFMA: gfx950's block-scaled MFMA
+// (v_mfma_scale_f32_32x32x64_f8f6f4, E2M1 operands) with the NVFP4 scales
+// applied exactly.  The instruction scales each 32-element K-slot by a power
+// of two (E8M0), which cannot represent an E4M3 scale, and it sums the
+// slots, so one 16-element group goes alone into one instruction (its codes
+// in the first half of slot 0, everything else zero, E8M0 scales 2^0).  That
+// yields the exact group partial P[m][n] = sum_k vA vW, which the VALU folds
+// in as acc += P * (sA[m,g] * sW[n,g]) in fp32 (the scale product is exact).
+// 1/4 of each MFMA's K carries data and the rescale costs two VALU ops per
+// output element per group; the in-LDS dequant (variant 0) is the faster
+// exact path on this chip.
+//
+// Tiling: 256 threads = 2 x 2 waves, workgroup tile 128 x 128, wave tile
+// 64 x 64 = 2 x 2 MFMA 32x32 tiles; 8 scale groups per LDS stage (codes
+// staged as bytes, scales decoded to fp32 once per workgroup).
+// ---------------------------------------------------------------------------
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+namespace fp4scaled {
+constexpr int BM = 128, BN = 128, G = 8;  // G scale groups per LDS stage
+}
+
+template <int OUT>
+__global__ __launch_bounds__(256) void gemm_fp4_scaled_kernel(
+    const uint8_t *__restrict__ ca, const uint8_t *__restrict__ sa, const float *__restrict__ ga,
+    const uint8_t *__restrict__ cw, const uint8_t *__restrict__ sw, const float *__restrict__ gw,
+    int64_t M, int64_t N, int64_t K, void *__restrict__ y, unsigned tiles_n) {
+    using namespace fp4scaled;
+    // [group][row]: a lane's 8-byte fragment read is row-contiguous (no bank conflicts)
+    __shared__ __attribute__((aligned(16))) uint2 codes_a[G][BM], codes_w[G][BN];
+    __shared__ __attribute__((aligned(16))) float sca[G][BM], scw[G][BN];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * BM, n0 = (int64_t)(blockIdx.x % tiles_n) * BN;
+    const int64_t nb = K / 16, rb = K / 2;
+
+    // staging role: row tid/2 of both tiles, groups 4*(tid&1) .. +3
+    const int sr = tid >> 1, sg = 4 * (tid & 1);
+    const int64_t gm = m0 + sr < M ? m0 + sr : M - 1;  // clamped; rows past M are never stored
+    const int64_t gn = n0 + sr < N ? n0 + sr : N - 1;
+
+    v16f acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
+
+    for (int64_t g0 = 0; g0 < nb; g0 += G) {
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int gl = sg + q;
+            const bool kin = g0 + gl < nb;
+            const int64_t gi = kin ? g0 + gl : nb - 1;
+            const uint2 a = *reinterpret_cast<const uint2 *>(ca + gm * rb + 8 * gi);
+            const uint2 w = *reinterpret_cast<const uint2 *>(cw + gn * rb + 8 * gi);
+            const float fa = e4m3_value(sa[gm * nb + gi]), fw = e4m3_value(sw[gn * nb + gi]);
+            codes_a[gl][sr] = kin ? a : make_uint2(0u, 0u);
+            codes_w[gl][sr] = kin ? w : make_uint2(0u, 0u);
+            sca[gl][sr] = kin ? fa : 0.0f;
+            scw[gl][sr] = kin ? fw : 0.0f;
+        }
+        __syncthreads();
+#pragma unroll 2
+        for (int gl = 0; gl < G; gl++) {
+            v8i fa[2], fb[2];
+            float s_a[2][16], s_w[2];
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                const int ra = wm * 64 + i * 32 + (lane & 31);
+                const int rw = wn * 64 + i * 32 + (lane & 31);
+                // lanes 32..63 carry K positions 32..63 of the instruction: zero
+                const uint2 a = codes_a[gl][ra], w = codes_w[gl][rw];
+                const bool lo = lane < 32;
+                fa[i] = (v8i){lo ? (int)a.x : 0, lo ? (int)a.y : 0, 0, 0, 0, 0, 0, 0};
+                fb[i] = (v8i){lo ? (int)w.x : 0, lo ? (int)w.y : 0, 0, 0, 0, 0, 0, 0};
+                s_w[i] = scw[gl][rw];
+#pragma unroll
+                for (int r4 = 0; r4 < 4; r4++) {
+                    const float4 v = *reinterpret_cast<const float4 *>(
+                        &sca[gl][wm * 64 + i * 32 + 8 * r4 + 4 * (lane >> 5)]);
+                    s_a[i][4 * r4 + 0] = v.x;
+                    s_a[i][4 * r4 + 1] = v.y;
+                    s_a[i][4 * r4 + 2] = v.z;
+                    s_a[i][4 * r4 + 3] = v.w;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+#pragma unroll
+                for (int j = 0; j < 2; j++) {
+                    const v16f zero = {};
+                    // format 4 = E2M1 for both operands, E8M0 scales 127 = 2^0
+                    const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        fa[i], fb[j], zero, 4, 4, 0, 127, 0, 127);
+#pragma unroll
+                    for (int r = 0; r < 16; r++) {
+                        // p (<= 576, a multiple of 1/4) times an E4M3 x E4M3 product
+                        // is exact in fp32, so the fused multiply-add rounds once,
+                        // exactly like a separate multiply and add would
+                        acc[i][j][r] = __builtin_fmaf(p[r], s_a[i][r] * s_w[j], acc[i][j][r]);
+                    }
+                }
+            }
+        }
+    }
+
+    const float gA = *ga, gW = *gw;
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int64_t col = n0 + wn * 64 + j * 32 + (lane & 31);
+            if (col >= N) continue;
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int64_t row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                if (row >= M) continue;
+                const float v = (acc[i][j][r] * gA) * gW;
+                if constexpr (OUT == 0)
+                    static_cast<float *>(y)[row * N + col] = v;
+                else
+                    static_cast<uint16_t *>(y)[row * N + col] = (uint16_t)f32_to_bf16(v);
+            }
+        }
+}
+
 template <class KernelFn>
 static hipError_t allow_lds(KernelFn fn, size_t bytes) {
     return hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
@@ -392,7 +523,6 @@ hipError_t launch_gemm_nvfp4(hipStream_t s, const uint8_t *ca, const uint8_t *sa
                              const float *gw, int64_t M, int64_t N, int64_t K, int out_dtype,
                              void *y, int variant) {
     using namespace fp4gemm;
-    (void)variant;
     if (M == 0 || N == 0) return hipSuccess;
     static const hipError_t attr = [] {
         hipError_t e = allow_lds(gemm_fp4_f16_kernel<0>, 2 * STAGE);
@@ -405,6 +535,14 @@ hipError_t launch_gemm_nvfp4(hipStream_t s, const uint8_t *ca, const uint8_t *sa
     const int64_t tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
     const dim3 grid((unsigned)(tm * tn)), block(256);
     const unsigned utm = (unsigned)tm, utn = (unsigned)tn;
+    if (variant == 1) {
+        const int64_t sm = (M + fp4scaled::BM - 1) / fp4scaled::BM, sn = (N + fp4scaled::BN - 1) / fp4scaled::BN;
+        if (out_dtype == 0)
+            hipLaunchKernelGGL(gemm_fp4_scaled_kernel<0>, dim3((unsigned)(sm * sn)), block, 0, s, ca, sa, ga, cw, sw, gw, M, N, K, y, (unsigned)sn);
+        else
+            hipLaunchKernelGGL(gemm_fp4_scaled_kernel<1>, dim3((unsigned)(sm * sn)), block, 0, s, ca, sa, ga, cw, sw, gw, M, N, K, y, (unsigned)sn);
+        return hipGetLastError();
+    }
     const bool fast = K % (4 * 16) == 0;
     if (fast && out_dtype == 0)
         hipLaunchKernelGGL(gemm_fp4_fast_kernel<0>, grid, block, 2 * STAGE, s, ca, sa, ga, cw, sw, gw, M, N, K, y, utm, utn);

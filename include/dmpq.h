@@ -68,9 +68,14 @@ enum { DMPQ_NO_HADAMARD = 1 };
 enum { DMPQ_W8_FROM_NVFP4 = 0, DMPQ_W8_DIRECT = 1 };
 /* TDC step modes. */
 enum { DMPQ_TDC_SKIP = 0, DMPQ_TDC_REFRESH = 1 };
-/* NVFP4 GEMM variants: 0 = exact E2M1 x E4M3 -> bf16 dequant in LDS feeding
- * bf16 MFMA. */
-enum { DMPQ_FP4_BF16_DEQUANT = 0 };
+/* NVFP4 GEMM variants (both exact; only the fp32 accumulation order differs):
+ * 0 = E2M1 x E4M3 products dequantized to 16-bit floats in LDS (exact: at
+ *     most 6 significant bits) feeding 16-bit MFMA -- the fast path;
+ * 1 = the chip's block-scaled f8f6f4 MFMA on raw E2M1 codes, one 16-element
+ *     group per instruction, E4M3 scales applied to the exact group partials
+ *     in fp32 (kept for measurement; its power-of-two per-32 scales cannot
+ *     carry E4M3 scales inside the instruction). */
+enum { DMPQ_FP4_BF16_DEQUANT = 0, DMPQ_FP4_SCALED_MFMA = 1 };
 /* Workspace users. */
 enum { DMPQ_OP_GAMMA = 0, DMPQ_OP_QUANT_NVFP4 = 1, DMPQ_OP_TDC = 2, DMPQ_OP_PREP_WEIGHT = 3 };
 
@@ -154,7 +159,8 @@ dmpq_status dmpq_qgemm_int8(hipStream_t stream, const int8_t *qa, const float *s
  * accumulated in fp32 (every product E2M1 x E4M3 is exact; only the fp32
  * accumulation rounds).  ca/sa/d_ga: activation codes [M x K/2], E4M3
  * scales [M x K/16], tensor scale (device fp32); cw/sw/d_gw likewise for the
- * weight [N x K].  out_dtype F32 or BF16.  variant: DMPQ_FP4_BF16_DEQUANT.
+ * weight [N x K].  out_dtype F32 or BF16.  variant: DMPQ_FP4_BF16_DEQUANT or
+ * DMPQ_FP4_SCALED_MFMA.
  * ------------------------------------------------------------------------- */
 dmpq_status dmpq_qgemm_nvfp4(hipStream_t stream, const uint8_t *ca, const uint8_t *sa,
                              const float *d_ga, const uint8_t *cw, const uint8_t *sw,

@@ -1,9 +1,10 @@
 """GPU parity: INT8 and NVFP4 quantized GEMMs against the oracle.
 
 INT8: int32 accumulators and the fp32 epilogue bit-exact (and bf16 output =
-RNE of that fp32).  NVFP4: per element |y - y_ref| <= 1e-5 * B with B =
-gA gW sum_k |a_k||w_k| (the fp32 summation scale), since only the fp32
-accumulation order is free.  Full CogVideoX-like shapes are checked on a
+RNE of that fp32).  NVFP4 (both variants: 16-bit dequant + MFMA, and the
+block-scaled f8f6f4 MFMA with fp32 rescale): per element |y - y_ref| <=
+1e-5 * B with B = gA gW sum_k |a_k||w_k| (the fp32 summation scale), since
+only the fp32 accumulation order is free.  Full CogVideoX-like shapes are checked on a
 deterministic row sample (every 211th row plus the last 3 rows).
 """
 import numpy as np
@@ -38,11 +39,11 @@ def _run_int8(qa, sa, qw, sw, out_dtype):
     return y
 
 
-def _run_nvfp4(ca, sa, ga, cw, sw, gw, out_dtype=dm.OUT_F32):
+def _run_nvfp4(ca, sa, ga, cw, sw, gw, out_dtype=dm.OUT_F32, variant=dm.FP4_BF16_DEQUANT):
     M, N = ca.shape[0], cw.shape[0]
     y = empty((M, N), np.float32 if out_dtype == dm.OUT_F32 else np.uint16)
     dm.qgemm_nvfp4(dev(ca), dev(sa), dev(np.array([ga], np.float32)), dev(cw), dev(sw),
-                   dev(np.array([gw], np.float32)), y, out_dtype)
+                   dev(np.array([gw], np.float32)), y, out_dtype, variant)
     torch.cuda.synchronize()
     return y
 
@@ -58,19 +59,24 @@ def _check_int8(orc, qa, sa, qw, sw, rows=None):
     assert np.array_equal(yb, workloads.to_bf16_bits(y0))
 
 
-def _check_nvfp4(orc, ca, sa, ga, cw, sw, gw, rows=None):
+FP4_VARIANTS = (dm.FP4_BF16_DEQUANT, dm.FP4_SCALED_MFMA)
+
+
+def _check_nvfp4(orc, ca, sa, ga, cw, sw, gw, rows=None, variants=FP4_VARIANTS):
+    """Both GEMM variants against one oracle evaluation."""
     y0, b0 = orc.gemm_nvfp4(ca, sa, ga, cw, sw, gw, rows=rows)
     sel = slice(None) if rows is None else torch.from_numpy(rows).cuda()
-    y1 = host(_run_nvfp4(ca, sa, ga, cw, sw, gw)[sel]).astype(np.float64)
-    err = np.abs(y1 - y0)
-    assert np.all(err <= TOL * b0), float((err / np.maximum(b0, 1e-300)).max())
-    # report-style check: typical relative error is far below the bound
-    big = np.abs(y0) > 1e-3 * b0
-    if big.any():
-        assert np.median(err[big] / np.abs(y0[big])) < 1e-5
-    yb = host(_run_nvfp4(ca, sa, ga, cw, sw, gw, dm.OUT_BF16)[sel], np.uint16)
-    ybf = workloads.bf16_bits_to_f32(yb).astype(np.float64)
-    assert np.all(np.abs(ybf - y0) <= TOL * b0 + 2.0 ** -8 * np.abs(y0))
+    for v in variants:
+        y1 = host(_run_nvfp4(ca, sa, ga, cw, sw, gw, variant=v)[sel]).astype(np.float64)
+        err = np.abs(y1 - y0)
+        assert np.all(err <= TOL * b0), (v, float((err / np.maximum(b0, 1e-300)).max()))
+        # report-style check: typical relative error is far below the bound
+        big = np.abs(y0) > 1e-3 * b0
+        if big.any():
+            assert np.median(err[big] / np.abs(y0[big])) < 1e-5, v
+        yb = host(_run_nvfp4(ca, sa, ga, cw, sw, gw, dm.OUT_BF16, v)[sel], np.uint16)
+        ybf = workloads.bf16_bits_to_f32(yb).astype(np.float64)
+        assert np.all(np.abs(ybf - y0) <= TOL * b0 + 2.0 ** -8 * np.abs(y0)), v
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 16), (256, 256, 256), (200, 136, 80), (129, 257, 384),
@@ -127,8 +133,10 @@ def test_gemm_empty():
     dm.qgemm_int8(empty((0, 32), np.int8), empty((0,), np.float32), empty((8, 32), np.int8),
                   empty((8,), np.float32), y)
     y2 = empty((4, 0), np.float32)
-    dm.qgemm_nvfp4(empty((4, 16), np.uint8), empty((4, 2), np.uint8), torch.ones(1, device="cuda"),
-                   empty((0, 16), np.uint8), empty((0, 2), np.uint8), torch.ones(1, device="cuda"), y2)
+    for v in FP4_VARIANTS:
+        dm.qgemm_nvfp4(empty((4, 16), np.uint8), empty((4, 2), np.uint8), torch.ones(1, device="cuda"),
+                       empty((0, 16), np.uint8), empty((0, 2), np.uint8), torch.ones(1, device="cuda"),
+                       y2, dm.OUT_F32, v)
     torch.cuda.synchronize()
 
 
