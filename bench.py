@@ -42,6 +42,17 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=512,
                    help="rows of the qkv linear the oracle runs for the CPU baseline")
+    p.add_argument("--calibrate-mib", type=int, default=0,
+                   help="before warmup, run the TDC skip kernel (a plain streaming kernel: two "
+                        "reads and one write per element) 3 times over buffers of this many MiB, "
+                        "the known-size reference for the HBM byte counters")
+    p.add_argument("--summarize-stats", nargs=2, metavar=("KERNEL_STATS_CSV", "OUT_MD"),
+                   help="(no GPU) write the markdown summary of a rocprofv3 --stats run")
+    p.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"),
+                   help="(no GPU) turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of "
+                        "'bench.py --calibrate-mib N' into per-launch HBM bytes of the GEMMs")
+    p.add_argument("--command", default="",
+                   help="the command that produced the csv, recorded in the summary")
     return p.parse_args()
 
 
@@ -76,6 +87,12 @@ class KernelTimer:
 
 def main():
     args = parse()
+    if args.summarize_stats:
+        summarize_stats(*args.summarize_stats, args.command)
+        return
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic, args.command)
+        return
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} requested, but this build runs on one GPU only "
               "(the hot path is token-parallel; the multi-GPU sharding is design-only)",
@@ -176,6 +193,18 @@ def main():
             blk["delta_valid"] = True
         gemm_ops_step = ops
 
+    calib = None
+    if args.calibrate_mib > 0:
+        n = args.calibrate_mib * (1 << 20) // 2
+        cx = torch.zeros(n, dtype=torch.int16, device="cuda")
+        cd = torch.zeros(n, dtype=torch.int16, device="cuda")
+        co = torch.empty(n, dtype=torch.int16, device="cuda")
+        for _ in range(3):
+            dm.tdc_step(dm.TDC_SKIP, cx, co, cd, True)
+        torch.cuda.synchronize()
+        del cx, cd, co
+        calib = dict(kernel=CALIB_KERNEL, elements=n, read_bytes=4 * n, write_bytes=2 * n)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -211,6 +240,7 @@ def main():
     d = kernels[dom]
     roofline = dict(kernel=dom, bound=d["bound"], achieved=d["achieved"], peak=d["peak"],
                     unit=d["unit"], frac=d["frac"], traffic=None)
+    roofline.update(measured_traffic(dom))
     q_bytes = sum(ksum[n]["work"] for n in ksum if n.startswith("hadamard_quant"))
     q_ms = sum(ksum[n]["total_ms"] for n in ksum if n.startswith("hadamard_quant"))
 
@@ -239,6 +269,8 @@ def main():
         "roofline": roofline,
         "setup_s": round(setup_s, 1),
     }
+    if calib is not None:
+        result["copy_calibration"] = calib
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_rows)
     print(json.dumps(result), flush=True)
@@ -269,6 +301,136 @@ def cpu_baseline(rows: int) -> dict:
             "kind": "oracle",
             "sample": f"{rows} tokens of the qkv linear ({N}x{K}), INT8 and NVFP4 routes, "
                       f"quant + GEMM, {dt:.1f} s"}
+
+
+# ---- HBM byte counters and profile summaries ---------------------------------
+# The kernels behind each timed entry point and the sources they are built from:
+# a stored traffic figure is used only while these sources are unchanged.
+GEMM_KERNELS = {"qgemm_nvfp4": "dmpq::gemm_fp4_fast_kernel<1>",
+                "qgemm_int8": "dmpq::gemm_i8_dma_kernel<1>"}
+GEMM_SOURCES = {"qgemm_nvfp4": ["gemm_nvfp4.hip", "gemm_common.hpp", "device.hpp", "internal.hpp"],
+                "qgemm_int8": ["gemm_int8.hip", "gemm_common.hpp", "device.hpp", "internal.hpp"]}
+CALIB_KERNEL = "dmpq::tdc_skip_kernel"
+HERE = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_JSON = os.path.join(HERE, "profiles", "traffic_qgemm_cogvideox5b.json")
+
+
+def sources_sha256(api: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES[api]:
+        with open(os.path.join(HERE, "dynamic_mixed_precision_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def gemm_algorithmic_bytes(api: str) -> float:
+    """Average compulsory bytes of one GEMM launch of the step: operands once
+    (codes + scales) and the bf16 output once, over the four linear shapes."""
+    import workloads as wl
+    cfg = wl.COGVIDEOX_5B
+    M = cfg.M
+    tot = 0.0
+    for lin in cfg.linears:
+        N, K = lin.N, lin.K
+        if api == "qgemm_nvfp4":
+            tot += (M + N) * (K / 2 + K / 16) + 8
+        else:
+            tot += (M + N) * (K + 4)
+        tot += 2.0 * M * N
+    return tot / len(cfg.linears)
+
+
+def measured_traffic(api: str) -> dict:
+    """traffic = counter-measured HBM bytes per launch (calibrated), or None
+    when no measurement exists or the kernel's sources changed since."""
+    out = {"traffic_unit": "bytes/launch"}
+    if api not in GEMM_KERNELS:
+        return out
+    out["algorithmic_bytes_per_launch"] = round(gemm_algorithmic_bytes(api))
+    if not os.path.exists(TRAFFIC_JSON):
+        return out
+    with open(TRAFFIC_JSON) as f:
+        rec = json.load(f).get(api)
+    if rec is None or rec["sources_sha256"] != sources_sha256(api):
+        out["traffic_note"] = "kernel changed since the counters were taken"
+        return out
+    out["traffic"] = rec["bytes_per_launch"]
+    out["traffic_over_algorithmic"] = round(rec["bytes_per_launch"] / out["algorithmic_bytes_per_launch"], 3)
+    return out
+
+
+def _counter_rows(path: str, counter: str):
+    import csv
+    with open(path) as f:
+        return [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+
+
+def _per_kernel_kib(rows, kernel: str):
+    """Counter value (KiB) of every dispatch of `kernel`, in dispatch order."""
+    sel = {}
+    for r in rows:
+        if kernel + "(" in r["Kernel_Name"]:
+            sel[int(r["Dispatch_Id"])] = sel.get(int(r["Dispatch_Id"]), 0.0) + float(r["Counter_Value"])
+    return [sel[k] for k in sorted(sel)]
+
+
+def summarize_traffic(fetch_csv: str, write_csv: str, out_json: str, command: str) -> None:
+    fr, wr = _counter_rows(fetch_csv, "FETCH_SIZE"), _counter_rows(write_csv, "WRITE_SIZE")
+    cf, cw = _per_kernel_kib(fr, CALIB_KERNEL), _per_kernel_kib(wr, CALIB_KERNEL)
+    if len(cf) != 3 or len(cw) != 3:
+        raise SystemExit(f"expected 3 calibration dispatches, got {len(cf)}, {len(cw)}")
+    # the calibration buffers' size is recorded in the command (--calibrate-mib N)
+    mib = int(command.split("--calibrate-mib")[1].split()[0])
+    n = mib * (1 << 20) // 2
+    f_read = 4.0 * n / (1024.0 * sum(cf) / 3)
+    f_write = 2.0 * n / (1024.0 * sum(cw) / 3)
+    rec = {"command": command, "calibration": {
+        "kernel": CALIB_KERNEL, "elements": n, "read_bytes": 4 * n, "write_bytes": 2 * n,
+        "fetch_kib_per_dispatch": cf, "write_kib_per_dispatch": cw,
+        "fetch_factor": round(f_read, 5), "write_factor": round(f_write, 5)}}
+    for api, kname in GEMM_KERNELS.items():
+        f, w = _per_kernel_kib(fr, kname), _per_kernel_kib(wr, kname)
+        if not f or len(f) != len(w):
+            continue
+        fb = 1024.0 * f_read * sum(f) / len(f)
+        wb = 1024.0 * f_write * sum(w) / len(w)
+        alg = gemm_algorithmic_bytes(api)
+        rec[api] = {"kernel": kname, "dispatches": len(f), "sources_sha256": sources_sha256(api),
+                    "fetch_kib_avg_raw": round(sum(f) / len(f), 1),
+                    "write_kib_avg_raw": round(sum(w) / len(w), 1),
+                    "fetch_bytes_per_launch": round(fb), "write_bytes_per_launch": round(wb),
+                    "bytes_per_launch": round(fb + wb),
+                    "algorithmic_bytes_per_launch": round(alg),
+                    "traffic_over_algorithmic": round((fb + wb) / alg, 3)}
+    with open(out_json, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec, indent=1))
+
+
+def summarize_stats(stats_csv: str, out_md: str, command: str) -> None:
+    import csv
+    import re
+    with open(stats_csv) as f:
+        rows = list(csv.DictReader(f))
+    lines = ["# rocprofv3 kernel stats: bench.py step, CogVideoX-5B-like batch "
+             "(17776 tokens, 4 blocks x 4 linears, 2 INT8 + 2 NVFP4 blocks)", "",
+             "Command (run from /tmp, repository at $GRAFT_REPO_ROOT):", "", "```", command, "```", "",
+             "| kernel | calls | avg us | min us | max us | share of GPU time |",
+             "|---|---|---|---|---|---|"]
+    for r in rows:
+        if "dmpq" not in r["Name"]:
+            continue
+        name = re.sub(r"\(.*", "", r["Name"]).replace("void ", "")
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['Percentage']):.1f}% |")
+    other = sum(float(r["Percentage"]) for r in rows if "dmpq" not in r["Name"])
+    lines += ["", f"Other kernels (torch input generation, setup): {other:.1f}% of GPU time.", ""]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
 
 
 if __name__ == "__main__":
