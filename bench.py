@@ -306,7 +306,7 @@ def cpu_baseline(rows: int) -> dict:
 # ---- HBM byte counters and profile summaries ---------------------------------
 # The kernels behind each timed entry point and the sources they are built from:
 # a stored traffic figure is used only while these sources are unchanged.
-GEMM_KERNELS = {"qgemm_nvfp4": "dmpq::gemm_fp4_fast_kernel<1>",
+GEMM_KERNELS = {"qgemm_nvfp4": "dmpq::gemm_fp4_dma_kernel<1>",
                 "qgemm_int8": "dmpq::gemm_i8_dma_kernel<1>"}
 GEMM_SOURCES = {"qgemm_nvfp4": ["gemm_nvfp4.hip", "gemm_common.hpp", "device.hpp", "internal.hpp"],
                 "qgemm_int8": ["gemm_int8.hip", "gemm_common.hpp", "device.hpp", "internal.hpp"]}

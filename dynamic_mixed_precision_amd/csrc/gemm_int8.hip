@@ -182,9 +182,10 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(
 // base + 16 * lane of a wave's 1 KB block), so no staging registers and no
 // LDS write instructions are needed.  Rows are 128 bytes; the 16-byte chunk
 // kc of row r is stored at slot kc ^ ((r >> 1) & 7), which makes the 32-row
-// fragment reads conflict-free on the 64-bank LDS.  Per stage: wait for the
-// stage's loads and barrier, read every fragment of the stage into registers,
-// issue the next stage's loads into the other buffer, then 64 MFMAs per wave.
+// fragment reads conflict-free on the 64-bank LDS.  Two stage buffers; the
+// DMA of stage kt+2 is issued during stage kt, as soon as every wave has read
+// its last fragments of stage kt, and fragments are read one k-step ahead of
+// the MFMAs that use them, across stage boundaries too.
 // Out-of-range rows (ragged M, N) load a clamped row; their outputs are never
 // stored.
 // ---------------------------------------------------------------------------
@@ -198,6 +199,73 @@ constexpr size_t LDS_BYTES = NBUF * STAGE > 4 * EpiBand<4>::BYTES ? NBUF * STAGE
 }  // namespace i8dma
 
 __device__ __forceinline__ int swz128(int row, int kc) { return kc ^ ((row >> 1) & 7); }
+
+// Per-lane state of the DMA kernel: DMA sources and fragment rows.
+struct I8DmaLane {
+    const int8_t *srcA[i8dma::BLOCKS], *srcW[i8dma::BLOCKS];
+    int ra[4], rw[4];
+    int wave, hk;
+};
+
+// waitcnt immediate that waits for at most n outstanding vector memory ops
+// (expcnt and lgkmcnt left free)
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+__device__ __forceinline__ void i8dma_issue(int8_t *dst, const I8DmaLane &L, int64_t k0) {
+    using namespace i8dma;
+    typedef __attribute__((address_space(3))) void lds_void;
+#pragma unroll
+    for (int q = 0; q < BLOCKS; q++) {
+        const int b = L.wave + 4 * q;
+        __builtin_amdgcn_global_load_lds((const void *)(L.srcA[q] + k0), (lds_void *)(dst + b * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void *)(L.srcW[q] + k0), (lds_void *)(dst + TILE + b * 1024), 16, 0, 0);
+    }
+}
+
+// Fragments of k-step s (32 K values) of the stage held in `buf`.
+__device__ __forceinline__ void i8dma_frags(const int8_t *buf, const I8DmaLane &L, int s, v4i a[4], v4i b[4]) {
+    using namespace i8dma;
+    const int kc = 2 * s + L.hk;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        a[i] = *reinterpret_cast<const v4i *>(buf + L.ra[i] * BK + swz128(L.ra[i], kc) * 16);
+        b[i] = *reinterpret_cast<const v4i *>(buf + TILE + L.rw[i] * BK + swz128(L.rw[i], kc) * 16);
+    }
+}
+
+__device__ __forceinline__ void i8_mfma16(v16i (&acc)[4][4], const v4i a[4], const v4i b[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[j], a[i], acc[i][j], 0, 0, 0);
+}
+
+// One stage: on entry a0/b0 and a1/b1 hold k-steps 0 and 1 of the stage in
+// `cur`.  After k-step 2 the wave waits for the DMA of the next stage (into
+// `nxt`) and for every wave to finish reading `cur`, reuses `cur` for the DMA
+// two stages ahead, and reads k-steps 0 and 1 of the next stage while k-step
+// 3 runs.  `cur` and `nxt` are separate restrict parameters so that, once
+// inlined, the compiler knows the reads of `nxt` cannot alias the DMA into
+// `cur` and does not wait for it.
+__device__ __forceinline__ void i8dma_stage(int8_t *__restrict__ cur, const int8_t *__restrict__ nxt,
+                                            bool has_next, bool issue, int64_t k_issue,
+                                            const I8DmaLane &L, v16i (&acc)[4][4],
+                                            v4i (&a0)[4], v4i (&b0)[4], v4i (&a1)[4], v4i (&b1)[4]) {
+    i8_mfma16(acc, a0, b0);
+    i8dma_frags(cur, L, 2, a0, b0);
+    i8_mfma16(acc, a1, b1);
+    i8dma_frags(cur, L, 3, a1, b1);
+    i8_mfma16(acc, a0, b0);
+    if (has_next) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's DMA of the next stage
+        __syncthreads();                           // ... every wave's, and `cur` is free
+        if (issue) i8dma_issue(cur, L, k_issue);
+        i8dma_frags(nxt, L, 0, a0, b0);
+    }
+    i8_mfma16(acc, a1, b1);
+    if (has_next) i8dma_frags(nxt, L, 1, a1, b1);
+}
 
 template <int OUT>
 __global__ __launch_bounds__(256, 1) void gemm_i8_dma_kernel(
@@ -221,8 +289,10 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_dma_kernel(
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0;
 
     // Per-lane source offsets of this wave's load blocks: block b = wave + 4q
-    // covers tile rows 8b .. 8b+7; lane L fills row 8b + L/8, slot L%8.
-    const int8_t *srcA[BLOCKS], *srcW[BLOCKS];
+    // covers tile rows 8b .. 8b+7; lane l fills row 8b + l/8, slot l%8.
+    I8DmaLane L;
+    L.wave = wave;
+    L.hk = lane >> 5;
 #pragma unroll
     for (int q = 0; q < BLOCKS; q++) {
         const int b = wave + 4 * q;
@@ -230,50 +300,32 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_dma_kernel(
         const int kc = swz128(row, lane & 7);
         const int64_t gm = m0 + row < M ? m0 + row : M - 1;
         const int64_t gn = n0 + row < N ? n0 + row : N - 1;
-        srcA[q] = A + gm * K + kc * 16;
-        srcW[q] = W + gn * K + kc * 16;
+        L.srcA[q] = A + gm * K + kc * 16;
+        L.srcW[q] = W + gn * K + kc * 16;
     }
-    typedef __attribute__((address_space(3))) void lds_void;
-#define DMPQ_I8_DMA(buf, k0)                                                                   \
-    _Pragma("unroll") for (int q = 0; q < BLOCKS; q++) {                                       \
-        const int b = wave + 4 * q;                                                            \
-        __builtin_amdgcn_global_load_lds((const void *)(srcA[q] + (k0)),                       \
-                                         (lds_void *)(lds + (buf) * STAGE + b * 1024), 16, 0, 0); \
-        __builtin_amdgcn_global_load_lds((const void *)(srcW[q] + (k0)),                       \
-                                         (lds_void *)(lds + (buf) * STAGE + TILE + b * 1024), 16, 0, 0); \
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        L.ra[i] = wm * 128 + i * 32 + (lane & 31);
+        L.rw[i] = wn * 128 + i * 32 + (lane & 31);
     }
 
     const int nk = (int)(K / BK);
-    DMPQ_I8_DMA(0, 0)
-    for (int kt = 0; kt < nk; kt++) {
-        const int cur = kt & 1;
-        __builtin_amdgcn_s_waitcnt(0xC07F & ~0xC00F);  // vmcnt(0): this wave's loads of stage kt
-        __syncthreads();                               // ... and every other wave's
-        v4i a[4][4], b[4][4];
-        const int8_t *base = lds + cur * STAGE;
-#pragma unroll
-        for (int s = 0; s < 4; s++) {
-            const int kc = 2 * s + (lane >> 5);
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int ra = wm * 128 + i * 32 + (lane & 31);
-                const int rb = wn * 128 + i * 32 + (lane & 31);
-                a[s][i] = *reinterpret_cast<const v4i *>(base + ra * BK + swz128(ra, kc) * 16);
-                b[s][i] = *reinterpret_cast<const v4i *>(base + TILE + rb * BK + swz128(rb, kc) * 16);
-            }
-        }
-        if (kt + 1 < nk) {
-            DMPQ_I8_DMA(cur ^ 1, (int64_t)(kt + 1) * BK)
-        }
-#pragma unroll
-        for (int s = 0; s < 4; s++)
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-#pragma unroll
-                for (int j = 0; j < 4; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[s][j], a[s][i], acc[i][j], 0, 0, 0);
+    i8dma_issue(lds, L, 0);
+    if (nk > 1) {
+        i8dma_issue(lds + STAGE, L, BK);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * BLOCKS));  // stage 0 only
+    } else {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
-#undef DMPQ_I8_DMA
+    __syncthreads();
+    v4i a0[4], b0[4], a1[4], b1[4];
+    i8dma_frags(lds, L, 0, a0, b0);
+    i8dma_frags(lds, L, 1, a1, b1);
+    for (int kt = 0; kt < nk; kt++) {
+        int8_t *cur = lds + (kt & 1) * STAGE;
+        int8_t *nxt = lds + ((kt & 1) ^ 1) * STAGE;
+        i8dma_stage(cur, nxt, kt + 1 < nk, kt + 2 < nk, (int64_t)(kt + 2) * BK, L, acc, a0, b0, a1, b1);
+    }
     __syncthreads();  // every wave is done reading the stage buffers before they hold bands
 
     constexpr int ES = OUT == 1 ? 2 : 4;

@@ -14,14 +14,18 @@
 // Dequant per code byte: v_cvt_scalef32_pk_f16_fp4 (scale 1.0; that
 // converter uses only the exponent of its scale operand, so the E4M3 scale is
 // applied separately) gives two fp16 values, then one v_pk_mul_f16 by the
-// block's scale.  The dequantized tiles go to LDS once per workgroup.
+// block's scale.
 //
-// Tiling: 256 threads = 2 x 2 waves, workgroup tile 256 x 256, wave tile
-// 128 x 128 = 4 x 4 MFMA 32x32x16 tiles.  K advances 64 elements (4 scale
-// groups) per stage through a double-buffered LDS (fp16 rows of 128 bytes
-// padded to 144).  While the MFMAs of stage kt run, the next stage is
-// dequantized into the other LDS buffer in four parts placed between the
-// four k-steps, and the codes of stage kt+2 are loaded into registers.
+// Tiling (all paths of variant 0): 256 threads = 2 x 2 waves, workgroup tile
+// 256 x 256, wave tile 128 x 128 = 4 x 4 MFMA 32x32x16 tiles.  Three paths:
+//  * K % 256 == 0 (the DiT shapes): raw codes and scales are copied into LDS
+//    by DMA and each wave dequantizes its own fragments into registers
+//    (gemm_fp4_dma_kernel);
+//  * K % 64 == 0: codes are loaded into registers, dequantized once per
+//    workgroup into a double-buffered fp16 LDS tile (gemm_fp4_fast_kernel);
+//  * any K % 16 == 0: as the previous, with the K tail masked
+//    (gemm_fp4_f16_kernel).
+// Variant 1 (gemm_fp4_scaled_kernel) uses the block-scaled MFMA instead.
 #include "device.hpp"
 #include "gemm_common.hpp"
 #include "internal.hpp"
@@ -381,6 +385,203 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_fast_kernel(
     fp4_epilogue<OUT>(acc, lds, ga, gw, M, N, m0, n0, wave, wm, wn, lane, y);
 }
 
+// One k-step fragment: the 8 codes of 32-bit word S of a 16-byte piece, times
+// the piece's scale (element 0 of s2 for words 0-1, element 1 for words 2-3).
+template <int S>
+__device__ __forceinline__ v8h dq8(const uint4 c, const v2h s2) {
+    const uint32_t w = S == 0 ? c.x : S == 1 ? c.y : S == 2 ? c.z : c.w;
+    const v2h sc = S < 2 ? __builtin_shufflevector(s2, s2, 0, 0) : __builtin_shufflevector(s2, s2, 1, 1);
+    const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sc;
+    const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sc;
+    const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sc;
+    const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sc;
+    return (v8h){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// ---------------------------------------------------------------------------
+// DMA path (K % 256 == 0).  Raw codes and scales go from global memory
+// straight into LDS with global_load_lds_dwordx4, whole 128-byte rows per
+// stage (8 rows per instruction), and every wave dequantizes the fragments of
+// its own MFMAs from LDS into registers.  Compared with staging dequantized
+// tiles, the load path touches one cache line per 128 bytes instead of one per
+// 32, and LDS holds 4.5 bits per element instead of 16.
+//
+// Stage: 256 K elements, per operand 256 rows x 128 code bytes (piece p of a
+// row, 16 bytes = K positions 32p .. 32p+31, stored at slot p ^ ((row >> 1) & 7)
+// so the 32-row fragment reads are conflict-free) and 256 rows x 16 scale
+// bytes; two stages in flight.  K order inside a 64-element chunk c: lane half
+// h holds piece 2c + h and feeds k-step s the positions 8s .. 8s+7 of it (the
+// same order on both operands, so products pair the same elements).
+// ---------------------------------------------------------------------------
+namespace fp4dma {
+constexpr int BM = 256, BN = 256, BKE = 256;
+constexpr int CROW = BKE / 2, SROW = BKE / 16;  // code / scale bytes per row per stage
+constexpr int CODES = BM * CROW, SCALES = BM * SROW;
+constexpr int STAGE = 2 * CODES + 2 * SCALES;   // A codes, W codes, A scales, W scales
+constexpr int LDS_BYTES = 2 * STAGE;
+static_assert(4 * EpiBand<4>::BYTES <= LDS_BYTES, "epilogue bands fit in the stage buffers");
+constexpr unsigned GROUP_M = 8;
+}  // namespace fp4dma
+
+// One stage of the DMA kernel: issue the DMA of the next stage into `nxt`
+// (when `issue`), then run the stage held in `cur`.  The two buffers are
+// separate restrict parameters so that, once inlined, the compiler knows the
+// stage's LDS reads cannot alias the DMA in flight and does not wait for it.
+struct Fp4DmaLane {
+    const uint8_t *srcA[8], *srcW[8], *srcSA, *srcSW;
+    int ra[4], rw[4];
+    int wave, hk, sh;
+};
+
+__device__ __forceinline__ void fp4dma_stage(const uint8_t *__restrict__ cur, uint8_t *__restrict__ nxt,
+                                             bool issue, int64_t st_next, const Fp4DmaLane &L,
+                                             v16f (&acc)[4][4]) {
+    using namespace fp4dma;
+    typedef __attribute__((address_space(3))) void lds_void;
+    if (issue) {
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+            const int b = L.wave + 4 * q;
+            __builtin_amdgcn_global_load_lds((const void *)(L.srcA[q] + st_next * CROW),
+                                             (lds_void *)(nxt + b * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)(L.srcW[q] + st_next * CROW),
+                                             (lds_void *)(nxt + CODES + b * 1024), 16, 0, 0);
+        }
+        __builtin_amdgcn_global_load_lds((const void *)(L.srcSA + st_next * SROW),
+                                         (lds_void *)(nxt + 2 * CODES + L.wave * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void *)(L.srcSW + st_next * SROW),
+                                         (lds_void *)(nxt + 2 * CODES + SCALES + L.wave * 1024), 16, 0, 0);
+    }
+    uint4 sA[4], sW[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        sA[i] = *reinterpret_cast<const uint4 *>(cur + 2 * CODES + L.ra[i] * SROW);
+        sW[i] = *reinterpret_cast<const uint4 *>(cur + 2 * CODES + SCALES + L.rw[i] * SROW);
+    }
+#define DMPQ_F4D_CODES(dA, dW, c)                                                              \
+    _Pragma("unroll") for (int i = 0; i < 4; i++) {                                            \
+        dA[i] = *reinterpret_cast<const uint4 *>(                                              \
+            cur + L.ra[i] * CROW + (((2 * (c) + L.hk) ^ ((L.ra[i] >> 1) & 7)) * 16));          \
+        dW[i] = *reinterpret_cast<const uint4 *>(                                              \
+            cur + CODES + L.rw[i] * CROW + (((2 * (c) + L.hk) ^ ((L.rw[i] >> 1) & 7)) * 16));  \
+    }
+#define DMPQ_F4D_DQ(cA, cW, scA, scW, S, fa, fb)                                               \
+    _Pragma("unroll") for (int i = 0; i < 4; i++) {                                            \
+        fa[i] = dq8<S>(cA[i], scA[i]);                                                         \
+        fb[i] = dq8<S>(cW[i], scW[i]);                                                         \
+    }
+#define DMPQ_F4D_MFMA(fa, fb)                                                                  \
+    _Pragma("unroll") for (int i = 0; i < 4; i++)                                              \
+        _Pragma("unroll") for (int j = 0; j < 4; j++)                                          \
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+#define DMPQ_F4D_CHUNK(cA, cW, c)                                                              \
+    {                                                                                          \
+        v2h scA[4], scW[4];                                                                    \
+        _Pragma("unroll") for (int i = 0; i < 4; i++) {                                        \
+            const uint32_t wa = (c) == 0 ? sA[i].x : (c) == 1 ? sA[i].y : (c) == 2 ? sA[i].z : sA[i].w; \
+            const uint32_t ww = (c) == 0 ? sW[i].x : (c) == 1 ? sW[i].y : (c) == 2 ? sW[i].z : sW[i].w; \
+            scA[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wa >> L.sh, 1.0f, false);        \
+            scW[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ww >> L.sh, 1.0f, false);        \
+        }                                                                                      \
+        v8h fa0[4], fb0[4], fa1[4], fb1[4];                                                    \
+        DMPQ_F4D_DQ(cA, cW, scA, scW, 0, fa0, fb0)                                             \
+        DMPQ_F4D_DQ(cA, cW, scA, scW, 1, fa1, fb1)                                             \
+        DMPQ_F4D_MFMA(fa0, fb0)                                                                \
+        DMPQ_F4D_DQ(cA, cW, scA, scW, 2, fa0, fb0)                                             \
+        DMPQ_F4D_MFMA(fa1, fb1)                                                                \
+        DMPQ_F4D_DQ(cA, cW, scA, scW, 3, fa1, fb1)                                             \
+        DMPQ_F4D_MFMA(fa0, fb0)                                                                \
+        DMPQ_F4D_MFMA(fa1, fb1)                                                                \
+    }
+    uint4 cA0[4], cW0[4], cA1[4], cW1[4];
+    DMPQ_F4D_CODES(cA0, cW0, 0)
+    DMPQ_F4D_CODES(cA1, cW1, 1)
+    DMPQ_F4D_CHUNK(cA0, cW0, 0)
+    DMPQ_F4D_CODES(cA0, cW0, 2)
+    DMPQ_F4D_CHUNK(cA1, cW1, 1)
+    DMPQ_F4D_CODES(cA1, cW1, 3)
+    DMPQ_F4D_CHUNK(cA0, cW0, 2)
+    DMPQ_F4D_CHUNK(cA1, cW1, 3)
+#undef DMPQ_F4D_CODES
+#undef DMPQ_F4D_DQ
+#undef DMPQ_F4D_MFMA
+#undef DMPQ_F4D_CHUNK
+}
+
+template <int OUT>
+__global__ __launch_bounds__(256, 1) void gemm_fp4_dma_kernel(
+    const uint8_t *__restrict__ ca, const uint8_t *__restrict__ sa, const float *__restrict__ ga,
+    const uint8_t *__restrict__ cw, const uint8_t *__restrict__ sw, const float *__restrict__ gw,
+    int64_t M, int64_t N, int64_t K, void *__restrict__ y, unsigned tiles_m, unsigned tiles_n) {
+    using namespace fp4dma;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const TileCoord tc = tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, GROUP_M);
+    const int64_t m0 = (int64_t)tc.m * BM, n0 = (int64_t)tc.n * BN;
+    const int64_t nb = K / 16, rb = K / 2;
+    const int nk = (int)(K / BKE);
+
+    v16f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
+
+    // DMA sources.  Code block b = wave + 4q (q = 0..7) covers tile rows
+    // 8b .. 8b+7, lane l filling slot l % 8 of row 8b + l / 8; scale block
+    // `wave` covers rows 64 wave .. +63, one 16-byte row per lane.  Rows past
+    // M or N load a clamped row; their outputs are never stored.
+    Fp4DmaLane L;
+    L.wave = wave;
+    L.hk = lane >> 5;
+    L.sh = 16 * L.hk;
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+        const int row = 8 * (wave + 4 * q) + (lane >> 3);
+        const int piece = (lane & 7) ^ ((row >> 1) & 7);
+        const int64_t gm = m0 + row < M ? m0 + row : M - 1;
+        const int64_t gn = n0 + row < N ? n0 + row : N - 1;
+        L.srcA[q] = ca + gm * rb + piece * 16;
+        L.srcW[q] = cw + gn * rb + piece * 16;
+    }
+    {
+        const int row = 64 * wave + lane;
+        const int64_t gm = m0 + row < M ? m0 + row : M - 1;
+        const int64_t gn = n0 + row < N ? n0 + row : N - 1;
+        L.srcSA = sa + gm * nb;
+        L.srcSW = sw + gn * nb;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        L.ra[i] = wm * 128 + i * 32 + (lane & 31);
+        L.rw[i] = wn * 128 + i * 32 + (lane & 31);
+    }
+
+    {
+        typedef __attribute__((address_space(3))) void lds_void;
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+            const int b = wave + 4 * q;
+            __builtin_amdgcn_global_load_lds((const void *)L.srcA[q], (lds_void *)(lds + b * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)L.srcW[q], (lds_void *)(lds + CODES + b * 1024), 16, 0, 0);
+        }
+        __builtin_amdgcn_global_load_lds((const void *)L.srcSA, (lds_void *)(lds + 2 * CODES + wave * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void *)L.srcSW, (lds_void *)(lds + 2 * CODES + SCALES + wave * 1024), 16, 0, 0);
+    }
+    for (int kt = 0; kt < nk; kt++) {
+        __builtin_amdgcn_s_waitcnt(0xC07F & ~0xC00F);  // vmcnt(0): this wave's loads of stage kt
+        __syncthreads();                               // ... and every other wave's
+        fp4dma_stage(lds + (kt & 1) * STAGE, lds + ((kt & 1) ^ 1) * STAGE, kt + 1 < nk, kt + 1, L, acc);
+    }
+    __syncthreads();  // every wave is done reading the stage buffers before they hold bands
+
+    fp4_epilogue<OUT>(acc, lds, ga, gw, M, N, m0, n0, wave, wm, wn, lane, y);
+}
+
 // ---------------------------------------------------------------------------
 // Variant DMPQ_FP4_SCALED_MFMA: gfx950's block-scaled MFMA
 // (v_mfma_scale_f32_32x32x64_f8f6f4, E2M1 operands) with the NVFP4 scales
@@ -529,6 +730,8 @@ hipError_t launch_gemm_nvfp4(hipStream_t s, const uint8_t *ca, const uint8_t *sa
         if (e == hipSuccess) e = allow_lds(gemm_fp4_f16_kernel<1>, 2 * STAGE);
         if (e == hipSuccess) e = allow_lds(gemm_fp4_fast_kernel<0>, 2 * STAGE);
         if (e == hipSuccess) e = allow_lds(gemm_fp4_fast_kernel<1>, 2 * STAGE);
+        if (e == hipSuccess) e = allow_lds(gemm_fp4_dma_kernel<0>, fp4dma::LDS_BYTES);
+        if (e == hipSuccess) e = allow_lds(gemm_fp4_dma_kernel<1>, fp4dma::LDS_BYTES);
         return e;
     }();
     if (attr != hipSuccess) return attr;
@@ -544,6 +747,13 @@ hipError_t launch_gemm_nvfp4(hipStream_t s, const uint8_t *ca, const uint8_t *sa
         return hipGetLastError();
     }
     const bool fast = K % (4 * 16) == 0;
+    if (K % fp4dma::BKE == 0) {
+        if (out_dtype == 0)
+            hipLaunchKernelGGL(gemm_fp4_dma_kernel<0>, grid, block, fp4dma::LDS_BYTES, s, ca, sa, ga, cw, sw, gw, M, N, K, y, utm, utn);
+        else
+            hipLaunchKernelGGL(gemm_fp4_dma_kernel<1>, grid, block, fp4dma::LDS_BYTES, s, ca, sa, ga, cw, sw, gw, M, N, K, y, utm, utn);
+        return hipGetLastError();
+    }
     if (fast && out_dtype == 0)
         hipLaunchKernelGGL(gemm_fp4_fast_kernel<0>, grid, block, 2 * STAGE, s, ca, sa, ga, cw, sw, gw, M, N, K, y, utm, utn);
     else if (fast)
