@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device.hpp"
+
 namespace dmpq {
 
 // Map a 1-D workgroup id onto an (m, n) output tile.
@@ -70,7 +72,9 @@ __device__ __forceinline__ void epi_band_to_global(const uint8_t *band, void *y,
         if (row >= M || col >= N) continue;
         uint8_t *dst = static_cast<uint8_t *>(y) + (row * N + col) * ESIZE;
         if (vec && col + PER <= N) {
-            *reinterpret_cast<uint4 *>(dst) = v;
+            // streaming store: every tile of a launch finishes at about the same
+            // time, and the burst of outputs drains faster without L2 allocation
+            store_nt16(dst, v);
         } else {
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll

@@ -203,33 +203,44 @@ __device__ __forceinline__ int swz128(int row, int kc) { return kc ^ ((row >> 1)
 // Per-lane state of the DMA kernel: DMA sources and fragment rows.
 struct I8DmaLane {
     const int8_t *srcA[i8dma::BLOCKS], *srcW[i8dma::BLOCKS];
-    int ra[4], rw[4];
-    int wave, hk;
+    int offA, offW;  // byte offset of the lane's first fragment row (A; W incl. the A tile)
+    int sw, hk;      // swizzle key of the lane's rows, K half
+    int wave;
 };
 
 // waitcnt immediate that waits for at most n outstanding vector memory ops
 // (expcnt and lgkmcnt left free)
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-__device__ __forceinline__ void i8dma_issue(int8_t *dst, const I8DmaLane &L, int64_t k0) {
+// Fragments of k-step s (32 K values) of the stage held in `buf`.  Rows
+// ra = wm*128 + 32i + lane%32 all share the swizzle key ((lane%32) >> 1) & 7,
+// so the row block i only adds the constant 32*i*BK (an immediate offset).
+__device__ __forceinline__ void i8dma_frags(const int8_t *buf, const I8DmaLane &L, int s, v4i a[4], v4i b[4]) {
     using namespace i8dma;
-    typedef __attribute__((address_space(3))) void lds_void;
+    const int slot = ((2 * s + L.hk) ^ L.sw) * 16;
+    const int8_t *pa = buf + L.offA + slot;
+    const int8_t *pb = buf + L.offW + slot;
 #pragma unroll
-    for (int q = 0; q < BLOCKS; q++) {
-        const int b = L.wave + 4 * q;
-        __builtin_amdgcn_global_load_lds((const void *)(L.srcA[q] + k0), (lds_void *)(dst + b * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void *)(L.srcW[q] + k0), (lds_void *)(dst + TILE + b * 1024), 16, 0, 0);
+    for (int i = 0; i < 4; i++) {
+        a[i] = *reinterpret_cast<const v4i *>(pa + i * 32 * BK);
+        b[i] = *reinterpret_cast<const v4i *>(pb + i * 32 * BK);
     }
 }
 
-// Fragments of k-step s (32 K values) of the stage held in `buf`.
-__device__ __forceinline__ void i8dma_frags(const int8_t *buf, const I8DmaLane &L, int s, v4i a[4], v4i b[4]) {
+// One DMA instruction of a stage: q-th 1 KB block of operand `op` (0 = A, 1 = W).
+__device__ __forceinline__ void i8dma_one(int8_t *dst, const I8DmaLane &L, int64_t k0, int q, int op) {
     using namespace i8dma;
-    const int kc = 2 * s + L.hk;
+    typedef __attribute__((address_space(3))) void lds_void;
+    const int b = L.wave + 4 * q;
+    const int8_t *src = (op ? L.srcW[q] : L.srcA[q]) + k0;
+    __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(dst + op * TILE + b * 1024), 16, 0, 0);
+}
+
+__device__ __forceinline__ void i8dma_issue(int8_t *dst, const I8DmaLane &L, int64_t k0) {
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        a[i] = *reinterpret_cast<const v4i *>(buf + L.ra[i] * BK + swz128(L.ra[i], kc) * 16);
-        b[i] = *reinterpret_cast<const v4i *>(buf + TILE + L.rw[i] * BK + swz128(L.rw[i], kc) * 16);
+    for (int q = 0; q < i8dma::BLOCKS; q++) {
+        i8dma_one(dst, L, k0, q, 0);
+        i8dma_one(dst, L, k0, q, 1);
     }
 }
 
@@ -241,18 +252,45 @@ __device__ __forceinline__ void i8_mfma16(v16i (&acc)[4][4], const v4i a[4], con
             acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[j], a[i], acc[i][j], 0, 0, 0);
 }
 
-// One stage: on entry a0/b0 and a1/b1 hold k-steps 0 and 1 of the stage in
-// `cur`.  After k-step 2 the wave waits for the DMA of the next stage (into
-// `nxt`) and for every wave to finish reading `cur`, reuses `cur` for the DMA
-// two stages ahead, and reads k-steps 0 and 1 of the next stage while k-step
-// 3 runs.  `cur` and `nxt` are separate restrict parameters so that, once
-// inlined, the compiler knows the reads of `nxt` cannot alias the DMA into
-// `cur` and does not wait for it.
-__device__ __forceinline__ void i8dma_stage(int8_t *__restrict__ cur, const int8_t *__restrict__ nxt,
-                                            bool has_next, bool issue, int64_t k_issue,
+// 16 MFMAs with half of a stage's DMA (blocks q = 4h .. 4h+3 of both
+// operands) placed one instruction after every two MFMAs, so that the
+// workgroup's DMA reaches the texture unit spread over the MFMA stream
+// instead of in one burst that stalls instruction issue.
+__device__ __forceinline__ void i8_mfma16_dma(v16i (&acc)[4][4], const v4i a[4], const v4i b[4],
+                                              int8_t *dst, const I8DmaLane &L, int64_t k0, int h) {
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[j], a[i], acc[i][j], 0, 0, 0);
+            const int t = 4 * i + j;
+            if (t & 1) i8dma_one(dst, L, k0, 4 * h + (t >> 2), (t >> 1) & 1);
+        }
+#pragma unroll
+    for (int t = 0; t < 8; t++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 VMEM read (the DMA)
+    }
+}
+
+// One stage.  On entry a0/b0 and a1/b1 hold k-steps 0 and 1 of the stage in
+// `cur`.  With the MFMAs of k-step 0 the wave issues the second half of the
+// next stage's DMA into `nxt` (its first half went out with the previous
+// stage's last k-step).  After k-step 2 it waits for that DMA and for every
+// wave to finish reading `cur`, reads k-step 0 of the next stage, and with the
+// MFMAs of k-step 3 issues the first half of the DMA two stages ahead into
+// `cur`.  Both DMA halves are issued on every stage so that the MFMA code has
+// no branches (the accumulators would not survive them in registers); where
+// no such stage exists the caller passes a stage whose bytes the target
+// buffer already holds or that nobody reads again, so any read racing with
+// it sees unchanged data.  `cur` and `nxt` are separate restrict parameters
+// so that, once inlined, the compiler knows the reads of `nxt` cannot alias
+// the DMA into `cur` and does not wait for it.
+__device__ __forceinline__ void i8dma_stage(int8_t *__restrict__ cur, int8_t *__restrict__ nxt,
+                                            bool has_next, int64_t k_second, int64_t k_first,
                                             const I8DmaLane &L, v16i (&acc)[4][4],
                                             v4i (&a0)[4], v4i (&b0)[4], v4i (&a1)[4], v4i (&b1)[4]) {
-    i8_mfma16(acc, a0, b0);
+    i8_mfma16_dma(acc, a0, b0, nxt, L, k_second, 1);
     i8dma_frags(cur, L, 2, a0, b0);
     i8_mfma16(acc, a1, b1);
     i8dma_frags(cur, L, 3, a1, b1);
@@ -260,10 +298,9 @@ __device__ __forceinline__ void i8dma_stage(int8_t *__restrict__ cur, const int8
     if (has_next) {
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's DMA of the next stage
         __syncthreads();                           // ... every wave's, and `cur` is free
-        if (issue) i8dma_issue(cur, L, k_issue);
         i8dma_frags(nxt, L, 0, a0, b0);
     }
-    i8_mfma16(acc, a1, b1);
+    i8_mfma16_dma(acc, a1, b1, cur, L, k_first, 0);
     if (has_next) i8dma_frags(nxt, L, 1, a1, b1);
 }
 
@@ -303,11 +340,9 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_dma_kernel(
         L.srcA[q] = A + gm * K + kc * 16;
         L.srcW[q] = W + gn * K + kc * 16;
     }
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        L.ra[i] = wm * 128 + i * 32 + (lane & 31);
-        L.rw[i] = wn * 128 + i * 32 + (lane & 31);
-    }
+    L.offA = (wm * 128 + (lane & 31)) * BK;
+    L.offW = TILE + (wn * 128 + (lane & 31)) * BK;
+    L.sw = ((lane & 31) >> 1) & 7;
 
     const int nk = (int)(K / BK);
     i8dma_issue(lds, L, 0);
@@ -324,8 +359,14 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_dma_kernel(
     for (int kt = 0; kt < nk; kt++) {
         int8_t *cur = lds + (kt & 1) * STAGE;
         int8_t *nxt = lds + ((kt & 1) ^ 1) * STAGE;
-        i8dma_stage(cur, nxt, kt + 1 < nk, kt + 2 < nk, (int64_t)(kt + 2) * BK, L, acc, a0, b0, a1, b1);
+        // second half into nxt: stage kt+1 (kt = 0 repeats the prologue's
+        // copy of it; after the last stage nxt is never read); first half
+        // into cur: stage kt+2, or stage kt itself when there is none
+        const int64_t k_second = (int64_t)(kt + 1 < nk ? kt + 1 : nk - 1) * BK;
+        const int64_t k_first = (int64_t)(kt + 2 < nk ? kt + 2 : kt) * BK;
+        i8dma_stage(cur, nxt, kt + 1 < nk, k_second, k_first, L, acc, a0, b0, a1, b1);
     }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the last stage's DMA has landed
     __syncthreads();  // every wave is done reading the stage buffers before they hold bands
 
     constexpr int ES = OUT == 1 ? 2 : 4;
