@@ -423,58 +423,72 @@ static_assert(4 * EpiBand<4>::BYTES <= LDS_BYTES, "epilogue bands fit in the sta
 constexpr unsigned GROUP_M = 8;
 }  // namespace fp4dma
 
-// One stage of the DMA kernel: issue the DMA of the next stage into `nxt`
-// (when `issue`), then run the stage held in `cur`.  The two buffers are
-// separate restrict parameters so that, once inlined, the compiler knows the
-// stage's LDS reads cannot alias the DMA in flight and does not wait for it.
+// Per-lane state of the DMA kernel.  Fragment rows ra = wm*128 + 32i + lane%32
+// share the swizzle key ((lane%32) >> 1) & 7, so the row block i only adds a
+// constant (an immediate offset) to the lane's base addresses.
 struct Fp4DmaLane {
     const uint8_t *srcA[8], *srcW[8], *srcSA, *srcSW;
-    int ra[4], rw[4];
-    int wave, hk, sh;
+    int offA, offW, offSA, offSW;  // byte offsets of the lane's first fragment row in a stage
+    int wave, hk, sh, sw;
 };
 
-__device__ __forceinline__ void fp4dma_stage(const uint8_t *__restrict__ cur, uint8_t *__restrict__ nxt,
-                                             bool issue, int64_t st_next, const Fp4DmaLane &L,
-                                             v16f (&acc)[4][4]) {
+// DMA instruction d (0..17) of a stage: code blocks q = d/2 of A (d even) and
+// W (d odd), then the A and the W scale block.
+__device__ __forceinline__ void fp4dma_one(uint8_t *dst, const Fp4DmaLane &L, int64_t st, int d) {
     using namespace fp4dma;
     typedef __attribute__((address_space(3))) void lds_void;
-    if (issue) {
-#pragma unroll
-        for (int q = 0; q < 8; q++) {
-            const int b = L.wave + 4 * q;
-            __builtin_amdgcn_global_load_lds((const void *)(L.srcA[q] + st_next * CROW),
-                                             (lds_void *)(nxt + b * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void *)(L.srcW[q] + st_next * CROW),
-                                             (lds_void *)(nxt + CODES + b * 1024), 16, 0, 0);
-        }
-        __builtin_amdgcn_global_load_lds((const void *)(L.srcSA + st_next * SROW),
-                                         (lds_void *)(nxt + 2 * CODES + L.wave * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void *)(L.srcSW + st_next * SROW),
-                                         (lds_void *)(nxt + 2 * CODES + SCALES + L.wave * 1024), 16, 0, 0);
+    if (d < 16) {
+        const int q = d >> 1, b = L.wave + 4 * q;
+        const uint8_t *src = ((d & 1) ? L.srcW[q] : L.srcA[q]) + st * CROW;
+        __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(dst + (d & 1) * CODES + b * 1024), 16, 0, 0);
+    } else {
+        const uint8_t *src = (d == 17 ? L.srcSW : L.srcSA) + st * SROW;
+        __builtin_amdgcn_global_load_lds((const void *)src,
+                                         (lds_void *)(dst + 2 * CODES + (d == 17) * SCALES + L.wave * 1024), 16, 0, 0);
     }
+}
+
+// One stage of the DMA kernel: run the stage held in `cur` while the DMA of
+// stage st_next goes into `nxt`, its 18 instructions spread over the MFMAs of
+// the first 64-element chunk (one after every third MFMA) rather than issued
+// in one burst.  The DMA is issued on every stage so that no branch wraps the
+// MFMA code; after the last stage the caller passes a stage nobody reads
+// again.  The two buffers are separate restrict parameters so that, once
+// inlined, the compiler knows the stage's LDS reads cannot alias the DMA in
+// flight and does not wait for it.
+__device__ __forceinline__ void fp4dma_stage(const uint8_t *__restrict__ cur, uint8_t *__restrict__ nxt,
+                                             int64_t st_next, const Fp4DmaLane &L,
+                                             v16f (&acc)[4][4]) {
+    using namespace fp4dma;
     uint4 sA[4], sW[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        sA[i] = *reinterpret_cast<const uint4 *>(cur + 2 * CODES + L.ra[i] * SROW);
-        sW[i] = *reinterpret_cast<const uint4 *>(cur + 2 * CODES + SCALES + L.rw[i] * SROW);
+        sA[i] = *reinterpret_cast<const uint4 *>(cur + L.offSA + i * 32 * SROW);
+        sW[i] = *reinterpret_cast<const uint4 *>(cur + L.offSW + i * 32 * SROW);
     }
 #define DMPQ_F4D_CODES(dA, dW, c)                                                              \
-    _Pragma("unroll") for (int i = 0; i < 4; i++) {                                            \
-        dA[i] = *reinterpret_cast<const uint4 *>(                                              \
-            cur + L.ra[i] * CROW + (((2 * (c) + L.hk) ^ ((L.ra[i] >> 1) & 7)) * 16));          \
-        dW[i] = *reinterpret_cast<const uint4 *>(                                              \
-            cur + CODES + L.rw[i] * CROW + (((2 * (c) + L.hk) ^ ((L.rw[i] >> 1) & 7)) * 16));  \
+    {                                                                                          \
+        const int slot = ((2 * (c) + L.hk) ^ L.sw) * 16;                                       \
+        _Pragma("unroll") for (int i = 0; i < 4; i++) {                                        \
+            dA[i] = *reinterpret_cast<const uint4 *>(cur + L.offA + slot + i * 32 * CROW);     \
+            dW[i] = *reinterpret_cast<const uint4 *>(cur + L.offW + slot + i * 32 * CROW);     \
+        }                                                                                      \
     }
 #define DMPQ_F4D_DQ(cA, cW, scA, scW, S, fa, fb)                                               \
     _Pragma("unroll") for (int i = 0; i < 4; i++) {                                            \
         fa[i] = dq8<S>(cA[i], scA[i]);                                                         \
         fb[i] = dq8<S>(cW[i], scW[i]);                                                         \
     }
-#define DMPQ_F4D_MFMA(fa, fb)                                                                  \
+// 16 MFMAs; with DMA (D0 >= 0) instructions D0, D0+1, ... (below 18) after
+// MFMAs 2, 5, 8, 11, 14
+#define DMPQ_F4D_MFMA(fa, fb, D0)                                                              \
     _Pragma("unroll") for (int i = 0; i < 4; i++)                                              \
-        _Pragma("unroll") for (int j = 0; j < 4; j++)                                          \
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
-#define DMPQ_F4D_CHUNK(cA, cW, c)                                                              \
+        _Pragma("unroll") for (int j = 0; j < 4; j++) {                                        \
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0); \
+            const int t = 4 * i + j;                                                           \
+            if ((D0) >= 0 && t % 3 == 2 && (D0) + t / 3 < 18) fp4dma_one(nxt, L, st_next, (D0) + t / 3); \
+        }
+#define DMPQ_F4D_CHUNK(cA, cW, c, D0)                                                          \
     {                                                                                          \
         v2h scA[4], scW[4];                                                                    \
         _Pragma("unroll") for (int i = 0; i < 4; i++) {                                        \
@@ -486,22 +500,22 @@ __device__ __forceinline__ void fp4dma_stage(const uint8_t *__restrict__ cur, ui
         v8h fa0[4], fb0[4], fa1[4], fb1[4];                                                    \
         DMPQ_F4D_DQ(cA, cW, scA, scW, 0, fa0, fb0)                                             \
         DMPQ_F4D_DQ(cA, cW, scA, scW, 1, fa1, fb1)                                             \
-        DMPQ_F4D_MFMA(fa0, fb0)                                                                \
+        DMPQ_F4D_MFMA(fa0, fb0, (D0))                                                          \
         DMPQ_F4D_DQ(cA, cW, scA, scW, 2, fa0, fb0)                                             \
-        DMPQ_F4D_MFMA(fa1, fb1)                                                                \
+        DMPQ_F4D_MFMA(fa1, fb1, (D0) < 0 ? -1 : (D0) + 5)                                      \
         DMPQ_F4D_DQ(cA, cW, scA, scW, 3, fa1, fb1)                                             \
-        DMPQ_F4D_MFMA(fa0, fb0)                                                                \
-        DMPQ_F4D_MFMA(fa1, fb1)                                                                \
+        DMPQ_F4D_MFMA(fa0, fb0, (D0) < 0 ? -1 : (D0) + 10)                                     \
+        DMPQ_F4D_MFMA(fa1, fb1, (D0) < 0 ? -1 : (D0) + 15)                                     \
     }
     uint4 cA0[4], cW0[4], cA1[4], cW1[4];
     DMPQ_F4D_CODES(cA0, cW0, 0)
     DMPQ_F4D_CODES(cA1, cW1, 1)
-    DMPQ_F4D_CHUNK(cA0, cW0, 0)
+    DMPQ_F4D_CHUNK(cA0, cW0, 0, 0)
     DMPQ_F4D_CODES(cA0, cW0, 2)
-    DMPQ_F4D_CHUNK(cA1, cW1, 1)
+    DMPQ_F4D_CHUNK(cA1, cW1, 1, -1)
     DMPQ_F4D_CODES(cA1, cW1, 3)
-    DMPQ_F4D_CHUNK(cA0, cW0, 2)
-    DMPQ_F4D_CHUNK(cA1, cW1, 3)
+    DMPQ_F4D_CHUNK(cA0, cW0, 2, -1)
+    DMPQ_F4D_CHUNK(cA1, cW1, 3, -1)
 #undef DMPQ_F4D_CODES
 #undef DMPQ_F4D_DQ
 #undef DMPQ_F4D_MFMA
@@ -555,28 +569,21 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_dma_kernel(
         L.srcSA = sa + gm * nb;
         L.srcSW = sw + gn * nb;
     }
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        L.ra[i] = wm * 128 + i * 32 + (lane & 31);
-        L.rw[i] = wn * 128 + i * 32 + (lane & 31);
-    }
+    L.offA = (wm * 128 + (lane & 31)) * CROW;
+    L.offW = CODES + (wn * 128 + (lane & 31)) * CROW;
+    L.offSA = 2 * CODES + (wm * 128 + (lane & 31)) * SROW;
+    L.offSW = 2 * CODES + SCALES + (wn * 128 + (lane & 31)) * SROW;
+    L.sw = ((lane & 31) >> 1) & 7;
 
-    {
-        typedef __attribute__((address_space(3))) void lds_void;
 #pragma unroll
-        for (int q = 0; q < 8; q++) {
-            const int b = wave + 4 * q;
-            __builtin_amdgcn_global_load_lds((const void *)L.srcA[q], (lds_void *)(lds + b * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void *)L.srcW[q], (lds_void *)(lds + CODES + b * 1024), 16, 0, 0);
-        }
-        __builtin_amdgcn_global_load_lds((const void *)L.srcSA, (lds_void *)(lds + 2 * CODES + wave * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void *)L.srcSW, (lds_void *)(lds + 2 * CODES + SCALES + wave * 1024), 16, 0, 0);
-    }
+    for (int d = 0; d < 18; d++) fp4dma_one(lds, L, 0, d);
     for (int kt = 0; kt < nk; kt++) {
         __builtin_amdgcn_s_waitcnt(0xC07F & ~0xC00F);  // vmcnt(0): this wave's loads of stage kt
         __syncthreads();                               // ... and every other wave's
-        fp4dma_stage(lds + (kt & 1) * STAGE, lds + ((kt & 1) ^ 1) * STAGE, kt + 1 < nk, kt + 1, L, acc);
+        // after the last stage the copy goes to a buffer nobody reads again
+        fp4dma_stage(lds + (kt & 1) * STAGE, lds + ((kt & 1) ^ 1) * STAGE, kt + 1 < nk ? kt + 1 : kt, L, acc);
     }
+    __builtin_amdgcn_s_waitcnt(0xC07F & ~0xC00F);  // the last copy has landed
     __syncthreads();  // every wave is done reading the stage buffers before they hold bands
 
     fp4_epilogue<OUT>(acc, lds, ga, gw, M, N, m0, n0, wave, wm, wn, lane, y);
