@@ -77,6 +77,7 @@ def _declare(L):
         "orc_quant_nvfp4": (C.c_int, [_p(u16), i64, i64, C.c_int, _p(u8), _p(u8), _p(f32)]),
         "orc_prep_weight": (C.c_int, [_p(u16), i64, i64, C.c_int, _p(u8), _p(u8), _p(f32),
                                       _p(i8), _p(f32)]),
+        "orc_w8_from_nvfp4": (C.c_int, [_p(u8), _p(u8), _p(f32), i64, i64, _p(i8), _p(f32)]),
         "orc_gemm_int8": (C.c_int, [_p(i8), _p(f32), _p(i8), _p(f32), i64, i64, i64,
                                     _p(i64), i64, _p(i32), _p(f32)]),
         "orc_gemm_nvfp4": (C.c_int, [_p(u8), _p(u8), f32, _p(u8), _p(u8), f32, i64, i64, i64,
@@ -188,6 +189,22 @@ def prep_weight(w: np.ndarray, int8_mode: int = W8_FROM_NVFP4):
     if rc != 0:
         raise ValueError(f"orc_prep_weight: bad shape/mode {w.shape} {int8_mode}")
     return dict(cw=cw, sw=sw, gw=float(gw[0]), qw=qw, sw_row=swr)
+
+
+def w8_from_nvfp4(cw: np.ndarray, sw: np.ndarray, gw: float):
+    """INT8 weight (qw [N x K], sw_row [N]) derived from an NVFP4 weight."""
+    cw = np.ascontiguousarray(cw, np.uint8)
+    sw = np.ascontiguousarray(sw, np.uint8)
+    N, K = cw.shape[0], 2 * cw.shape[1]
+    assert sw.shape == (N, K // 16)
+    g = np.array([gw], np.float32)
+    qw = np.empty((N, K), np.int8)
+    swr = np.empty(N, np.float32)
+    rc = lib().orc_w8_from_nvfp4(_ptr(cw, C.c_uint8), _ptr(sw, C.c_uint8), _ptr(g, C.c_float),
+                                 N, K, _ptr(qw, C.c_int8), _ptr(swr, C.c_float))
+    if rc != 0:
+        raise ValueError(f"orc_w8_from_nvfp4: bad shape {N} x {K}")
+    return qw, swr
 
 
 # ---- GEMMs ----------------------------------------------------------------

@@ -279,17 +279,10 @@ int orc_quant_nvfp4(const uint16_t *x, int64_t M, int64_t K, int flags,
  * channel INT8 quant of the rotated bf16 weight (same rule as activations).
  * ==================================================================== */
 
-int orc_prep_weight(const uint16_t *w, int64_t N, int64_t K, int int8_mode,
-                    uint8_t *cw, uint8_t *sw, float *gw,
-                    int8_t *qw, float *sw_row)
+int orc_w8_from_nvfp4(const uint8_t *cw, const uint8_t *sw, const float *gw,
+                      int64_t N, int64_t K, int8_t *qw, float *sw_row)
 {
     if (bad_shape(N, K))
-        return -1;
-    if (orc_quant_nvfp4(w, N, K, 0, cw, sw, gw) != 0)
-        return -1;
-    if (int8_mode == ORC_W8_DIRECT)
-        return orc_quant_int8(w, N, K, 0, qw, sw_row);
-    if (int8_mode != ORC_W8_FROM_NVFP4)
         return -1;
     const int64_t nb = K / 16;
     const float g = *gw;
@@ -325,6 +318,21 @@ int orc_prep_weight(const uint16_t *w, int64_t N, int64_t K, int int8_mode,
         free(wd);
     }
     return 0;
+}
+
+int orc_prep_weight(const uint16_t *w, int64_t N, int64_t K, int int8_mode,
+                    uint8_t *cw, uint8_t *sw, float *gw,
+                    int8_t *qw, float *sw_row)
+{
+    if (bad_shape(N, K))
+        return -1;
+    if (orc_quant_nvfp4(w, N, K, 0, cw, sw, gw) != 0)
+        return -1;
+    if (int8_mode == ORC_W8_DIRECT)
+        return orc_quant_int8(w, N, K, 0, qw, sw_row);
+    if (int8_mode != ORC_W8_FROM_NVFP4)
+        return -1;
+    return orc_w8_from_nvfp4(cw, sw, gw, N, K, qw, sw_row);
 }
 
 /* ======================================================================

@@ -66,6 +66,9 @@ int orc_quant_nvfp4(const uint16_t *x, int64_t M, int64_t K, int flags,
 int orc_prep_weight(const uint16_t *w, int64_t N, int64_t K, int int8_mode,
                     uint8_t *cw, uint8_t *sw, float *gw,
                     int8_t *qw, float *sw_row);
+/* The FROM_NVFP4 step alone: INT8 weight from an NVFP4 weight (cw, sw, gw). */
+int orc_w8_from_nvfp4(const uint8_t *cw, const uint8_t *sw, const float *gw,
+                      int64_t N, int64_t K, int8_t *qw, float *sw_row);
 
 /* ---- GEMMs (rows == NULL: all M rows; else the n_rows listed rows, and the
  *      outputs hold n_rows x N values in list order) -------------------- */

@@ -185,6 +185,47 @@ def test_prep_weight_int8_from_nvfp4(orc):
     assert np.array_equal(np.sign(p["qw"]), np.sign(np.round(wd / p["sw_row"][:, None])))
 
 
+def _pack_nibbles(codes):
+    codes = np.asarray(codes, np.uint8)
+    return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+
+
+def test_w8_from_nvfp4_closed_form(orc):
+    # g = 127/128 and a row amax of 4 * g = 127/32 make 127/amax exactly 32 in
+    # fp32, so every code is the round-half-even of v * s * 127/4 in exact
+    # rational arithmetic (E2M1 values from the OCP table; E4M3 0x38 = 1.0,
+    # 0x30 = 0.5).  v*s = 2 lands on the tie 63.5 -> 64.
+    from fractions import Fraction
+    e2m1 = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3),
+            Fraction(4), Fraction(6)]
+    K = 32
+    row0 = [0, 1, 2, 3, 4, 5, 6, 9, 10, 11, 12, 13, 14, 8, 1, 6,    # group 0: scale 1.0
+            7, 15, 5, 13, 3, 11, 1, 9, 4, 12, 2, 10, 6, 14, 0, 8]   # group 1: scale 0.5
+    row1 = [c ^ 8 for c in row0]                                    # every sign flipped
+    row2 = [0] * K                                                  # all zero
+    codes = np.array([row0, row1, row2], np.uint8)
+    scales = np.array([[0x38, 0x30]] * 3, np.uint8)
+    g = Fraction(127, 128)
+    qw, swr = orc.w8_from_nvfp4(_pack_nibbles(codes), scales, float(g))
+    for n in range(2):
+        for k in range(K):
+            c = int(codes[n, k])
+            v = e2m1[c & 7] * (-1 if c & 8 else 1)
+            s = Fraction(1) if k < 16 else Fraction(1, 2)
+            want = round(v * s * g * 32)  # Fraction.__round__ ties to even
+            assert qw[n, k] == want, (n, k, c, want, qw[n, k])
+        assert swr[n] == np.float32(1 / 32)
+    assert np.all(qw[2] == 0) and swr[2] == 0.0
+    assert qw[0, 4] == 64  # the tie: v*s = 2
+
+
+def test_w8_from_nvfp4_matches_prep_weight(orc):
+    rng = np.random.default_rng(14)
+    p = orc.prep_weight(workloads.weight(rng, 33, 96))
+    qw, swr = orc.w8_from_nvfp4(p["cw"], p["sw"], p["gw"])
+    assert np.array_equal(qw, p["qw"]) and np.array_equal(swr.view(np.uint32), p["sw_row"].view(np.uint32))
+
+
 def test_prep_weight_direct_is_int8_quant(orc):
     rng = np.random.default_rng(12)
     w = workloads.weight(rng, 24, 48)
