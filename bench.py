@@ -9,7 +9,9 @@ One step is one pass of the whole hot path over a CogVideoX-5B-like batch
      0.05, 0.40, so two blocks route to INT8 and two to NVFP4);
   2. per block, per linear (qkv 9216x3072, out 3072x3072, ffn_up 12288x3072,
      ffn_down 3072x12288): Hadamard + activation quant at the routed
-     precision, then the quantized GEMM against offline-prepared weights;
+     precision, then the quantized GEMM against the offline NVFP4 weights;
+     an INT8-routed linear first converts its NVFP4 weight to INT8 into one
+     shared scratch buffer (only the 4.5-bit weights are kept);
   3. per block, the Temporal Delta Cache refresh (delta, four L1 sums).
 Inputs are synthetic (seeded, drawn on the device) and resident in HBM
 before timing; weights are prepared once, outside the timed region.
@@ -39,6 +41,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--out-dtype", choices=["bf16", "f32"], default="bf16",
                    help="GEMM output type (bf16 feeds the next layer; f32 is the parity contract)")
+    p.add_argument("--int8-weights", choices=["convert", "stored"], default="convert",
+                   help="convert: only NVFP4 weights are kept and an INT8-routed linear converts its "
+                        "weight into one scratch buffer right before its GEMM (the method's weight "
+                        "handling); stored: use INT8 weights prepared offline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=512,
                    help="rows of the qkv linear the oracle runs for the CPU baseline")
@@ -148,6 +154,9 @@ def main():
                     sc=torch.empty((M, K // 16), dtype=torch.uint8, device="cuda"),
                     g=torch.zeros(1, device="cuda")) for K in ks}
     ybuf = {lin.name: torch.empty((M, lin.N), dtype=ydt, device="cuda") for lin in cfg.linears}
+    big = max(lin.N * lin.K for lin in cfg.linears)
+    w8_scratch = torch.empty(big, dtype=torch.int8, device="cuda")
+    s8_scratch = torch.empty(max(lin.N for lin in cfg.linears), device="cuda")
     ws = dm.new_workspace(dm.OP_TDC)
     gsums = torch.zeros((n_blocks, 2), dtype=torch.float64, device="cuda")
     tsums = torch.zeros((n_blocks, 4), dtype=torch.float64, device="cuda")
@@ -180,7 +189,13 @@ def main():
                 if routes[b][li] == dm.ROUTE_INT8:
                     kt("hadamard_quant_int8", 3.0 * M * lin.K + 4.0 * M,
                        dm.hadamard_quant_int8, L["x"], qb["q"], qb["s"])
-                    kt("qgemm_int8", flops, dm.qgemm_int8, qb["q"], qb["s"], L["qw"], L["swr"],
+                    qw, swr = L["qw"], L["swr"]
+                    if args.int8_weights == "convert":
+                        qw = w8_scratch[:lin.N * lin.K].view(lin.N, lin.K)
+                        swr = s8_scratch[:lin.N]
+                        kt("weight_int8_from_nvfp4", (0.5 + 1.0 / 16 + 1.0) * lin.N * lin.K + 8.0 * lin.N,
+                           dm.weight_int8_from_nvfp4, L["cw"], L["sw"], L["gw"], qw, swr)
+                    kt("qgemm_int8", flops, dm.qgemm_int8, qb["q"], qb["s"], qw, swr,
                        ybuf[lin.name], out_dtype)
                 else:
                     kt("hadamard_quant_nvfp4", (2.0 + 0.5 + 1.0 / 16) * M * lin.K + 4.0,
@@ -221,6 +236,7 @@ def main():
     # ---- per-kernel figures and the roofline of the dominant kernel -----------
     ksum = kt.summary(args.steps)
     peaks = {"hadamard_quant_int8": ("hbm", HBM_GBPS, "GB/s"),
+             "weight_int8_from_nvfp4": ("hbm", HBM_GBPS, "GB/s"),
              "hadamard_quant_nvfp4": ("hbm", HBM_GBPS, "GB/s"),
              "gamma_sums": ("hbm", HBM_GBPS, "GB/s"),
              "tdc_step_refresh": ("hbm", HBM_GBPS, "GB/s"),
@@ -263,6 +279,7 @@ def main():
                    "tokens": M, "hidden": H, "blocks": n_blocks,
                    "routes_per_block": ["INT8" if r[0] else "NVFP4" for r in routes_seen[-1]],
                    "gemm_out": args.out_dtype,
+                   "int8_weights": args.int8_weights,
                    "gemm_tera_ops_per_step": round(gemm_ops_step / 1e12, 3)},
         "act_quant_GBps": round(q_bytes * 1e-9 / (q_ms * 1e-3), 1),
         "kernels": kernels,

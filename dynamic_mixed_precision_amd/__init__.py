@@ -30,7 +30,7 @@ OP_GAMMA, OP_QUANT_NVFP4, OP_TDC, OP_PREP_WEIGHT = 0, 1, 2, 3
 EXPORTS = ("dmpq_last_error", "dmpq_version", "dmpq_workspace_bytes", "dmpq_gamma_sums",
            "dmpq_gate_and_route", "dmpq_hadamard_quant_int8", "dmpq_hadamard_quant_nvfp4",
            "dmpq_qgemm_int8", "dmpq_qgemm_nvfp4", "dmpq_tdc_init", "dmpq_tdc_decide",
-           "dmpq_tdc_step", "dmpq_tdc_commit", "dmpq_prep_weight")
+           "dmpq_tdc_step", "dmpq_tdc_commit", "dmpq_prep_weight", "dmpq_weight_int8_from_nvfp4")
 
 
 class DmpqError(RuntimeError):
@@ -82,6 +82,7 @@ def _declare(L):
         "dmpq_tdc_step": (i32, [vp, i32, vp, vp, vp, i64, i32, vp, vp, C.c_size_t]),
         "dmpq_tdc_commit": (i32, [C.POINTER(TdcState), i32, pd]),
         "dmpq_prep_weight": (i32, [vp, vp, i64, i64, i32, vp, vp, vp, vp, vp, vp, C.c_size_t]),
+        "dmpq_weight_int8_from_nvfp4": (i32, [vp, vp, vp, vp, i64, i64, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -214,3 +215,10 @@ def prep_weight(w, cw, sw, gw, qw, sw_row, ws, int8_mode: int = W8_FROM_NVFP4,
     _check(lib().dmpq_prep_weight(_stream(stream), _ptr(w), N, K, int8_mode, _ptr(cw), _ptr(sw),
                                   _ptr(gw), _ptr(qw), _ptr(sw_row), _ptr(ws), ws.numel()),
            "dmpq_prep_weight")
+
+
+def weight_int8_from_nvfp4(cw, sw, gw, qw, sw_row, stream=None) -> None:
+    """INT8 weight (qw, sw_row) from the NVFP4 weight (cw, sw, gw)."""
+    N, K = cw.shape[0], 2 * cw.shape[1]
+    _check(lib().dmpq_weight_int8_from_nvfp4(_stream(stream), _ptr(cw), _ptr(sw), _ptr(gw), N, K,
+                                             _ptr(qw), _ptr(sw_row)), "dmpq_weight_int8_from_nvfp4")

@@ -287,4 +287,20 @@ dmpq_status dmpq_prep_weight(hipStream_t stream, const uint16_t *w, int64_t N, i
     return hip_status(e, __func__);
 }
 
+dmpq_status dmpq_weight_int8_from_nvfp4(hipStream_t stream, const uint8_t *cw, const uint8_t *sw,
+                                        const float *d_gw, int64_t N, int64_t K, int8_t *qw,
+                                        float *sw_row) {
+    if (N < 0) return fail(DMPQ_ERR_BAD_SHAPE, "%s: N = %lld < 0", __func__, (long long)N);
+    if (dmpq_status s = check_k(__func__, K)) return s;
+    REQUIRE_PTR_N(cw, N);
+    REQUIRE_PTR_N(sw, N);
+    REQUIRE_PTR(d_gw);
+    REQUIRE_PTR_N(qw, N);
+    REQUIRE_PTR_N(sw_row, N);
+    if (!hq_int8_supported(K))
+        return fail(DMPQ_ERR_UNSUPPORTED, "%s: K = %lld exceeds 32768", __func__, (long long)K);
+    if (N == 0) return ok();
+    return hip_status(launch_w8_from_nvfp4(stream, cw, sw, d_gw, N, K, qw, sw_row), __func__);
+}
+
 }  // extern "C"

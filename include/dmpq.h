@@ -226,6 +226,22 @@ dmpq_status dmpq_prep_weight(hipStream_t stream, const uint16_t *w, int64_t N, i
                              int int8_mode, uint8_t *cw, uint8_t *sw, float *d_gw, int8_t *qw,
                              float *sw_row, void *ws, size_t ws_bytes);
 
+/* ---------------------------------------------------------------------------
+ * INT8 weight from the NVFP4 weight, when an INT8-routed linear needs it
+ * ([gist-zh] §2.A weight-handling bullet: weights are kept in NVFP4 and
+ * converted for the INT8 GEMM).  With it a model stores only the 4.5-bit
+ * weights and converts one linear's weight into a scratch INT8 buffer right
+ * before its INT8 GEMM.  Same rule as DMPQ_W8_FROM_NVFP4 of dmpq_prep_weight
+ * (bit-identical output): wd = (E2M1value * E4M3value) * gw, per row
+ * s = amax/127, q = RNE(wd * (127/amax)) clamped to +-127; a row whose
+ * 127/amax is not finite gets s = 0 and q = 0.
+ * cw [N x K/2], sw [N x K/16] E4M3, d_gw fp32 (device) -> qw [N x K] int8,
+ * sw_row [N] fp32.  K % 16 == 0, K <= 32768.  Stream-ordered; no workspace.
+ * ------------------------------------------------------------------------- */
+dmpq_status dmpq_weight_int8_from_nvfp4(hipStream_t stream, const uint8_t *cw, const uint8_t *sw,
+                                        const float *d_gw, int64_t N, int64_t K, int8_t *qw,
+                                        float *sw_row);
+
 #ifdef __cplusplus
 }
 #endif

@@ -125,6 +125,13 @@ def test_validation_before_launch(monkeypatch):
             sums=_Fake((4,)), ws=None)
     _expect(1, dm.prep_weight, _Fake((8, 32)), _Fake((8, 16)), _Fake((8, 2)), _Fake((1,)),
             _Fake((8, 32)), _Fake((8,)), _Fake((65792,)), int8_mode=3)
+    # cw [N x K/2]: K = 2 * 12 = 24 is not a multiple of 16; K = 2 * 32768 is too large
+    _expect(2, dm.weight_int8_from_nvfp4, _Fake((8, 12)), _Fake((8, 1)), _Fake((1,)),
+            _Fake((8, 24)), _Fake((8,)))
+    _expect(4, dm.weight_int8_from_nvfp4, _Fake((8, 32768)), _Fake((8, 4096)), _Fake((1,)),
+            _Fake((8, 65536)), _Fake((8,)))
+    _expect(3, dm.weight_int8_from_nvfp4, _Fake((8, 16)), _Fake((8, 2)), _Fake((1,), addr=0x10004),
+            _Fake((8, 32)), _Fake((8,)))
 
 
 def test_null_pointer_rejected():

@@ -143,6 +143,42 @@ def test_prep_weight_parity(orc, mode, N, K):
     assert np.array_equal(host(qw), ref["qw"])
 
 
+@pytest.mark.parametrize("N,K", [(1, 16), (33, 96), (5760, 1920), (70, 12288), (9216, 3072)])
+def test_weight_int8_from_nvfp4_parity(orc, N, K):
+    # the conversion an INT8-routed linear runs on its NVFP4 weight: bit-exact
+    # against the oracle, and identical to what dmpq_prep_weight stores
+    require_gpu()
+    say(f"weight_int8_from_nvfp4 N={N} K={K}")
+    w = workloads.weight(np.random.default_rng(3 * N + K), N, K)
+    ref = orc.prep_weight(w)
+    qw, swr = empty((N, K), np.int8), empty((N,), np.float32)
+    dm.weight_int8_from_nvfp4(dev(ref["cw"]), dev(ref["sw"]), dev(np.array([ref["gw"]], np.float32)),
+                              qw, swr)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(qw), ref["qw"])
+    assert np.array_equal(host(swr).view(np.uint32), ref["sw_row"].view(np.uint32))
+
+
+def test_weight_int8_from_nvfp4_random_codes(orc):
+    # arbitrary codes, every finite E4M3 scale, a tensor scale far from 1, and
+    # an all-zero row
+    require_gpu()
+    say("weight_int8_from_nvfp4 random codes")
+    rng = np.random.default_rng(63)
+    N, K = 130, 2080
+    cw = rng.integers(0, 256, (N, K // 2)).astype(np.uint8)
+    sw = rng.integers(0, 0x7F, (N, K // 16)).astype(np.uint8)
+    cw[5] = 0
+    for g in (3.0517578e-05, 0.75, 1.7e3):
+        q_ref, s_ref = orc.w8_from_nvfp4(cw, sw, g)
+        qw, swr = empty((N, K), np.int8), empty((N,), np.float32)
+        dm.weight_int8_from_nvfp4(dev(cw), dev(sw), dev(np.array([g], np.float32)), qw, swr)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(qw), q_ref)
+        assert np.array_equal(host(swr).view(np.uint32), s_ref.view(np.uint32))
+        assert np.all(host(qw)[5] == 0) and host(swr)[5] == 0
+
+
 def test_quant_subnormal_inputs(orc):
     # bf16 subnormals (below 2^-126) must be kept, not flushed, through the
     # Hadamard and both quantizers
