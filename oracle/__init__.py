@@ -78,6 +78,10 @@ def _declare(L):
         "orc_prep_weight": (C.c_int, [_p(u16), i64, i64, C.c_int, _p(u8), _p(u8), _p(f32),
                                       _p(i8), _p(f32)]),
         "orc_w8_from_nvfp4": (C.c_int, [_p(u8), _p(u8), _p(f32), i64, i64, _p(i8), _p(f32)]),
+        "orc_outlier_count": (i64, [_p(u16), i64, i64, C.c_double]),
+        "orc_outlier_count_band": (None, [_p(u16), i64, i64, C.c_double, C.c_double, _p(i64), _p(i64)]),
+        "orc_pdr_force": (C.c_int, [i64, i64, C.c_double]),
+        "orc_gemm_bf16": (C.c_int, [_p(u16), _p(u16), i64, i64, i64, _p(i64), i64, _p(f64), _p(f64)]),
         "orc_gemm_int8": (C.c_int, [_p(i8), _p(f32), _p(i8), _p(f32), i64, i64, i64,
                                     _p(i64), i64, _p(i32), _p(f32)]),
         "orc_gemm_nvfp4": (C.c_int, [_p(u8), _p(u8), f32, _p(u8), _p(u8), f32, i64, i64, i64,
@@ -326,3 +330,41 @@ def nibbles(codes: np.ndarray) -> np.ndarray:
     lo = codes & 15
     hi = codes >> 4
     return np.stack([lo, hi], axis=-1).reshape(codes.shape[0], -1)
+
+
+# ---- Purified Delta Refresh and the BF16 route ------------------------------
+
+def outlier_count(x, kappa: float) -> int:
+    """Elements with x^2 * K > kappa^2 * (sum of the row's squares)."""
+    x = _u16(x)
+    M, K = x.shape
+    return int(lib().orc_outlier_count(_ptr(x, C.c_uint16), M, K, float(kappa)))
+
+
+def outlier_count_band(x, kappa: float, rel: float):
+    x = _u16(x)
+    M, K = x.shape
+    lo, hi = np.zeros(1, np.int64), np.zeros(1, np.int64)
+    lib().orc_outlier_count_band(_ptr(x, C.c_uint16), M, K, float(kappa), float(rel),
+                                 _ptr(lo, C.c_int64), _ptr(hi, C.c_int64))
+    return int(lo[0]), int(hi[0])
+
+
+def pdr_force(count: int, n: int, rho: float) -> bool:
+    return bool(lib().orc_pdr_force(int(count), int(n), float(rho)))
+
+
+def gemm_bf16(x, w, rows=None):
+    """fp64 reference y = x w^T over bf16 operands, and the bound sum |x w|."""
+    x, w = _u16(x), _u16(w)
+    M, K = x.shape
+    N = w.shape[0]
+    assert w.shape[1] == K
+    r, R = _rows(rows, M)
+    y = np.empty((R, N), np.float64)
+    b = np.empty((R, N), np.float64)
+    rc = lib().orc_gemm_bf16(_ptr(x, C.c_uint16), _ptr(w, C.c_uint16), M, N, K, _ptr(r, C.c_int64), R,
+                             _ptr(y, C.c_double), _ptr(b, C.c_double))
+    if rc != 0:
+        raise ValueError("orc_gemm_bf16: bad shape or row")
+    return y, b

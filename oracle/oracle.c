@@ -560,3 +560,106 @@ void orc_tdc_commit_refresh(orc_tdc_state *st, const double sums[4])
     st->gamma = rel_ratio(sums[0], sums[1]);
     st->gamma_valid = 1;
 }
+
+/* ======================================================================
+ * Purified Delta Refresh ([gist-en] §2.C "Solution"; [gist-it] §2.C;
+ * [gist-zh] §2.C).  Before a refresh writes a block's delta into the cache,
+ * the block input is checked for outliers; a high outlier ratio computes the
+ * block's linears in full precision (BF16 operands, fp32 accumulation, no
+ * quantization) for that step, so the cached delta carries no quantization
+ * noise.  The pages do not define "outlier": here an element x of token row
+ * m (K channels) is an outlier when |x| > kappa * RMS(row m), tested exactly
+ * as x^2 * K > (kappa * kappa) * S_m with S_m = sum_k x_k^2 in fp64 (the
+ * square of a bf16 value is exact in fp64).  The ratio is outliers / (M K);
+ * the block is forced to BF16 when it is strictly above rho.
+ * ==================================================================== */
+
+int64_t orc_outlier_count(const uint16_t *x, int64_t M, int64_t K, double kappa)
+{
+    const double kk = kappa * kappa;
+    int64_t count = 0;
+#pragma omp parallel for schedule(static) reduction(+ : count)
+    for (int64_t m = 0; m < M; m++) {
+        double S = 0.0;
+        for (int64_t k = 0; k < K; k++) {
+            double v = (double)orc_bf16_value(x[m * K + k]);
+            S += v * v;
+        }
+        const double rhs = kk * S;
+        for (int64_t k = 0; k < K; k++) {
+            double v = (double)orc_bf16_value(x[m * K + k]);
+            if (v * v * (double)K > rhs)
+                count++;
+        }
+    }
+    return count;
+}
+
+/* The same count with the threshold moved by a relative band: lo counts the
+ * elements above rhs*(1+rel), hi those above rhs*(1-rel).  A result whose row
+ * sums were added in another order lies in [lo, hi]. */
+void orc_outlier_count_band(const uint16_t *x, int64_t M, int64_t K, double kappa,
+                            double rel, int64_t *lo, int64_t *hi)
+{
+    const double kk = kappa * kappa;
+    int64_t clo = 0, chi = 0;
+#pragma omp parallel for schedule(static) reduction(+ : clo, chi)
+    for (int64_t m = 0; m < M; m++) {
+        double S = 0.0;
+        for (int64_t k = 0; k < K; k++) {
+            double v = (double)orc_bf16_value(x[m * K + k]);
+            S += v * v;
+        }
+        const double rhs = kk * S;
+        for (int64_t k = 0; k < K; k++) {
+            double v = (double)orc_bf16_value(x[m * K + k]);
+            double t = v * v * (double)K;
+            if (t > rhs * (1.0 + rel))
+                clo++;
+            if (t > rhs * (1.0 - rel))
+                chi++;
+        }
+    }
+    *lo = clo;
+    *hi = chi;
+}
+
+int orc_pdr_force(int64_t count, int64_t n, double rho)
+{
+    if (n <= 0)
+        return 0;
+    return (double)count / (double)n > rho;
+}
+
+/* Full-precision linear of the BF16 route: y[m,n] = sum_k x[m,k] w[n,k] over
+ * bf16 operands, products and sums in fp64; bound[m,n] = sum_k |x w|. */
+int orc_gemm_bf16(const uint16_t *x, const uint16_t *w, int64_t M, int64_t N, int64_t K,
+                  const int64_t *rows, int64_t n_rows, double *y, double *bound)
+{
+    if (M < 0 || N < 0 || K <= 0)
+        return -1;
+    const int64_t R = rows ? n_rows : M;
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
+    for (int64_t i = 0; i < R; i++) {
+        int64_t m = rows ? rows[i] : i;
+        if (m < 0 || m >= M) {
+            err = 1;
+            continue;
+        }
+        for (int64_t n = 0; n < N; n++) {
+            double sum = 0.0, babs = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                double p = (double)orc_bf16_value(x[m * K + k]) *
+                           (double)orc_bf16_value(w[n * K + k]);
+                sum += p;
+                babs += fabs(p);
+            }
+            if (y)
+                y[i * N + n] = sum;
+            if (bound)
+                bound[i * N + n] = babs;
+        }
+    }
+    return err ? -1 : 0;
+}

@@ -26,7 +26,9 @@
  *   - the NVFP4 -> INT8 weight conversion (per-output-channel absmax requant);
  *   - Gamma's base (L1 norm of the block input) and TDC "similarity" read as
  *     the relative L1 distance of the last two deltas;
- *   - alpha, beta, tau, eps_sim, delta_acc values (synthetic).
+ *   - alpha, beta, tau, eps_sim, delta_acc values (synthetic);
+ *   - PDR's "outlier" (|x| above kappa times the token row's RMS) and its
+ *     kappa and rho values.
  */
 #ifndef DMPQ_ORACLE_H
 #define DMPQ_ORACLE_H
@@ -111,6 +113,14 @@ void orc_tdc_refresh(const uint16_t *x_in, const uint16_t *x_out,
                      double sums[4]);
 void orc_tdc_commit_skip(orc_tdc_state *st);
 void orc_tdc_commit_refresh(orc_tdc_state *st, const double sums[4]);
+
+/* ---- Purified Delta Refresh and the BF16 route ---------------------- */
+int64_t orc_outlier_count(const uint16_t *x, int64_t M, int64_t K, double kappa);
+void orc_outlier_count_band(const uint16_t *x, int64_t M, int64_t K, double kappa,
+                            double rel, int64_t *lo, int64_t *hi);
+int orc_pdr_force(int64_t count, int64_t n, double rho);
+int orc_gemm_bf16(const uint16_t *x, const uint16_t *w, int64_t M, int64_t N, int64_t K,
+                  const int64_t *rows, int64_t n_rows, double *y, double *bound);
 
 #ifdef __cplusplus
 }
