@@ -18,19 +18,20 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdmpq.so")
 
 OK = 0
-ROUTE_NVFP4, ROUTE_INT8 = 0, 1
+ROUTE_NVFP4, ROUTE_INT8, ROUTE_BF16 = 0, 1, 2
 OUT_F32, OUT_BF16, OUT_I32 = 0, 1, 2
 NO_HADAMARD = 1
 W8_FROM_NVFP4, W8_DIRECT = 0, 1
 TDC_SKIP, TDC_REFRESH = 0, 1
 FP4_BF16_DEQUANT = 0
 FP4_SCALED_MFMA = 1
-OP_GAMMA, OP_QUANT_NVFP4, OP_TDC, OP_PREP_WEIGHT = 0, 1, 2, 3
+OP_GAMMA, OP_QUANT_NVFP4, OP_TDC, OP_PREP_WEIGHT, OP_OUTLIER = 0, 1, 2, 3, 4
 
 EXPORTS = ("dmpq_last_error", "dmpq_version", "dmpq_workspace_bytes", "dmpq_gamma_sums",
            "dmpq_gate_and_route", "dmpq_hadamard_quant_int8", "dmpq_hadamard_quant_nvfp4",
            "dmpq_qgemm_int8", "dmpq_qgemm_nvfp4", "dmpq_tdc_init", "dmpq_tdc_decide",
-           "dmpq_tdc_step", "dmpq_tdc_commit", "dmpq_prep_weight", "dmpq_weight_int8_from_nvfp4")
+           "dmpq_tdc_step", "dmpq_tdc_commit", "dmpq_prep_weight", "dmpq_weight_int8_from_nvfp4",
+           "dmpq_outlier_count", "dmpq_pdr_decide", "dmpq_gemm_bf16")
 
 
 class DmpqError(RuntimeError):
@@ -83,6 +84,9 @@ def _declare(L):
         "dmpq_tdc_commit": (i32, [C.POINTER(TdcState), i32, pd]),
         "dmpq_prep_weight": (i32, [vp, vp, i64, i64, i32, vp, vp, vp, vp, vp, vp, C.c_size_t]),
         "dmpq_weight_int8_from_nvfp4": (i32, [vp, vp, vp, vp, i64, i64, vp, vp]),
+        "dmpq_outlier_count": (i32, [vp, vp, i64, i64, f64, vp, vp, C.c_size_t]),
+        "dmpq_pdr_decide": (i32, [f64, i64, f64, C.POINTER(C.c_int)]),
+        "dmpq_gemm_bf16": (i32, [vp, vp, vp, i64, i64, i64, i32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -222,3 +226,24 @@ def weight_int8_from_nvfp4(cw, sw, gw, qw, sw_row, stream=None) -> None:
     N, K = cw.shape[0], 2 * cw.shape[1]
     _check(lib().dmpq_weight_int8_from_nvfp4(_stream(stream), _ptr(cw), _ptr(sw), _ptr(gw), N, K,
                                              _ptr(qw), _ptr(sw_row)), "dmpq_weight_int8_from_nvfp4")
+
+
+def outlier_count(x, kappa: float, count, ws, stream=None) -> None:
+    """PDR outlier count of x [M x K] bf16 (as int16 bits) into count (fp64[1])."""
+    M, K = x.shape
+    _check(lib().dmpq_outlier_count(_stream(stream), _ptr(x), M, K, float(kappa), _ptr(count),
+                                    _ptr(ws), ws.numel()), "dmpq_outlier_count")
+
+
+def pdr_decide(count: float, n: int, rho: float) -> bool:
+    force = C.c_int(0)
+    _check(lib().dmpq_pdr_decide(float(count), int(n), float(rho), C.byref(force)), "dmpq_pdr_decide")
+    return bool(force.value)
+
+
+def gemm_bf16(x, w, y, out_dtype: int = OUT_F32, stream=None) -> None:
+    """Full-precision linear y = x w^T over bf16 operands (fp32 accumulation)."""
+    M, K = x.shape
+    N = w.shape[0]
+    _check(lib().dmpq_gemm_bf16(_stream(stream), _ptr(x), _ptr(w), M, N, K, out_dtype, _ptr(y)),
+           "dmpq_gemm_bf16")

@@ -87,7 +87,8 @@ size_t dmpq_workspace_bytes(int op, int64_t M, int64_t K) {
         case DMPQ_OP_GAMMA:
         case DMPQ_OP_QUANT_NVFP4:
         case DMPQ_OP_TDC:
-        case DMPQ_OP_PREP_WEIGHT: return kWsBytes;
+        case DMPQ_OP_PREP_WEIGHT:
+        case DMPQ_OP_OUTLIER: return kWsBytes;
     }
     return 0;
 }
@@ -301,6 +302,38 @@ dmpq_status dmpq_weight_int8_from_nvfp4(hipStream_t stream, const uint8_t *cw, c
         return fail(DMPQ_ERR_UNSUPPORTED, "%s: K = %lld exceeds 32768", __func__, (long long)K);
     if (N == 0) return ok();
     return hip_status(launch_w8_from_nvfp4(stream, cw, sw, d_gw, N, K, qw, sw_row), __func__);
+}
+
+dmpq_status dmpq_outlier_count(hipStream_t stream, const uint16_t *x, int64_t M, int64_t K,
+                               double kappa, double *d_count, void *ws, size_t ws_bytes) {
+    if (M < 0) return fail(DMPQ_ERR_BAD_SHAPE, "%s: M = %lld < 0", __func__, (long long)M);
+    if (dmpq_status s = check_k(__func__, K)) return s;
+    REQUIRE_PTR_N(x, M);
+    REQUIRE_PTR(d_count);
+    if (!(kappa >= 0.0) || !isfinite(kappa))
+        return fail(DMPQ_ERR_INVALID_ARG, "%s: kappa = %g must be finite and >= 0", __func__, kappa);
+    if (!hq_int8_supported(K))
+        return fail(DMPQ_ERR_UNSUPPORTED, "%s: K = %lld exceeds 32768", __func__, (long long)K);
+    if (dmpq_status s = check_ws(__func__, ws, ws_bytes)) return s;
+    return hip_status(launch_outlier_count(stream, x, M, K, kappa, d_count, Workspace(ws)), __func__);
+}
+
+dmpq_status dmpq_pdr_decide(double h_count, int64_t n, double rho, int *h_force) {
+    REQUIRE_HOST(h_force);
+    if (n < 0) return fail(DMPQ_ERR_BAD_SHAPE, "%s: n = %lld < 0", __func__, (long long)n);
+    *h_force = n > 0 && h_count / (double)n > rho;
+    return ok();
+}
+
+dmpq_status dmpq_gemm_bf16(hipStream_t stream, const uint16_t *x, const uint16_t *w, int64_t M,
+                           int64_t N, int64_t K, int out_dtype, void *y) {
+    if (dmpq_status s = check_gemm(__func__, M, N, K)) return s;
+    REQUIRE_PTR_N(x, M);
+    REQUIRE_PTR_N(w, N);
+    REQUIRE_PTR_N(y, M * N);
+    if (out_dtype != DMPQ_OUT_F32 && out_dtype != DMPQ_OUT_BF16)
+        return fail(DMPQ_ERR_INVALID_ARG, "%s: out_dtype %d is not F32 or BF16", __func__, out_dtype);
+    return hip_status(launch_gemm_bf16(stream, x, w, M, N, K, out_dtype, y), __func__);
 }
 
 }  // extern "C"

@@ -17,12 +17,10 @@
 // with one barrier per stage.
 #include "device.hpp"
 #include "gemm_common.hpp"
+#include "gemm_dma.hpp"
 #include "internal.hpp"
 
 namespace dmpq {
-
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
 
 namespace i8gemm {
 constexpr int BM = 256, BN = 256, BK = 128;
@@ -177,197 +175,26 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Fast path for K % 128 == 0: operand tiles go from global memory straight into
-// LDS with gfx950's global_load_lds_dwordx4 (each lane's 16 bytes land at
-// base + 16 * lane of a wave's 1 KB block), so no staging registers and no
-// LDS write instructions are needed.  Rows are 128 bytes; the 16-byte chunk
-// kc of row r is stored at slot kc ^ ((r >> 1) & 7), which makes the 32-row
-// fragment reads conflict-free on the 64-bank LDS.  Two stage buffers; the
-// DMA of stage kt+2 is issued during stage kt, as soon as every wave has read
-// its last fragments of stage kt, and fragments are read one k-step ahead of
-// the MFMAs that use them, across stage boundaries too.
-// Out-of-range rows (ragged M, N) load a clamped row; their outputs are never
-// stored.
+// Fast path for K % 128 == 0: the DMA-fed main loop of gemm_dma.hpp with i8
+// MFMA (v_mfma_i32_32x32x32_i8), then the scaled epilogue.
 // ---------------------------------------------------------------------------
-namespace i8dma {
-constexpr int BM = 256, BN = 256, BK = 128;
-constexpr int TILE = BM * BK;        // bytes per operand per stage
-constexpr int STAGE = 2 * TILE;      // A tile + W tile
-constexpr int NBUF = 2;
-constexpr int BLOCKS = TILE / 1024 / 4;  // 1 KB load blocks per wave per operand
-constexpr size_t LDS_BYTES = NBUF * STAGE > 4 * EpiBand<4>::BYTES ? NBUF * STAGE : 4 * EpiBand<4>::BYTES;
-}  // namespace i8dma
-
-__device__ __forceinline__ int swz128(int row, int kc) { return kc ^ ((row >> 1) & 7); }
-
-// Per-lane state of the DMA kernel: DMA sources and fragment rows.
-struct I8DmaLane {
-    const int8_t *srcA[i8dma::BLOCKS], *srcW[i8dma::BLOCKS];
-    int offA, offW;  // byte offset of the lane's first fragment row (A; W incl. the A tile)
-    int sw, hk;      // swizzle key of the lane's rows, K half
-    int wave;
-};
-
-// waitcnt immediate that waits for at most n outstanding vector memory ops
-// (expcnt and lgkmcnt left free)
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-
-// Fragments of k-step s (32 K values) of the stage held in `buf`.  Rows
-// ra = wm*128 + 32i + lane%32 all share the swizzle key ((lane%32) >> 1) & 7,
-// so the row block i only adds the constant 32*i*BK (an immediate offset).
-__device__ __forceinline__ void i8dma_frags(const int8_t *buf, const I8DmaLane &L, int s, v4i a[4], v4i b[4]) {
-    using namespace i8dma;
-    const int slot = ((2 * s + L.hk) ^ L.sw) * 16;
-    const int8_t *pa = buf + L.offA + slot;
-    const int8_t *pb = buf + L.offW + slot;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        a[i] = *reinterpret_cast<const v4i *>(pa + i * 32 * BK);
-        b[i] = *reinterpret_cast<const v4i *>(pb + i * 32 * BK);
-    }
-}
-
-// One DMA instruction of a stage: q-th 1 KB block of operand `op` (0 = A, 1 = W).
-__device__ __forceinline__ void i8dma_one(int8_t *dst, const I8DmaLane &L, int64_t k0, int q, int op) {
-    using namespace i8dma;
-    typedef __attribute__((address_space(3))) void lds_void;
-    const int b = L.wave + 4 * q;
-    const int8_t *src = (op ? L.srcW[q] : L.srcA[q]) + k0;
-    __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(dst + op * TILE + b * 1024), 16, 0, 0);
-}
-
-__device__ __forceinline__ void i8dma_issue(int8_t *dst, const I8DmaLane &L, int64_t k0) {
-#pragma unroll
-    for (int q = 0; q < i8dma::BLOCKS; q++) {
-        i8dma_one(dst, L, k0, q, 0);
-        i8dma_one(dst, L, k0, q, 1);
-    }
-}
-
-__device__ __forceinline__ void i8_mfma16(v16i (&acc)[4][4], const v4i a[4], const v4i b[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[j], a[i], acc[i][j], 0, 0, 0);
-}
-
-// 16 MFMAs with half of a stage's DMA (blocks q = 4h .. 4h+3 of both
-// operands) placed one instruction after every two MFMAs, so that the
-// workgroup's DMA reaches the texture unit spread over the MFMA stream
-// instead of in one burst that stalls instruction issue.
-__device__ __forceinline__ void i8_mfma16_dma(v16i (&acc)[4][4], const v4i a[4], const v4i b[4],
-                                              int8_t *dst, const I8DmaLane &L, int64_t k0, int h) {
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[j], a[i], acc[i][j], 0, 0, 0);
-            const int t = 4 * i + j;
-            if (t & 1) i8dma_one(dst, L, k0, 4 * h + (t >> 2), (t >> 1) & 1);
-        }
-#pragma unroll
-    for (int t = 0; t < 8; t++) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 VMEM read (the DMA)
-    }
-}
-
-// One stage.  On entry a0/b0 and a1/b1 hold k-steps 0 and 1 of the stage in
-// `cur`.  With the MFMAs of k-step 0 the wave issues the second half of the
-// next stage's DMA into `nxt` (its first half went out with the previous
-// stage's last k-step).  After k-step 2 it waits for that DMA and for every
-// wave to finish reading `cur`, reads k-step 0 of the next stage, and with the
-// MFMAs of k-step 3 issues the first half of the DMA two stages ahead into
-// `cur`.  Both DMA halves are issued on every stage so that the MFMA code has
-// no branches (the accumulators would not survive them in registers); where
-// no such stage exists the caller passes a stage whose bytes the target
-// buffer already holds or that nobody reads again, so any read racing with
-// it sees unchanged data.  `cur` and `nxt` are separate restrict parameters
-// so that, once inlined, the compiler knows the reads of `nxt` cannot alias
-// the DMA into `cur` and does not wait for it.
-__device__ __forceinline__ void i8dma_stage(int8_t *__restrict__ cur, int8_t *__restrict__ nxt,
-                                            bool has_next, int64_t k_second, int64_t k_first,
-                                            const I8DmaLane &L, v16i (&acc)[4][4],
-                                            v4i (&a0)[4], v4i (&b0)[4], v4i (&a1)[4], v4i (&b1)[4]) {
-    i8_mfma16_dma(acc, a0, b0, nxt, L, k_second, 1);
-    i8dma_frags(cur, L, 2, a0, b0);
-    i8_mfma16(acc, a1, b1);
-    i8dma_frags(cur, L, 3, a1, b1);
-    i8_mfma16(acc, a0, b0);
-    if (has_next) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's DMA of the next stage
-        __syncthreads();                           // ... every wave's, and `cur` is free
-        i8dma_frags(nxt, L, 0, a0, b0);
-    }
-    i8_mfma16_dma(acc, a1, b1, cur, L, k_first, 0);
-    if (has_next) i8dma_frags(nxt, L, 1, a1, b1);
-}
-
 template <int OUT>
 __global__ __launch_bounds__(256, 1) void gemm_i8_dma_kernel(
     const int8_t *__restrict__ A, const float *__restrict__ sa, const int8_t *__restrict__ W,
     const float *__restrict__ sw, int64_t M, int64_t N, int64_t K, void *__restrict__ y,
     unsigned tiles_m, unsigned tiles_n) {
-    using namespace i8dma;
+    using namespace gdma;
     extern __shared__ __attribute__((aligned(16))) int8_t lds[];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const TileCoord tc = tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, i8gemm::GROUP_M);
+    const TileCoord tc = tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, GROUP_M);
     const int64_t m0 = (int64_t)tc.m * BM, n0 = (int64_t)tc.n * BN;
 
     v16i acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-#pragma unroll
-            for (int r = 0; r < 16; r++) acc[i][j][r] = 0;
-
-    // Per-lane source offsets of this wave's load blocks: block b = wave + 4q
-    // covers tile rows 8b .. 8b+7; lane l fills row 8b + l/8, slot l%8.
-    I8DmaLane L;
-    L.wave = wave;
-    L.hk = lane >> 5;
-#pragma unroll
-    for (int q = 0; q < BLOCKS; q++) {
-        const int b = wave + 4 * q;
-        const int row = 8 * b + (lane >> 3);
-        const int kc = swz128(row, lane & 7);
-        const int64_t gm = m0 + row < M ? m0 + row : M - 1;
-        const int64_t gn = n0 + row < N ? n0 + row : N - 1;
-        L.srcA[q] = A + gm * K + kc * 16;
-        L.srcW[q] = W + gn * K + kc * 16;
-    }
-    L.offA = (wm * 128 + (lane & 31)) * BK;
-    L.offW = TILE + (wn * 128 + (lane & 31)) * BK;
-    L.sw = ((lane & 31) >> 1) & 7;
-
-    const int nk = (int)(K / BK);
-    i8dma_issue(lds, L, 0);
-    if (nk > 1) {
-        i8dma_issue(lds + STAGE, L, BK);
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * BLOCKS));  // stage 0 only
-    } else {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    }
-    __syncthreads();
-    v4i a0[4], b0[4], a1[4], b1[4];
-    i8dma_frags(lds, L, 0, a0, b0);
-    i8dma_frags(lds, L, 1, a1, b1);
-    for (int kt = 0; kt < nk; kt++) {
-        int8_t *cur = lds + (kt & 1) * STAGE;
-        int8_t *nxt = lds + ((kt & 1) ^ 1) * STAGE;
-        // second half into nxt: stage kt+1 (kt = 0 repeats the prologue's
-        // copy of it; after the last stage nxt is never read); first half
-        // into cur: stage kt+2, or stage kt itself when there is none
-        const int64_t k_second = (int64_t)(kt + 1 < nk ? kt + 1 : nk - 1) * BK;
-        const int64_t k_first = (int64_t)(kt + 2 < nk ? kt + 2 : kt) * BK;
-        i8dma_stage(cur, nxt, kt + 1 < nk, k_second, k_first, L, acc, a0, b0, a1, b1);
-    }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the last stage's DMA has landed
-    __syncthreads();  // every wave is done reading the stage buffers before they hold bands
+    dma_gemm_mainloop<OpI8, false>(reinterpret_cast<const uint8_t *>(A),
+                                   reinterpret_cast<const uint8_t *>(W), M, N, K, m0, n0,
+                                   reinterpret_cast<uint8_t *>(lds), acc);
 
     constexpr int ES = OUT == 1 ? 2 : 4;
     using Band = EpiBand<ES>;
@@ -428,7 +255,7 @@ hipError_t launch_gemm_int8(hipStream_t s, const int8_t *qa, const float *sa, co
                               reinterpret_cast<const void *>(gemm_i8_dma_kernel<1>),
                               reinterpret_cast<const void *>(gemm_i8_dma_kernel<2>)};
         const size_t bytes[6] = {2 * i8gemm::STAGE, 2 * i8gemm::STAGE, 2 * i8gemm::STAGE,
-                                 i8dma::LDS_BYTES, i8dma::LDS_BYTES, i8dma::LDS_BYTES};
+                                 gdma::LDS_BYTES, gdma::LDS_BYTES, gdma::LDS_BYTES};
         for (int f = 0; f < 6; f++) {
             hipError_t e = hipFuncSetAttribute(fns[f], hipFuncAttributeMaxDynamicSharedMemorySize,
                                                (int)bytes[f]);
@@ -440,8 +267,8 @@ hipError_t launch_gemm_int8(hipStream_t s, const int8_t *qa, const float *sa, co
     const int64_t tm = (M + 255) / 256, tn = (N + 255) / 256;
     const dim3 grid((unsigned)(tm * tn)), block(256);
     const unsigned utm = (unsigned)tm, utn = (unsigned)tn;
-    if (K % i8dma::BK == 0) {
-        const size_t lds = i8dma::LDS_BYTES;
+    if (K % gdma::BK == 0) {
+        const size_t lds = gdma::LDS_BYTES;
         if (out_dtype == 0)
             hipLaunchKernelGGL(gemm_i8_dma_kernel<0>, grid, block, lds, s, qa, sa, qw, sw, M, N, K, y, utm, utn);
         else if (out_dtype == 1)

@@ -81,45 +81,15 @@ __device__ __forceinline__ void dequant32_fast(const uint4 c, uint32_t s01, uint
     }
 }
 
-// Epilogue shared by the NVFP4 kernels (operands swapped as in the INT8
-// GEMM): lane l owns activation row m = l % 32 of A-subtile i and four
-// consecutive output columns 8g + 4*(l/32) + 0..3 of W-subtile j per register
-// group g.  y = (acc * gA) * gW, staged per wave through LDS in two 64-row
-// bands and stored row-contiguous.  Callers end their main loop with a
-// barrier, so the stage buffers are free.
+// Epilogue of the NVFP4 kernels: y = (acc * gA) * gW through the per-wave LDS
+// bands (callers end their main loop with a barrier, so the stage buffers are
+// free).
 template <int OUT>
 __device__ __forceinline__ void fp4_epilogue(v16f (&acc)[4][4], uint8_t *lds, const float *ga,
                                              const float *gw, int64_t M, int64_t N, int64_t m0,
                                              int64_t n0, int wave, int wm, int wn, int lane,
                                              void *y) {
-    constexpr int ES = OUT == 1 ? 2 : 4;
-    using Band = EpiBand<ES>;
-    const float gA = *ga, gW = *gw;
-    const int lm = lane & 31, lh = lane >> 5;
-    uint8_t *band = lds + wave * Band::BYTES;
-    const bool vec = ((N * ES) & 15) == 0;
-#pragma unroll
-    for (int h = 0; h < 2; h++) {
-#pragma unroll
-        for (int ii = 0; ii < 2; ii++) {
-            const int i = 2 * h + ii;
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-#pragma unroll
-                for (int g = 0; g < 4; g++) {
-                    uint8_t *dst = band + (ii * 32 + lm) * Band::STRIDE + (j * 32 + 8 * g + 4 * lh) * ES;
-                    float v4[4];
-#pragma unroll
-                    for (int e = 0; e < 4; e++) v4[e] = (acc[i][j][4 * g + e] * gA) * gW;
-                    if constexpr (OUT == 0)
-                        *reinterpret_cast<float4 *>(dst) = make_float4(v4[0], v4[1], v4[2], v4[3]);
-                    else
-                        *reinterpret_cast<uint2 *>(dst) = make_uint2(cvt_pk_bf16(v4[0], v4[1]), cvt_pk_bf16(v4[2], v4[3]));
-                }
-            }
-        }
-        epi_band_to_global<ES>(band, y, M, N, m0 + wm * 128 + h * 64, n0 + wn * 128, lane, vec);
-    }
+    f32_band_epilogue<OUT>(acc, lds, *ga, *gw, M, N, m0, n0, wave, wm, wn, lane, y);
 }
 
 template <int OUT>

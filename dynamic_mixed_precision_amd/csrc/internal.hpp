@@ -42,6 +42,13 @@ hipError_t launch_tdc_refresh(hipStream_t s, const uint16_t *x_in, const uint16_
 hipError_t launch_gemm_int8(hipStream_t s, const int8_t *qa, const float *sa, const int8_t *qw,
                             const float *sw, int64_t M, int64_t N, int64_t K, int out_dtype,
                             void *y);
+hipError_t launch_gemm_bf16(hipStream_t s, const uint16_t *x, const uint16_t *w, int64_t M,
+                            int64_t N, int64_t K, int out_dtype, void *y);
+hipError_t launch_outlier_count(hipStream_t s, const uint16_t *x, int64_t M, int64_t K,
+                                double kappa, double *count, const Workspace &ws);
+// Sum ns values per partial over nparts partials, in a fixed order, into out[ns].
+hipError_t launch_finalize_sums(hipStream_t s, const double *partial, int nparts, int ns,
+                                double *out);
 hipError_t launch_gemm_nvfp4(hipStream_t s, const uint8_t *ca, const uint8_t *sa,
                              const float *ga, const uint8_t *cw, const uint8_t *sw,
                              const float *gw, int64_t M, int64_t N, int64_t K, int out_dtype,

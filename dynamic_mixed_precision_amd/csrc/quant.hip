@@ -201,6 +201,108 @@ hipError_t launch_w8_from_nvfp4(hipStream_t s, const uint8_t *cw, const uint8_t 
 }
 
 // ---------------------------------------------------------------------------
+// Outlier count of the Purified Delta Refresh check (gist.science summaries,
+// §2.C: before a refresh writes the cached delta, a block input with a high
+// outlier ratio is computed in full precision).  An element x of a token row
+// (K channels, raw input, no Hadamard) counts when x^2 * K > kappa^2 * S with
+// S = the row's sum of squares, all in fp64: each square of a bf16 value is
+// exact, and S is added in a fixed order (per lane, then a fixed tree).  The
+// row stays in registers between the sum and the count.  Each workgroup
+// writes its count to partial[blockIdx.x]; finalize_sums adds them.
+// ---------------------------------------------------------------------------
+template <int W>
+__device__ __forceinline__ double group_sum_d(double v) {
+#pragma unroll
+    for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, W);
+    return v;
+}
+
+template <int LPR, int BPL>
+__global__ __launch_bounds__(256) void outlier_count_kernel(const uint16_t *__restrict__ x, int64_t M,
+                                                           int64_t K, double kk,
+                                                           double *__restrict__ partial) {
+    static_assert(LPR >= 16 && LPR <= 256 && 256 % LPR == 0, "lanes per row");
+    constexpr int ROWS = 256 / LPR;
+    __shared__ double red[4];
+    const int tid = threadIdx.x;
+    const int lr = tid % LPR;
+    const int nblk = (int)(K / 16);
+    const double dK = (double)K;
+    double cnt = 0.0;
+    for (int64_t r0 = (int64_t)blockIdx.x * ROWS; r0 < M; r0 += (int64_t)gridDim.x * ROWS) {
+        const int64_t row = r0 + tid / LPR;
+        const bool row_ok = row < M;
+        float v[BPL][16];
+        double s = 0.0;
+#pragma unroll
+        for (int i = 0; i < BPL; i++) {
+            const int b = lr + i * LPR;
+            if (row_ok && b < nblk) {
+                const uint4 *p = reinterpret_cast<const uint4 *>(x + row * K + 16 * (int64_t)b);
+                unpack16(load_nt16(p), load_nt16(p + 1), v[i]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 16; j++) v[i][j] = 0.0f;
+            }
+#pragma unroll
+            for (int j = 0; j < 16; j++) s += (double)v[i][j] * (double)v[i][j];
+        }
+        if constexpr (LPR <= kWave) {
+            s = group_sum_d<LPR>(s);
+        } else {
+            s = wave_sum(s);
+            if ((tid & (kWave - 1)) == 0) red[tid / kWave] = s;
+            __syncthreads();
+            constexpr int WPR = LPR / kWave;
+            const int w0 = (tid / LPR) * WPR;
+            double t = red[w0];
+#pragma unroll
+            for (int w = 1; w < WPR; w++) t += red[w0 + w];
+            s = t;
+            __syncthreads();
+        }
+        const double rhs = kk * s;
+        // zero padding never counts: 0 > rhs is false for rhs >= 0 (or NaN)
+#pragma unroll
+        for (int i = 0; i < BPL; i++)
+#pragma unroll
+            for (int j = 0; j < 16; j++)
+                cnt += ((double)v[i][j] * (double)v[i][j] * dK > rhs) ? 1.0 : 0.0;
+    }
+    cnt = wave_sum(cnt);
+    if ((tid & (kWave - 1)) == 0) red[tid / kWave] = cnt;
+    __syncthreads();
+    if (tid == 0) partial[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+hipError_t launch_outlier_count(hipStream_t s, const uint16_t *x, int64_t M, int64_t K,
+                                double kappa, double *count, const Workspace &ws) {
+    RowPlan p;
+    if (!plan_rows(K, &p)) return hipErrorInvalidValue;
+    const double kk = kappa * kappa;
+    const int64_t rows = 256 / p.lpr;
+    const int64_t groups64 = (M + rows - 1) / rows;
+    const int groups = (int)(groups64 < kMaxPartials ? groups64 : kMaxPartials);
+    if (groups > 0) {
+        const dim3 grid((unsigned)groups);
+        switch (p.lpr * 16 + p.bpl) {
+#define DMPQ_OC(L, B)                                                                            \
+    case L * 16 + B:                                                                             \
+        hipLaunchKernelGGL((outlier_count_kernel<L, B>), grid, dim3(256), 0, s, x, M, K, kk, ws.partial); \
+        break;
+#define DMPQ_OC_L(L) DMPQ_OC(L, 1) DMPQ_OC(L, 2) DMPQ_OC(L, 3) DMPQ_OC(L, 4) DMPQ_OC(L, 6) DMPQ_OC(L, 8)
+            DMPQ_OC_L(16) DMPQ_OC_L(32) DMPQ_OC_L(64) DMPQ_OC_L(128) DMPQ_OC_L(256)
+#undef DMPQ_OC_L
+#undef DMPQ_OC
+            default: return hipErrorInvalidValue;
+        }
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return launch_finalize_sums(s, ws.partial, groups, 1, count);
+}
+
+// ---------------------------------------------------------------------------
 // NVFP4, pass 1: absmax of the rotated tensor.  Each workgroup writes the max
 // of its share to partial[blockIdx.x]; pass 2 reduces the partials itself
 // (max is order independent).  No cross-workgroup fence is needed: the kernel

@@ -275,4 +275,15 @@ hipError_t launch_tdc_refresh(hipStream_t st, const uint16_t *x_in, const uint16
     return hipGetLastError();
 }
 
+hipError_t launch_finalize_sums(hipStream_t st, const double *partial, int nparts, int ns,
+                                double *out) {
+    switch (ns) {
+        case 1: hipLaunchKernelGGL(finalize_sums_kernel<1>, dim3(1), dim3(256), 0, st, partial, nparts, out); break;
+        case 2: hipLaunchKernelGGL(finalize_sums_kernel<2>, dim3(1), dim3(256), 0, st, partial, nparts, out); break;
+        case 4: hipLaunchKernelGGL(finalize_sums_kernel<4>, dim3(1), dim3(256), 0, st, partial, nparts, out); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace dmpq

@@ -57,8 +57,9 @@ typedef enum dmpq_status {
 } dmpq_status;
 
 /* Routes of a linear layer (DMPQ assigns NVFP4 to temporally stable layers,
- * INT8 to volatile ones: [gist-en] §2.A, [abstract]). */
-enum { DMPQ_ROUTE_NVFP4 = 0, DMPQ_ROUTE_INT8 = 1 };
+ * INT8 to volatile ones: [gist-en] §2.A, [abstract]; PDR forces full
+ * precision on a refresh whose input has many outliers: [gist-en] §2.C). */
+enum { DMPQ_ROUTE_NVFP4 = 0, DMPQ_ROUTE_INT8 = 1, DMPQ_ROUTE_BF16 = 2 };
 /* GEMM output types: fp32 (the contract), bf16 (RNE of the fp32 value), and
  * the raw int32 accumulators of the INT8 GEMM (test mode). */
 enum { DMPQ_OUT_F32 = 0, DMPQ_OUT_BF16 = 1, DMPQ_OUT_I32 = 2 };
@@ -77,7 +78,8 @@ enum { DMPQ_TDC_SKIP = 0, DMPQ_TDC_REFRESH = 1 };
  *     carry E4M3 scales inside the instruction). */
 enum { DMPQ_FP4_BF16_DEQUANT = 0, DMPQ_FP4_SCALED_MFMA = 1 };
 /* Workspace users. */
-enum { DMPQ_OP_GAMMA = 0, DMPQ_OP_QUANT_NVFP4 = 1, DMPQ_OP_TDC = 2, DMPQ_OP_PREP_WEIGHT = 3 };
+enum { DMPQ_OP_GAMMA = 0, DMPQ_OP_QUANT_NVFP4 = 1, DMPQ_OP_TDC = 2, DMPQ_OP_PREP_WEIGHT = 3,
+       DMPQ_OP_OUTLIER = 4 };
 
 /* Message describing the calling thread's last error ("" if none). */
 const char *dmpq_last_error(void);
@@ -241,6 +243,36 @@ dmpq_status dmpq_prep_weight(hipStream_t stream, const uint16_t *w, int64_t N, i
 dmpq_status dmpq_weight_int8_from_nvfp4(hipStream_t stream, const uint8_t *cw, const uint8_t *sw,
                                         const float *d_gw, int64_t N, int64_t K, int8_t *qw,
                                         float *sw_row);
+
+/* ---------------------------------------------------------------------------
+ * Purified Delta Refresh ([gist-en] §2.C "Solution"; [gist-it] §2.C;
+ * [gist-zh] §2.C): before a refresh writes a block's delta into the cache,
+ * the block input is checked for outliers; a high outlier ratio computes the
+ * block's linears in full precision (BF16) for that step, so the cached delta
+ * carries no quantization noise.  The pages define neither "outlier" nor the
+ * threshold; this library's reading:
+ *   an element x of token row m (K channels, raw input) is an outlier when
+ *   x^2 * K > kappa^2 * S_m, S_m = sum_k x_k^2, all in fp64 (|x| above kappa
+ *   times the row's RMS); the block is forced to BF16 when
+ *   count / (M K) > rho (strictly).
+ *
+ * Device count: x [M x K] bf16 -> *d_count (fp64, an exact integer).  S_m is
+ * added in a fixed order, so the result is deterministic; it can differ from
+ * a differently ordered sum only for elements within about 1e-15 relative of
+ * the threshold.  K % 16 == 0, K <= 32768.  ws: DMPQ_OP_OUTLIER workspace.
+ * ------------------------------------------------------------------------- */
+dmpq_status dmpq_outlier_count(hipStream_t stream, const uint16_t *x, int64_t M, int64_t K,
+                               double kappa, double *d_count, void *ws, size_t ws_bytes);
+
+/* Host decision: *h_force = 1 when n > 0 and h_count / n > rho, else 0. */
+dmpq_status dmpq_pdr_decide(double h_count, int64_t n, double rho, int *h_force);
+
+/* Full-precision linear of the PDR route: y[m,n] = sum_k x[m,k] w[n,k] over
+ * bf16 operands (x [M x K], w [N x K] = the original, unrotated bf16 weight),
+ * exact products, fp32 accumulation in an unspecified order.  out_dtype F32
+ * or BF16 (RNE of the fp32 value).  K % 16 == 0; any M, N >= 0. */
+dmpq_status dmpq_gemm_bf16(hipStream_t stream, const uint16_t *x, const uint16_t *w, int64_t M,
+                           int64_t N, int64_t K, int out_dtype, void *y);
 
 #ifdef __cplusplus
 }
