@@ -12,7 +12,12 @@ last two residual deltas are similar and the accumulated error allows it,
 reusing the cached delta, and otherwise recomputes and refreshes the cache
 (§2.B); the block's Gamma from its last computed step routes its linears
 (§2.A), and a block resuming after a skip has no Gamma and falls back to INT8
-(§2.C).
+(§2.C).  With Purified Delta Refresh enabled (§2.C), a refresh first counts
+the outliers of the block input; a ratio above rho computes every linear of
+the block in BF16 for that step, overriding both the router and the INT8
+fallback, so that the delta written to the cache is free of quantization
+noise.  That check needs the block input of the current step, so it costs
+one extra device->host copy per refreshed block.
 """
 from __future__ import annotations
 
@@ -21,8 +26,9 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-from . import (OP_TDC, TDC_REFRESH, TDC_SKIP, gate_and_route, new_workspace, tdc_commit,
-               tdc_decide, tdc_init, tdc_step)
+from . import (OP_OUTLIER, OP_TDC, ROUTE_BF16, TDC_REFRESH, TDC_SKIP, gate_and_route,
+               new_workspace, outlier_count, pdr_decide, tdc_commit, tdc_decide, tdc_init,
+               tdc_step)
 
 
 @dataclass
@@ -38,11 +44,18 @@ class BlockCache:
 
 class TdcScheduler:
     def __init__(self, n_blocks: int, numel: int, alpha, beta, tau: float, eps_sim: float,
-                 delta_acc: float, device="cuda"):
+                 delta_acc: float, device="cuda", pdr=None):
+        """pdr: None, or (kappa, rho) of the Purified Delta Refresh check."""
         self.alpha = np.ascontiguousarray(alpha, np.float64)
         self.beta = np.ascontiguousarray(beta, np.float64)
         self.tau, self.eps_sim, self.delta_acc = float(tau), float(eps_sim), float(delta_acc)
         self.ws = new_workspace(OP_TDC, device)
+        self.pdr = None if pdr is None else (float(pdr[0]), float(pdr[1]))
+        if self.pdr is not None:
+            self.ws_out = new_workspace(OP_OUTLIER, device)
+            self.count = torch.zeros(1, dtype=torch.float64, device=device)
+            self.count_host = torch.zeros(1, dtype=torch.float64).pin_memory()
+        self.last_ratio = None
         self.blocks = [BlockCache(state=tdc_init(),
                                   delta=torch.zeros(numel, dtype=torch.int16, device=device),
                                   sums=torch.zeros(4, dtype=torch.float64, device=device),
@@ -69,6 +82,24 @@ class TdcScheduler:
         b = self.blocks[i]
         sums2 = b.last_sums2 if b.state.gamma_valid else None
         return gate_and_route(sums2, self.alpha, self.beta, self.tau)
+
+    def refresh_routes(self, i: int, x_in: torch.Tensor):
+        """Routes for a refresh of block i on input x_in [tokens x channels]:
+        all BF16 when PDR is on and the outlier ratio exceeds rho, else routes(i).
+        Returns (gamma, errors, routes, forced)."""
+        g, e, r = self.routes(i)
+        if self.pdr is None:
+            return g, e, r, False
+        kappa, rho = self.pdr
+        outlier_count(x_in, kappa, self.count, self.ws_out)
+        self.count_host.copy_(self.count)  # synchronous: the decision gates this step's linears
+        n = x_in.numel()
+        c = float(self.count_host[0])
+        self.last_ratio = c / n if n else 0.0
+        forced = pdr_decide(c, n, rho)
+        if forced:
+            r = np.full(len(r), ROUTE_BF16, np.uint8)
+        return g, e, r, forced
 
     def skip(self, i: int, x_in: torch.Tensor, x_out: torch.Tensor) -> None:
         b = self.blocks[i]

@@ -16,6 +16,7 @@ class ProxyLinear:
     def __init__(self, w_bf16: torch.Tensor, ws):
         N, K = w_bf16.shape
         self.N, self.K = N, K
+        self.w = w_bf16.contiguous()  # the original weight, for the BF16 (PDR) route
         self.cw = torch.empty((N, K // 2), dtype=torch.uint8, device="cuda")
         self.sw = torch.empty((N, K // 16), dtype=torch.uint8, device="cuda")
         self.gw = torch.zeros(1, device="cuda")
@@ -35,10 +36,13 @@ class QuantBuffers:
 
 def routed_linear(x: torch.Tensor, lin: ProxyLinear, route: int, qb: QuantBuffers, ws,
                   hook=None) -> torch.Tensor:
-    """Hadamard + quant at the routed precision, then the quantized GEMM (bf16 out)."""
+    """Hadamard + quant at the routed precision, then the quantized GEMM (bf16 out);
+    the BF16 route is the unquantized GEMM on the original weight."""
     M = x.shape[0]
     y = torch.empty((M, lin.N), dtype=torch.bfloat16, device="cuda")
-    if route == dm.ROUTE_INT8:
+    if route == dm.ROUTE_BF16:
+        dm.gemm_bf16(x.view(torch.int16), lin.w.view(torch.int16), y, dm.OUT_BF16)
+    elif route == dm.ROUTE_INT8:
         dm.hadamard_quant_int8(x, qb.q, qb.s)
         dm.qgemm_int8(qb.q, qb.s, lin.qw, lin.swr, y, dm.OUT_BF16)
     else:
