@@ -3,10 +3,13 @@
 
 One step is one pass of the whole hot path over a CogVideoX-5B-like batch
 (17776 tokens, hidden 3072, FFN 12288) of four DiT blocks:
-  1. Gamma sums of every block (its input/output at the previous step), one
-     device->host copy of the sums, then the host router E = alpha*Gamma+beta
-     (alpha=1, beta=0, tau=0.2; the synthetic blocks have Gamma ~ 0.05, 0.40,
-     0.05, 0.40, so two blocks route to INT8 and two to NVFP4);
+  1. Gamma sums of every block (its input/output at the previous step) and
+     the Purified Delta Refresh outlier count of every block input (kappa=4;
+     the synthetic inputs have a ratio near 0.7%, below rho=1%, so no block is
+     forced to BF16), one device->host copy of the sums, then the host router
+     E = alpha*Gamma+beta (alpha=1, beta=0, tau=0.2; the synthetic blocks have
+     Gamma ~ 0.05, 0.40, 0.05, 0.40, so two blocks route to INT8 and two to
+     NVFP4) and the PDR decision;
   2. per block, per linear (qkv 9216x3072, out 3072x3072, ffn_up 12288x3072,
      ffn_down 3072x12288): Hadamard + activation quant at the routed
      precision, then the quantized GEMM against the offline NVFP4 weights;
@@ -45,6 +48,9 @@ def parse():
                    help="convert: only NVFP4 weights are kept and an INT8-routed linear converts its "
                         "weight into one scratch buffer right before its GEMM (the method's weight "
                         "handling); stored: use INT8 weights prepared offline")
+    p.add_argument("--pdr", default="4,0.01", metavar="KAPPA,RHO",
+                   help="Purified Delta Refresh check of every block input ('off' to skip it); "
+                        "a block above rho runs its linears as BF16 GEMMs")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=512,
                    help="rows of the qkv linear the oracle runs for the CPU baseline")
@@ -125,6 +131,8 @@ def main():
     beta = np.full(len(cfg.linears), wl.ROUTER_5B["beta"])
     tau = wl.ROUTER_5B["tau"]
 
+    pdr = None if args.pdr == "off" else tuple(float(v) for v in args.pdr.split(","))
+
     # ---- inputs and offline weight prep (untimed) -----------------------------
     t0 = time.time()
     blocks = []
@@ -143,6 +151,7 @@ def main():
                       qw=torch.empty((lin.N, lin.K), dtype=torch.int8, device="cuda"),
                       swr=torch.empty(lin.N, device="cuda"))
             dm.prep_weight(w, pw["cw"], pw["sw"], pw["gw"], pw["qw"], pw["swr"], ws_prep)
+            pw["w"] = w.view(torch.int16) if pdr is not None else None
             del w
             lins.append(dict(lin=lin, x=x, **pw))
         blocks.append(dict(x_in=x_in, x_out=x_out, lins=lins,
@@ -158,13 +167,17 @@ def main():
     w8_scratch = torch.empty(big, dtype=torch.int8, device="cuda")
     s8_scratch = torch.empty(max(lin.N for lin in cfg.linears), device="cuda")
     ws = dm.new_workspace(dm.OP_TDC)
-    gsums = torch.zeros((n_blocks, 2), dtype=torch.float64, device="cuda")
     tsums = torch.zeros((n_blocks, 4), dtype=torch.float64, device="cuda")
-    gsums_host = torch.zeros((n_blocks, 2), dtype=torch.float64).pin_memory()
+    # per block: S1, S2 at [b, 0:2] and the outlier count at [b, 2] (rows of
+    # 32 bytes keep every device pointer 16-byte aligned)
+    gsums_host = torch.zeros((n_blocks, 4), dtype=torch.float64).pin_memory()
+    gsums = torch.zeros((n_blocks, 4), dtype=torch.float64, device="cuda")
+    ws_out = dm.new_workspace(dm.OP_OUTLIER)
     torch.cuda.synchronize()
     setup_s = time.time() - t0
 
     kt = KernelTimer(torch)
+    pdr_ratio = [None] * n_blocks
     gemm_ops_step = 0
     routes_seen = []
 
@@ -172,11 +185,19 @@ def main():
         nonlocal gemm_ops_step
         # 1. Gamma predictor + router: one device->host boundary per step
         for b, blk in enumerate(blocks):
-            kt("gamma_sums", 4.0 * M * H, dm.gamma_sums, blk["x_in"], blk["x_out"], gsums[b], ws)
+            kt("gamma_sums", 4.0 * M * H, dm.gamma_sums, blk["x_in"], blk["x_out"], gsums[b, :2], ws)
+            if pdr is not None:
+                kt("outlier_count", 2.0 * M * H, dm.outlier_count, blk["x_in"].view(M, H), pdr[0],
+                   gsums[b, 2:3], ws_out)
         gsums_host.copy_(gsums, non_blocking=True)
         torch.cuda.current_stream().synchronize()
-        routes = [dm.gate_and_route(gsums_host[b].numpy(), alpha, beta, tau)[2]
+        routes = [dm.gate_and_route(gsums_host[b, :2].numpy(), alpha, beta, tau)[2]
                   for b in range(n_blocks)]
+        if pdr is not None:
+            for b in range(n_blocks):
+                if dm.pdr_decide(float(gsums_host[b, 2]), M * H, pdr[1]):
+                    routes[b] = np.full(len(routes[b]), dm.ROUTE_BF16, np.uint8)
+                pdr_ratio[b] = float(gsums_host[b, 2]) / (M * H)
         routes_seen.append([r.tolist() for r in routes])
         ops = 0
         # 2. quantized linears at the routed precision
@@ -186,7 +207,10 @@ def main():
                 qb = qbuf[lin.K]
                 flops = 2.0 * M * lin.N * lin.K
                 ops += flops
-                if routes[b][li] == dm.ROUTE_INT8:
+                if routes[b][li] == dm.ROUTE_BF16:
+                    kt("gemm_bf16", flops, dm.gemm_bf16, L["x"].view(M, lin.K), L["w"], ybuf[lin.name],
+                       out_dtype)
+                elif routes[b][li] == dm.ROUTE_INT8:
                     kt("hadamard_quant_int8", 3.0 * M * lin.K + 4.0 * M,
                        dm.hadamard_quant_int8, L["x"], qb["q"], qb["s"])
                     qw, swr = L["qw"], L["swr"]
@@ -237,6 +261,8 @@ def main():
     ksum = kt.summary(args.steps)
     peaks = {"hadamard_quant_int8": ("hbm", HBM_GBPS, "GB/s"),
              "weight_int8_from_nvfp4": ("hbm", HBM_GBPS, "GB/s"),
+             "outlier_count": ("hbm", HBM_GBPS, "GB/s"),
+             "gemm_bf16": ("mfma", PEAK_BF16_TFLOPS, "TFLOP/s"),
              "hadamard_quant_nvfp4": ("hbm", HBM_GBPS, "GB/s"),
              "gamma_sums": ("hbm", HBM_GBPS, "GB/s"),
              "tdc_step_refresh": ("hbm", HBM_GBPS, "GB/s"),
@@ -277,7 +303,9 @@ def main():
                                "(qkv 9216x3072, out 3072x3072, ffn_up 12288x3072, "
                                "ffn_down 3072x12288), 17776 tokens, hidden 3072",
                    "tokens": M, "hidden": H, "blocks": n_blocks,
-                   "routes_per_block": ["INT8" if r[0] else "NVFP4" for r in routes_seen[-1]],
+                   "routes_per_block": [{0: "NVFP4", 1: "INT8", 2: "BF16"}[r[0]] for r in routes_seen[-1]],
+                   "pdr": None if pdr is None else {"kappa": pdr[0], "rho": pdr[1],
+                                                    "outlier_ratio_per_block": [round(v, 5) for v in pdr_ratio]},
                    "gemm_out": args.out_dtype,
                    "int8_weights": args.int8_weights,
                    "gemm_tera_ops_per_step": round(gemm_ops_step / 1e12, 3)},

@@ -228,24 +228,27 @@ __global__ __launch_bounds__(256) void outlier_count_kernel(const uint16_t *__re
     const int lr = tid % LPR;
     const int nblk = (int)(K / 16);
     const double dK = (double)K;
-    double cnt = 0.0;
+    int cnt = 0;
     for (int64_t r0 = (int64_t)blockIdx.x * ROWS; r0 < M; r0 += (int64_t)gridDim.x * ROWS) {
         const int64_t row = r0 + tid / LPR;
         const bool row_ok = row < M;
-        float v[BPL][16];
+        // the row stays in registers as raw bf16 (8 words per 16-block)
+        uint4 raw[BPL][2];
         double s = 0.0;
 #pragma unroll
         for (int i = 0; i < BPL; i++) {
             const int b = lr + i * LPR;
             if (row_ok && b < nblk) {
                 const uint4 *p = reinterpret_cast<const uint4 *>(x + row * K + 16 * (int64_t)b);
-                unpack16(load_nt16(p), load_nt16(p + 1), v[i]);
+                raw[i][0] = load_nt16(p);
+                raw[i][1] = load_nt16(p + 1);
             } else {
-#pragma unroll
-                for (int j = 0; j < 16; j++) v[i][j] = 0.0f;
+                raw[i][0] = raw[i][1] = make_uint4(0u, 0u, 0u, 0u);
             }
+            float v[16];
+            unpack16(raw[i][0], raw[i][1], v);
 #pragma unroll
-            for (int j = 0; j < 16; j++) s += (double)v[i][j] * (double)v[i][j];
+            for (int j = 0; j < 16; j++) s += (double)v[j] * (double)v[j];
         }
         if constexpr (LPR <= kWave) {
             s = group_sum_d<LPR>(s);
@@ -264,13 +267,22 @@ __global__ __launch_bounds__(256) void outlier_count_kernel(const uint16_t *__re
         const double rhs = kk * s;
         // zero padding never counts: 0 > rhs is false for rhs >= 0 (or NaN)
 #pragma unroll
-        for (int i = 0; i < BPL; i++)
+        for (int i = 0; i < BPL; i++) {
+            float v[16];
+            unpack16(raw[i][0], raw[i][1], v);
+            // |x|^2 in fp64 (exact; fp32 would overflow or underflow at bf16's range),
+            // written differently from the sum above so that the compiler does not
+            // keep 16*BPL fp64 squares live across the row reduction
 #pragma unroll
-            for (int j = 0; j < 16; j++)
-                cnt += ((double)v[i][j] * (double)v[i][j] * dK > rhs) ? 1.0 : 0.0;
+            for (int j = 0; j < 16; j++) {
+                const double a = __builtin_fabs((double)v[j]);
+                cnt += (a * a * dK > rhs) ? 1 : 0;
+            }
+        }
     }
-    cnt = wave_sum(cnt);
-    if ((tid & (kWave - 1)) == 0) red[tid / kWave] = cnt;
+    double tot = (double)cnt;
+    tot = wave_sum(tot);
+    if ((tid & (kWave - 1)) == 0) red[tid / kWave] = tot;
     __syncthreads();
     if (tid == 0) partial[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
 }
