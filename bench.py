@@ -354,7 +354,7 @@ def cpu_baseline(rows: int) -> dict:
 GEMM_KERNELS = {"qgemm_nvfp4": "dmpq::gemm_fp4_dma_kernel<1>",
                 "qgemm_int8": "dmpq::gemm_i8_dma_kernel<1>"}
 GEMM_SOURCES = {"qgemm_nvfp4": ["gemm_nvfp4.hip", "gemm_common.hpp", "device.hpp", "internal.hpp"],
-                "qgemm_int8": ["gemm_int8.hip", "gemm_common.hpp", "device.hpp", "internal.hpp"]}
+                "qgemm_int8": ["gemm_int8.hip", "gemm_dma.hpp", "gemm_common.hpp", "device.hpp", "internal.hpp"]}
 CALIB_KERNEL = "dmpq::tdc_skip_kernel"
 HERE = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_JSON = os.path.join(HERE, "profiles", "traffic_qgemm_cogvideox5b.json")
