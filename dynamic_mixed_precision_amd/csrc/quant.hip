@@ -333,8 +333,8 @@ __global__ __launch_bounds__(256) void nvfp4_amax_kernel(const uint16_t *__restr
     for (; b + stride < nblocks; b += 2 * stride) {  // two blocks in flight per lane
         const uint4 *p0 = reinterpret_cast<const uint4 *>(x + 16 * b);
         const uint4 *p1 = reinterpret_cast<const uint4 *>(x + 16 * (b + stride));
-        uint4 a0 = load_nt16(p0), a1 = load_nt16(p0 + 1);
-        uint4 c0 = load_nt16(p1), c1 = load_nt16(p1 + 1);
+        uint4 a0 = p0[0], a1 = p0[1];
+        uint4 c0 = p1[0], c1 = p1[1];
         float v[16], w[16];
         unpack16(a0, a1, v);
         unpack16(c0, c1, w);
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(256) void nvfp4_amax_kernel(const uint16_t *__restr
     if (b < nblocks) {
         const uint4 *p0 = reinterpret_cast<const uint4 *>(x + 16 * b);
         float v[16];
-        unpack16(load_nt16(p0), load_nt16(p0 + 1), v);
+        unpack16(p0[0], p0[1], v);
         if (!(flags & 1)) fwht16(v);
 #pragma unroll
         for (int j = 0; j < 16; j++) m = fmaxf(m, __builtin_fabsf(v[j]));

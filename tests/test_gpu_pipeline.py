@@ -4,7 +4,10 @@
 0.05, 0.40, 0.05, 0.40 route (alpha = 1, beta = 0, tau = 0.2) to NVFP4, INT8,
 NVFP4, INT8; the Gamma sums, routes, activation quantization (every row) and
 the GEMM (row sample) of each block's linears match the oracle.
-1080p-like (106306 tokens): the FFN-up linear (12288 x 3072) on both routes.
+2B-like (17776 tokens, hidden 1920): every linear (QKV 5760 x 1920, out
+1920 x 1920, FFN up 7680 x 1920, FFN down 1920 x 7680) on both routes.
+1080p-like (106306 tokens): the FFN-up (12288 x 3072) and FFN-down
+(3072 x 12288) linears on both routes.
 """
 import numpy as np
 import pytest
@@ -90,3 +93,21 @@ def test_1080p_ffn_up_linear(orc, route):
     M, N, K = wl.M_1080P, 12288, 3072
     say(f"1080p-like ffn_up M={M} N={N} K={K} route={route}")
     _linear_parity(orc, np.random.default_rng(1080 + route), M, N, K, route, _rows(M, 8861))
+
+
+def test_cogvideox2b_linears(orc):
+    require_gpu()
+    cfg = wl.COGVIDEOX_2B
+    for li, lin in enumerate(cfg.linears):
+        for route in (dm.ROUTE_NVFP4, dm.ROUTE_INT8):
+            say(f"2B-like linear {lin.name} N={lin.N} K={lin.K} route={route}")
+            _linear_parity(orc, np.random.default_rng(200 + 10 * li + route), cfg.M, lin.N, lin.K,
+                           route, _rows(cfg.M, 1481))
+
+
+@pytest.mark.parametrize("route", [0, 1])
+def test_1080p_ffn_down_linear(orc, route):
+    require_gpu()
+    M, N, K = wl.M_1080P, 3072, 12288
+    say(f"1080p-like ffn_down M={M} N={N} K={K} route={route}")
+    _linear_parity(orc, np.random.default_rng(1090 + route), M, N, K, route, _rows(M, 8861))
