@@ -81,6 +81,7 @@ def _declare(L):
         "orc_outlier_count": (i64, [_p(u16), i64, i64, C.c_double]),
         "orc_outlier_count_band": (None, [_p(u16), i64, i64, C.c_double, C.c_double, _p(i64), _p(i64)]),
         "orc_pdr_force": (C.c_int, [i64, i64, C.c_double]),
+        "orc_gelu": (C.c_double, [C.c_double]),
         "orc_gemm_bf16": (C.c_int, [_p(u16), _p(u16), i64, i64, i64, _p(i64), i64, _p(f64), _p(f64)]),
         "orc_gemm_int8": (C.c_int, [_p(i8), _p(f32), _p(i8), _p(f32), i64, i64, i64,
                                     _p(i64), i64, _p(i32), _p(f32)]),
@@ -368,3 +369,10 @@ def gemm_bf16(x, w, rows=None):
     if rc != 0:
         raise ValueError("orc_gemm_bf16: bad shape or row")
     return y, b
+
+
+def gelu(x):
+    """Exact-erf GELU in fp64, elementwise over an array (or a scalar)."""
+    f = lib().orc_gelu
+    a = np.asarray(x, np.float64)
+    return np.vectorize(f, otypes=[np.float64])(a) if a.ndim else float(f(float(a)))

@@ -663,3 +663,16 @@ int orc_gemm_bf16(const uint16_t *x, const uint16_t *w, int64_t M, int64_t N, in
     }
     return err ? -1 : 0;
 }
+
+/* ======================================================================
+ * GELU of a DiT feed-forward layer, applied in the producing GEMM's
+ * epilogue when the next layer's quantization prologue is fused there (the
+ * pages ask the online Hadamard to add little overhead: [gist-en] §2.A
+ * "Outlier Smoothing").  Exact erf form, GELU(x) = x Phi(x), in fp64 as
+ * 0.5 x erfc(-x / sqrt 2), which does not cancel for negative x.
+ * ==================================================================== */
+
+double orc_gelu(double x)
+{
+    return 0.5 * x * erfc(-x / sqrt(2.0));
+}

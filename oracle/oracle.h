@@ -122,6 +122,9 @@ int orc_pdr_force(int64_t count, int64_t n, double rho);
 int orc_gemm_bf16(const uint16_t *x, const uint16_t *w, int64_t M, int64_t N, int64_t K,
                   const int64_t *rows, int64_t n_rows, double *y, double *bound);
 
+/* ---- GELU (fused producer epilogue) --------------------------------- */
+double orc_gelu(double x);
+
 #ifdef __cplusplus
 }
 #endif
