@@ -15,6 +15,10 @@ One step is one pass of the whole hot path over a CogVideoX-5B-like batch
      precision, then the quantized GEMM against the offline NVFP4 weights;
      an INT8-routed linear first converts its NVFP4 weight to INT8 into one
      shared scratch buffer (only the 4.5-bit weights are kept);
+     with --fuse-ffn on, ffn_down consumes ffn_up's output instead: the
+     ffn_up GEMM applies GELU in its epilogue and, when ffn_down is routed to
+     NVFP4, also leaves the per-tile Hadamard amax that lets ffn_down's
+     quantizer skip its amax pass (this adds the GELU's work to the step);
   3. per block, the Temporal Delta Cache refresh (delta, four L1 sums).
 Inputs are synthetic (seeded, drawn on the device) and resident in HBM
 before timing; weights are prepared once, outside the timed region.
@@ -51,6 +55,10 @@ def parse():
     p.add_argument("--pdr", default="4,0.01", metavar="KAPPA,RHO",
                    help="Purified Delta Refresh check of every block input ('off' to skip it); "
                         "a block above rho runs its linears as BF16 GEMMs")
+    p.add_argument("--fuse-ffn", choices=["on", "off"], default="off",
+                   help="on: ffn_down's input is ffn_up's output, GELU and the next NVFP4 amax are "
+                        "fused into ffn_up's GEMM epilogue (needs --out-dtype bf16); off: every "
+                        "linear reads its own synthetic input (the linears alone)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=512,
                    help="rows of the qkv linear the oracle runs for the CPU baseline")
@@ -173,6 +181,13 @@ def main():
     gsums_host = torch.zeros((n_blocks, 4), dtype=torch.float64).pin_memory()
     gsums = torch.zeros((n_blocks, 4), dtype=torch.float64, device="cuda")
     ws_out = dm.new_workspace(dm.OP_OUTLIER)
+    fuse = args.fuse_ffn == "on"
+    if fuse and out_dtype != dm.OUT_BF16:
+        print("bench.py: --fuse-ffn on needs --out-dtype bf16", file=sys.stderr)
+        sys.exit(2)
+    names = [lin.name for lin in cfg.linears]
+    i_up, i_down = names.index("ffn_up"), names.index("ffn_down")
+    ws_amax = dm.new_workspace(dm.OP_GEMM_AMAX, "cuda", M, cfg.linears[i_up].N)
     torch.cuda.synchronize()
     setup_s = time.time() - t0
 
@@ -207,25 +222,36 @@ def main():
                 qb = qbuf[lin.K]
                 flops = 2.0 * M * lin.N * lin.K
                 ops += flops
-                if routes[b][li] == dm.ROUTE_BF16:
-                    kt("gemm_bf16", flops, dm.gemm_bf16, L["x"].view(M, lin.K), L["w"], ybuf[lin.name],
-                       out_dtype)
-                elif routes[b][li] == dm.ROUTE_INT8:
+                route = routes[b][li]
+                x, epi, qflags, qws = L["x"], 0, 0, ws
+                if fuse and li == i_up:
+                    epi = dm.EPI_GELU
+                    if routes[b][i_down] == dm.ROUTE_NVFP4:
+                        epi |= dm.EPI_NVFP4_AMAX
+                if fuse and li == i_down:
+                    x = ybuf[names[i_up]].view(torch.int16)
+                    if route == dm.ROUTE_NVFP4:
+                        qflags, qws = dm.AMAX_GIVEN, ws_amax
+                if route == dm.ROUTE_BF16:
+                    kt("gemm_bf16", flops, dm.gemm_bf16_ex, x.view(M, lin.K), L["w"], ybuf[lin.name],
+                       epi, ws_amax, out_dtype)
+                elif route == dm.ROUTE_INT8:
                     kt("hadamard_quant_int8", 3.0 * M * lin.K + 4.0 * M,
-                       dm.hadamard_quant_int8, L["x"], qb["q"], qb["s"])
+                       dm.hadamard_quant_int8, x, qb["q"], qb["s"])
                     qw, swr = L["qw"], L["swr"]
                     if args.int8_weights == "convert":
                         qw = w8_scratch[:lin.N * lin.K].view(lin.N, lin.K)
                         swr = s8_scratch[:lin.N]
                         kt("weight_int8_from_nvfp4", (0.5 + 1.0 / 16 + 1.0) * lin.N * lin.K + 8.0 * lin.N,
                            dm.weight_int8_from_nvfp4, L["cw"], L["sw"], L["gw"], qw, swr)
-                    kt("qgemm_int8", flops, dm.qgemm_int8, qb["q"], qb["s"], qw, swr,
-                       ybuf[lin.name], out_dtype)
+                    kt("qgemm_int8", flops, dm.qgemm_int8_ex, qb["q"], qb["s"], qw, swr,
+                       ybuf[lin.name], epi, ws_amax, out_dtype)
                 else:
-                    kt("hadamard_quant_nvfp4", (2.0 + 0.5 + 1.0 / 16) * M * lin.K + 4.0,
-                       dm.hadamard_quant_nvfp4, L["x"], qb["c"], qb["sc"], qb["g"], ws)
-                    kt("qgemm_nvfp4", flops, dm.qgemm_nvfp4, qb["c"], qb["sc"], qb["g"], L["cw"],
-                       L["sw"], L["gw"], ybuf[lin.name], out_dtype)
+                    kt("hadamard_quant_nvfp4_given" if qflags else "hadamard_quant_nvfp4",
+                       (2.0 + 0.5 + 1.0 / 16) * M * lin.K + 4.0,
+                       dm.hadamard_quant_nvfp4, x, qb["c"], qb["sc"], qb["g"], qws, qflags)
+                    kt("qgemm_nvfp4", flops, dm.qgemm_nvfp4_ex, qb["c"], qb["sc"], qb["g"], L["cw"],
+                       L["sw"], L["gw"], ybuf[lin.name], epi, ws_amax, out_dtype)
             # 3. Temporal Delta Cache refresh of the block
             kt("tdc_step_refresh", 8.0 * M * H, dm.tdc_step, dm.TDC_REFRESH, blk["x_in"],
                blk["x_out"], blk["delta"], blk["delta_valid"], tsums[b], ws)
@@ -264,6 +290,7 @@ def main():
              "outlier_count": ("hbm", HBM_GBPS, "GB/s"),
              "gemm_bf16": ("mfma", PEAK_BF16_TFLOPS, "TFLOP/s"),
              "hadamard_quant_nvfp4": ("hbm", HBM_GBPS, "GB/s"),
+             "hadamard_quant_nvfp4_given": ("hbm", HBM_GBPS, "GB/s"),
              "gamma_sums": ("hbm", HBM_GBPS, "GB/s"),
              "tdc_step_refresh": ("hbm", HBM_GBPS, "GB/s"),
              "qgemm_int8": ("mfma", PEAK_INT8_TOPS, "TOPS"),
@@ -308,6 +335,7 @@ def main():
                                                     "outlier_ratio_per_block": [round(v, 5) for v in pdr_ratio]},
                    "gemm_out": args.out_dtype,
                    "int8_weights": args.int8_weights,
+                   "ffn_fused": fuse,
                    "gemm_tera_ops_per_step": round(gemm_ops_step / 1e12, 3)},
         "act_quant_GBps": round(q_bytes * 1e-9 / (q_ms * 1e-3), 1),
         "kernels": kernels,
@@ -351,8 +379,10 @@ def cpu_baseline(rows: int) -> dict:
 # ---- HBM byte counters and profile summaries ---------------------------------
 # The kernels behind each timed entry point and the sources they are built from:
 # a stored traffic figure is used only while these sources are unchanged.
-GEMM_KERNELS = {"qgemm_nvfp4": "dmpq::gemm_fp4_dma_kernel<1>",
-                "qgemm_int8": "dmpq::gemm_i8_dma_kernel<1>"}
+# bf16-output instantiations of the DMA-fed GEMM kernels, every epilogue
+# ('*' matches the epilogue template argument)
+GEMM_KERNELS = {"qgemm_nvfp4": "dmpq::gemm_fp4_dma_kernel<1, *>",
+                "qgemm_int8": "dmpq::gemm_i8_dma_kernel<1, *>"}
 GEMM_SOURCES = {"qgemm_nvfp4": ["gemm_nvfp4.hip", "gemm_common.hpp", "device.hpp", "internal.hpp"],
                 "qgemm_int8": ["gemm_int8.hip", "gemm_dma.hpp", "gemm_common.hpp", "device.hpp", "internal.hpp"]}
 CALIB_KERNEL = "dmpq::tdc_skip_kernel"
@@ -411,11 +441,17 @@ def _counter_rows(path: str, counter: str):
         return [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
 
 
+def _kernel_re(kernel: str):
+    import re
+    return re.compile(re.escape(kernel).replace(r"\*", r"\d+") + r"\(")
+
+
 def _per_kernel_kib(rows, kernel: str):
     """Counter value (KiB) of every dispatch of `kernel`, in dispatch order."""
+    pat = _kernel_re(kernel)
     sel = {}
     for r in rows:
-        if kernel + "(" in r["Kernel_Name"]:
+        if pat.search(r["Kernel_Name"]):
             sel[int(r["Dispatch_Id"])] = sel.get(int(r["Dispatch_Id"]), 0.0) + float(r["Counter_Value"])
     return [sel[k] for k in sorted(sel)]
 

@@ -20,18 +20,20 @@ LIB_PATH = os.path.join(_HERE, "libdmpq.so")
 OK = 0
 ROUTE_NVFP4, ROUTE_INT8, ROUTE_BF16 = 0, 1, 2
 OUT_F32, OUT_BF16, OUT_I32 = 0, 1, 2
-NO_HADAMARD = 1
+NO_HADAMARD, AMAX_GIVEN = 1, 2
+EPI_GELU, EPI_NVFP4_AMAX = 1, 2
 W8_FROM_NVFP4, W8_DIRECT = 0, 1
 TDC_SKIP, TDC_REFRESH = 0, 1
 FP4_BF16_DEQUANT = 0
 FP4_SCALED_MFMA = 1
-OP_GAMMA, OP_QUANT_NVFP4, OP_TDC, OP_PREP_WEIGHT, OP_OUTLIER = 0, 1, 2, 3, 4
+OP_GAMMA, OP_QUANT_NVFP4, OP_TDC, OP_PREP_WEIGHT, OP_OUTLIER, OP_GEMM_AMAX = 0, 1, 2, 3, 4, 5
 
 EXPORTS = ("dmpq_last_error", "dmpq_version", "dmpq_workspace_bytes", "dmpq_gamma_sums",
            "dmpq_gate_and_route", "dmpq_hadamard_quant_int8", "dmpq_hadamard_quant_nvfp4",
            "dmpq_qgemm_int8", "dmpq_qgemm_nvfp4", "dmpq_tdc_init", "dmpq_tdc_decide",
            "dmpq_tdc_step", "dmpq_tdc_commit", "dmpq_prep_weight", "dmpq_weight_int8_from_nvfp4",
-           "dmpq_outlier_count", "dmpq_pdr_decide", "dmpq_gemm_bf16")
+           "dmpq_outlier_count", "dmpq_pdr_decide", "dmpq_gemm_bf16", "dmpq_qgemm_int8_ex",
+           "dmpq_qgemm_nvfp4_ex", "dmpq_gemm_bf16_ex")
 
 
 class DmpqError(RuntimeError):
@@ -87,6 +89,10 @@ def _declare(L):
         "dmpq_outlier_count": (i32, [vp, vp, i64, i64, f64, vp, vp, C.c_size_t]),
         "dmpq_pdr_decide": (i32, [f64, i64, f64, C.POINTER(C.c_int)]),
         "dmpq_gemm_bf16": (i32, [vp, vp, vp, i64, i64, i64, i32, vp]),
+        "dmpq_qgemm_int8_ex": (i32, [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, i32, vp, C.c_size_t]),
+        "dmpq_qgemm_nvfp4_ex": (i32, [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, i32, vp,
+                                      C.c_size_t]),
+        "dmpq_gemm_bf16_ex": (i32, [vp, vp, vp, i64, i64, i64, i32, vp, i32, vp, C.c_size_t]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -128,10 +134,10 @@ def workspace_bytes(op: int, M: int = 0, K: int = 0) -> int:
     return int(lib().dmpq_workspace_bytes(op, M, K))
 
 
-def new_workspace(op: int, device="cuda"):
-    """Zero-filled workspace tensor for ``op`` (the C ABI's first-use rule)."""
+def new_workspace(op: int, device="cuda", M: int = 0, K: int = 0):
+    """Zero-filled workspace tensor for ``op`` (sizes M, K for OP_GEMM_AMAX)."""
     import torch
-    return torch.zeros(workspace_bytes(op), dtype=torch.uint8, device=device)
+    return torch.zeros(workspace_bytes(op, M, K), dtype=torch.uint8, device=device)
 
 
 def gamma_sums(x_in, x_out, sums, ws, stream=None) -> None:
@@ -247,3 +253,37 @@ def gemm_bf16(x, w, y, out_dtype: int = OUT_F32, stream=None) -> None:
     N = w.shape[0]
     _check(lib().dmpq_gemm_bf16(_stream(stream), _ptr(x), _ptr(w), M, N, K, out_dtype, _ptr(y)),
            "dmpq_gemm_bf16")
+
+
+def _ws(ws):
+    return (None, 0) if ws is None else (_ptr(ws), ws.numel())
+
+
+def qgemm_int8_ex(qa, sa, qw, sw, y, epilogue: int, ws=None, out_dtype: int = OUT_BF16,
+                  stream=None) -> None:
+    """qgemm_int8 with a producer epilogue (EPI_GELU, EPI_NVFP4_AMAX)."""
+    M, K = qa.shape
+    N = qw.shape[0]
+    _check(lib().dmpq_qgemm_int8_ex(_stream(stream), _ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), M, N,
+                                    K, out_dtype, _ptr(y), epilogue, *_ws(ws)),
+           "dmpq_qgemm_int8_ex")
+
+
+def qgemm_nvfp4_ex(ca, sa, ga, cw, sw, gw, y, epilogue: int, ws=None, out_dtype: int = OUT_BF16,
+                   stream=None) -> None:
+    """qgemm_nvfp4 (BF16-dequant variant) with a producer epilogue."""
+    M, K = ca.shape[0], 2 * ca.shape[1]
+    N = cw.shape[0]
+    _check(lib().dmpq_qgemm_nvfp4_ex(_stream(stream), _ptr(ca), _ptr(sa), _ptr(ga), _ptr(cw),
+                                     _ptr(sw), _ptr(gw), M, N, K, out_dtype, _ptr(y), epilogue,
+                                     *_ws(ws)),
+           "dmpq_qgemm_nvfp4_ex")
+
+
+def gemm_bf16_ex(x, w, y, epilogue: int, ws=None, out_dtype: int = OUT_BF16, stream=None) -> None:
+    """gemm_bf16 with a producer epilogue."""
+    M, K = x.shape
+    N = w.shape[0]
+    _check(lib().dmpq_gemm_bf16_ex(_stream(stream), _ptr(x), _ptr(w), M, N, K, out_dtype, _ptr(y),
+                                   epilogue, *_ws(ws)),
+           "dmpq_gemm_bf16_ex")

@@ -67,6 +67,27 @@ dmpq_status check_ws(const char *fn, const void *ws, size_t bytes) {
     return DMPQ_OK;
 }
 
+// Epilogue of a *_ex GEMM: known bits, bf16 output, and for the fused amax
+// N % 16 == 0 and a workspace that holds one float per 256 x 256 tile.
+dmpq_status check_epilogue(const char *fn, int64_t M, int64_t N, int out_dtype, int epilogue,
+                           const void *ws, size_t ws_bytes) {
+    if (epilogue & ~(DMPQ_EPI_GELU | DMPQ_EPI_NVFP4_AMAX))
+        return fail(DMPQ_ERR_INVALID_ARG, "%s: unknown epilogue %d", fn, epilogue);
+    if (out_dtype != DMPQ_OUT_BF16)
+        return fail(DMPQ_ERR_UNSUPPORTED, "%s: epilogues need DMPQ_OUT_BF16 (got %d)", fn, out_dtype);
+    if (epilogue & DMPQ_EPI_NVFP4_AMAX) {
+        if (N % 16 != 0)
+            return fail(DMPQ_ERR_BAD_SHAPE, "%s: the fused amax needs N %% 16 == 0 (N = %lld)", fn,
+                        (long long)N);
+        const size_t need = (size_t)gemm_tiles(M, N) * sizeof(float);
+        if (!ws) return fail(DMPQ_ERR_WORKSPACE, "%s: workspace is NULL", fn);
+        if (!aligned16(ws)) return fail(DMPQ_ERR_MISALIGNED, "%s: workspace is not 16-byte aligned", fn);
+        if (ws_bytes < need)
+            return fail(DMPQ_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, ws_bytes, need);
+    }
+    return DMPQ_OK;
+}
+
 double rel_ratio(double num, double den) {
     if (den == 0.0) return num == 0.0 ? 0.0 : INFINITY;
     return num / den;
@@ -81,9 +102,12 @@ const char *dmpq_last_error(void) { return g_err; }
 const char *dmpq_version(void) { return "dmpq 0.1 gfx950"; }
 
 size_t dmpq_workspace_bytes(int op, int64_t M, int64_t K) {
-    (void)M;
-    (void)K;
     switch (op) {
+        case DMPQ_OP_GEMM_AMAX: {
+            if (M < 0 || K < 0) return 0;
+            const size_t tiles = (size_t)gemm_tiles(M, K);
+            return tiles * sizeof(float) > kWsBytes ? tiles * sizeof(float) : kWsBytes;
+        }
         case DMPQ_OP_GAMMA:
         case DMPQ_OP_QUANT_NVFP4:
         case DMPQ_OP_TDC:
@@ -150,8 +174,14 @@ dmpq_status dmpq_hadamard_quant_nvfp4(hipStream_t stream, const uint16_t *x, int
     REQUIRE_PTR_N(codes, M);
     REQUIRE_PTR_N(scales, M);
     REQUIRE_PTR(d_g);
-    if (flags & ~DMPQ_NO_HADAMARD) return fail(DMPQ_ERR_INVALID_ARG, "%s: unknown flags %d", __func__, flags);
+    if (flags & ~(DMPQ_NO_HADAMARD | DMPQ_AMAX_GIVEN))
+        return fail(DMPQ_ERR_INVALID_ARG, "%s: unknown flags %d", __func__, flags);
+    if ((flags & DMPQ_NO_HADAMARD) && (flags & DMPQ_AMAX_GIVEN))
+        return fail(DMPQ_ERR_INVALID_ARG, "%s: DMPQ_AMAX_GIVEN needs the rotation", __func__);
     if (dmpq_status s = check_ws(__func__, ws, ws_bytes)) return s;
+    if ((flags & DMPQ_AMAX_GIVEN) && ws_bytes < dmpq_workspace_bytes(DMPQ_OP_GEMM_AMAX, M, K))
+        return fail(DMPQ_ERR_WORKSPACE, "%s: workspace has %zu bytes, the producer's tile maxima need %zu",
+                    __func__, ws_bytes, dmpq_workspace_bytes(DMPQ_OP_GEMM_AMAX, M, K));
     return hip_status(launch_hq_nvfp4(stream, x, M, K, flags, codes, scales, d_g, Workspace(ws)),
                       __func__);
 }
@@ -178,7 +208,24 @@ dmpq_status dmpq_qgemm_int8(hipStream_t stream, const int8_t *qa, const float *s
     REQUIRE_PTR_N(y, M * N);
     if (out_dtype != DMPQ_OUT_F32 && out_dtype != DMPQ_OUT_BF16 && out_dtype != DMPQ_OUT_I32)
         return fail(DMPQ_ERR_INVALID_ARG, "%s: unknown out_dtype %d", __func__, out_dtype);
-    return hip_status(launch_gemm_int8(stream, qa, sa, qw, sw, M, N, K, out_dtype, y), __func__);
+    return hip_status(launch_gemm_int8(stream, qa, sa, qw, sw, M, N, K, out_dtype, y, 0, nullptr),
+                      __func__);
+}
+
+dmpq_status dmpq_qgemm_int8_ex(hipStream_t stream, const int8_t *qa, const float *sa,
+                               const int8_t *qw, const float *sw, int64_t M, int64_t N, int64_t K,
+                               int out_dtype, void *y, int epilogue, void *ws, size_t ws_bytes) {
+    if (epilogue == 0) return dmpq_qgemm_int8(stream, qa, sa, qw, sw, M, N, K, out_dtype, y);
+    if (dmpq_status s = check_gemm(__func__, M, N, K)) return s;
+    REQUIRE_PTR_N(qa, M);
+    REQUIRE_PTR_N(sa, M);
+    REQUIRE_PTR_N(qw, N);
+    REQUIRE_PTR_N(sw, N);
+    REQUIRE_PTR_N(y, M * N);
+    if (dmpq_status s = check_epilogue(__func__, M, N, out_dtype, epilogue, ws, ws_bytes)) return s;
+    return hip_status(launch_gemm_int8(stream, qa, sa, qw, sw, M, N, K, out_dtype, y, epilogue,
+                                       static_cast<float *>(ws)),
+                      __func__);
 }
 
 dmpq_status dmpq_qgemm_nvfp4(hipStream_t stream, const uint8_t *ca, const uint8_t *sa,
@@ -200,7 +247,28 @@ dmpq_status dmpq_qgemm_nvfp4(hipStream_t stream, const uint8_t *ca, const uint8_
     if (variant != DMPQ_FP4_BF16_DEQUANT && variant != DMPQ_FP4_SCALED_MFMA)
         return fail(DMPQ_ERR_INVALID_ARG, "%s: unknown variant %d", __func__, variant);
     return hip_status(launch_gemm_nvfp4(stream, ca, sa, d_ga, cw, sw, d_gw, M, N, K, out_dtype,
-                                        y, variant),
+                                        y, variant, 0, nullptr),
+                      __func__);
+}
+
+dmpq_status dmpq_qgemm_nvfp4_ex(hipStream_t stream, const uint8_t *ca, const uint8_t *sa,
+                                const float *d_ga, const uint8_t *cw, const uint8_t *sw,
+                                const float *d_gw, int64_t M, int64_t N, int64_t K,
+                                int out_dtype, void *y, int epilogue, void *ws, size_t ws_bytes) {
+    if (epilogue == 0)
+        return dmpq_qgemm_nvfp4(stream, ca, sa, d_ga, cw, sw, d_gw, M, N, K, out_dtype, y,
+                                DMPQ_FP4_BF16_DEQUANT);
+    if (dmpq_status s = check_gemm(__func__, M, N, K)) return s;
+    REQUIRE_PTR_N(ca, M);
+    REQUIRE_PTR_N(sa, M);
+    REQUIRE_PTR_N(d_ga, M * N);
+    REQUIRE_PTR_N(cw, N);
+    REQUIRE_PTR_N(sw, N);
+    REQUIRE_PTR_N(d_gw, M * N);
+    REQUIRE_PTR_N(y, M * N);
+    if (dmpq_status s = check_epilogue(__func__, M, N, out_dtype, epilogue, ws, ws_bytes)) return s;
+    return hip_status(launch_gemm_nvfp4(stream, ca, sa, d_ga, cw, sw, d_gw, M, N, K, out_dtype, y,
+                                        DMPQ_FP4_BF16_DEQUANT, epilogue, static_cast<float *>(ws)),
                       __func__);
 }
 
@@ -333,7 +401,21 @@ dmpq_status dmpq_gemm_bf16(hipStream_t stream, const uint16_t *x, const uint16_t
     REQUIRE_PTR_N(y, M * N);
     if (out_dtype != DMPQ_OUT_F32 && out_dtype != DMPQ_OUT_BF16)
         return fail(DMPQ_ERR_INVALID_ARG, "%s: out_dtype %d is not F32 or BF16", __func__, out_dtype);
-    return hip_status(launch_gemm_bf16(stream, x, w, M, N, K, out_dtype, y), __func__);
+    return hip_status(launch_gemm_bf16(stream, x, w, M, N, K, out_dtype, y, 0, nullptr), __func__);
+}
+
+dmpq_status dmpq_gemm_bf16_ex(hipStream_t stream, const uint16_t *x, const uint16_t *w, int64_t M,
+                              int64_t N, int64_t K, int out_dtype, void *y, int epilogue, void *ws,
+                              size_t ws_bytes) {
+    if (epilogue == 0) return dmpq_gemm_bf16(stream, x, w, M, N, K, out_dtype, y);
+    if (dmpq_status s = check_gemm(__func__, M, N, K)) return s;
+    REQUIRE_PTR_N(x, M);
+    REQUIRE_PTR_N(w, N);
+    REQUIRE_PTR_N(y, M * N);
+    if (dmpq_status s = check_epilogue(__func__, M, N, out_dtype, epilogue, ws, ws_bytes)) return s;
+    return hip_status(launch_gemm_bf16(stream, x, w, M, N, K, out_dtype, y, epilogue,
+                                       static_cast<float *>(ws)),
+                      __func__);
 }
 
 }  // extern "C"

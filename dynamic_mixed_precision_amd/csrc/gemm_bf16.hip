@@ -15,10 +15,10 @@
 
 namespace dmpq {
 
-template <int OUT, bool TAIL>
+template <int OUT, bool TAIL, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, int64_t M, int64_t N,
-    int64_t K, void *__restrict__ y, unsigned tiles_m, unsigned tiles_n) {
+    int64_t K, void *__restrict__ y, unsigned tiles_m, unsigned tiles_n, float *__restrict__ partial) {
     using namespace gdma;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tid = threadIdx.x;
@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(
     dma_gemm_mainloop<OpBF16, TAIL>(reinterpret_cast<const uint8_t *>(x),
                                     reinterpret_cast<const uint8_t *>(w), M, N, 2 * K, m0, n0,
                                     lds, acc);
-    f32_band_epilogue<OUT>(acc, lds, 1.0f, 1.0f, M, N, m0, n0, wave, wm, wn, lane, y);
+    f32_band_epilogue<OUT, EPI>(acc, lds, 1.0f, 1.0f, M, N, m0, n0, wave, wm, wn, lane, y, partial);
 }
 
 template <class KernelFn>
@@ -40,31 +40,40 @@ static hipError_t allow_lds(KernelFn fn, size_t bytes) {
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-hipError_t launch_gemm_bf16(hipStream_t s, const uint16_t *x, const uint16_t *w, int64_t M,
-                            int64_t N, int64_t K, int out_dtype, void *y) {
+template <int OUT, int EPI>
+static hipError_t launch_bf16_paths(hipStream_t s, const uint16_t *x, const uint16_t *w, int64_t M,
+                                    int64_t N, int64_t K, void *y, float *partial) {
     using namespace gdma;
-    if (M == 0 || N == 0) return hipSuccess;
     static const hipError_t attr = [] {
-        hipError_t e = allow_lds(gemm_bf16_kernel<0, false>, LDS_BYTES);
-        if (e == hipSuccess) e = allow_lds(gemm_bf16_kernel<1, false>, LDS_BYTES);
-        if (e == hipSuccess) e = allow_lds(gemm_bf16_kernel<0, true>, LDS_BYTES);
-        if (e == hipSuccess) e = allow_lds(gemm_bf16_kernel<1, true>, LDS_BYTES);
+        hipError_t e = allow_lds(gemm_bf16_kernel<OUT, false, EPI>, LDS_BYTES);
+        if (e == hipSuccess) e = allow_lds(gemm_bf16_kernel<OUT, true, EPI>, LDS_BYTES);
         return e;
     }();
     if (attr != hipSuccess) return attr;
     const int64_t tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
     const dim3 grid((unsigned)(tm * tn)), block(256);
     const unsigned utm = (unsigned)tm, utn = (unsigned)tn;
-    const bool tail = (2 * K) % BK != 0;
-    if (!tail && out_dtype == 0)
-        hipLaunchKernelGGL((gemm_bf16_kernel<0, false>), grid, block, LDS_BYTES, s, x, w, M, N, K, y, utm, utn);
-    else if (!tail)
-        hipLaunchKernelGGL((gemm_bf16_kernel<1, false>), grid, block, LDS_BYTES, s, x, w, M, N, K, y, utm, utn);
-    else if (out_dtype == 0)
-        hipLaunchKernelGGL((gemm_bf16_kernel<0, true>), grid, block, LDS_BYTES, s, x, w, M, N, K, y, utm, utn);
+    if ((2 * K) % BK == 0)
+        hipLaunchKernelGGL((gemm_bf16_kernel<OUT, false, EPI>), grid, block, LDS_BYTES, s, x, w, M, N, K, y,
+                           utm, utn, partial);
     else
-        hipLaunchKernelGGL((gemm_bf16_kernel<1, true>), grid, block, LDS_BYTES, s, x, w, M, N, K, y, utm, utn);
+        hipLaunchKernelGGL((gemm_bf16_kernel<OUT, true, EPI>), grid, block, LDS_BYTES, s, x, w, M, N, K, y,
+                           utm, utn, partial);
     return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16(hipStream_t s, const uint16_t *x, const uint16_t *w, int64_t M,
+                            int64_t N, int64_t K, int out_dtype, void *y, int epi, float *partial) {
+    if (M == 0 || N == 0) return hipSuccess;
+    if (out_dtype == 0 && epi == 0) return launch_bf16_paths<0, 0>(s, x, w, M, N, K, y, partial);
+    if (out_dtype != 1) return hipErrorInvalidValue;
+    switch (epi) {
+        case 0: return launch_bf16_paths<1, 0>(s, x, w, M, N, K, y, partial);
+        case 1: return launch_bf16_paths<1, 1>(s, x, w, M, N, K, y, partial);
+        case 2: return launch_bf16_paths<1, 2>(s, x, w, M, N, K, y, partial);
+        case 3: return launch_bf16_paths<1, 3>(s, x, w, M, N, K, y, partial);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace dmpq

@@ -54,21 +54,101 @@ struct EpiBand {
     static constexpr int ROWS_PER_PASS = 64 / LANES_PER_ROW;
 };
 
+// Epilogue options (bit flags).  kEpiGelu: GELU(v) = v Phi(v) of the output
+// value as a separate bf16 (or fp32) activation op would see it: the GEMM
+// result is rounded to the output type first, GELU runs in fp32 and its
+// result is rounded again.  kEpiAmax (bf16 output, N % 16 == 0): the maximum
+// of |FWHT16(row block)| over the stored bf16 values of the tile -- the next
+// layer's NVFP4 tensor-amax term, with the same fp32 butterfly order as the
+// quantizer -- is written to partial[blockIdx.x].
+enum { kEpiGelu = 1, kEpiAmax = 2 };
+
+// GELU(v) = v Phi(v) = (v / 2) erfc(-v / sqrt 2) in fp32.  erfc comes from
+// the Chebyshev fit published in Numerical Recipes (Press et al., section
+// 6.2, "erfcc": erfc(z) = t exp(-z^2 + P(t)), t = 1 / (1 + z/2), z >= 0, and
+// 2 - erfc(-x) for x < 0), whose fractional error is below 1.2e-7 for every
+// argument.  The fp32 evaluation adds a few ulp plus the rounding of the
+// exponent, a relative error of about v^2 * 1.2e-7 in erfc's tail.  About 20
+// VALU operations, no branches: the library erfcf costs several times that.
+__device__ __forceinline__ float gelu_f32(float v) {
+    const float x = v * -0.70710678118654752f;
+    const float z = __builtin_fabsf(x);
+    const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.5f, z, 1.0f));
+    float p = 0.17087277f;
+    p = __builtin_fmaf(t, p, -0.82215223f);
+    p = __builtin_fmaf(t, p, 1.48851587f);
+    p = __builtin_fmaf(t, p, -1.13520398f);
+    p = __builtin_fmaf(t, p, 0.27886807f);
+    p = __builtin_fmaf(t, p, -0.18628806f);
+    p = __builtin_fmaf(t, p, 0.09678418f);
+    p = __builtin_fmaf(t, p, 0.37409196f);
+    p = __builtin_fmaf(t, p, 1.00002368f);
+    p = __builtin_fmaf(t, p, -1.26551223f);
+    const float e = t * __builtin_amdgcn_exp2f(__builtin_fmaf(-z, z, p) * 1.44269504088896341f);
+    return 0.5f * v * (x >= 0.0f ? e : 2.0f - e);
+}
+
 // Copy one wave's LDS band (kEpiRows x 128 values of ESIZE bytes) to y at
 // (row0, col0), clipping to M x N.  vec: rows of y are 16-byte aligned.
-template <int ESIZE>
-__device__ __forceinline__ void epi_band_to_global(const uint8_t *band, void *y, int64_t M,
-                                                   int64_t N, int64_t row0, int64_t col0,
-                                                   int lane, bool vec) {
+// kEpiGelu: each value passes through GELU on its way out.  kEpiAmax (bf16
+// only): the two lanes holding one 16-block finish its Hadamard (stages 1,
+// 2, 4 in-lane, stage 8 across the lane pair, then * 1/4) and the lane's max
+// |value| over valid blocks is returned.
+template <int ESIZE, int EPI = 0>
+__device__ __forceinline__ float epi_band_to_global(const uint8_t *band, void *y, int64_t M,
+                                                    int64_t N, int64_t row0, int64_t col0,
+                                                    int lane, bool vec) {
     using B = EpiBand<ESIZE>;
     constexpr int PER = 16 / ESIZE;  // values per lane per pass
+    constexpr bool AMAX = (EPI & kEpiAmax) != 0;
+    static_assert(!AMAX || ESIZE == 2, "the fused amax reads bf16 outputs");
     const int chunk = lane % B::LANES_PER_ROW;
     const int64_t col = col0 + chunk * PER;
+    float amax = 0.0f;
 #pragma unroll 4
     for (int p = 0; p < kEpiRows / B::ROWS_PER_PASS; p++) {
         const int r = p * B::ROWS_PER_PASS + lane / B::LANES_PER_ROW;
         const int64_t row = row0 + r;
-        const uint4 v = *reinterpret_cast<const uint4 *>(band + r * B::STRIDE + chunk * 16);
+        uint4 v = *reinterpret_cast<const uint4 *>(band + r * B::STRIDE + chunk * 16);
+        if constexpr ((EPI & kEpiGelu) != 0) {
+            if constexpr (ESIZE == 2) {
+                v.x = cvt_pk_bf16(gelu_f32(bf16_lo(v.x)), gelu_f32(bf16_hi(v.x)));
+                v.y = cvt_pk_bf16(gelu_f32(bf16_lo(v.y)), gelu_f32(bf16_hi(v.y)));
+                v.z = cvt_pk_bf16(gelu_f32(bf16_lo(v.z)), gelu_f32(bf16_hi(v.z)));
+                v.w = cvt_pk_bf16(gelu_f32(bf16_lo(v.w)), gelu_f32(bf16_hi(v.w)));
+            } else {
+                v.x = __float_as_uint(gelu_f32(__uint_as_float(v.x)));
+                v.y = __float_as_uint(gelu_f32(__uint_as_float(v.y)));
+                v.z = __float_as_uint(gelu_f32(__uint_as_float(v.z)));
+                v.w = __float_as_uint(gelu_f32(__uint_as_float(v.w)));
+            }
+        }
+        if constexpr (AMAX) {
+            float f[8];
+            f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+            f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+#pragma unroll
+            for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+                for (int i = 0; i < 8; i++)
+                    if ((i & h) == 0) {
+                        const float a = f[i], b = f[i + h];
+                        f[i] = a + b;
+                        f[i + h] = a - b;
+                    }
+            const bool lo = (chunk & 1) == 0;  // this lane holds elements 0..7 of the block
+            float m = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                // the partner lane's value: DPP quad_perm [1, 0, 3, 2] swaps
+                // lanes 2k and 2k+1 inside the VALU (no LDS round trip)
+                const float o = __int_as_float(
+                    __builtin_amdgcn_mov_dpp(__float_as_int(f[i]), 0xB1, 0xF, 0xF, false));
+                const float w = lo ? f[i] + o : o - f[i];
+                m = fmaxf(m, __builtin_fabsf(w * 0.25f));
+            }
+            if (row < M && col < N) amax = fmaxf(amax, m);
+        }
         if (row >= M || col >= N) continue;
         uint8_t *dst = static_cast<uint8_t *>(y) + (row * N + col) * ESIZE;
         if (vec && col + PER <= N) {
@@ -87,31 +167,52 @@ __device__ __forceinline__ void epi_band_to_global(const uint8_t *band, void *y,
             }
         }
     }
+    return amax;
 }
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-// fp32 accumulators of a 128 x 128 wave tile in the transposed MFMA layout
-// (lane l owns row l % 32 of A-subtile i and four consecutive output columns
-// 8g + 4*(l/32) + 0..3 of W-subtile j per register group g) -> y =
-// (acc * gA) * gW in fp32 or bf16, staged per wave through LDS in two 64-row
-// bands and stored row-contiguous.  The caller guarantees that no other wave
+// The fused amax of a 256 x 256 tile: every wave's maximum, combined through
+// LDS, written by one lane.  Called by all four waves.
+__device__ __forceinline__ void epi_tile_amax(float m, int wave, int lane, float *partial) {
+    __shared__ float red[4];
+    m = wave_max(m);
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    if (wave == 0 && lane == 0) partial[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// Output scaling of fp32 accumulators: y = (acc * gA) * gW.
+struct EpiScaleF32 {
+    float gA, gW;
+    __device__ __forceinline__ void row(int64_t) {}
+    __device__ __forceinline__ float operator()(float a, int, int, int) const { return (a * gA) * gW; }
+};
+
+// Generic band epilogue: accumulators in the transposed MFMA layout (lane l
+// owns row l % 32 of A-subtile i and four consecutive output columns
+// 8g + 4*(l/32) + 0..3 of W-subtile j per register group g) -> sc (scaling)
+// -> (GELU) -> fp32 or bf16 into the per-wave LDS band, then row-contiguous
+// stores (and the fused amax).  The caller guarantees that no other wave
 // still reads this wave's band region.
-template <int OUT>
-__device__ __forceinline__ void f32_band_epilogue(v16f (&acc)[4][4], uint8_t *lds, float gA,
-                                                  float gW, int64_t M, int64_t N, int64_t m0,
-                                                  int64_t n0, int wave, int wm, int wn, int lane,
-                                                  void *y) {
+template <int OUT, int EPI, class AccV, class Scale>
+__device__ __forceinline__ void band_epilogue(AccV (&acc)[4][4], Scale &sc, uint8_t *lds, int64_t M,
+                                              int64_t N, int64_t m0, int64_t n0, int wave, int wm,
+                                              int wn, int lane, void *y, float *partial) {
     constexpr int ES = OUT == 1 ? 2 : 4;
+    constexpr bool AMAX = (EPI & kEpiAmax) != 0;
+    static_assert(!AMAX || OUT == 1, "the fused amax needs bf16 output");
     using Band = EpiBand<ES>;
     const int lm = lane & 31, lh = lane >> 5;
     uint8_t *band = lds + wave * Band::BYTES;
     const bool vec = ((N * ES) & 15) == 0;
+    float amax = 0.0f;
 #pragma unroll
     for (int h = 0; h < 2; h++) {
 #pragma unroll
         for (int ii = 0; ii < 2; ii++) {
             const int i = 2 * h + ii;
+            sc.row(m0 + wm * 128 + i * 32 + lm);
 #pragma unroll
             for (int j = 0; j < 4; j++) {
 #pragma unroll
@@ -119,7 +220,7 @@ __device__ __forceinline__ void f32_band_epilogue(v16f (&acc)[4][4], uint8_t *ld
                     uint8_t *dst = band + (ii * 32 + lm) * Band::STRIDE + (j * 32 + 8 * g + 4 * lh) * ES;
                     float v4[4];
 #pragma unroll
-                    for (int e = 0; e < 4; e++) v4[e] = (acc[i][j][4 * g + e] * gA) * gW;
+                    for (int e = 0; e < 4; e++) v4[e] = sc((float)acc[i][j][4 * g + e], j, g, e);
                     if constexpr (OUT == 0)
                         *reinterpret_cast<float4 *>(dst) = make_float4(v4[0], v4[1], v4[2], v4[3]);
                     else
@@ -127,8 +228,20 @@ __device__ __forceinline__ void f32_band_epilogue(v16f (&acc)[4][4], uint8_t *ld
                 }
             }
         }
-        epi_band_to_global<ES>(band, y, M, N, m0 + wm * 128 + h * 64, n0 + wn * 128, lane, vec);
+        amax = fmaxf(amax, epi_band_to_global<ES, EPI>(band, y, M, N, m0 + wm * 128 + h * 64,
+                                                        n0 + wn * 128, lane, vec));
     }
+    if constexpr (AMAX) epi_tile_amax(amax, wave, lane, partial);
+}
+
+// fp32 accumulators -> y = (acc * gA) * gW (fp32 or bf16).
+template <int OUT, int EPI = 0>
+__device__ __forceinline__ void f32_band_epilogue(v16f (&acc)[4][4], uint8_t *lds, float gA,
+                                                  float gW, int64_t M, int64_t N, int64_t m0,
+                                                  int64_t n0, int wave, int wm, int wn, int lane,
+                                                  void *y, float *partial = nullptr) {
+    EpiScaleF32 sc{gA, gW};
+    band_epilogue<OUT, EPI>(acc, sc, lds, M, N, m0, n0, wave, wm, wn, lane, y, partial);
 }
 
 }  // namespace dmpq

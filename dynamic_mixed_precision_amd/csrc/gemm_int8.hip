@@ -31,11 +31,70 @@ constexpr int LOADS = BM * BK / 16 / 256;     // 16-byte chunks per thread per o
 constexpr unsigned GROUP_M = 8;
 }  // namespace i8gemm
 
-template <int OUT>
+// Epilogue of both INT8 kernels, expanded in the kernel body (kept out of a
+// function: as a function the compiler spills a few registers of it to
+// scratch).  The MFMA runs with the W fragment as its first operand, so
+// acc[i][j] holds the transposed block: lane l owns activation row m = l % 32
+// of A-subtile i and, for register group g = r / 4, the four consecutive
+// output columns 8g + 4*(l/32) + 0..3 of W-subtile j.  OUT 0/1: y =
+// (float(acc) * sA[row]) * sW[col] (bit-exact in fp32), staged per wave
+// through LDS in two 64-row bands and stored row-contiguous, with GELU and
+// the fused amax per EPI; OUT 2: the raw int32 accumulators (test mode).  The
+// stage buffers must be free (both main loops end with a barrier).
+#define DMPQ_I8_EPILOGUE()                                                                        \
+    {                                                                                             \
+        constexpr int ES = OUT == 1 ? 2 : 4;                                                      \
+        using Band = EpiBand<ES>;                                                                 \
+        const int lm = lane & 31, lh = lane >> 5;                                                 \
+        float swv[4][4][4];                                                                       \
+        if constexpr (OUT != 2) {                                                                 \
+            _Pragma("unroll") for (int j = 0; j < 4; j++)                                         \
+                _Pragma("unroll") for (int g = 0; g < 4; g++)                                     \
+                    _Pragma("unroll") for (int e = 0; e < 4; e++) {                               \
+                const int64_t col = n0 + wn * 128 + j * 32 + 8 * g + 4 * lh + e;                  \
+                swv[j][g][e] = col < N ? sw[col] : 0.0f;                                          \
+            }                                                                                     \
+        }                                                                                         \
+        uint8_t *band = reinterpret_cast<uint8_t *>(lds) + wave * Band::BYTES;                    \
+        const bool vec = ((N * ES) & 15) == 0;                                                    \
+        float amax = 0.0f;                                                                        \
+        _Pragma("unroll") for (int h = 0; h < 2; h++) {                                           \
+            _Pragma("unroll") for (int ii = 0; ii < 2; ii++) {                                    \
+                const int i = 2 * h + ii;                                                         \
+                const int64_t row = m0 + wm * 128 + i * 32 + lm;                                  \
+                const float sar = row < M ? sa[row] : 0.0f;                                       \
+                _Pragma("unroll") for (int j = 0; j < 4; j++) {                                   \
+                    _Pragma("unroll") for (int g = 0; g < 4; g++) {                               \
+                        uint8_t *dst = band + (ii * 32 + lm) * Band::STRIDE + (j * 32 + 8 * g + 4 * lh) * ES; \
+                        if constexpr (OUT == 2) {                                                 \
+                            *reinterpret_cast<int4 *>(dst) =                                      \
+                                make_int4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], \
+                                          acc[i][j][4 * g + 3]);                                  \
+                        } else {                                                                  \
+                            float v4[4];                                                          \
+                            _Pragma("unroll") for (int e = 0; e < 4; e++) v4[e] =                 \
+                                ((float)acc[i][j][4 * g + e] * sar) * swv[j][g][e];               \
+                            if constexpr (OUT == 0)                                               \
+                                *reinterpret_cast<float4 *>(dst) = make_float4(v4[0], v4[1], v4[2], v4[3]); \
+                            else                                                                  \
+                                *reinterpret_cast<uint2 *>(dst) =                                 \
+                                    make_uint2(cvt_pk_bf16(v4[0], v4[1]), cvt_pk_bf16(v4[2], v4[3])); \
+                        }                                                                         \
+                    }                                                                             \
+                }                                                                                 \
+            }                                                                                     \
+            const float m = epi_band_to_global<ES, EPI>(band, y, M, N, m0 + wm * 128 + h * 64,    \
+                                                        n0 + wn * 128, lane, vec);                \
+            if constexpr ((EPI & kEpiAmax) != 0) amax = fmaxf(amax, m);                           \
+        }                                                                                         \
+        if constexpr ((EPI & kEpiAmax) != 0) epi_tile_amax(amax, wave, lane, partial);            \
+    }
+
+template <int OUT, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(
     const int8_t *__restrict__ A, const float *__restrict__ sa, const int8_t *__restrict__ W,
     const float *__restrict__ sw, int64_t M, int64_t N, int64_t K, void *__restrict__ y,
-    unsigned tiles_m, unsigned tiles_n) {
+    unsigned tiles_m, unsigned tiles_n, float *__restrict__ partial) {
     using namespace i8gemm;
     extern __shared__ __attribute__((aligned(16))) int8_t lds[];
     const int tid = threadIdx.x;
@@ -121,68 +180,18 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(
 #undef DMPQ_I8_GLOAD
 #undef DMPQ_I8_SSTORE
 
-    // Epilogue.  The MFMA runs with the W fragment as its first operand, so
-    // acc[i][j] holds the transposed block: lane l owns activation row
-    // m = l % 32 of A-subtile i and, for register group g = r / 4, the four
-    // consecutive output columns 8g + 4*(l/32) + 0..3 of W-subtile j.  Values
-    // are scaled here, staged per wave through LDS in two 64-row bands, and
-    // stored row-contiguous (the last loop iteration ended with a barrier, so
-    // the stage buffers are free).
-    constexpr int ES = OUT == 1 ? 2 : 4;
-    using Band = EpiBand<ES>;
-    const int lm = lane & 31, lh = lane >> 5;
-    float swv[4][4][4];
-#pragma unroll
-    for (int j = 0; j < 4; j++)
-#pragma unroll
-        for (int g = 0; g < 4; g++)
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int64_t col = n0 + wn * 128 + j * 32 + 8 * g + 4 * lh + e;
-                swv[j][g][e] = col < N ? sw[col] : 0.0f;
-            }
-    uint8_t *band = reinterpret_cast<uint8_t *>(lds) + wave * Band::BYTES;
-    const bool vec = ((N * ES) & 15) == 0;
-#pragma unroll
-    for (int h = 0; h < 2; h++) {
-#pragma unroll
-        for (int ii = 0; ii < 2; ii++) {
-            const int i = 2 * h + ii;
-            const int64_t row = m0 + wm * 128 + i * 32 + lm;
-            const float sar = row < M ? sa[row] : 0.0f;
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-#pragma unroll
-                for (int g = 0; g < 4; g++) {
-                    uint8_t *dst = band + (ii * 32 + lm) * Band::STRIDE + (j * 32 + 8 * g + 4 * lh) * ES;
-                    if constexpr (OUT == 2) {
-                        *reinterpret_cast<int4 *>(dst) = make_int4(acc[i][j][4 * g], acc[i][j][4 * g + 1],
-                                                                   acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-                    } else {
-                        float v4[4];
-#pragma unroll
-                        for (int e = 0; e < 4; e++) v4[e] = ((float)acc[i][j][4 * g + e] * sar) * swv[j][g][e];
-                        if constexpr (OUT == 0)
-                            *reinterpret_cast<float4 *>(dst) = make_float4(v4[0], v4[1], v4[2], v4[3]);
-                        else
-                            *reinterpret_cast<uint2 *>(dst) = make_uint2(cvt_pk_bf16(v4[0], v4[1]), cvt_pk_bf16(v4[2], v4[3]));
-                    }
-                }
-            }
-        }
-        epi_band_to_global<ES>(band, y, M, N, m0 + wm * 128 + h * 64, n0 + wn * 128, lane, vec);
-    }
+    DMPQ_I8_EPILOGUE()
 }
 
 // ---------------------------------------------------------------------------
 // Fast path for K % 128 == 0: the DMA-fed main loop of gemm_dma.hpp with i8
 // MFMA (v_mfma_i32_32x32x32_i8), then the scaled epilogue.
 // ---------------------------------------------------------------------------
-template <int OUT>
+template <int OUT, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_i8_dma_kernel(
     const int8_t *__restrict__ A, const float *__restrict__ sa, const int8_t *__restrict__ W,
     const float *__restrict__ sw, int64_t M, int64_t N, int64_t K, void *__restrict__ y,
-    unsigned tiles_m, unsigned tiles_n) {
+    unsigned tiles_m, unsigned tiles_n, float *__restrict__ partial) {
     using namespace gdma;
     extern __shared__ __attribute__((aligned(16))) int8_t lds[];
     const int tid = threadIdx.x;
@@ -196,95 +205,54 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_dma_kernel(
                                    reinterpret_cast<const uint8_t *>(W), M, N, K, m0, n0,
                                    reinterpret_cast<uint8_t *>(lds), acc);
 
-    constexpr int ES = OUT == 1 ? 2 : 4;
-    using Band = EpiBand<ES>;
-    const int lm = lane & 31, lh = lane >> 5;
-    float swv[4][4][4];
-#pragma unroll
-    for (int j = 0; j < 4; j++)
-#pragma unroll
-        for (int g = 0; g < 4; g++)
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int64_t col = n0 + wn * 128 + j * 32 + 8 * g + 4 * lh + e;
-                swv[j][g][e] = col < N ? sw[col] : 0.0f;
-            }
-    uint8_t *band = reinterpret_cast<uint8_t *>(lds) + wave * Band::BYTES;
-    const bool vec = ((N * ES) & 15) == 0;
-#pragma unroll
-    for (int h = 0; h < 2; h++) {
-#pragma unroll
-        for (int ii = 0; ii < 2; ii++) {
-            const int i = 2 * h + ii;
-            const int64_t row = m0 + wm * 128 + i * 32 + lm;
-            const float sar = row < M ? sa[row] : 0.0f;
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-#pragma unroll
-                for (int g = 0; g < 4; g++) {
-                    uint8_t *dst = band + (ii * 32 + lm) * Band::STRIDE + (j * 32 + 8 * g + 4 * lh) * ES;
-                    if constexpr (OUT == 2) {
-                        *reinterpret_cast<int4 *>(dst) = make_int4(acc[i][j][4 * g], acc[i][j][4 * g + 1],
-                                                                   acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-                    } else {
-                        float v4[4];
-#pragma unroll
-                        for (int e = 0; e < 4; e++) v4[e] = ((float)acc[i][j][4 * g + e] * sar) * swv[j][g][e];
-                        if constexpr (OUT == 0)
-                            *reinterpret_cast<float4 *>(dst) = make_float4(v4[0], v4[1], v4[2], v4[3]);
-                        else
-                            *reinterpret_cast<uint2 *>(dst) = make_uint2(cvt_pk_bf16(v4[0], v4[1]), cvt_pk_bf16(v4[2], v4[3]));
-                    }
-                }
-            }
-        }
-        epi_band_to_global<ES>(band, y, M, N, m0 + wm * 128 + h * 64, n0 + wn * 128, lane, vec);
-    }
+    DMPQ_I8_EPILOGUE()
 }
 
-hipError_t launch_gemm_int8(hipStream_t s, const int8_t *qa, const float *sa, const int8_t *qw,
-                            const float *sw, int64_t M, int64_t N, int64_t K, int out_dtype,
-                            void *y) {
-    if (M == 0 || N == 0) return hipSuccess;
+template <int OUT, int EPI>
+static hipError_t launch_i8_paths(hipStream_t s, const int8_t *qa, const float *sa, const int8_t *qw,
+                                  const float *sw, int64_t M, int64_t N, int64_t K, void *y,
+                                  float *partial) {
     // Kernels need more dynamic LDS than the default limit: opt in once.
     static const hipError_t attr = [] {
-        const void *fns[6] = {reinterpret_cast<const void *>(gemm_i8_kernel<0>),
-                              reinterpret_cast<const void *>(gemm_i8_kernel<1>),
-                              reinterpret_cast<const void *>(gemm_i8_kernel<2>),
-                              reinterpret_cast<const void *>(gemm_i8_dma_kernel<0>),
-                              reinterpret_cast<const void *>(gemm_i8_dma_kernel<1>),
-                              reinterpret_cast<const void *>(gemm_i8_dma_kernel<2>)};
-        const size_t bytes[6] = {2 * i8gemm::STAGE, 2 * i8gemm::STAGE, 2 * i8gemm::STAGE,
-                                 gdma::LDS_BYTES, gdma::LDS_BYTES, gdma::LDS_BYTES};
-        for (int f = 0; f < 6; f++) {
-            hipError_t e = hipFuncSetAttribute(fns[f], hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (int)bytes[f]);
-            if (e != hipSuccess) return e;
-        }
-        return hipSuccess;
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_i8_kernel<OUT, EPI>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)(2 * i8gemm::STAGE));
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_i8_dma_kernel<OUT, EPI>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)gdma::LDS_BYTES);
+        return e;
     }();
     if (attr != hipSuccess) return attr;
     const int64_t tm = (M + 255) / 256, tn = (N + 255) / 256;
     const dim3 grid((unsigned)(tm * tn)), block(256);
     const unsigned utm = (unsigned)tm, utn = (unsigned)tn;
-    if (K % gdma::BK == 0) {
-        const size_t lds = gdma::LDS_BYTES;
-        if (out_dtype == 0)
-            hipLaunchKernelGGL(gemm_i8_dma_kernel<0>, grid, block, lds, s, qa, sa, qw, sw, M, N, K, y, utm, utn);
-        else if (out_dtype == 1)
-            hipLaunchKernelGGL(gemm_i8_dma_kernel<1>, grid, block, lds, s, qa, sa, qw, sw, M, N, K, y, utm, utn);
-        else
-            hipLaunchKernelGGL(gemm_i8_dma_kernel<2>, grid, block, lds, s, qa, sa, qw, sw, M, N, K, y, utm, utn);
-    } else {
-        const size_t lds = 2 * i8gemm::STAGE;
-        if (out_dtype == 0)
-            hipLaunchKernelGGL(gemm_i8_kernel<0>, grid, block, lds, s, qa, sa, qw, sw, M, N, K, y, utm, utn);
-        else if (out_dtype == 1)
-            hipLaunchKernelGGL(gemm_i8_kernel<1>, grid, block, lds, s, qa, sa, qw, sw, M, N, K, y, utm, utn);
-        else
-            hipLaunchKernelGGL(gemm_i8_kernel<2>, grid, block, lds, s, qa, sa, qw, sw, M, N, K, y, utm, utn);
-    }
+    if (K % gdma::BK == 0)
+        hipLaunchKernelGGL((gemm_i8_dma_kernel<OUT, EPI>), grid, block, gdma::LDS_BYTES, s, qa, sa, qw, sw, M,
+                           N, K, y, utm, utn, partial);
+    else
+        hipLaunchKernelGGL((gemm_i8_kernel<OUT, EPI>), grid, block, 2 * i8gemm::STAGE, s, qa, sa, qw, sw, M,
+                           N, K, y, utm, utn, partial);
     return hipGetLastError();
+}
+
+hipError_t launch_gemm_int8(hipStream_t s, const int8_t *qa, const float *sa, const int8_t *qw,
+                            const float *sw, int64_t M, int64_t N, int64_t K, int out_dtype,
+                            void *y, int epi, float *partial) {
+    if (M == 0 || N == 0) return hipSuccess;
+    if (epi == 0) {
+        switch (out_dtype) {
+            case 0: return launch_i8_paths<0, 0>(s, qa, sa, qw, sw, M, N, K, y, partial);
+            case 1: return launch_i8_paths<1, 0>(s, qa, sa, qw, sw, M, N, K, y, partial);
+            case 2: return launch_i8_paths<2, 0>(s, qa, sa, qw, sw, M, N, K, y, partial);
+        }
+        return hipErrorInvalidValue;
+    }
+    if (out_dtype != 1) return hipErrorInvalidValue;
+    switch (epi) {
+        case 1: return launch_i8_paths<1, 1>(s, qa, sa, qw, sw, M, N, K, y, partial);
+        case 2: return launch_i8_paths<1, 2>(s, qa, sa, qw, sw, M, N, K, y, partial);
+        case 3: return launch_i8_paths<1, 3>(s, qa, sa, qw, sw, M, N, K, y, partial);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace dmpq

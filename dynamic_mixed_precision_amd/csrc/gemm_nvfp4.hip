@@ -84,19 +84,20 @@ __device__ __forceinline__ void dequant32_fast(const uint4 c, uint32_t s01, uint
 // Epilogue of the NVFP4 kernels: y = (acc * gA) * gW through the per-wave LDS
 // bands (callers end their main loop with a barrier, so the stage buffers are
 // free).
-template <int OUT>
+template <int OUT, int EPI>
 __device__ __forceinline__ void fp4_epilogue(v16f (&acc)[4][4], uint8_t *lds, const float *ga,
                                              const float *gw, int64_t M, int64_t N, int64_t m0,
                                              int64_t n0, int wave, int wm, int wn, int lane,
-                                             void *y) {
-    f32_band_epilogue<OUT>(acc, lds, *ga, *gw, M, N, m0, n0, wave, wm, wn, lane, y);
+                                             void *y, float *partial) {
+    f32_band_epilogue<OUT, EPI>(acc, lds, *ga, *gw, M, N, m0, n0, wave, wm, wn, lane, y, partial);
 }
 
-template <int OUT>
+template <int OUT, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_fp4_f16_kernel(
     const uint8_t *__restrict__ ca, const uint8_t *__restrict__ sa, const float *__restrict__ ga,
     const uint8_t *__restrict__ cw, const uint8_t *__restrict__ sw, const float *__restrict__ gw,
-    int64_t M, int64_t N, int64_t K, void *__restrict__ y, unsigned tiles_m, unsigned tiles_n) {
+    int64_t M, int64_t N, int64_t K, void *__restrict__ y, unsigned tiles_m, unsigned tiles_n,
+    float *__restrict__ partial) {
     using namespace fp4gemm;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tid = threadIdx.x;
@@ -228,7 +229,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_f16_kernel(
 #undef DMPQ_F4_MFMA
 #undef DMPQ_F4_ITER
 
-    fp4_epilogue<OUT>(acc, lds, ga, gw, M, N, m0, n0, wave, wm, wn, lane, y);
+    fp4_epilogue<OUT, EPI>(acc, lds, ga, gw, M, N, m0, n0, wave, wm, wn, lane, y, partial);
 }
 
 // ---------------------------------------------------------------------------
@@ -238,11 +239,12 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_f16_kernel(
 // code load and one 2-byte scale load from per-lane pointers fixed for the
 // whole K loop; scales are decoded by the hardware fp8 converter.
 // ---------------------------------------------------------------------------
-template <int OUT>
+template <int OUT, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_fp4_fast_kernel(
     const uint8_t *__restrict__ ca, const uint8_t *__restrict__ sa, const float *__restrict__ ga,
     const uint8_t *__restrict__ cw, const uint8_t *__restrict__ sw, const float *__restrict__ gw,
-    int64_t M, int64_t N, int64_t K, void *__restrict__ y, unsigned tiles_m, unsigned tiles_n) {
+    int64_t M, int64_t N, int64_t K, void *__restrict__ y, unsigned tiles_m, unsigned tiles_n,
+    float *__restrict__ partial) {
     using namespace fp4gemm;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tid = threadIdx.x;
@@ -352,7 +354,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_fast_kernel(
 #undef DMPQ_F4F_MFMA
 #undef DMPQ_F4F_ITER
 
-    fp4_epilogue<OUT>(acc, lds, ga, gw, M, N, m0, n0, wave, wm, wn, lane, y);
+    fp4_epilogue<OUT, EPI>(acc, lds, ga, gw, M, N, m0, n0, wave, wm, wn, lane, y, partial);
 }
 
 // One k-step fragment: the 8 codes of 32-bit word S of a 16-byte piece, times
@@ -492,11 +494,12 @@ __device__ __forceinline__ void fp4dma_stage(const uint8_t *__restrict__ cur, ui
 #undef DMPQ_F4D_CHUNK
 }
 
-template <int OUT>
+template <int OUT, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_fp4_dma_kernel(
     const uint8_t *__restrict__ ca, const uint8_t *__restrict__ sa, const float *__restrict__ ga,
     const uint8_t *__restrict__ cw, const uint8_t *__restrict__ sw, const float *__restrict__ gw,
-    int64_t M, int64_t N, int64_t K, void *__restrict__ y, unsigned tiles_m, unsigned tiles_n) {
+    int64_t M, int64_t N, int64_t K, void *__restrict__ y, unsigned tiles_m, unsigned tiles_n,
+    float *__restrict__ partial) {
     using namespace fp4dma;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tid = threadIdx.x;
@@ -556,7 +559,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_dma_kernel(
     __builtin_amdgcn_s_waitcnt(0xC07F & ~0xC00F);  // the last copy has landed
     __syncthreads();  // every wave is done reading the stage buffers before they hold bands
 
-    fp4_epilogue<OUT>(acc, lds, ga, gw, M, N, m0, n0, wave, wm, wn, lane, y);
+    fp4_epilogue<OUT, EPI>(acc, lds, ga, gw, M, N, m0, n0, wave, wm, wn, lane, y, partial);
 }
 
 // ---------------------------------------------------------------------------
@@ -696,50 +699,58 @@ static hipError_t allow_lds(KernelFn fn, size_t bytes) {
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-hipError_t launch_gemm_nvfp4(hipStream_t s, const uint8_t *ca, const uint8_t *sa,
-                             const float *ga, const uint8_t *cw, const uint8_t *sw,
-                             const float *gw, int64_t M, int64_t N, int64_t K, int out_dtype,
-                             void *y, int variant) {
+template <int OUT, int EPI>
+static hipError_t launch_fp4_paths(hipStream_t s, const uint8_t *ca, const uint8_t *sa,
+                                   const float *ga, const uint8_t *cw, const uint8_t *sw,
+                                   const float *gw, int64_t M, int64_t N, int64_t K, void *y,
+                                   float *partial) {
     using namespace fp4gemm;
-    if (M == 0 || N == 0) return hipSuccess;
     static const hipError_t attr = [] {
-        hipError_t e = allow_lds(gemm_fp4_f16_kernel<0>, 2 * STAGE);
-        if (e == hipSuccess) e = allow_lds(gemm_fp4_f16_kernel<1>, 2 * STAGE);
-        if (e == hipSuccess) e = allow_lds(gemm_fp4_fast_kernel<0>, 2 * STAGE);
-        if (e == hipSuccess) e = allow_lds(gemm_fp4_fast_kernel<1>, 2 * STAGE);
-        if (e == hipSuccess) e = allow_lds(gemm_fp4_dma_kernel<0>, fp4dma::LDS_BYTES);
-        if (e == hipSuccess) e = allow_lds(gemm_fp4_dma_kernel<1>, fp4dma::LDS_BYTES);
+        hipError_t e = allow_lds(gemm_fp4_f16_kernel<OUT, EPI>, 2 * STAGE);
+        if (e == hipSuccess) e = allow_lds(gemm_fp4_fast_kernel<OUT, EPI>, 2 * STAGE);
+        if (e == hipSuccess) e = allow_lds(gemm_fp4_dma_kernel<OUT, EPI>, fp4dma::LDS_BYTES);
         return e;
     }();
     if (attr != hipSuccess) return attr;
     const int64_t tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
     const dim3 grid((unsigned)(tm * tn)), block(256);
     const unsigned utm = (unsigned)tm, utn = (unsigned)tn;
+    if (K % fp4dma::BKE == 0)
+        hipLaunchKernelGGL((gemm_fp4_dma_kernel<OUT, EPI>), grid, block, fp4dma::LDS_BYTES, s, ca, sa, ga,
+                           cw, sw, gw, M, N, K, y, utm, utn, partial);
+    else if (K % (4 * 16) == 0)
+        hipLaunchKernelGGL((gemm_fp4_fast_kernel<OUT, EPI>), grid, block, 2 * STAGE, s, ca, sa, ga, cw,
+                           sw, gw, M, N, K, y, utm, utn, partial);
+    else
+        hipLaunchKernelGGL((gemm_fp4_f16_kernel<OUT, EPI>), grid, block, 2 * STAGE, s, ca, sa, ga, cw,
+                           sw, gw, M, N, K, y, utm, utn, partial);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_nvfp4(hipStream_t s, const uint8_t *ca, const uint8_t *sa,
+                             const float *ga, const uint8_t *cw, const uint8_t *sw,
+                             const float *gw, int64_t M, int64_t N, int64_t K, int out_dtype,
+                             void *y, int variant, int epi, float *partial) {
+    if (M == 0 || N == 0) return hipSuccess;
     if (variant == 1) {
+        if (epi != 0) return hipErrorInvalidValue;
         const int64_t sm = (M + fp4scaled::BM - 1) / fp4scaled::BM, sn = (N + fp4scaled::BN - 1) / fp4scaled::BN;
+        const dim3 block(256);
         if (out_dtype == 0)
             hipLaunchKernelGGL(gemm_fp4_scaled_kernel<0>, dim3((unsigned)(sm * sn)), block, 0, s, ca, sa, ga, cw, sw, gw, M, N, K, y, (unsigned)sn);
         else
             hipLaunchKernelGGL(gemm_fp4_scaled_kernel<1>, dim3((unsigned)(sm * sn)), block, 0, s, ca, sa, ga, cw, sw, gw, M, N, K, y, (unsigned)sn);
         return hipGetLastError();
     }
-    const bool fast = K % (4 * 16) == 0;
-    if (K % fp4dma::BKE == 0) {
-        if (out_dtype == 0)
-            hipLaunchKernelGGL(gemm_fp4_dma_kernel<0>, grid, block, fp4dma::LDS_BYTES, s, ca, sa, ga, cw, sw, gw, M, N, K, y, utm, utn);
-        else
-            hipLaunchKernelGGL(gemm_fp4_dma_kernel<1>, grid, block, fp4dma::LDS_BYTES, s, ca, sa, ga, cw, sw, gw, M, N, K, y, utm, utn);
-        return hipGetLastError();
+    if (out_dtype == 0 && epi == 0) return launch_fp4_paths<0, 0>(s, ca, sa, ga, cw, sw, gw, M, N, K, y, partial);
+    if (out_dtype != 1) return hipErrorInvalidValue;
+    switch (epi) {
+        case 0: return launch_fp4_paths<1, 0>(s, ca, sa, ga, cw, sw, gw, M, N, K, y, partial);
+        case 1: return launch_fp4_paths<1, 1>(s, ca, sa, ga, cw, sw, gw, M, N, K, y, partial);
+        case 2: return launch_fp4_paths<1, 2>(s, ca, sa, ga, cw, sw, gw, M, N, K, y, partial);
+        case 3: return launch_fp4_paths<1, 3>(s, ca, sa, ga, cw, sw, gw, M, N, K, y, partial);
     }
-    if (fast && out_dtype == 0)
-        hipLaunchKernelGGL(gemm_fp4_fast_kernel<0>, grid, block, 2 * STAGE, s, ca, sa, ga, cw, sw, gw, M, N, K, y, utm, utn);
-    else if (fast)
-        hipLaunchKernelGGL(gemm_fp4_fast_kernel<1>, grid, block, 2 * STAGE, s, ca, sa, ga, cw, sw, gw, M, N, K, y, utm, utn);
-    else if (out_dtype == 0)
-        hipLaunchKernelGGL(gemm_fp4_f16_kernel<0>, grid, block, 2 * STAGE, s, ca, sa, ga, cw, sw, gw, M, N, K, y, utm, utn);
-    else
-        hipLaunchKernelGGL(gemm_fp4_f16_kernel<1>, grid, block, 2 * STAGE, s, ca, sa, ga, cw, sw, gw, M, N, K, y, utm, utn);
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }
 
 }  // namespace dmpq

@@ -26,6 +26,9 @@ hipError_t launch_hq_int8(hipStream_t s, const uint16_t *x, int64_t M, int64_t K
                           int8_t *q, float *s_row);
 hipError_t launch_hq_nvfp4(hipStream_t s, const uint16_t *x, int64_t M, int64_t K, int flags,
                            uint8_t *codes, uint8_t *scales, float *g, const Workspace &ws);
+// Output tiles of the GEMMs (256 x 256 on every path that takes an epilogue):
+// the number of per-tile maxima a fused-amax GEMM writes.
+inline int64_t gemm_tiles(int64_t M, int64_t N) { return ((M + 255) / 256) * ((N + 255) / 256); }
 hipError_t launch_w8_from_nvfp4(hipStream_t s, const uint8_t *cw, const uint8_t *sw,
                                 const float *gw, int64_t N, int64_t K, int8_t *qw,
                                 float *sw_row);
@@ -39,11 +42,13 @@ hipError_t launch_tdc_refresh(hipStream_t s, const uint16_t *x_in, const uint16_
                               uint16_t *delta, int64_t n, int delta_valid, double *sums,
                               const Workspace &ws);
 
+// epi: bit 0 GELU, bit 1 fused NVFP4 amax of the output into partial[tile]
+// (bf16 output only); the GEMM tile is 256 x 256 on every path.
 hipError_t launch_gemm_int8(hipStream_t s, const int8_t *qa, const float *sa, const int8_t *qw,
                             const float *sw, int64_t M, int64_t N, int64_t K, int out_dtype,
-                            void *y);
+                            void *y, int epi, float *partial);
 hipError_t launch_gemm_bf16(hipStream_t s, const uint16_t *x, const uint16_t *w, int64_t M,
-                            int64_t N, int64_t K, int out_dtype, void *y);
+                            int64_t N, int64_t K, int out_dtype, void *y, int epi, float *partial);
 hipError_t launch_outlier_count(hipStream_t s, const uint16_t *x, int64_t M, int64_t K,
                                 double kappa, double *count, const Workspace &ws);
 // Sum ns values per partial over nparts partials, in a fixed order, into out[ns].
@@ -52,7 +57,7 @@ hipError_t launch_finalize_sums(hipStream_t s, const double *partial, int nparts
 hipError_t launch_gemm_nvfp4(hipStream_t s, const uint8_t *ca, const uint8_t *sa,
                              const float *ga, const uint8_t *cw, const uint8_t *sw,
                              const float *gw, int64_t M, int64_t N, int64_t K, int out_dtype,
-                             void *y, int variant);
+                             void *y, int variant, int epi, float *partial);
 
 // Grid for a grid-stride loop over `work` items with 256 threads per group.
 inline unsigned stride_grid(int64_t work, int64_t per_group, unsigned cap) {

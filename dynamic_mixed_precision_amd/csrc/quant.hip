@@ -425,17 +425,41 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t *__rest
     }
 }
 
+// DMPQ_AMAX_GIVEN: one workgroup folds the producer GEMM's per-tile maxima
+// into partial[0] (every read precedes the barrier, so the in-place write is
+// safe), and pass 2 then reduces that single partial.
+__global__ __launch_bounds__(1024) void amax_fold_kernel(float *__restrict__ partial, int64_t n) {
+    __shared__ float red[16];
+    const int tid = threadIdx.x;
+    float m = 0.0f;
+    for (int64_t i = tid; i < n; i += 1024) m = fmaxf(m, partial[i]);
+    m = wave_max(m);
+    if ((tid & (kWave - 1)) == 0) red[tid / kWave] = m;
+    __syncthreads();
+    if (tid == 0) {
+        float a = red[0];
+        for (int w = 1; w < 16; w++) a = fmaxf(a, red[w]);
+        partial[0] = a;
+    }
+}
+
 hipError_t launch_hq_nvfp4(hipStream_t s, const uint16_t *x, int64_t M, int64_t K, int flags,
                            uint8_t *codes, uint8_t *scales, float *g, const Workspace &ws) {
     const int64_t nblocks = M * (K / 16);
     float *partial = reinterpret_cast<float *>(ws.partial);
-    const unsigned ga = stride_grid(nblocks, 256 * 4, kAmaxGroups);
-    hipLaunchKernelGGL(nvfp4_amax_kernel, dim3(ga), dim3(256), 0, s, x, nblocks, flags, partial);
+    unsigned nparts;
+    if (flags & 2) {
+        hipLaunchKernelGGL(amax_fold_kernel, dim3(1), dim3(1024), 0, s, partial, gemm_tiles(M, K));
+        nparts = 1;
+    } else {
+        nparts = stride_grid(nblocks, 256 * 4, kAmaxGroups);
+        hipLaunchKernelGGL(nvfp4_amax_kernel, dim3(nparts), dim3(256), 0, s, x, nblocks, flags, partial);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned gb = stride_grid(nblocks, 256 * 2, 8192);
-    hipLaunchKernelGGL(nvfp4_quant_kernel, dim3(gb), dim3(256), 0, s, x, nblocks, flags, partial,
-                       (int)ga, codes, scales, g);
+    hipLaunchKernelGGL(nvfp4_quant_kernel, dim3(gb), dim3(256), 0, s, x, nblocks, flags & 1, partial,
+                       (int)nparts, codes, scales, g);
     return hipGetLastError();
 }
 

@@ -63,8 +63,13 @@ enum { DMPQ_ROUTE_NVFP4 = 0, DMPQ_ROUTE_INT8 = 1, DMPQ_ROUTE_BF16 = 2 };
 /* GEMM output types: fp32 (the contract), bf16 (RNE of the fp32 value), and
  * the raw int32 accumulators of the INT8 GEMM (test mode). */
 enum { DMPQ_OUT_F32 = 0, DMPQ_OUT_BF16 = 1, DMPQ_OUT_I32 = 2 };
-/* Quantizer flags: bit 0 skips the block Hadamard (test hook). */
-enum { DMPQ_NO_HADAMARD = 1 };
+/* Quantizer flags: bit 0 skips the block Hadamard (test hook); bit 1 (NVFP4
+ * only) takes the tensor amax from the tile maxima a producer GEMM left in
+ * the workspace (DMPQ_EPI_NVFP4_AMAX) instead of reading x for it. */
+enum { DMPQ_NO_HADAMARD = 1, DMPQ_AMAX_GIVEN = 2 };
+/* Producer epilogues of the *_ex GEMMs (bit flags, BF16 output only):
+ * GELU on the way out, and the next linear's NVFP4 tensor-amax term. */
+enum { DMPQ_EPI_GELU = 1, DMPQ_EPI_NVFP4_AMAX = 2 };
 /* INT8 weight derivation in dmpq_prep_weight. */
 enum { DMPQ_W8_FROM_NVFP4 = 0, DMPQ_W8_DIRECT = 1 };
 /* TDC step modes. */
@@ -79,14 +84,16 @@ enum { DMPQ_TDC_SKIP = 0, DMPQ_TDC_REFRESH = 1 };
 enum { DMPQ_FP4_BF16_DEQUANT = 0, DMPQ_FP4_SCALED_MFMA = 1 };
 /* Workspace users. */
 enum { DMPQ_OP_GAMMA = 0, DMPQ_OP_QUANT_NVFP4 = 1, DMPQ_OP_TDC = 2, DMPQ_OP_PREP_WEIGHT = 3,
-       DMPQ_OP_OUTLIER = 4 };
+       DMPQ_OP_OUTLIER = 4, DMPQ_OP_GEMM_AMAX = 5 };
 
 /* Message describing the calling thread's last error ("" if none). */
 const char *dmpq_last_error(void);
 /* Library version string. */
 const char *dmpq_version(void);
-/* Bytes of workspace the op needs (sizes M, K are accepted for future use;
- * the current kernels need a fixed amount). 0 for an unknown op. */
+/* Bytes of workspace the op needs, 0 for an unknown op.  Most ops need a
+ * fixed amount.  DMPQ_OP_GEMM_AMAX (a fused-amax producer GEMM and the
+ * NVFP4 quantization of its output) depends on the output's shape: pass the
+ * GEMM's M and N as (M, K). */
 size_t dmpq_workspace_bytes(int op, int64_t M, int64_t K);
 
 /* ---------------------------------------------------------------------------
@@ -139,6 +146,11 @@ dmpq_status dmpq_hadamard_quant_int8(hipStream_t stream, const uint16_t *x, int6
  * nibble of byte i; scales [M x K/16] uint8.  A zero tensor gives g = 0 and
  * all-zero outputs.  Two passes over x (tensor amax, then codes).
  * ws: dmpq_workspace_bytes(DMPQ_OP_QUANT_NVFP4, M, K) bytes.
+ * flags DMPQ_AMAX_GIVEN: x is the output of a *_ex GEMM with
+ * DMPQ_EPI_NVFP4_AMAX, and ws is the workspace that GEMM wrote, untouched
+ * since (dmpq_workspace_bytes(DMPQ_OP_GEMM_AMAX, M, K) bytes).  A comes from
+ * the GEMM's per-tile maxima, so x is read once; the outputs are the same
+ * bits as without the flag.  Not combinable with DMPQ_NO_HADAMARD.
  * ------------------------------------------------------------------------- */
 dmpq_status dmpq_hadamard_quant_nvfp4(hipStream_t stream, const uint16_t *x, int64_t M,
                                       int64_t K, int flags, uint8_t *codes, uint8_t *scales,
@@ -273,6 +285,34 @@ dmpq_status dmpq_pdr_decide(double h_count, int64_t n, double rho, int *h_force)
  * or BF16 (RNE of the fp32 value).  K % 16 == 0; any M, N >= 0. */
 dmpq_status dmpq_gemm_bf16(hipStream_t stream, const uint16_t *x, const uint16_t *w, int64_t M,
                            int64_t N, int64_t K, int out_dtype, void *y);
+
+/* ---------------------------------------------------------------------------
+ * Producer-fused epilogues: the three linears above with an epilogue that
+ * prepares the next linear's input ([gist-en] §2.A "Outlier Smoothing": the
+ * rotation must cost little, so its tensor-wide pass is folded into the GEMM
+ * that produces the tensor).  out_dtype must be DMPQ_OUT_BF16 when
+ * epilogue != 0; epilogue 0 is the plain call.
+ *   DMPQ_EPI_GELU: y = bf16(GELU(float(bf16(v)))) for the linear's value v,
+ *     GELU(u) = u * Phi(u) = u/2 * erfc(-u/sqrt 2) in fp32 -- the same result
+ *     as a separate bf16 GELU after the GEMM, up to GELU's own rounding.
+ *   DMPQ_EPI_NVFP4_AMAX: the kernel also writes, per 256 x 256 output tile,
+ *     max |H16 rotation of its 16-blocks| over the stored y (the rotation and
+ *     fp32 order of dmpq_hadamard_quant_nvfp4) into ws, for a following
+ *     dmpq_hadamard_quant_nvfp4(y, M, N, DMPQ_AMAX_GIVEN, ..., ws).  Needs
+ *     N % 16 == 0 and ws of dmpq_workspace_bytes(DMPQ_OP_GEMM_AMAX, M, N)
+ *     bytes; ws may be NULL otherwise.
+ * The NVFP4 variant is always DMPQ_FP4_BF16_DEQUANT.
+ * ------------------------------------------------------------------------- */
+dmpq_status dmpq_qgemm_int8_ex(hipStream_t stream, const int8_t *qa, const float *sa,
+                               const int8_t *qw, const float *sw, int64_t M, int64_t N, int64_t K,
+                               int out_dtype, void *y, int epilogue, void *ws, size_t ws_bytes);
+dmpq_status dmpq_qgemm_nvfp4_ex(hipStream_t stream, const uint8_t *ca, const uint8_t *sa,
+                                const float *d_ga, const uint8_t *cw, const uint8_t *sw,
+                                const float *d_gw, int64_t M, int64_t N, int64_t K,
+                                int out_dtype, void *y, int epilogue, void *ws, size_t ws_bytes);
+dmpq_status dmpq_gemm_bf16_ex(hipStream_t stream, const uint16_t *x, const uint16_t *w, int64_t M,
+                              int64_t N, int64_t K, int out_dtype, void *y, int epilogue, void *ws,
+                              size_t ws_bytes);
 
 #ifdef __cplusplus
 }

@@ -134,6 +134,41 @@ def test_validation_before_launch(monkeypatch):
             _Fake((8, 32)), _Fake((8,)))
 
 
+def test_fused_epilogue_validation(monkeypatch):
+    """Producer-epilogue GEMMs and the quantizer's given-amax flag reject
+    bad combinations before any launch."""
+    monkeypatch.setattr(dm, "_stream", lambda s=None: 0)
+    M, N, K = 300, 48, 64
+    qa, sa, qw, sw = _Fake((M, K)), _Fake((M,)), _Fake((N, K)), _Fake((N,))
+    y = _Fake((M, N))
+    need = dm.workspace_bytes(dm.OP_GEMM_AMAX, M, N)
+    assert need >= 4 * 2 * 1 and need >= dm.workspace_bytes(dm.OP_QUANT_NVFP4)
+    # 2^20 x 2^16 outputs = 16384 tiles: the size grows past the fixed workspace
+    assert dm.workspace_bytes(dm.OP_GEMM_AMAX, 1 << 20, 1 << 16) == 4 * 4096 * 256
+    assert dm.workspace_bytes(dm.OP_GEMM_AMAX, -1, 16) == 0
+    _expect(1, dm.qgemm_int8_ex, qa, sa, qw, sw, y, 4)                          # unknown bit
+    _expect(4, dm.qgemm_int8_ex, qa, sa, qw, sw, y, dm.EPI_GELU, out_dtype=dm.OUT_F32)
+    _expect(2, dm.qgemm_int8_ex, qa, sa, _Fake((40, K)), _Fake((40,)), _Fake((M, 40)),
+            dm.EPI_NVFP4_AMAX, ws=_Fake((need,), numel=need))                   # N % 16
+    _expect(6, dm.qgemm_int8_ex, qa, sa, qw, sw, y, dm.EPI_NVFP4_AMAX)          # no workspace
+    _expect(6, dm.qgemm_int8_ex, qa, sa, qw, sw, y, dm.EPI_NVFP4_AMAX, ws=_Fake((4,), numel=4))
+    _expect(3, dm.gemm_bf16_ex, _Fake((M, K)), _Fake((N, K)), y, dm.EPI_NVFP4_AMAX,
+            ws=_Fake((need,), numel=need, addr=0x10008))
+    _expect(4, dm.qgemm_nvfp4_ex, _Fake((M, K // 2)), _Fake((M, K // 16)), _Fake((1,)),
+            _Fake((N, K // 2)), _Fake((N, K // 16)), _Fake((1,)), y, dm.EPI_GELU,
+            out_dtype=dm.OUT_F32)
+    x = _Fake((M, N))
+    ws = _Fake((need,), numel=need)
+    _expect(1, dm.hadamard_quant_nvfp4, x, _Fake((M, N // 2)), _Fake((M, N // 16)), _Fake((1,)),
+            ws, flags=dm.AMAX_GIVEN | dm.NO_HADAMARD)
+    _expect(1, dm.hadamard_quant_nvfp4, x, _Fake((M, N // 2)), _Fake((M, N // 16)), _Fake((1,)),
+            ws, flags=4)
+    big = 1 << 20
+    small = dm.workspace_bytes(dm.OP_QUANT_NVFP4)
+    _expect(6, dm.hadamard_quant_nvfp4, _Fake((big, 1 << 16)), _Fake((big, 1 << 15)),
+            _Fake((big, 1 << 12)), _Fake((1,)), _Fake((small,), numel=small), flags=dm.AMAX_GIVEN)
+
+
 def test_null_pointer_rejected():
     L = dm.lib()
     st = L.dmpq_hadamard_quant_int8(None, None, 4, 32, 0, None, None)
