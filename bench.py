@@ -12,7 +12,9 @@ One step is one pass of the whole hot path over a CogVideoX-5B-like batch
      NVFP4) and the PDR decision;
   2. per block, per linear (qkv 9216x3072, out 3072x3072, ffn_up 12288x3072,
      ffn_down 3072x12288): Hadamard + activation quant at the routed
-     precision, then the quantized GEMM against the offline NVFP4 weights;
+     precision, then the quantized GEMM against the offline NVFP4 weights
+     (with the GEMM workspace, so the last partial wave of tiles is split
+     along K);
      an INT8-routed linear first converts its NVFP4 weight to INT8 into one
      shared scratch buffer (only the 4.5-bit weights are kept);
      with --fuse-ffn on, ffn_down consumes ffn_up's output instead: the
@@ -59,6 +61,9 @@ def parse():
                    help="on: ffn_down's input is ffn_up's output, GELU and the next NVFP4 amax are "
                         "fused into ffn_up's GEMM epilogue (needs --out-dtype bf16); off: every "
                         "linear reads its own synthetic input (the linears alone)")
+    p.add_argument("--tail-split", choices=["on", "off"], default="on",
+                   help="on: the GEMMs get the full workspace, so the last partial wave of tiles is "
+                        "split along K; off: a workspace with room for the fused-amax maxima only")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=512,
                    help="rows of the qkv linear the oracle runs for the CPU baseline")
@@ -77,19 +82,32 @@ def parse():
 
 
 class KernelTimer:
-    """HIP events around each library call on the current stream."""
+    """HIP events around each library call on the current stream.  The events
+    are created before the timed region (prepare), so inside it a call costs
+    only the two event records."""
 
     def __init__(self, torch):
         self.torch = torch
         self.rec = {}
         self.on = False
+        self.calls = 0          # calls seen while off (counts one step's calls)
+        self.pool = []
+
+    def prepare(self, n):
+        ev = self.torch.cuda.Event
+        self.pool = [(ev(enable_timing=True), ev(enable_timing=True)) for _ in range(n)]
+        self.pool.reverse()
 
     def __call__(self, name, work, fn, *a, **kw):
         if not self.on:
+            self.calls += 1
             fn(*a, **kw)
             return
-        s = self.torch.cuda.Event(enable_timing=True)
-        e = self.torch.cuda.Event(enable_timing=True)
+        if self.pool:
+            s, e = self.pool.pop()
+        else:
+            s = self.torch.cuda.Event(enable_timing=True)
+            e = self.torch.cuda.Event(enable_timing=True)
         s.record()
         fn(*a, **kw)
         e.record()
@@ -187,7 +205,10 @@ def main():
         sys.exit(2)
     names = [lin.name for lin in cfg.linears]
     i_up, i_down = names.index("ffn_up"), names.index("ffn_down")
-    ws_amax = dm.new_workspace(dm.OP_GEMM_AMAX, "cuda", M, cfg.linears[i_up].N)
+    # the GEMMs' workspace: fused-amax maxima, then the split area of the
+    # last partial wave of tiles (sized for the widest output)
+    ws_gemm = dm.new_workspace(dm.OP_GEMM if args.tail_split == "on" else dm.OP_GEMM_AMAX, "cuda", M,
+                               max(lin.N for lin in cfg.linears))
     torch.cuda.synchronize()
     setup_s = time.time() - t0
 
@@ -231,10 +252,10 @@ def main():
                 if fuse and li == i_down:
                     x = ybuf[names[i_up]].view(torch.int16)
                     if route == dm.ROUTE_NVFP4:
-                        qflags, qws = dm.AMAX_GIVEN, ws_amax
+                        qflags, qws = dm.AMAX_GIVEN, ws_gemm
                 if route == dm.ROUTE_BF16:
                     kt("gemm_bf16", flops, dm.gemm_bf16_ex, x.view(M, lin.K), L["w"], ybuf[lin.name],
-                       epi, ws_amax, out_dtype)
+                       epi, ws_gemm, out_dtype)
                 elif route == dm.ROUTE_INT8:
                     kt("hadamard_quant_int8", 3.0 * M * lin.K + 4.0 * M,
                        dm.hadamard_quant_int8, x, qb["q"], qb["s"])
@@ -245,13 +266,13 @@ def main():
                         kt("weight_int8_from_nvfp4", (0.5 + 1.0 / 16 + 1.0) * lin.N * lin.K + 8.0 * lin.N,
                            dm.weight_int8_from_nvfp4, L["cw"], L["sw"], L["gw"], qw, swr)
                     kt("qgemm_int8", flops, dm.qgemm_int8_ex, qb["q"], qb["s"], qw, swr,
-                       ybuf[lin.name], epi, ws_amax, out_dtype)
+                       ybuf[lin.name], epi, ws_gemm, out_dtype)
                 else:
                     kt("hadamard_quant_nvfp4_given" if qflags else "hadamard_quant_nvfp4",
                        (2.0 + 0.5 + 1.0 / 16) * M * lin.K + 4.0,
                        dm.hadamard_quant_nvfp4, x, qb["c"], qb["sc"], qb["g"], qws, qflags)
                     kt("qgemm_nvfp4", flops, dm.qgemm_nvfp4_ex, qb["c"], qb["sc"], qb["g"], L["cw"],
-                       L["sw"], L["gw"], ybuf[lin.name], epi, ws_amax, out_dtype)
+                       L["sw"], L["gw"], ybuf[lin.name], epi, ws_gemm, out_dtype)
             # 3. Temporal Delta Cache refresh of the block
             kt("tdc_step_refresh", 8.0 * M * H, dm.tdc_step, dm.TDC_REFRESH, blk["x_in"],
                blk["x_out"], blk["delta"], blk["delta_valid"], tsums[b], ws)
@@ -271,7 +292,9 @@ def main():
         calib = dict(kernel=CALIB_KERNEL, elements=n, read_bytes=4 * n, write_bytes=2 * n)
 
     for _ in range(args.warmup):
+        kt.calls = 0
         step()
+    kt.prepare(kt.calls * args.steps)
     torch.cuda.synchronize()
     kt.on = True
     t_start = time.perf_counter()
@@ -336,6 +359,7 @@ def main():
                    "gemm_out": args.out_dtype,
                    "int8_weights": args.int8_weights,
                    "ffn_fused": fuse,
+                   "tail_split": args.tail_split == "on",
                    "gemm_tera_ops_per_step": round(gemm_ops_step / 1e12, 3)},
         "act_quant_GBps": round(q_bytes * 1e-9 / (q_ms * 1e-3), 1),
         "kernels": kernels,

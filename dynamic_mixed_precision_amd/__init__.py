@@ -26,7 +26,7 @@ W8_FROM_NVFP4, W8_DIRECT = 0, 1
 TDC_SKIP, TDC_REFRESH = 0, 1
 FP4_BF16_DEQUANT = 0
 FP4_SCALED_MFMA = 1
-OP_GAMMA, OP_QUANT_NVFP4, OP_TDC, OP_PREP_WEIGHT, OP_OUTLIER, OP_GEMM_AMAX = 0, 1, 2, 3, 4, 5
+OP_GAMMA, OP_QUANT_NVFP4, OP_TDC, OP_PREP_WEIGHT, OP_OUTLIER, OP_GEMM_AMAX, OP_GEMM = 0, 1, 2, 3, 4, 5, 6
 
 EXPORTS = ("dmpq_last_error", "dmpq_version", "dmpq_workspace_bytes", "dmpq_gamma_sums",
            "dmpq_gate_and_route", "dmpq_hadamard_quant_int8", "dmpq_hadamard_quant_nvfp4",
@@ -259,9 +259,10 @@ def _ws(ws):
     return (None, 0) if ws is None else (_ptr(ws), ws.numel())
 
 
-def qgemm_int8_ex(qa, sa, qw, sw, y, epilogue: int, ws=None, out_dtype: int = OUT_BF16,
+def qgemm_int8_ex(qa, sa, qw, sw, y, epilogue: int = 0, ws=None, out_dtype: int = OUT_BF16,
                   stream=None) -> None:
-    """qgemm_int8 with a producer epilogue (EPI_GELU, EPI_NVFP4_AMAX)."""
+    """qgemm_int8 with a producer epilogue (EPI_GELU, EPI_NVFP4_AMAX); with an
+    OP_GEMM workspace the last partial wave of tiles is split along K."""
     M, K = qa.shape
     N = qw.shape[0]
     _check(lib().dmpq_qgemm_int8_ex(_stream(stream), _ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), M, N,
@@ -269,9 +270,10 @@ def qgemm_int8_ex(qa, sa, qw, sw, y, epilogue: int, ws=None, out_dtype: int = OU
            "dmpq_qgemm_int8_ex")
 
 
-def qgemm_nvfp4_ex(ca, sa, ga, cw, sw, gw, y, epilogue: int, ws=None, out_dtype: int = OUT_BF16,
+def qgemm_nvfp4_ex(ca, sa, ga, cw, sw, gw, y, epilogue: int = 0, ws=None, out_dtype: int = OUT_BF16,
                    stream=None) -> None:
-    """qgemm_nvfp4 (BF16-dequant variant) with a producer epilogue."""
+    """qgemm_nvfp4 (BF16-dequant variant) with a producer epilogue and the
+    optional tail split."""
     M, K = ca.shape[0], 2 * ca.shape[1]
     N = cw.shape[0]
     _check(lib().dmpq_qgemm_nvfp4_ex(_stream(stream), _ptr(ca), _ptr(sa), _ptr(ga), _ptr(cw),
@@ -280,8 +282,9 @@ def qgemm_nvfp4_ex(ca, sa, ga, cw, sw, gw, y, epilogue: int, ws=None, out_dtype:
            "dmpq_qgemm_nvfp4_ex")
 
 
-def gemm_bf16_ex(x, w, y, epilogue: int, ws=None, out_dtype: int = OUT_BF16, stream=None) -> None:
-    """gemm_bf16 with a producer epilogue."""
+def gemm_bf16_ex(x, w, y, epilogue: int = 0, ws=None, out_dtype: int = OUT_BF16,
+                 stream=None) -> None:
+    """gemm_bf16 with a producer epilogue and the optional tail split."""
     M, K = x.shape
     N = w.shape[0]
     _check(lib().dmpq_gemm_bf16_ex(_stream(stream), _ptr(x), _ptr(w), M, N, K, out_dtype, _ptr(y),

@@ -67,25 +67,41 @@ dmpq_status check_ws(const char *fn, const void *ws, size_t bytes) {
     return DMPQ_OK;
 }
 
-// Epilogue of a *_ex GEMM: known bits, bf16 output, and for the fused amax
-// N % 16 == 0 and a workspace that holds one float per 256 x 256 tile.
-dmpq_status check_epilogue(const char *fn, int64_t M, int64_t N, int out_dtype, int epilogue,
-                           const void *ws, size_t ws_bytes) {
+// Workspace of a *_ex GEMM: the fused-amax maxima (one float per 256 x 256
+// tile, rounded up to 256 bytes), then the split area.
+size_t gemm_slot_bytes(int64_t M, int64_t N) {
+    return ((size_t)gemm_tiles(M, N) * sizeof(float) + 255) / 256 * 256;
+}
+
+// Epilogue of a *_ex GEMM: known bits, bf16 output for a nonzero epilogue,
+// and for the fused amax N % 16 == 0 and a workspace that holds one float per
+// tile.  `outs`: the output types the GEMM itself accepts.
+dmpq_status check_epilogue(const char *fn, int64_t M, int64_t N, int out_dtype, int outs,
+                           int epilogue, const void *ws, size_t ws_bytes) {
     if (epilogue & ~(DMPQ_EPI_GELU | DMPQ_EPI_NVFP4_AMAX))
         return fail(DMPQ_ERR_INVALID_ARG, "%s: unknown epilogue %d", fn, epilogue);
-    if (out_dtype != DMPQ_OUT_BF16)
+    if (out_dtype < 0 || out_dtype > 2 || !((outs >> out_dtype) & 1))
+        return fail(DMPQ_ERR_INVALID_ARG, "%s: unknown out_dtype %d", fn, out_dtype);
+    if (epilogue != 0 && out_dtype != DMPQ_OUT_BF16)
         return fail(DMPQ_ERR_UNSUPPORTED, "%s: epilogues need DMPQ_OUT_BF16 (got %d)", fn, out_dtype);
+    if (ws && !aligned16(ws)) return fail(DMPQ_ERR_MISALIGNED, "%s: workspace is not 16-byte aligned", fn);
     if (epilogue & DMPQ_EPI_NVFP4_AMAX) {
         if (N % 16 != 0)
             return fail(DMPQ_ERR_BAD_SHAPE, "%s: the fused amax needs N %% 16 == 0 (N = %lld)", fn,
                         (long long)N);
         const size_t need = (size_t)gemm_tiles(M, N) * sizeof(float);
         if (!ws) return fail(DMPQ_ERR_WORKSPACE, "%s: workspace is NULL", fn);
-        if (!aligned16(ws)) return fail(DMPQ_ERR_MISALIGNED, "%s: workspace is not 16-byte aligned", fn);
         if (ws_bytes < need)
             return fail(DMPQ_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, ws_bytes, need);
     }
     return DMPQ_OK;
+}
+
+// The split area of a *_ex GEMM's workspace, or NULL when it is too small.
+uint32_t *split_area(void *ws, size_t ws_bytes, int64_t M, int64_t N) {
+    const size_t off = gemm_slot_bytes(M, N);
+    if (!ws || ws_bytes < off + kSplitAreaBytes) return nullptr;
+    return reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(ws) + off);
 }
 
 double rel_ratio(double num, double den) {
@@ -108,6 +124,9 @@ size_t dmpq_workspace_bytes(int op, int64_t M, int64_t K) {
             const size_t tiles = (size_t)gemm_tiles(M, K);
             return tiles * sizeof(float) > kWsBytes ? tiles * sizeof(float) : kWsBytes;
         }
+        case DMPQ_OP_GEMM:
+            if (M < 0 || K < 0) return 0;
+            return gemm_slot_bytes(M, K) + kSplitAreaBytes;
         case DMPQ_OP_GAMMA:
         case DMPQ_OP_QUANT_NVFP4:
         case DMPQ_OP_TDC:
@@ -208,23 +227,22 @@ dmpq_status dmpq_qgemm_int8(hipStream_t stream, const int8_t *qa, const float *s
     REQUIRE_PTR_N(y, M * N);
     if (out_dtype != DMPQ_OUT_F32 && out_dtype != DMPQ_OUT_BF16 && out_dtype != DMPQ_OUT_I32)
         return fail(DMPQ_ERR_INVALID_ARG, "%s: unknown out_dtype %d", __func__, out_dtype);
-    return hip_status(launch_gemm_int8(stream, qa, sa, qw, sw, M, N, K, out_dtype, y, 0, nullptr),
+    return hip_status(launch_gemm_int8(stream, qa, sa, qw, sw, M, N, K, out_dtype, y, 0, nullptr, nullptr),
                       __func__);
 }
 
 dmpq_status dmpq_qgemm_int8_ex(hipStream_t stream, const int8_t *qa, const float *sa,
                                const int8_t *qw, const float *sw, int64_t M, int64_t N, int64_t K,
                                int out_dtype, void *y, int epilogue, void *ws, size_t ws_bytes) {
-    if (epilogue == 0) return dmpq_qgemm_int8(stream, qa, sa, qw, sw, M, N, K, out_dtype, y);
     if (dmpq_status s = check_gemm(__func__, M, N, K)) return s;
     REQUIRE_PTR_N(qa, M);
     REQUIRE_PTR_N(sa, M);
     REQUIRE_PTR_N(qw, N);
     REQUIRE_PTR_N(sw, N);
     REQUIRE_PTR_N(y, M * N);
-    if (dmpq_status s = check_epilogue(__func__, M, N, out_dtype, epilogue, ws, ws_bytes)) return s;
+    if (dmpq_status s = check_epilogue(__func__, M, N, out_dtype, 7, epilogue, ws, ws_bytes)) return s;
     return hip_status(launch_gemm_int8(stream, qa, sa, qw, sw, M, N, K, out_dtype, y, epilogue,
-                                       static_cast<float *>(ws)),
+                                       static_cast<float *>(ws), split_area(ws, ws_bytes, M, N)),
                       __func__);
 }
 
@@ -247,7 +265,7 @@ dmpq_status dmpq_qgemm_nvfp4(hipStream_t stream, const uint8_t *ca, const uint8_
     if (variant != DMPQ_FP4_BF16_DEQUANT && variant != DMPQ_FP4_SCALED_MFMA)
         return fail(DMPQ_ERR_INVALID_ARG, "%s: unknown variant %d", __func__, variant);
     return hip_status(launch_gemm_nvfp4(stream, ca, sa, d_ga, cw, sw, d_gw, M, N, K, out_dtype,
-                                        y, variant, 0, nullptr),
+                                        y, variant, 0, nullptr, nullptr),
                       __func__);
 }
 
@@ -255,9 +273,6 @@ dmpq_status dmpq_qgemm_nvfp4_ex(hipStream_t stream, const uint8_t *ca, const uin
                                 const float *d_ga, const uint8_t *cw, const uint8_t *sw,
                                 const float *d_gw, int64_t M, int64_t N, int64_t K,
                                 int out_dtype, void *y, int epilogue, void *ws, size_t ws_bytes) {
-    if (epilogue == 0)
-        return dmpq_qgemm_nvfp4(stream, ca, sa, d_ga, cw, sw, d_gw, M, N, K, out_dtype, y,
-                                DMPQ_FP4_BF16_DEQUANT);
     if (dmpq_status s = check_gemm(__func__, M, N, K)) return s;
     REQUIRE_PTR_N(ca, M);
     REQUIRE_PTR_N(sa, M);
@@ -266,9 +281,10 @@ dmpq_status dmpq_qgemm_nvfp4_ex(hipStream_t stream, const uint8_t *ca, const uin
     REQUIRE_PTR_N(sw, N);
     REQUIRE_PTR_N(d_gw, M * N);
     REQUIRE_PTR_N(y, M * N);
-    if (dmpq_status s = check_epilogue(__func__, M, N, out_dtype, epilogue, ws, ws_bytes)) return s;
+    if (dmpq_status s = check_epilogue(__func__, M, N, out_dtype, 3, epilogue, ws, ws_bytes)) return s;
     return hip_status(launch_gemm_nvfp4(stream, ca, sa, d_ga, cw, sw, d_gw, M, N, K, out_dtype, y,
-                                        DMPQ_FP4_BF16_DEQUANT, epilogue, static_cast<float *>(ws)),
+                                        DMPQ_FP4_BF16_DEQUANT, epilogue, static_cast<float *>(ws),
+                                        split_area(ws, ws_bytes, M, N)),
                       __func__);
 }
 
@@ -401,20 +417,20 @@ dmpq_status dmpq_gemm_bf16(hipStream_t stream, const uint16_t *x, const uint16_t
     REQUIRE_PTR_N(y, M * N);
     if (out_dtype != DMPQ_OUT_F32 && out_dtype != DMPQ_OUT_BF16)
         return fail(DMPQ_ERR_INVALID_ARG, "%s: out_dtype %d is not F32 or BF16", __func__, out_dtype);
-    return hip_status(launch_gemm_bf16(stream, x, w, M, N, K, out_dtype, y, 0, nullptr), __func__);
+    return hip_status(launch_gemm_bf16(stream, x, w, M, N, K, out_dtype, y, 0, nullptr, nullptr),
+                      __func__);
 }
 
 dmpq_status dmpq_gemm_bf16_ex(hipStream_t stream, const uint16_t *x, const uint16_t *w, int64_t M,
                               int64_t N, int64_t K, int out_dtype, void *y, int epilogue, void *ws,
                               size_t ws_bytes) {
-    if (epilogue == 0) return dmpq_gemm_bf16(stream, x, w, M, N, K, out_dtype, y);
     if (dmpq_status s = check_gemm(__func__, M, N, K)) return s;
     REQUIRE_PTR_N(x, M);
     REQUIRE_PTR_N(w, N);
     REQUIRE_PTR_N(y, M * N);
-    if (dmpq_status s = check_epilogue(__func__, M, N, out_dtype, epilogue, ws, ws_bytes)) return s;
+    if (dmpq_status s = check_epilogue(__func__, M, N, out_dtype, 3, epilogue, ws, ws_bytes)) return s;
     return hip_status(launch_gemm_bf16(stream, x, w, M, N, K, out_dtype, y, epilogue,
-                                       static_cast<float *>(ws)),
+                                       static_cast<float *>(ws), split_area(ws, ws_bytes, M, N)),
                       __func__);
 }
 

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "device.hpp"
+#include "internal.hpp"
 
 namespace dmpq {
 
@@ -20,17 +21,84 @@ struct TileCoord {
     unsigned m, n;
 };
 
-__device__ __forceinline__ TileCoord tile_of(unsigned bid, unsigned nwg, unsigned tiles_m,
-                                             unsigned tiles_n, unsigned group_m) {
+__device__ __forceinline__ unsigned xcd_order(unsigned bid, unsigned nwg) {
     const unsigned full = nwg & ~7u;
-    unsigned pid = bid;
-    if (bid < full) pid = (bid & 7u) * (full >> 3) + (bid >> 3);
+    return bid < full ? (bid & 7u) * (full >> 3) + (bid >> 3) : bid;
+}
+
+__device__ __forceinline__ TileCoord tile_at(unsigned pid, unsigned tiles_m, unsigned tiles_n,
+                                             unsigned group_m) {
     const unsigned per_group = group_m * tiles_n;
     const unsigned g = pid / per_group;
     const unsigned first_m = g * group_m;
     const unsigned rows = min(tiles_m - first_m, group_m);
     const unsigned in_group = pid - g * per_group;
     return TileCoord{first_m + in_group % rows, in_group / rows};
+}
+
+__device__ __forceinline__ TileCoord tile_of(unsigned bid, unsigned nwg, unsigned tiles_m,
+                                             unsigned tiles_n, unsigned group_m) {
+    return tile_at(xcd_order(bid, nwg), tiles_m, tiles_n, group_m);
+}
+
+// A split workgroup of a SplitPlan launch: workgroup j runs the K stages
+// [s * nk / splits, (s + 1) * nk / splits) of tail tile full + j / splits,
+// s = j % splits.
+struct SplitUnit {
+    TileCoord tc;
+    int kt0, kt1;
+};
+
+__device__ __forceinline__ SplitUnit split_unit(const SplitPlan &sp, unsigned tiles_m, unsigned tiles_n,
+                                                unsigned group_m) {
+    const unsigned j = blockIdx.x;
+    const unsigned s = j % sp.splits;
+    SplitUnit u;
+    u.tc = tile_at(sp.full + j / sp.splits, tiles_m, tiles_n, group_m);
+    u.kt0 = (int)((int64_t)s * sp.nk / sp.splits);
+    u.kt1 = (int)((int64_t)(s + 1) * sp.nk / sp.splits);
+    return u;
+}
+
+// Host: the split plan of a launch of `tiles` tiles with nk K stages each.
+// The tail is split into as many parts as fit in one wave of kMaxSplitUnits
+// workgroups (at most one stage each; 2, 3, 4 or 8 parts); a tail that
+// cannot be split at least in two is not split.
+inline SplitPlan plan_split(int64_t tiles, int nk, bool enable) {
+    SplitPlan p{(unsigned)tiles, 0u, 1u, nk};
+    const int64_t tail = tiles % 256;
+    if (!enable || tail == 0) return p;
+    int64_t S = (int64_t)kMaxSplitUnits / tail;
+    if (S > nk) S = nk;
+    S = S >= 8 ? 8 : S >= 4 ? 4 : S;  // 2, 3, 4 or 8: the fixup is compiled per count
+    if (S < 2) return p;
+    p.full = (unsigned)(tiles - tail);
+    p.tail = (unsigned)tail;
+    p.splits = (unsigned)S;
+    return p;
+}
+
+// Raw accumulators of one split workgroup: 256 words per thread, as 64
+// 16-byte pieces (register group g of MFMA block (i, j) is piece 4(4i+j)+g);
+// for each piece the workgroup writes 4 KB contiguously.
+template <class AccV>
+__device__ __forceinline__ void store_split_partial(const AccV (&acc)[4][4], uint32_t *part, int tid) {
+    typedef decltype(acc[0][0][0] + 0) T;
+    uint4 *p4 = reinterpret_cast<uint4 *>(part);
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                // copy the elements out first: a bit cast of a vector-element
+                // lvalue reads from the vector's base, i.e. element 0
+                const T v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
+                const T v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+                p4[((i * 4 + j) * 4 + g) * 256 + tid] =
+                    make_uint4(__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1),
+                               __builtin_bit_cast(uint32_t, v2), __builtin_bit_cast(uint32_t, v3));
+            }
 }
 
 }  // namespace dmpq
@@ -60,7 +128,7 @@ struct EpiBand {
 // result is rounded again.  kEpiAmax (bf16 output, N % 16 == 0): the maximum
 // of |FWHT16(row block)| over the stored bf16 values of the tile -- the next
 // layer's NVFP4 tensor-amax term, with the same fp32 butterfly order as the
-// quantizer -- is written to partial[blockIdx.x].
+// quantizer -- is written to the tile's entry of the maxima.
 enum { kEpiGelu = 1, kEpiAmax = 2 };
 
 // GELU(v) = v Phi(v) = (v / 2) erfc(-v / sqrt 2) in fp32.  erfc comes from
@@ -173,13 +241,14 @@ __device__ __forceinline__ float epi_band_to_global(const uint8_t *band, void *y
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 // The fused amax of a 256 x 256 tile: every wave's maximum, combined through
-// LDS, written by one lane.  Called by all four waves.
-__device__ __forceinline__ void epi_tile_amax(float m, int wave, int lane, float *partial) {
+// LDS, written by one lane to *slot (the tile's own entry).  Called by all
+// four waves.
+__device__ __forceinline__ void epi_tile_amax(float m, int wave, int lane, float *slot) {
     __shared__ float red[4];
     m = wave_max(m);
     if (lane == 0) red[wave] = m;
     __syncthreads();
-    if (wave == 0 && lane == 0) partial[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    if (wave == 0 && lane == 0) *slot = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
 // Output scaling of fp32 accumulators: y = (acc * gA) * gW.
@@ -198,7 +267,7 @@ struct EpiScaleF32 {
 template <int OUT, int EPI, class AccV, class Scale>
 __device__ __forceinline__ void band_epilogue(AccV (&acc)[4][4], Scale &sc, uint8_t *lds, int64_t M,
                                               int64_t N, int64_t m0, int64_t n0, int wave, int wm,
-                                              int wn, int lane, void *y, float *partial) {
+                                              int wn, int lane, void *y, float *slot) {
     constexpr int ES = OUT == 1 ? 2 : 4;
     constexpr bool AMAX = (EPI & kEpiAmax) != 0;
     static_assert(!AMAX || OUT == 1, "the fused amax needs bf16 output");
@@ -231,17 +300,88 @@ __device__ __forceinline__ void band_epilogue(AccV (&acc)[4][4], Scale &sc, uint
         amax = fmaxf(amax, epi_band_to_global<ES, EPI>(band, y, M, N, m0 + wm * 128 + h * 64,
                                                         n0 + wn * 128, lane, vec));
     }
-    if constexpr (AMAX) epi_tile_amax(amax, wave, lane, partial);
+    if constexpr (AMAX) epi_tile_amax(amax, wave, lane, slot);
 }
 
-// fp32 accumulators -> y = (acc * gA) * gW (fp32 or bf16).
+// fp32 accumulators -> y = (acc * gA) * gW (fp32 or bf16).  slot: the tile's
+// entry of the fused-amax maxima (used with kEpiAmax only).
 template <int OUT, int EPI = 0>
 __device__ __forceinline__ void f32_band_epilogue(v16f (&acc)[4][4], uint8_t *lds, float gA,
                                                   float gW, int64_t M, int64_t N, int64_t m0,
                                                   int64_t n0, int wave, int wm, int wn, int lane,
-                                                  void *y, float *partial = nullptr) {
+                                                  void *y, float *slot = nullptr) {
     EpiScaleF32 sc{gA, gW};
-    band_epilogue<OUT, EPI>(acc, sc, lds, M, N, m0, n0, wave, wm, wn, lane, y, partial);
+    band_epilogue<OUT, EPI>(acc, sc, lds, M, N, m0, n0, wave, wm, wn, lane, y, slot);
+}
+
+// The epilogue of one 128 x 128 quadrant of a split tile, run by a
+// one-wave workgroup straight from the tile's partials (no accumulator
+// array: a register-resident tile plus the loads in flight would spill).
+// For each MFMA block (i, j), the lane's four 16-byte pieces of all S
+// splits are loaded together, added in split order as T (int32: exact;
+// fp32: fixed order), scaled by sc and written to the band; the band then
+// goes out as in band_epilogue.  part: the tile's first split; wave:
+// the quadrant (the wave of the whole-tile kernels whose lanes' layout the
+// partials follow).  The fused amax goes to *slot by an atomic max (the
+// split kernel zeroed it; the maximum does not depend on the order).
+template <int OUT, int EPI, class T, int S, class Scale>
+__device__ __forceinline__ void split_fixup_epilogue(const uint32_t *part, Scale &sc, uint8_t *lds,
+                                                     int64_t M, int64_t N, int64_t m0, int64_t n0,
+                                                     int wave, int lane, void *y, float *slot) {
+    constexpr int ES = OUT == 1 ? 2 : 4;
+    using Band = EpiBand<ES>;
+    constexpr size_t kPieces = kSplitWords / 4;
+    const uint4 *p4 = reinterpret_cast<const uint4 *>(part);
+    const int wm = wave >> 1, wn = wave & 1, tid = wave * 64 + lane;
+    const int lm = lane & 31, lh = lane >> 5;
+    uint8_t *band = lds;
+    const bool vec = ((N * ES) & 15) == 0;
+    float amax = 0.0f;
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ii++) {
+            const int i = 2 * h + ii;
+            sc.row(m0 + wm * 128 + i * 32 + lm);
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                uint4 v[S][4];
+#pragma unroll
+                for (int s = 0; s < S; s++)
+#pragma unroll
+                    for (int g = 0; g < 4; g++) v[s][g] = p4[s * kPieces + ((i * 4 + j) * 4 + g) * 256 + tid];
+#pragma unroll
+                for (int g = 0; g < 4; g++) {
+                    T x[4] = {__builtin_bit_cast(T, v[0][g].x), __builtin_bit_cast(T, v[0][g].y),
+                              __builtin_bit_cast(T, v[0][g].z), __builtin_bit_cast(T, v[0][g].w)};
+#pragma unroll
+                    for (int s = 1; s < S; s++) {
+                        x[0] += __builtin_bit_cast(T, v[s][g].x);
+                        x[1] += __builtin_bit_cast(T, v[s][g].y);
+                        x[2] += __builtin_bit_cast(T, v[s][g].z);
+                        x[3] += __builtin_bit_cast(T, v[s][g].w);
+                    }
+                    float v4[4];
+#pragma unroll
+                    for (int e = 0; e < 4; e++) v4[e] = sc((float)x[e], j, g, e);
+                    uint8_t *dst = band + (ii * 32 + lm) * Band::STRIDE + (j * 32 + 8 * g + 4 * lh) * ES;
+                    if constexpr (OUT == 0)
+                        *reinterpret_cast<float4 *>(dst) = make_float4(v4[0], v4[1], v4[2], v4[3]);
+                    else
+                        *reinterpret_cast<uint2 *>(dst) = make_uint2(cvt_pk_bf16(v4[0], v4[1]), cvt_pk_bf16(v4[2], v4[3]));
+                }
+                // bound the loads in flight (one block's, two for few splits)
+                if (S > 4 || (j & 1)) __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        amax = fmaxf(amax, epi_band_to_global<ES, EPI>(band, y, M, N, m0 + wm * 128 + h * 64,
+                                                       n0 + wn * 128, lane, vec));
+    }
+    if constexpr ((EPI & kEpiAmax) != 0) {
+        // non-negative floats order as their bit patterns
+        amax = wave_max(amax);
+        if (lane == 0) atomicMax(reinterpret_cast<unsigned *>(slot), __float_as_uint(amax));
+    }
 }
 
 }  // namespace dmpq

@@ -196,15 +196,17 @@ __device__ __forceinline__ int dma_valid(int64_t Kb, int kt) {
     return (int)(left < gdma::BK ? left : gdma::BK);
 }
 
-// The whole main loop of one workgroup tile: acc = A[m0.., :] W[n0.., :]^T,
-// with operand rows of Kb bytes (Kb % 32 == 0; Kb % 128 == 0 unless TAIL).
-// On return every DMA has landed and every wave has left the stage buffers,
-// so `lds` is free for the epilogue.
+// The whole main loop of one workgroup tile over a K range: acc = A[m0.., k]
+// W[n0.., k]^T for the Kb bytes of every row that start at A and W (the
+// range's first byte; rows are ld bytes apart).  Kb % 32 == 0, and
+// Kb % 128 == 0 unless TAIL.  On return every DMA has landed and every wave
+// has left the stage buffers, so `lds` is free for the epilogue.
 template <class Op, bool TAIL>
 __device__ __forceinline__ void dma_gemm_mainloop(const uint8_t *__restrict__ A,
                                                   const uint8_t *__restrict__ W, int64_t M,
-                                                  int64_t N, int64_t Kb, int64_t m0, int64_t n0,
-                                                  uint8_t *lds, typename Op::acc_t (&acc)[4][4]) {
+                                                  int64_t N, int64_t ld, int64_t Kb, int64_t m0,
+                                                  int64_t n0, uint8_t *lds,
+                                                  typename Op::acc_t (&acc)[4][4]) {
     using namespace gdma;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -229,8 +231,8 @@ __device__ __forceinline__ void dma_gemm_mainloop(const uint8_t *__restrict__ A,
         const int64_t gm = m0 + row < M ? m0 + row : M - 1;
         const int64_t gn = n0 + row < N ? n0 + row : N - 1;
         L.kc[q] = kc;
-        L.srcA[q] = A + gm * Kb + kc * 16;
-        L.srcW[q] = W + gn * Kb + kc * 16;
+        L.srcA[q] = A + gm * ld + kc * 16;
+        L.srcW[q] = W + gn * ld + kc * 16;
     }
     L.offA = (wm * 128 + (lane & 31)) * BK;
     L.offW = TILE + (wn * 128 + (lane & 31)) * BK;

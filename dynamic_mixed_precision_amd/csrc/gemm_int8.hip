@@ -40,7 +40,8 @@ constexpr unsigned GROUP_M = 8;
 // (float(acc) * sA[row]) * sW[col] (bit-exact in fp32), staged per wave
 // through LDS in two 64-row bands and stored row-contiguous, with GELU and
 // the fused amax per EPI; OUT 2: the raw int32 accumulators (test mode).  The
-// stage buffers must be free (both main loops end with a barrier).
+// stage buffers must be free (both main loops end with a barrier).  pid:
+// the tile's slot among the fused-amax maxima.
 #define DMPQ_I8_EPILOGUE()                                                                        \
     {                                                                                             \
         constexpr int ES = OUT == 1 ? 2 : 4;                                                      \
@@ -87,7 +88,7 @@ constexpr unsigned GROUP_M = 8;
                                                         n0 + wn * 128, lane, vec);                \
             if constexpr ((EPI & kEpiAmax) != 0) amax = fmaxf(amax, m);                           \
         }                                                                                         \
-        if constexpr ((EPI & kEpiAmax) != 0) epi_tile_amax(amax, wave, lane, partial);            \
+        if constexpr ((EPI & kEpiAmax) != 0) epi_tile_amax(amax, wave, lane, partial + pid);      \
     }
 
 template <int OUT, int EPI>
@@ -100,7 +101,8 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const TileCoord tc = tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, GROUP_M);
+    const unsigned pid = xcd_order(blockIdx.x, gridDim.x);
+    const TileCoord tc = tile_at(pid, tiles_m, tiles_n, GROUP_M);
     const int64_t m0 = (int64_t)tc.m * BM, n0 = (int64_t)tc.n * BN;
 
     v16i acc[4][4];
@@ -197,60 +199,147 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_dma_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const TileCoord tc = tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, GROUP_M);
+    const unsigned pid = xcd_order(blockIdx.x, gridDim.x);
+    const TileCoord tc = tile_at(pid, tiles_m, tiles_n, GROUP_M);
     const int64_t m0 = (int64_t)tc.m * BM, n0 = (int64_t)tc.n * BN;
 
     v16i acc[4][4];
     dma_gemm_mainloop<OpI8, false>(reinterpret_cast<const uint8_t *>(A),
-                                   reinterpret_cast<const uint8_t *>(W), M, N, K, m0, n0,
+                                   reinterpret_cast<const uint8_t *>(W), M, N, K, K, m0, n0,
                                    reinterpret_cast<uint8_t *>(lds), acc);
-
     DMPQ_I8_EPILOGUE()
 }
 
+// The split workgroups of a SplitPlan launch: the main loop over this
+// workgroup's K stages, then the raw int32 accumulators to the split area.
+// The first split of a tile also zeroes the tile's fused-amax slot (partial
+// may be NULL), which the fixup then raises by atomic max.
+__global__ __launch_bounds__(256, 1) void gemm_i8_split_kernel(
+    const int8_t *__restrict__ A, const int8_t *__restrict__ W, int64_t M, int64_t N, int64_t K,
+    unsigned tiles_m, unsigned tiles_n, SplitPlan sp, uint32_t *__restrict__ spart,
+    float *__restrict__ partial) {
+    using namespace gdma;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds8[];
+    const SplitUnit u = split_unit(sp, tiles_m, tiles_n, GROUP_M);
+    if (partial && u.kt0 == 0 && threadIdx.x == 0) partial[sp.full + blockIdx.x / sp.splits] = 0.0f;
+    const int64_t k0 = (int64_t)u.kt0 * BK;
+    v16i acc[4][4];
+    dma_gemm_mainloop<OpI8, false>(reinterpret_cast<const uint8_t *>(A) + k0,
+                                   reinterpret_cast<const uint8_t *>(W) + k0, M, N, K,
+                                   (int64_t)u.kt1 * BK - k0, (int64_t)u.tc.m * BM, (int64_t)u.tc.n * BN,
+                                   lds8, acc);
+    store_split_partial(acc, spart + (size_t)blockIdx.x * kSplitWords, threadIdx.x);
+}
+
+// Output scaling of the INT8 fixup: y = (float(acc) * sA[row]) * sW[col],
+// bit-exact in fp32.  c0: first output column of the lane's (j, g) groups.
+struct EpiScaleI8 {
+    const float *sa, *sw;
+    int64_t M, N, c0;
+    float sar;
+    __device__ __forceinline__ void row(int64_t r) { sar = r < M ? sa[r] : 0.0f; }
+    __device__ __forceinline__ float operator()(float a, int j, int g, int e) const {
+        const int64_t col = c0 + j * 32 + 8 * g + e;
+        return (a * sar) * (col < N ? sw[col] : 0.0f);
+    }
+};
+
+// The tail tiles of a split launch: the int32 partials of each tile's split
+// workgroups added in split order (exact), then the same scaled epilogue.
+// One workgroup of one wave per 128 x 128 quadrant (4 per tail tile).
+template <int OUT, int EPI, int S>
+__global__ __launch_bounds__(64) void gemm_i8_fixup_kernel(
+    const float *__restrict__ sa, const float *__restrict__ sw, int64_t M, int64_t N,
+    void *__restrict__ y, unsigned tiles_m, unsigned tiles_n, float *__restrict__ partial,
+    SplitPlan sp, const uint32_t *__restrict__ spart) {
+    using namespace gdma;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds8[];
+    const int lane = threadIdx.x, wave = blockIdx.x & 3;
+    const unsigned t = blockIdx.x >> 2, pid = sp.full + t;
+    const TileCoord tc = tile_at(pid, tiles_m, tiles_n, GROUP_M);
+    const int64_t m0 = (int64_t)tc.m * BM, n0 = (int64_t)tc.n * BN;
+    EpiScaleI8 sc{sa, sw, M, N, n0 + (wave & 1) * 128 + 4 * (lane >> 5), 0.0f};
+    split_fixup_epilogue<OUT, EPI, int, S>(spart + (size_t)t * S * kSplitWords, sc, lds8, M, N, m0, n0, wave,
+                                           lane, y, (EPI & kEpiAmax) ? partial + pid : nullptr);
+}
+
+template <class KernelFn>
+static hipError_t allow_lds(KernelFn fn, size_t bytes) {
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+// spart: the split area (kSplitAreaBytes), or NULL for no split.
 template <int OUT, int EPI>
 static hipError_t launch_i8_paths(hipStream_t s, const int8_t *qa, const float *sa, const int8_t *qw,
                                   const float *sw, int64_t M, int64_t N, int64_t K, void *y,
-                                  float *partial) {
+                                  float *partial, uint32_t *spart) {
+    constexpr bool CAN_SPLIT = OUT != 2;
     // Kernels need more dynamic LDS than the default limit: opt in once.
     static const hipError_t attr = [] {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_i8_kernel<OUT, EPI>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)(2 * i8gemm::STAGE));
-        if (e == hipSuccess)
-            e = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_i8_dma_kernel<OUT, EPI>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)gdma::LDS_BYTES);
+        hipError_t e = allow_lds(gemm_i8_kernel<OUT, EPI>, 2 * i8gemm::STAGE);
+        if (e == hipSuccess) e = allow_lds(gemm_i8_dma_kernel<OUT, EPI>, gdma::LDS_BYTES);
+        if (e == hipSuccess) e = allow_lds(gemm_i8_split_kernel, gdma::LDS_BYTES);
+
         return e;
     }();
     if (attr != hipSuccess) return attr;
     const int64_t tm = (M + 255) / 256, tn = (N + 255) / 256;
-    const dim3 grid((unsigned)(tm * tn)), block(256);
+    const dim3 block(256);
     const unsigned utm = (unsigned)tm, utn = (unsigned)tn;
-    if (K % gdma::BK == 0)
-        hipLaunchKernelGGL((gemm_i8_dma_kernel<OUT, EPI>), grid, block, gdma::LDS_BYTES, s, qa, sa, qw, sw, M,
-                           N, K, y, utm, utn, partial);
-    else
-        hipLaunchKernelGGL((gemm_i8_kernel<OUT, EPI>), grid, block, 2 * i8gemm::STAGE, s, qa, sa, qw, sw, M,
-                           N, K, y, utm, utn, partial);
+    if (K % gdma::BK != 0) {
+        hipLaunchKernelGGL((gemm_i8_kernel<OUT, EPI>), dim3((unsigned)(tm * tn)), block, 2 * i8gemm::STAGE, s, qa,
+                           sa, qw, sw, M, N, K, y, utm, utn, partial);
+        return hipGetLastError();
+    }
+    const SplitPlan sp = plan_split(tm * tn, (int)(K / gdma::BK), CAN_SPLIT && spart != nullptr && K >= kSplitMinKInt8);
+    if (sp.full > 0) {
+        hipLaunchKernelGGL((gemm_i8_dma_kernel<OUT, EPI>), dim3(sp.full), block, gdma::LDS_BYTES, s, qa, sa, qw,
+                           sw, M, N, K, y, utm, utn, partial);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if constexpr (CAN_SPLIT) {
+        if (sp.splits > 1) {
+            hipLaunchKernelGGL(gemm_i8_split_kernel, dim3(sp.tail * sp.splits), block, gdma::LDS_BYTES, s, qa, qw,
+                               M, N, K, utm, utn, sp, spart, (EPI & kEpiAmax) ? partial : nullptr);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            const dim3 fg(4 * sp.tail), fb(64);
+            const size_t fl = EpiBand<OUT == 1 ? 2 : 4>::BYTES;
+            const uint32_t *cp = spart;
+#define DMPQ_I8_FIX(S_)                                                                          \
+    case S_:                                                                                     \
+        hipLaunchKernelGGL((gemm_i8_fixup_kernel<OUT, EPI, S_>), fg, fb, fl, s, sa, sw, M, N, y, utm, utn, \
+                           partial, sp, cp);                                                     \
+        break;
+            switch (sp.splits) {
+                DMPQ_I8_FIX(2) DMPQ_I8_FIX(3) DMPQ_I8_FIX(4) DMPQ_I8_FIX(8)
+                default: return hipErrorInvalidValue;
+            }
+#undef DMPQ_I8_FIX
+        }
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_gemm_int8(hipStream_t s, const int8_t *qa, const float *sa, const int8_t *qw,
                             const float *sw, int64_t M, int64_t N, int64_t K, int out_dtype,
-                            void *y, int epi, float *partial) {
+                            void *y, int epi, float *partial, uint32_t *spart) {
     if (M == 0 || N == 0) return hipSuccess;
     if (epi == 0) {
         switch (out_dtype) {
-            case 0: return launch_i8_paths<0, 0>(s, qa, sa, qw, sw, M, N, K, y, partial);
-            case 1: return launch_i8_paths<1, 0>(s, qa, sa, qw, sw, M, N, K, y, partial);
-            case 2: return launch_i8_paths<2, 0>(s, qa, sa, qw, sw, M, N, K, y, partial);
+            case 0: return launch_i8_paths<0, 0>(s, qa, sa, qw, sw, M, N, K, y, partial, spart);
+            case 1: return launch_i8_paths<1, 0>(s, qa, sa, qw, sw, M, N, K, y, partial, spart);
+            case 2: return launch_i8_paths<2, 0>(s, qa, sa, qw, sw, M, N, K, y, partial, spart);
         }
         return hipErrorInvalidValue;
     }
     if (out_dtype != 1) return hipErrorInvalidValue;
     switch (epi) {
-        case 1: return launch_i8_paths<1, 1>(s, qa, sa, qw, sw, M, N, K, y, partial);
-        case 2: return launch_i8_paths<1, 2>(s, qa, sa, qw, sw, M, N, K, y, partial);
-        case 3: return launch_i8_paths<1, 3>(s, qa, sa, qw, sw, M, N, K, y, partial);
+        case 1: return launch_i8_paths<1, 1>(s, qa, sa, qw, sw, M, N, K, y, partial, spart);
+        case 2: return launch_i8_paths<1, 2>(s, qa, sa, qw, sw, M, N, K, y, partial, spart);
+        case 3: return launch_i8_paths<1, 3>(s, qa, sa, qw, sw, M, N, K, y, partial, spart);
     }
     return hipErrorInvalidValue;
 }

@@ -83,13 +83,14 @@ __device__ __forceinline__ void dequant32_fast(const uint4 c, uint32_t s01, uint
 
 // Epilogue of the NVFP4 kernels: y = (acc * gA) * gW through the per-wave LDS
 // bands (callers end their main loop with a barrier, so the stage buffers are
-// free).
+// free); pid: the tile's slot among the fused-amax maxima.
 template <int OUT, int EPI>
 __device__ __forceinline__ void fp4_epilogue(v16f (&acc)[4][4], uint8_t *lds, const float *ga,
                                              const float *gw, int64_t M, int64_t N, int64_t m0,
                                              int64_t n0, int wave, int wm, int wn, int lane,
-                                             void *y, float *partial) {
-    f32_band_epilogue<OUT, EPI>(acc, lds, *ga, *gw, M, N, m0, n0, wave, wm, wn, lane, y, partial);
+                                             void *y, float *partial, unsigned pid) {
+    f32_band_epilogue<OUT, EPI>(acc, lds, *ga, *gw, M, N, m0, n0, wave, wm, wn, lane, y,
+                                (EPI & kEpiAmax) ? partial + pid : nullptr);
 }
 
 template <int OUT, int EPI>
@@ -103,7 +104,8 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_f16_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const TileCoord tc = tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, GROUP_M);
+    const unsigned pid = xcd_order(blockIdx.x, gridDim.x);
+    const TileCoord tc = tile_at(pid, tiles_m, tiles_n, GROUP_M);
     const int64_t m0 = (int64_t)tc.m * BM, n0 = (int64_t)tc.n * BN;
     const int64_t nb = K / 16;  // scale groups per row
     const int64_t rb = K / 2;   // code bytes per row
@@ -229,7 +231,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_f16_kernel(
 #undef DMPQ_F4_MFMA
 #undef DMPQ_F4_ITER
 
-    fp4_epilogue<OUT, EPI>(acc, lds, ga, gw, M, N, m0, n0, wave, wm, wn, lane, y, partial);
+    fp4_epilogue<OUT, EPI>(acc, lds, ga, gw, M, N, m0, n0, wave, wm, wn, lane, y, partial, pid);
 }
 
 // ---------------------------------------------------------------------------
@@ -250,7 +252,8 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_fast_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const TileCoord tc = tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, GROUP_M);
+    const unsigned pid = xcd_order(blockIdx.x, gridDim.x);
+    const TileCoord tc = tile_at(pid, tiles_m, tiles_n, GROUP_M);
     const int64_t m0 = (int64_t)tc.m * BM, n0 = (int64_t)tc.n * BN;
     const int64_t nb = K / 16, rb = K / 2;
     const int nk = (int)(nb / 4);
@@ -354,7 +357,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_fast_kernel(
 #undef DMPQ_F4F_MFMA
 #undef DMPQ_F4F_ITER
 
-    fp4_epilogue<OUT, EPI>(acc, lds, ga, gw, M, N, m0, n0, wave, wm, wn, lane, y, partial);
+    fp4_epilogue<OUT, EPI>(acc, lds, ga, gw, M, N, m0, n0, wave, wm, wn, lane, y, partial, pid);
 }
 
 // One k-step fragment: the 8 codes of 32-bit word S of a 16-byte piece, times
@@ -494,23 +497,19 @@ __device__ __forceinline__ void fp4dma_stage(const uint8_t *__restrict__ cur, ui
 #undef DMPQ_F4D_CHUNK
 }
 
-template <int OUT, int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_fp4_dma_kernel(
-    const uint8_t *__restrict__ ca, const uint8_t *__restrict__ sa, const float *__restrict__ ga,
-    const uint8_t *__restrict__ cw, const uint8_t *__restrict__ sw, const float *__restrict__ gw,
-    int64_t M, int64_t N, int64_t K, void *__restrict__ y, unsigned tiles_m, unsigned tiles_n,
-    float *__restrict__ partial) {
+// The main loop of the DMA kernel over stages kt0 .. kt1-1 of the tile at
+// (m0, n0); on return the stage buffers are free.
+__device__ __forceinline__ void fp4dma_mainloop(const uint8_t *__restrict__ ca, const uint8_t *__restrict__ sa,
+                                                const uint8_t *__restrict__ cw, const uint8_t *__restrict__ sw,
+                                                int64_t M, int64_t N, int64_t K, int64_t m0, int64_t n0,
+                                                int kt0, int kt1, uint8_t *lds, v16f (&acc)[4][4]) {
     using namespace fp4dma;
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const TileCoord tc = tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, GROUP_M);
-    const int64_t m0 = (int64_t)tc.m * BM, n0 = (int64_t)tc.n * BN;
     const int64_t nb = K / 16, rb = K / 2;
-    const int nk = (int)(K / BKE);
+    const int nk = kt1 - kt0;
 
-    v16f acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
@@ -549,17 +548,49 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_dma_kernel(
     L.sw = ((lane & 31) >> 1) & 7;
 
 #pragma unroll
-    for (int d = 0; d < 18; d++) fp4dma_one(lds, L, 0, d);
+    for (int d = 0; d < 18; d++) fp4dma_one(lds, L, kt0, d);
     for (int kt = 0; kt < nk; kt++) {
         __builtin_amdgcn_s_waitcnt(0xC07F & ~0xC00F);  // vmcnt(0): this wave's loads of stage kt
         __syncthreads();                               // ... and every other wave's
         // after the last stage the copy goes to a buffer nobody reads again
-        fp4dma_stage(lds + (kt & 1) * STAGE, lds + ((kt & 1) ^ 1) * STAGE, kt + 1 < nk ? kt + 1 : kt, L, acc);
+        fp4dma_stage(lds + (kt & 1) * STAGE, lds + ((kt & 1) ^ 1) * STAGE, kt0 + (kt + 1 < nk ? kt + 1 : kt), L,
+                     acc);
     }
     __builtin_amdgcn_s_waitcnt(0xC07F & ~0xC00F);  // the last copy has landed
     __syncthreads();  // every wave is done reading the stage buffers before they hold bands
+}
 
-    fp4_epilogue<OUT, EPI>(acc, lds, ga, gw, M, N, m0, n0, wave, wm, wn, lane, y, partial);
+template <int OUT, int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_fp4_dma_kernel(
+    const uint8_t *__restrict__ ca, const uint8_t *__restrict__ sa, const float *__restrict__ ga,
+    const uint8_t *__restrict__ cw, const uint8_t *__restrict__ sw, const float *__restrict__ gw,
+    int64_t M, int64_t N, int64_t K, void *__restrict__ y, unsigned tiles_m, unsigned tiles_n,
+    float *__restrict__ partial) {
+    using namespace fp4dma;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const unsigned pid = xcd_order(blockIdx.x, gridDim.x);
+    const TileCoord tc = tile_at(pid, tiles_m, tiles_n, GROUP_M);
+    const int64_t m0 = (int64_t)tc.m * BM, n0 = (int64_t)tc.n * BN;
+    v16f acc[4][4];
+    fp4dma_mainloop(ca, sa, cw, sw, M, N, K, m0, n0, 0, (int)(K / BKE), lds, acc);
+    fp4_epilogue<OUT, EPI>(acc, lds, ga, gw, M, N, m0, n0, wave, wm, wn, lane, y, partial, pid);
+}
+
+// The split workgroups of a SplitPlan launch (see gemm_i8_split_kernel).
+__global__ __launch_bounds__(256, 1) void gemm_fp4_split_kernel(
+    const uint8_t *__restrict__ ca, const uint8_t *__restrict__ sa, const uint8_t *__restrict__ cw,
+    const uint8_t *__restrict__ sw, int64_t M, int64_t N, int64_t K, unsigned tiles_m, unsigned tiles_n,
+    SplitPlan sp, uint32_t *__restrict__ spart, float *__restrict__ partial) {
+    using namespace fp4dma;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const SplitUnit u = split_unit(sp, tiles_m, tiles_n, GROUP_M);
+    if (partial && u.kt0 == 0 && threadIdx.x == 0) partial[sp.full + blockIdx.x / sp.splits] = 0.0f;
+    v16f acc[4][4];
+    fp4dma_mainloop(ca, sa, cw, sw, M, N, K, (int64_t)u.tc.m * BM, (int64_t)u.tc.n * BN, u.kt0, u.kt1, lds, acc);
+    store_split_partial(acc, spart + (size_t)blockIdx.x * kSplitWords, threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -703,34 +734,48 @@ template <int OUT, int EPI>
 static hipError_t launch_fp4_paths(hipStream_t s, const uint8_t *ca, const uint8_t *sa,
                                    const float *ga, const uint8_t *cw, const uint8_t *sw,
                                    const float *gw, int64_t M, int64_t N, int64_t K, void *y,
-                                   float *partial) {
+                                   float *partial, uint32_t *spart) {
     using namespace fp4gemm;
     static const hipError_t attr = [] {
         hipError_t e = allow_lds(gemm_fp4_f16_kernel<OUT, EPI>, 2 * STAGE);
         if (e == hipSuccess) e = allow_lds(gemm_fp4_fast_kernel<OUT, EPI>, 2 * STAGE);
         if (e == hipSuccess) e = allow_lds(gemm_fp4_dma_kernel<OUT, EPI>, fp4dma::LDS_BYTES);
+        if (e == hipSuccess) e = allow_lds(gemm_fp4_split_kernel, fp4dma::LDS_BYTES);
         return e;
     }();
     if (attr != hipSuccess) return attr;
     const int64_t tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
     const dim3 grid((unsigned)(tm * tn)), block(256);
     const unsigned utm = (unsigned)tm, utn = (unsigned)tn;
-    if (K % fp4dma::BKE == 0)
-        hipLaunchKernelGGL((gemm_fp4_dma_kernel<OUT, EPI>), grid, block, fp4dma::LDS_BYTES, s, ca, sa, ga,
-                           cw, sw, gw, M, N, K, y, utm, utn, partial);
-    else if (K % (4 * 16) == 0)
+    if (K % fp4dma::BKE == 0) {
+        const SplitPlan sp = plan_split(tm * tn, (int)(K / fp4dma::BKE), spart != nullptr);
+        if (sp.full > 0) {
+            hipLaunchKernelGGL((gemm_fp4_dma_kernel<OUT, EPI>), dim3(sp.full), block, fp4dma::LDS_BYTES, s, ca, sa,
+                               ga, cw, sw, gw, M, N, K, y, utm, utn, partial);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        if (sp.splits > 1) {
+            hipLaunchKernelGGL(gemm_fp4_split_kernel, dim3(sp.tail * sp.splits), block, fp4dma::LDS_BYTES, s, ca, sa,
+                               cw, sw, M, N, K, utm, utn, sp, spart, (EPI & kEpiAmax) ? partial : nullptr);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            return launch_f32_fixup(s, ga, gw, M, N, y, utm, utn, fp4dma::GROUP_M, partial, sp, spart, OUT, EPI);
+        }
+    } else if (K % (4 * 16) == 0) {
         hipLaunchKernelGGL((gemm_fp4_fast_kernel<OUT, EPI>), grid, block, 2 * STAGE, s, ca, sa, ga, cw,
                            sw, gw, M, N, K, y, utm, utn, partial);
-    else
+    } else {
         hipLaunchKernelGGL((gemm_fp4_f16_kernel<OUT, EPI>), grid, block, 2 * STAGE, s, ca, sa, ga, cw,
                            sw, gw, M, N, K, y, utm, utn, partial);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_gemm_nvfp4(hipStream_t s, const uint8_t *ca, const uint8_t *sa,
                              const float *ga, const uint8_t *cw, const uint8_t *sw,
                              const float *gw, int64_t M, int64_t N, int64_t K, int out_dtype,
-                             void *y, int variant, int epi, float *partial) {
+                             void *y, int variant, int epi, float *partial, uint32_t *spart) {
     if (M == 0 || N == 0) return hipSuccess;
     if (variant == 1) {
         if (epi != 0) return hipErrorInvalidValue;
@@ -742,13 +787,14 @@ hipError_t launch_gemm_nvfp4(hipStream_t s, const uint8_t *ca, const uint8_t *sa
             hipLaunchKernelGGL(gemm_fp4_scaled_kernel<1>, dim3((unsigned)(sm * sn)), block, 0, s, ca, sa, ga, cw, sw, gw, M, N, K, y, (unsigned)sn);
         return hipGetLastError();
     }
-    if (out_dtype == 0 && epi == 0) return launch_fp4_paths<0, 0>(s, ca, sa, ga, cw, sw, gw, M, N, K, y, partial);
+    if (out_dtype == 0 && epi == 0)
+        return launch_fp4_paths<0, 0>(s, ca, sa, ga, cw, sw, gw, M, N, K, y, partial, spart);
     if (out_dtype != 1) return hipErrorInvalidValue;
     switch (epi) {
-        case 0: return launch_fp4_paths<1, 0>(s, ca, sa, ga, cw, sw, gw, M, N, K, y, partial);
-        case 1: return launch_fp4_paths<1, 1>(s, ca, sa, ga, cw, sw, gw, M, N, K, y, partial);
-        case 2: return launch_fp4_paths<1, 2>(s, ca, sa, ga, cw, sw, gw, M, N, K, y, partial);
-        case 3: return launch_fp4_paths<1, 3>(s, ca, sa, ga, cw, sw, gw, M, N, K, y, partial);
+        case 0: return launch_fp4_paths<1, 0>(s, ca, sa, ga, cw, sw, gw, M, N, K, y, partial, spart);
+        case 1: return launch_fp4_paths<1, 1>(s, ca, sa, ga, cw, sw, gw, M, N, K, y, partial, spart);
+        case 2: return launch_fp4_paths<1, 2>(s, ca, sa, ga, cw, sw, gw, M, N, K, y, partial, spart);
+        case 3: return launch_fp4_paths<1, 3>(s, ca, sa, ga, cw, sw, gw, M, N, K, y, partial, spart);
     }
     return hipErrorInvalidValue;
 }

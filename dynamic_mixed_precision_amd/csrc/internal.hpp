@@ -42,13 +42,47 @@ hipError_t launch_tdc_refresh(hipStream_t s, const uint16_t *x_in, const uint16_
                               uint16_t *delta, int64_t n, int delta_valid, double *sums,
                               const Workspace &ws);
 
+// Split of the last, partial wave of GEMM tiles along K.  A launch of T
+// tiles on 256 CUs runs floor(T / 256) full waves and then a tail of T % 256
+// tiles that leaves most CUs idle for a whole tile's time.  With a split plan
+// the whole-tile kernel runs only the `full` tiles 0 .. full-1; a split
+// kernel then runs tail * splits workgroups, each taking the K stages
+// [s * nk / splits, (s + 1) * nk / splits) of one tail tile and storing its
+// raw accumulators (kSplitWords words) in the split area; a fixup kernel adds
+// each tail tile's partials in split order (deterministic) and runs the
+// normal epilogue.  The split work is a kernel of its own so that the
+// whole-tile kernel's register allocation is untouched.
+struct SplitPlan {
+    unsigned full;    // whole-tile workgroups (a multiple of 256), or every tile when splits == 1
+    unsigned tail;    // tiles split along K
+    unsigned splits;  // workgroups per tail tile (1: no split)
+    int nk;           // K stages of a whole tile
+};
+constexpr size_t kSplitWords = 256 * 256;  // 32-bit words per split workgroup
+constexpr unsigned kMaxSplitUnits = 256;   // split workgroups a launch may use
+constexpr size_t kSplitAreaBytes = kMaxSplitUnits * kSplitWords * 4;
+// Smallest K (elements) whose INT8 tail wave is split.  The INT8 tile is the
+// shortest per K (the i8 MFMA has twice the fp16 rate): at K = 3072 its tail
+// wave lasts about as long as the split's two extra launches and partial
+// traffic (measured on the 17776-token shapes), so only longer K pay.  The
+// NVFP4 and BF16 tails are split at every K.
+constexpr int64_t kSplitMinKInt8 = 4096;
+
 // epi: bit 0 GELU, bit 1 fused NVFP4 amax of the output into partial[tile]
-// (bf16 output only); the GEMM tile is 256 x 256 on every path.
+// (bf16 output only); the GEMM tile is 256 x 256 on every path.  spart: the
+// split area (kSplitAreaBytes), or NULL to run every tile whole.
 hipError_t launch_gemm_int8(hipStream_t s, const int8_t *qa, const float *sa, const int8_t *qw,
                             const float *sw, int64_t M, int64_t N, int64_t K, int out_dtype,
-                            void *y, int epi, float *partial);
+                            void *y, int epi, float *partial, uint32_t *spart);
 hipError_t launch_gemm_bf16(hipStream_t s, const uint16_t *x, const uint16_t *w, int64_t M,
-                            int64_t N, int64_t K, int out_dtype, void *y, int epi, float *partial);
+                            int64_t N, int64_t K, int out_dtype, void *y, int epi, float *partial,
+                            uint32_t *spart);
+// Fixup of a split launch with fp32 accumulators: y = (sum * gA) * gW (gA, gW
+// read from device memory; NULL reads as 1).
+hipError_t launch_f32_fixup(hipStream_t s, const float *ga, const float *gw, int64_t M, int64_t N,
+                            void *y, unsigned tiles_m, unsigned tiles_n, unsigned group_m,
+                            float *partial, const SplitPlan &sp, const uint32_t *spart,
+                            int out_dtype, int epi);
 hipError_t launch_outlier_count(hipStream_t s, const uint16_t *x, int64_t M, int64_t K,
                                 double kappa, double *count, const Workspace &ws);
 // Sum ns values per partial over nparts partials, in a fixed order, into out[ns].
@@ -57,7 +91,7 @@ hipError_t launch_finalize_sums(hipStream_t s, const double *partial, int nparts
 hipError_t launch_gemm_nvfp4(hipStream_t s, const uint8_t *ca, const uint8_t *sa,
                              const float *ga, const uint8_t *cw, const uint8_t *sw,
                              const float *gw, int64_t M, int64_t N, int64_t K, int out_dtype,
-                             void *y, int variant, int epi, float *partial);
+                             void *y, int variant, int epi, float *partial, uint32_t *spart);
 
 // Grid for a grid-stride loop over `work` items with 256 threads per group.
 inline unsigned stride_grid(int64_t work, int64_t per_group, unsigned cap) {

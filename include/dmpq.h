@@ -84,16 +84,17 @@ enum { DMPQ_TDC_SKIP = 0, DMPQ_TDC_REFRESH = 1 };
 enum { DMPQ_FP4_BF16_DEQUANT = 0, DMPQ_FP4_SCALED_MFMA = 1 };
 /* Workspace users. */
 enum { DMPQ_OP_GAMMA = 0, DMPQ_OP_QUANT_NVFP4 = 1, DMPQ_OP_TDC = 2, DMPQ_OP_PREP_WEIGHT = 3,
-       DMPQ_OP_OUTLIER = 4, DMPQ_OP_GEMM_AMAX = 5 };
+       DMPQ_OP_OUTLIER = 4, DMPQ_OP_GEMM_AMAX = 5, DMPQ_OP_GEMM = 6 };
 
 /* Message describing the calling thread's last error ("" if none). */
 const char *dmpq_last_error(void);
 /* Library version string. */
 const char *dmpq_version(void);
 /* Bytes of workspace the op needs, 0 for an unknown op.  Most ops need a
- * fixed amount.  DMPQ_OP_GEMM_AMAX (a fused-amax producer GEMM and the
- * NVFP4 quantization of its output) depends on the output's shape: pass the
- * GEMM's M and N as (M, K). */
+ * fixed amount.  Two depend on a GEMM's output shape (pass its M and N as
+ * (M, K)): DMPQ_OP_GEMM_AMAX, a fused-amax producer GEMM and the NVFP4
+ * quantization of its output; DMPQ_OP_GEMM, the full workspace of the *_ex
+ * GEMMs (the same tile maxima first, then 64 MiB for the K split). */
 size_t dmpq_workspace_bytes(int op, int64_t M, int64_t K);
 
 /* ---------------------------------------------------------------------------
@@ -291,7 +292,7 @@ dmpq_status dmpq_gemm_bf16(hipStream_t stream, const uint16_t *x, const uint16_t
  * prepares the next linear's input ([gist-en] §2.A "Outlier Smoothing": the
  * rotation must cost little, so its tensor-wide pass is folded into the GEMM
  * that produces the tensor).  out_dtype must be DMPQ_OUT_BF16 when
- * epilogue != 0; epilogue 0 is the plain call.
+ * epilogue != 0.
  *   DMPQ_EPI_GELU: y = bf16(GELU(float(bf16(v)))) for the linear's value v,
  *     GELU(u) = u * Phi(u) = u/2 * erfc(-u/sqrt 2) in fp32 -- the same result
  *     as a separate bf16 GELU after the GEMM, up to GELU's own rounding.
@@ -302,6 +303,17 @@ dmpq_status dmpq_gemm_bf16(hipStream_t stream, const uint16_t *x, const uint16_t
  *     N % 16 == 0 and ws of dmpq_workspace_bytes(DMPQ_OP_GEMM_AMAX, M, N)
  *     bytes; ws may be NULL otherwise.
  * The NVFP4 variant is always DMPQ_FP4_BF16_DEQUANT.
+ *
+ * Tail split: with ws of dmpq_workspace_bytes(DMPQ_OP_GEMM, M, N) bytes, the
+ * last partial wave of 256 x 256 tiles (the tiles beyond the last multiple
+ * of 256) is split along K over otherwise idle CUs, and a second kernel adds
+ * each tile's parts in a fixed order before the epilogue.  INT8 results are
+ * unchanged; NVFP4 and BF16 results differ from the unsplit ones only in the
+ * fp32 summation order (deterministic, within the same tolerance).  Applies
+ * on the DMA paths (INT8 K % 128 == 0 and K >= 4096, NVFP4 K % 256 == 0,
+ * every BF16 K) and not to the INT8 I32 output.  Calls that share a
+ * workspace must not overlap.
+ * epilogue 0 with ws NULL is the plain call.
  * ------------------------------------------------------------------------- */
 dmpq_status dmpq_qgemm_int8_ex(hipStream_t stream, const int8_t *qa, const float *sa,
                                const int8_t *qw, const float *sw, int64_t M, int64_t N, int64_t K,

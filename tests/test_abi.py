@@ -146,6 +146,14 @@ def test_fused_epilogue_validation(monkeypatch):
     # 2^20 x 2^16 outputs = 16384 tiles: the size grows past the fixed workspace
     assert dm.workspace_bytes(dm.OP_GEMM_AMAX, 1 << 20, 1 << 16) == 4 * 4096 * 256
     assert dm.workspace_bytes(dm.OP_GEMM_AMAX, -1, 16) == 0
+    # full GEMM workspace: the tile maxima rounded up to 256 bytes, then 64 MiB
+    assert dm.workspace_bytes(dm.OP_GEMM, M, N) == 256 + (64 << 20)
+    assert dm.workspace_bytes(dm.OP_GEMM, 17776, 3072) == 3584 + (64 << 20)
+    _expect(1, dm.qgemm_int8_ex, qa, sa, qw, sw, y, 0, out_dtype=5)
+    _expect(1, dm.qgemm_nvfp4_ex, _Fake((M, K // 2)), _Fake((M, K // 16)), _Fake((1,)),
+            _Fake((N, K // 2)), _Fake((N, K // 16)), _Fake((1,)), y, 0, out_dtype=dm.OUT_I32)
+    _expect(3, dm.gemm_bf16_ex, _Fake((M, K)), _Fake((N, K)), y, 0,
+            ws=_Fake((need,), numel=need, addr=0x10004))
     _expect(1, dm.qgemm_int8_ex, qa, sa, qw, sw, y, 4)                          # unknown bit
     _expect(4, dm.qgemm_int8_ex, qa, sa, qw, sw, y, dm.EPI_GELU, out_dtype=dm.OUT_F32)
     _expect(2, dm.qgemm_int8_ex, qa, sa, _Fake((40, K)), _Fake((40,)), _Fake((M, 40)),
