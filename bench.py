@@ -403,12 +403,17 @@ def cpu_baseline(rows: int) -> dict:
 # ---- HBM byte counters and profile summaries ---------------------------------
 # The kernels behind each timed entry point and the sources they are built from:
 # a stored traffic figure is used only while these sources are unchanged.
-# bf16-output instantiations of the DMA-fed GEMM kernels, every epilogue
-# ('*' matches the epilogue template argument)
-GEMM_KERNELS = {"qgemm_nvfp4": "dmpq::gemm_fp4_dma_kernel<1, *>",
-                "qgemm_int8": "dmpq::gemm_i8_dma_kernel<1, *>"}
-GEMM_SOURCES = {"qgemm_nvfp4": ["gemm_nvfp4.hip", "gemm_common.hpp", "device.hpp", "internal.hpp"],
-                "qgemm_int8": ["gemm_int8.hip", "gemm_dma.hpp", "gemm_common.hpp", "device.hpp", "internal.hpp"]}
+# The kernels of one GEMM call (bf16 output, every epilogue; '*' matches a
+# template argument): the whole-tile DMA kernel, which every call of the
+# step runs once, and the split and fixup kernels of its tail.
+GEMM_KERNELS = {"qgemm_nvfp4": ["dmpq::gemm_fp4_dma_kernel<1, *>", "dmpq::gemm_fp4_split_kernel",
+                                "dmpq::gemm_f32_fixup_kernel<1, *, *>"],
+                "qgemm_int8": ["dmpq::gemm_i8_dma_kernel<1, *>", "dmpq::gemm_i8_split_kernel",
+                               "dmpq::gemm_i8_fixup_kernel<1, *, *>"]}
+GEMM_SOURCES = {"qgemm_nvfp4": ["gemm_nvfp4.hip", "gemm_bf16.hip", "gemm_common.hpp", "device.hpp",
+                                "internal.hpp"],
+                "qgemm_int8": ["gemm_int8.hip", "gemm_dma.hpp", "gemm_common.hpp", "device.hpp",
+                               "internal.hpp"]}
 CALIB_KERNEL = "dmpq::tdc_skip_kernel"
 HERE = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_JSON = os.path.join(HERE, "profiles", "traffic_qgemm_cogvideox5b.json")
@@ -494,16 +499,19 @@ def summarize_traffic(fetch_csv: str, write_csv: str, out_json: str, command: st
         "kernel": CALIB_KERNEL, "elements": n, "read_bytes": 4 * n, "write_bytes": 2 * n,
         "fetch_kib_per_dispatch": cf, "write_kib_per_dispatch": cw,
         "fetch_factor": round(f_read, 5), "write_factor": round(f_write, 5)}}
-    for api, kname in GEMM_KERNELS.items():
-        f, w = _per_kernel_kib(fr, kname), _per_kernel_kib(wr, kname)
-        if not f or len(f) != len(w):
+    for api, knames in GEMM_KERNELS.items():
+        calls = len(_per_kernel_kib(fr, knames[0]))  # one whole-tile dispatch per call
+        f = [v for k in knames for v in _per_kernel_kib(fr, k)]
+        w = [v for k in knames for v in _per_kernel_kib(wr, k)]
+        if not calls or len(f) != len(w):
             continue
-        fb = 1024.0 * f_read * sum(f) / len(f)
-        wb = 1024.0 * f_write * sum(w) / len(w)
+        fb = 1024.0 * f_read * sum(f) / calls
+        wb = 1024.0 * f_write * sum(w) / calls
         alg = gemm_algorithmic_bytes(api)
-        rec[api] = {"kernel": kname, "dispatches": len(f), "sources_sha256": sources_sha256(api),
-                    "fetch_kib_avg_raw": round(sum(f) / len(f), 1),
-                    "write_kib_avg_raw": round(sum(w) / len(w), 1),
+        rec[api] = {"kernels": knames, "calls": calls, "dispatches": len(f),
+                    "sources_sha256": sources_sha256(api),
+                    "fetch_kib_per_call_raw": round(sum(f) / calls, 1),
+                    "write_kib_per_call_raw": round(sum(w) / calls, 1),
                     "fetch_bytes_per_launch": round(fb), "write_bytes_per_launch": round(wb),
                     "bytes_per_launch": round(fb + wb),
                     "algorithmic_bytes_per_launch": round(alg),
@@ -532,7 +540,18 @@ def summarize_stats(stats_csv: str, out_md: str, command: str) -> None:
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                      f"{float(r['Percentage']):.1f}% |")
     other = sum(float(r["Percentage"]) for r in rows if "dmpq" not in r["Name"])
-    lines += ["", f"Other kernels (torch input generation, setup): {other:.1f}% of GPU time.", ""]
+    lines += ["", f"Other kernels (torch input generation, setup): {other:.1f}% of GPU time.", "",
+              "Per GEMM call (whole-tile kernel, plus the split and fixup kernels of the tail; the",
+              "bench's HIP events time the same span):", "",
+              "| call | calls | kernels | us per call |", "|---|---|---|---|"]
+    for api, knames in GEMM_KERNELS.items():
+        pats = [_kernel_re(k) for k in knames]
+        sel = [r for r in rows if any(p.search(r["Name"]) for p in pats)]
+        calls = sum(int(r["Calls"]) for r in sel if pats[0].search(r["Name"]))
+        if calls:
+            tot = sum(int(r["Calls"]) * float(r["AverageNs"]) for r in sel) / 1e3
+            lines.append(f"| {api} | {calls} | {len(sel)} | {tot / calls:.1f} |")
+    lines.append("")
     with open(out_md, "w") as f:
         f.write("\n".join(lines))
     print("\n".join(lines))
