@@ -26,8 +26,11 @@ Inputs are synthetic (seeded, drawn on the device) and resident in HBM
 before timing; weights are prepared once, outside the timed region.
 
 Prints one JSON line.  value = qGEMM tera-ops per second of the whole step
-(all GEMM ops of the step / step wall time).  Per-kernel durations come from
-HIP events on the launch stream inside the timed region.
+(all GEMM ops of the step / step wall time).  Inside the timed region HIP
+events on the launch stream bracket the GEMM calls, which give the dominant
+kernel's per-launch duration (the roofline); the per-kernel table comes from
+as many further steps with events around every call (an event record costs
+several microseconds of GPU time, so the timed region keeps them few).
 """
 from __future__ import annotations
 
@@ -82,25 +85,30 @@ def parse():
 
 
 class KernelTimer:
-    """HIP events around each library call on the current stream.  The events
-    are created before the timed region (prepare), so inside it a call costs
-    only the two event records."""
+    """HIP events around library calls on the current stream.  The events are
+    created before timing starts (prepare), so a timed call costs only its two
+    event records; `only` restricts the events to the named calls (None: every
+    call).  Event records are not free (several us each), so the timed region
+    brackets only the GEMM calls and a separate pass times every call."""
 
     def __init__(self, torch):
         self.torch = torch
         self.rec = {}
         self.on = False
-        self.calls = 0          # calls seen while off (counts one step's calls)
+        self.only = None
+        self.calls = 0          # calls that would be timed, counted while off
         self.pool = []
 
     def prepare(self, n):
         ev = self.torch.cuda.Event
         self.pool = [(ev(enable_timing=True), ev(enable_timing=True)) for _ in range(n)]
         self.pool.reverse()
+        self.rec = {}
 
     def __call__(self, name, work, fn, *a, **kw):
-        if not self.on:
-            self.calls += 1
+        timed = self.only is None or name in self.only
+        if not self.on or not timed:
+            self.calls += timed
             fn(*a, **kw)
             return
         if self.pool:
@@ -119,7 +127,8 @@ class KernelTimer:
             ms = [s.elapsed_time(e) for s, e, _ in lst]
             work = sum(w for _, _, w in lst)
             out[name] = dict(calls_per_step=len(lst) / steps, total_ms=sum(ms),
-                             avg_us=1e3 * sum(ms) / len(ms), work=work)
+                             avg_us=1e3 * sum(ms) / len(ms),
+                             median_us=1e3 * sorted(ms)[len(ms) // 2], work=work)
         return out
 
 
@@ -291,6 +300,9 @@ def main():
         del cx, cd, co
         calib = dict(kernel=CALIB_KERNEL, elements=n, read_bytes=4 * n, write_bytes=2 * n)
 
+    # the timed region brackets the GEMM calls (the dominant-kernel
+    # candidates) with events; every other call runs without them
+    kt.only = GEMM_CALLS
     for _ in range(args.warmup):
         kt.calls = 0
         step()
@@ -305,8 +317,19 @@ def main():
     kt.on = False
     ms_per_step = 1e3 * elapsed / args.steps
     value = gemm_ops_step / (elapsed / args.steps) / 1e12
+    ktimed = kt.summary(args.steps)
 
-    # ---- per-kernel figures and the roofline of the dominant kernel -----------
+    # ---- per-kernel figures: events on every call, in as many extra steps -----
+    kt.only = None
+    kt.calls = 0
+    step()
+    kt.prepare(kt.calls * args.steps)
+    torch.cuda.synchronize()
+    kt.on = True
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt.on = False
     ksum = kt.summary(args.steps)
     peaks = {"hadamard_quant_int8": ("hbm", HBM_GBPS, "GB/s"),
              "weight_int8_from_nvfp4": ("hbm", HBM_GBPS, "GB/s"),
@@ -324,14 +347,19 @@ def main():
         scale = 1e-9 if unit == "GB/s" else 1e-12
         achieved = s["work"] * scale / (s["total_ms"] * 1e-3)
         kernels[name] = dict(calls_per_step=s["calls_per_step"], avg_us=round(s["avg_us"], 2),
-                             achieved=round(achieved, 2), unit=unit, bound=bound, peak=peak,
-                             frac=round(achieved / peak, 4))
+                             median_us=round(s["median_us"], 2), achieved=round(achieved, 2), unit=unit,
+                             bound=bound, peak=peak, frac=round(achieved / peak, 4))
         if name == "qgemm_nvfp4":
             kernels[name]["frac_of_bf16_pipe"] = round(achieved / PEAK_BF16_TFLOPS, 4)
     dom = max(ksum, key=lambda n: ksum[n]["total_ms"])
     d = kernels[dom]
+    if dom in ktimed:  # the dominant kernel as timed inside the timed region
+        t = ktimed[dom]
+        ach = t["work"] * (1e-9 if d["unit"] == "GB/s" else 1e-12) / (t["total_ms"] * 1e-3)
+        d = dict(d, achieved=round(ach, 2), frac=round(ach / d["peak"], 4), avg_us=round(t["avg_us"], 2))
     roofline = dict(kernel=dom, bound=d["bound"], achieved=d["achieved"], peak=d["peak"],
-                    unit=d["unit"], frac=d["frac"], traffic=None)
+                    unit=d["unit"], frac=d["frac"], traffic=None, avg_us_per_call=d["avg_us"],
+                    timed_in="timed region" if dom in ktimed else "per-kernel pass")
     roofline.update(measured_traffic(dom))
     q_bytes = sum(ksum[n]["work"] for n in ksum if n.startswith("hadamard_quant"))
     q_ms = sum(ksum[n]["total_ms"] for n in ksum if n.startswith("hadamard_quant"))
@@ -363,6 +391,7 @@ def main():
                    "gemm_tera_ops_per_step": round(gemm_ops_step / 1e12, 3)},
         "act_quant_GBps": round(q_bytes * 1e-9 / (q_ms * 1e-3), 1),
         "kernels": kernels,
+        "kernels_note": "per-call HIP events on every call, in as many untimed steps after the timed region",
         "roofline": roofline,
         "setup_s": round(setup_s, 1),
     }
@@ -406,6 +435,9 @@ def cpu_baseline(rows: int) -> dict:
 # The kernels of one GEMM call (bf16 output, every epilogue; '*' matches a
 # template argument): the whole-tile DMA kernel, which every call of the
 # step runs once, and the split and fixup kernels of its tail.
+# library calls bracketed by events inside the timed region
+GEMM_CALLS = ("qgemm_nvfp4", "qgemm_int8", "gemm_bf16")
+
 GEMM_KERNELS = {"qgemm_nvfp4": ["dmpq::gemm_fp4_dma_kernel<1, *>", "dmpq::gemm_fp4_split_kernel",
                                 "dmpq::gemm_f32_fixup_kernel<1, *, *>"],
                 "qgemm_int8": ["dmpq::gemm_i8_dma_kernel<1, *>", "dmpq::gemm_i8_split_kernel",
