@@ -75,7 +75,7 @@ def _declare(L):
         "dmpq_version": (C.c_char_p, []),
         "dmpq_workspace_bytes": (C.c_size_t, [i32, i64, i64]),
         "dmpq_gamma_sums": (i32, [vp, vp, vp, i64, vp, vp, C.c_size_t]),
-        "dmpq_gate_and_route": (i32, [pd, i32, pd, pd, f64, pd, pd, C.POINTER(C.c_uint8)]),
+        "dmpq_gate_and_route": (i32, [vp, i32, vp, vp, f64, vp, vp, vp]),
         "dmpq_hadamard_quant_int8": (i32, [vp, vp, i64, i64, i32, vp, vp]),
         "dmpq_hadamard_quant_nvfp4": (i32, [vp, vp, i64, i64, i32, vp, vp, vp, vp, C.c_size_t]),
         "dmpq_qgemm_int8": (i32, [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]),
@@ -147,20 +147,19 @@ def gamma_sums(x_in, x_out, sums, ws, stream=None) -> None:
 
 def gate_and_route(sums2, alpha, beta, tau: float):
     """Host router.  sums2: 2 floats or None (Gamma missing).
-    Returns (gamma, errors[n_lin], routes[n_lin])."""
+    Returns (gamma, errors[n_lin], routes[n_lin]).  Runs between the step's
+    device->host copy and its first launch, so it passes raw addresses (a
+    ctypes pointer cast costs tens of microseconds)."""
     a = np.ascontiguousarray(alpha, np.float64)
     b = np.ascontiguousarray(beta, np.float64)
     n = len(a)
     s = None if sums2 is None else np.ascontiguousarray(sums2, np.float64)
-    g = np.zeros(1, np.float64)
-    e = np.zeros(n, np.float64)
-    r = np.zeros(n, np.uint8)
-    pd = C.POINTER(C.c_double)
+    out = np.empty(1 + n, np.float64)  # gamma, then the errors
+    r = np.empty(n, np.uint8)
     _check(lib().dmpq_gate_and_route(
-        None if s is None else s.ctypes.data_as(pd), n, a.ctypes.data_as(pd),
-        b.ctypes.data_as(pd), tau, g.ctypes.data_as(pd), e.ctypes.data_as(pd),
-        r.ctypes.data_as(C.POINTER(C.c_uint8))), "dmpq_gate_and_route")
-    return float(g[0]), e, r
+        None if s is None else s.ctypes.data, n, a.ctypes.data, b.ctypes.data, tau,
+        out.ctypes.data, out.ctypes.data + 8, r.ctypes.data), "dmpq_gate_and_route")
+    return float(out[0]), out[1:], r
 
 
 def hadamard_quant_int8(x, q, s_row, flags: int = 0, stream=None) -> None:
