@@ -22,6 +22,7 @@ ROUTE_NVFP4, ROUTE_INT8, ROUTE_BF16 = 0, 1, 2
 OUT_F32, OUT_BF16, OUT_I32 = 0, 1, 2
 NO_HADAMARD, AMAX_GIVEN = 1, 2
 EPI_GELU, EPI_NVFP4_AMAX = 1, 2
+CODEC_E4M3, CODEC_E2M1 = 0, 1
 W8_FROM_NVFP4, W8_DIRECT = 0, 1
 TDC_SKIP, TDC_REFRESH = 0, 1
 FP4_BF16_DEQUANT = 0
@@ -33,7 +34,7 @@ EXPORTS = ("dmpq_last_error", "dmpq_version", "dmpq_workspace_bytes", "dmpq_gamm
            "dmpq_qgemm_int8", "dmpq_qgemm_nvfp4", "dmpq_tdc_init", "dmpq_tdc_decide",
            "dmpq_tdc_step", "dmpq_tdc_commit", "dmpq_prep_weight", "dmpq_weight_int8_from_nvfp4",
            "dmpq_outlier_count", "dmpq_pdr_decide", "dmpq_gemm_bf16", "dmpq_qgemm_int8_ex",
-           "dmpq_qgemm_nvfp4_ex", "dmpq_gemm_bf16_ex")
+           "dmpq_qgemm_nvfp4_ex", "dmpq_gemm_bf16_ex", "dmpq_selftest_codec")
 
 
 class DmpqError(RuntimeError):
@@ -93,6 +94,7 @@ def _declare(L):
         "dmpq_qgemm_nvfp4_ex": (i32, [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, i32, vp,
                                       C.c_size_t]),
         "dmpq_gemm_bf16_ex": (i32, [vp, vp, vp, i64, i64, i64, i32, vp, i32, vp, C.c_size_t]),
+        "dmpq_selftest_codec": (i32, [vp, i32, C.c_uint32, C.c_uint32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -289,3 +291,10 @@ def gemm_bf16_ex(x, w, y, epilogue: int = 0, ws=None, out_dtype: int = OUT_BF16,
     _check(lib().dmpq_gemm_bf16_ex(_stream(stream), _ptr(x), _ptr(w), M, N, K, out_dtype, _ptr(y),
                                    epilogue, *_ws(ws)),
            "dmpq_gemm_bf16_ex")
+
+
+def selftest_codec(codec: int, lo: int, hi: int, stats, stream=None) -> None:
+    """Per-code (lowest, highest, count) of the fp32 patterns [lo, hi) through
+    a device converter (CODEC_E4M3 or CODEC_E2M1); stats: uint32/int32 tensor."""
+    _check(lib().dmpq_selftest_codec(_stream(stream), codec, lo, hi, _ptr(stats)),
+           "dmpq_selftest_codec")

@@ -434,4 +434,15 @@ dmpq_status dmpq_gemm_bf16_ex(hipStream_t stream, const uint16_t *x, const uint1
                       __func__);
 }
 
+dmpq_status dmpq_selftest_codec(hipStream_t stream, int codec, uint32_t lo, uint32_t hi,
+                                uint32_t *d_stats) {
+    if (codec != DMPQ_CODEC_E4M3 && codec != DMPQ_CODEC_E2M1)
+        return fail(DMPQ_ERR_INVALID_ARG, "%s: unknown codec %d", __func__, codec);
+    if (lo > hi || hi > 0x7F800000u)
+        return fail(DMPQ_ERR_INVALID_ARG, "%s: patterns [%u, %u) are not finite non-negative floats",
+                    __func__, lo, hi);
+    REQUIRE_PTR(d_stats);
+    return hip_status(launch_codec_stats(stream, codec, lo, hi, d_stats), __func__);
+}
+
 }  // extern "C"

@@ -93,6 +93,10 @@ hipError_t launch_gemm_nvfp4(hipStream_t s, const uint8_t *ca, const uint8_t *sa
                              const float *gw, int64_t M, int64_t N, int64_t K, int out_dtype,
                              void *y, int variant, int epi, float *partial, uint32_t *spart);
 
+// Per-code (lowest, highest, count) of input bit patterns in [lo, hi) for the
+// device converters (codec 0: E4M3 encoder; 1: hardware E2M1 converter).
+hipError_t launch_codec_stats(hipStream_t s, int codec, uint32_t lo, uint32_t hi, uint32_t *stats);
+
 // Grid for a grid-stride loop over `work` items with 256 threads per group.
 inline unsigned stride_grid(int64_t work, int64_t per_group, unsigned cap) {
     int64_t g = (work + per_group - 1) / per_group;

@@ -326,6 +326,25 @@ dmpq_status dmpq_gemm_bf16_ex(hipStream_t stream, const uint16_t *x, const uint1
                               int64_t N, int64_t K, int out_dtype, void *y, int epilogue, void *ws,
                               size_t ws_bytes);
 
+/* ---------------------------------------------------------------------------
+ * Self-test of the device converters behind the quantizers ([gist-en] §1:
+ * NVFP4 codes are E2M1 with E4M3 block scales).  Not on the hot path.
+ * codec DMPQ_CODEC_E4M3: the block-scale encoder on non-negative inputs
+ *   (nearest E4M3, ties to even, saturating at 448); DMPQ_CODEC_E2M1: the
+ *   element converter (nearest E2M1, ties to even, saturating at 6, sign
+ *   kept) on +f and -f.  Over the fp32 bit patterns p in [lo, hi)
+ *   (0 <= lo <= hi <= 0x7F800000, i.e. finite non-negative floats f), for
+ *   each code c writes d_stats[3c] = the lowest p encoding to c (0xFFFFFFFF
+ *   if none), d_stats[3c+1] = the highest, d_stats[3c+2] = how many (codes
+ *   0..127 for E4M3; 0..15 for E2M1, the negated inputs in 8..15).  Both
+ *   converters are monotone in p, so these equal a reference encoder's
+ *   exactly when every pattern agrees.  d_stats: 384 (E4M3) or 48 (E2M1)
+ *   uint32, device.
+ * ------------------------------------------------------------------------- */
+enum { DMPQ_CODEC_E4M3 = 0, DMPQ_CODEC_E2M1 = 1 };
+dmpq_status dmpq_selftest_codec(hipStream_t stream, int codec, uint32_t lo, uint32_t hi,
+                                uint32_t *d_stats);
+
 #ifdef __cplusplus
 }
 #endif

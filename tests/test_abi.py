@@ -177,6 +177,13 @@ def test_fused_epilogue_validation(monkeypatch):
             _Fake((big, 1 << 12)), _Fake((1,)), _Fake((small,), numel=small), flags=dm.AMAX_GIVEN)
 
 
+def test_selftest_validation(monkeypatch):
+    monkeypatch.setattr(dm, "_stream", lambda s=None: 0)
+    _expect(1, dm.selftest_codec, 2, 0, 16, _Fake((384,)))
+    _expect(1, dm.selftest_codec, dm.CODEC_E4M3, 16, 0, _Fake((384,)))
+    _expect(1, dm.selftest_codec, dm.CODEC_E2M1, 0, 0x7F800001, _Fake((48,)))
+
+
 def test_null_pointer_rejected():
     L = dm.lib()
     st = L.dmpq_hadamard_quant_int8(None, None, 4, 32, 0, None, None)
