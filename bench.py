@@ -105,7 +105,7 @@ class KernelTimer:
         self.pool.reverse()
         self.rec = {}
 
-    def __call__(self, name, work, fn, *a, **kw):
+    def __call__(self, name, work, fn, *a, _shape=None, **kw):
         timed = self.only is None or name in self.only
         if not self.on or not timed:
             self.calls += timed
@@ -119,16 +119,21 @@ class KernelTimer:
         s.record()
         fn(*a, **kw)
         e.record()
-        self.rec.setdefault(name, []).append((s, e, work))
+        self.rec.setdefault(name, []).append((s, e, work, _shape))
 
-    def summary(self, steps):
-        out = {}
+    def summary(self, steps, by_shape=False):
+        groups = {}
         for name, lst in self.rec.items():
-            ms = [s.elapsed_time(e) for s, e, _ in lst]
-            work = sum(w for _, _, w in lst)
-            out[name] = dict(calls_per_step=len(lst) / steps, total_ms=sum(ms),
-                             avg_us=1e3 * sum(ms) / len(ms),
-                             median_us=1e3 * sorted(ms)[len(ms) // 2], work=work)
+            for rec in lst:
+                key = (name, rec[3]) if by_shape else name
+                groups.setdefault(key, []).append(rec)
+        out = {}
+        for key, lst in groups.items():
+            ms = [s.elapsed_time(e) for s, e, _, _ in lst]
+            work = sum(w for _, _, w, _ in lst)
+            out[key] = dict(calls_per_step=len(lst) / steps, total_ms=sum(ms),
+                            avg_us=1e3 * sum(ms) / len(ms),
+                            median_us=1e3 * sorted(ms)[len(ms) // 2], work=work)
         return out
 
 
@@ -230,10 +235,11 @@ def main():
         nonlocal gemm_ops_step
         # 1. Gamma predictor + router: one device->host boundary per step
         for b, blk in enumerate(blocks):
-            kt("gamma_sums", 4.0 * M * H, dm.gamma_sums, blk["x_in"], blk["x_out"], gsums[b, :2], ws)
+            kt("gamma_sums", 4.0 * M * H, dm.gamma_sums, blk["x_in"], blk["x_out"], gsums[b, :2], ws,
+               _shape=f"{M}x{H}")
             if pdr is not None:
                 kt("outlier_count", 2.0 * M * H, dm.outlier_count, blk["x_in"].view(M, H), pdr[0],
-                   gsums[b, 2:3], ws_out)
+                   gsums[b, 2:3], ws_out, _shape=f"{M}x{H}")
         gsums_host.copy_(gsums, non_blocking=True)
         torch.cuda.current_stream().synchronize()
         routes = [dm.gate_and_route(gsums_host[b, :2].numpy(), alpha, beta, tau)[2]
@@ -253,6 +259,7 @@ def main():
                 flops = 2.0 * M * lin.N * lin.K
                 ops += flops
                 route = routes[b][li]
+                gshape = f"{M}x{lin.N}x{lin.K}"
                 x, epi, qflags, qws = L["x"], 0, 0, ws
                 if fuse and li == i_up:
                     epi = dm.EPI_GELU
@@ -264,27 +271,29 @@ def main():
                         qflags, qws = dm.AMAX_GIVEN, ws_gemm
                 if route == dm.ROUTE_BF16:
                     kt("gemm_bf16", flops, dm.gemm_bf16_ex, x.view(M, lin.K), L["w"], ybuf[lin.name],
-                       epi, ws_gemm, out_dtype)
+                       epi, ws_gemm, out_dtype, _shape=gshape)
                 elif route == dm.ROUTE_INT8:
                     kt("hadamard_quant_int8", 3.0 * M * lin.K + 4.0 * M,
-                       dm.hadamard_quant_int8, x, qb["q"], qb["s"])
+                       dm.hadamard_quant_int8, x, qb["q"], qb["s"], _shape=f"{M}x{lin.K}")
                     qw, swr = L["qw"], L["swr"]
                     if args.int8_weights == "convert":
                         qw = w8_scratch[:lin.N * lin.K].view(lin.N, lin.K)
                         swr = s8_scratch[:lin.N]
                         kt("weight_int8_from_nvfp4", (0.5 + 1.0 / 16 + 1.0) * lin.N * lin.K + 8.0 * lin.N,
-                           dm.weight_int8_from_nvfp4, L["cw"], L["sw"], L["gw"], qw, swr)
+                           dm.weight_int8_from_nvfp4, L["cw"], L["sw"], L["gw"], qw, swr,
+                           _shape=f"{lin.N}x{lin.K}")
                     kt("qgemm_int8", flops, dm.qgemm_int8_ex, qb["q"], qb["s"], qw, swr,
-                       ybuf[lin.name], epi, ws_gemm, out_dtype)
+                       ybuf[lin.name], epi, ws_gemm, out_dtype, _shape=gshape)
                 else:
                     kt("hadamard_quant_nvfp4_given" if qflags else "hadamard_quant_nvfp4",
                        (2.0 + 0.5 + 1.0 / 16) * M * lin.K + 4.0,
-                       dm.hadamard_quant_nvfp4, x, qb["c"], qb["sc"], qb["g"], qws, qflags)
+                       dm.hadamard_quant_nvfp4, x, qb["c"], qb["sc"], qb["g"], qws, qflags,
+                       _shape=f"{M}x{lin.K}")
                     kt("qgemm_nvfp4", flops, dm.qgemm_nvfp4_ex, qb["c"], qb["sc"], qb["g"], L["cw"],
-                       L["sw"], L["gw"], ybuf[lin.name], epi, ws_gemm, out_dtype)
+                       L["sw"], L["gw"], ybuf[lin.name], epi, ws_gemm, out_dtype, _shape=gshape)
             # 3. Temporal Delta Cache refresh of the block
             kt("tdc_step_refresh", 8.0 * M * H, dm.tdc_step, dm.TDC_REFRESH, blk["x_in"],
-               blk["x_out"], blk["delta"], blk["delta_valid"], tsums[b], ws)
+               blk["x_out"], blk["delta"], blk["delta_valid"], tsums[b], ws, _shape=f"{M}x{H}")
             blk["delta_valid"] = True
         gemm_ops_step = ops
 
@@ -331,6 +340,7 @@ def main():
     torch.cuda.synchronize()
     kt.on = False
     ksum = kt.summary(args.steps)
+    kshape = kt.summary(args.steps, by_shape=True)
     peaks = {"hadamard_quant_int8": ("hbm", HBM_GBPS, "GB/s"),
              "weight_int8_from_nvfp4": ("hbm", HBM_GBPS, "GB/s"),
              "outlier_count": ("hbm", HBM_GBPS, "GB/s"),
@@ -351,6 +361,13 @@ def main():
                              bound=bound, peak=peak, frac=round(achieved / peak, 4))
         if name == "qgemm_nvfp4":
             kernels[name]["frac_of_bf16_pipe"] = round(achieved / PEAK_BF16_TFLOPS, 4)
+    by_shape = {}
+    for (name, shape), s in sorted(kshape.items()):
+        bound, peak, unit = peaks[name]
+        achieved = s["work"] * (1e-9 if unit == "GB/s" else 1e-12) / (s["total_ms"] * 1e-3)
+        by_shape[f"{name} {shape}"] = dict(calls_per_step=s["calls_per_step"], median_us=round(s["median_us"], 2),
+                                           achieved=round(achieved, 2), unit=unit,
+                                           frac=round(achieved / peak, 4))
     dom = max(ksum, key=lambda n: ksum[n]["total_ms"])
     d = kernels[dom]
     if dom in ktimed:  # the dominant kernel as timed inside the timed region
@@ -392,6 +409,7 @@ def main():
         "act_quant_GBps": round(q_bytes * 1e-9 / (q_ms * 1e-3), 1),
         "kernels": kernels,
         "kernels_note": "per-call HIP events on every call, in as many untimed steps after the timed region",
+        "kernels_by_shape": by_shape,
         "roofline": roofline,
         "setup_s": round(setup_s, 1),
     }
