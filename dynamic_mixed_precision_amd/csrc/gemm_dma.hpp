@@ -200,7 +200,10 @@ __device__ __forceinline__ int dma_valid(int64_t Kb, int kt) {
 // W[n0.., k]^T for the Kb bytes of every row that start at A and W (the
 // range's first byte; rows are ld bytes apart).  Kb % 32 == 0, and
 // Kb % 128 == 0 unless TAIL.  On return every DMA has landed and every wave
-// has left the stage buffers, so `lds` is free for the epilogue.
+// has left the stage buffers, so `lds` is free for the epilogue.  An LDS DMA
+// that the workgroup issued before the call (outside the stage buffers) has
+// landed and is visible to every wave once the first stage is: the wait for
+// that stage counts it, and the barrier after it publishes it.
 template <class Op, bool TAIL>
 __device__ __forceinline__ void dma_gemm_mainloop(const uint8_t *__restrict__ A,
                                                   const uint8_t *__restrict__ W, int64_t M,
@@ -246,7 +249,13 @@ __device__ __forceinline__ void dma_gemm_mainloop(const uint8_t *__restrict__ A,
     } else {
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
-    __syncthreads();
+    // A bare barrier: __syncthreads() would also wait for the second stage's
+    // DMA (its fence covers every outstanding load), which nothing reads yet.
+    // The empty asm statements keep the compiler from moving the first
+    // stage's LDS reads above it.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     v4i a0[4], b0[4], a1[4], b1[4];
     dma_frags<TAIL>(lds, L, 0, dma_valid(Kb, 0), a0, b0);
     dma_frags<TAIL>(lds, L, 1, dma_valid(Kb, 0), a1, b1);

@@ -31,6 +31,30 @@ constexpr int LOADS = BM * BK / 16 / 256;     // 16-byte chunks per thread per o
 constexpr unsigned GROUP_M = 8;
 }  // namespace i8gemm
 
+// The tile's row and column scales, staged in LDS past the stage buffers:
+// sA of rows m0 .. m0+255, then sW of columns n0 .. n0+255 (rows and columns
+// past M or N load the last one; those outputs are never stored).  Each wave
+// moves 64 of each with one LDS DMA (global_load_lds_dword) before its main
+// loop issues the first stage, so the values need no registers and no wait
+// of their own: the first stage's wait and barrier cover them, and the
+// epilogue reads them from LDS instead of issuing 68 guarded global loads per
+// lane after the last MFMA.
+constexpr int kI8ScaleBytes = 512 * sizeof(float);
+static_assert(2 * i8gemm::STAGE + kI8ScaleBytes <= 160 * 1024, "LDS of gemm_i8_kernel");
+static_assert(gdma::LDS_BYTES + kI8ScaleBytes <= 160 * 1024, "LDS of gemm_i8_dma_kernel");
+static_assert(gdma::LDS_BYTES % 16 == 0 && (2 * i8gemm::STAGE) % 16 == 0, "16-byte scale reads");
+
+__device__ __forceinline__ void i8_scale_dma(float *scl, const float *sa, const float *sw, int64_t M,
+                                             int64_t N, int64_t m0, int64_t n0, int tid) {
+    typedef __attribute__((address_space(3))) void lds_void;
+    const int wave = tid >> 6;
+    const int64_t r = m0 + tid, c = n0 + tid;
+    __builtin_amdgcn_global_load_lds((const void *)(sa + (r < M ? r : M - 1)),
+                                     (lds_void *)(scl + 64 * wave), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void *)(sw + (c < N ? c : N - 1)),
+                                     (lds_void *)(scl + 256 + 64 * wave), 4, 0, 0);
+}
+
 // Epilogue of both INT8 kernels, expanded in the kernel body (kept out of a
 // function: as a function the compiler spills a few registers of it to
 // scratch).  The MFMA runs with the W fragment as its first operand, so
@@ -40,21 +64,20 @@ constexpr unsigned GROUP_M = 8;
 // (float(acc) * sA[row]) * sW[col] (bit-exact in fp32), staged per wave
 // through LDS in two 64-row bands and stored row-contiguous, with GELU and
 // the fused amax per EPI; OUT 2: the raw int32 accumulators (test mode).  The
-// stage buffers must be free (both main loops end with a barrier).  pid:
-// the tile's slot among the fused-amax maxima.
-#define DMPQ_I8_EPILOGUE()                                                                        \
+// stage buffers must be free (both main loops end with a barrier).  SCL: the
+// tile's staged scales (i8_scale_dma).  pid: the tile's slot among the
+// fused-amax maxima.
+#define DMPQ_I8_EPILOGUE(SCL)                                                                     \
     {                                                                                             \
         constexpr int ES = OUT == 1 ? 2 : 4;                                                      \
         using Band = EpiBand<ES>;                                                                 \
         const int lm = lane & 31, lh = lane >> 5;                                                 \
-        float swv[4][4][4];                                                                       \
+        const float *scl_ = (SCL);                                                                \
+        float4 swv[4][4];                                                                         \
         if constexpr (OUT != 2) {                                                                 \
             _Pragma("unroll") for (int j = 0; j < 4; j++)                                         \
-                _Pragma("unroll") for (int g = 0; g < 4; g++)                                     \
-                    _Pragma("unroll") for (int e = 0; e < 4; e++) {                               \
-                const int64_t col = n0 + wn * 128 + j * 32 + 8 * g + 4 * lh + e;                  \
-                swv[j][g][e] = col < N ? sw[col] : 0.0f;                                          \
-            }                                                                                     \
+                _Pragma("unroll") for (int g = 0; g < 4; g++) swv[j][g] =                         \
+                    *reinterpret_cast<const float4 *>(scl_ + 256 + wn * 128 + j * 32 + 8 * g + 4 * lh); \
         }                                                                                         \
         uint8_t *band = reinterpret_cast<uint8_t *>(lds) + wave * Band::BYTES;                    \
         const bool vec = ((N * ES) & 15) == 0;                                                    \
@@ -62,8 +85,7 @@ constexpr unsigned GROUP_M = 8;
         _Pragma("unroll") for (int h = 0; h < 2; h++) {                                           \
             _Pragma("unroll") for (int ii = 0; ii < 2; ii++) {                                    \
                 const int i = 2 * h + ii;                                                         \
-                const int64_t row = m0 + wm * 128 + i * 32 + lm;                                  \
-                const float sar = row < M ? sa[row] : 0.0f;                                       \
+                const float sar = OUT == 2 ? 0.0f : scl_[wm * 128 + i * 32 + lm];                 \
                 _Pragma("unroll") for (int j = 0; j < 4; j++) {                                   \
                     _Pragma("unroll") for (int g = 0; g < 4; g++) {                               \
                         uint8_t *dst = band + (ii * 32 + lm) * Band::STRIDE + (j * 32 + 8 * g + 4 * lh) * ES; \
@@ -73,8 +95,10 @@ constexpr unsigned GROUP_M = 8;
                                           acc[i][j][4 * g + 3]);                                  \
                         } else {                                                                  \
                             float v4[4];                                                          \
-                            _Pragma("unroll") for (int e = 0; e < 4; e++) v4[e] =                 \
-                                ((float)acc[i][j][4 * g + e] * sar) * swv[j][g][e];               \
+                            v4[0] = ((float)acc[i][j][4 * g + 0] * sar) * swv[j][g].x;            \
+                            v4[1] = ((float)acc[i][j][4 * g + 1] * sar) * swv[j][g].y;            \
+                            v4[2] = ((float)acc[i][j][4 * g + 2] * sar) * swv[j][g].z;            \
+                            v4[3] = ((float)acc[i][j][4 * g + 3] * sar) * swv[j][g].w;            \
                             if constexpr (OUT == 0)                                               \
                                 *reinterpret_cast<float4 *>(dst) = make_float4(v4[0], v4[1], v4[2], v4[3]); \
                             else                                                                  \
@@ -148,8 +172,11 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(
             make_uint4(iw ? rw[j].x : 0u, iw ? rw[j].y : 0u, iw ? rw[j].z : 0u, iw ? rw[j].w : 0u); \
     }
 
+    float *scl = reinterpret_cast<float *>(lds + 2 * STAGE);
+    i8_scale_dma(scl, sa, sw, M, N, m0, n0, tid);
     DMPQ_I8_GLOAD(0)
     DMPQ_I8_SSTORE(0)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the scale DMA has landed
     __syncthreads();
 
     for (int kt = 0; kt < nk; kt++) {
@@ -182,7 +209,7 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(
 #undef DMPQ_I8_GLOAD
 #undef DMPQ_I8_SSTORE
 
-    DMPQ_I8_EPILOGUE()
+    DMPQ_I8_EPILOGUE(scl)
 }
 
 // ---------------------------------------------------------------------------
@@ -203,11 +230,13 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_dma_kernel(
     const TileCoord tc = tile_at(pid, tiles_m, tiles_n, GROUP_M);
     const int64_t m0 = (int64_t)tc.m * BM, n0 = (int64_t)tc.n * BN;
 
+    float *scl = reinterpret_cast<float *>(lds + LDS_BYTES);
+    i8_scale_dma(scl, sa, sw, M, N, m0, n0, tid);  // older than the first stage's DMA
     v16i acc[4][4];
     dma_gemm_mainloop<OpI8, false>(reinterpret_cast<const uint8_t *>(A),
                                    reinterpret_cast<const uint8_t *>(W), M, N, K, K, m0, n0,
                                    reinterpret_cast<uint8_t *>(lds), acc);
-    DMPQ_I8_EPILOGUE()
+    DMPQ_I8_EPILOGUE(scl)
 }
 
 // The split workgroups of a SplitPlan launch: the main loop over this
@@ -234,13 +263,32 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_split_kernel(
 // Output scaling of the INT8 fixup: y = (float(acc) * sA[row]) * sW[col],
 // bit-exact in fp32.  c0: first output column of the lane's (j, g) groups.
 struct EpiScaleI8 {
-    const float *sa, *sw;
-    int64_t M, N, c0;
+    const float *sa;
+    int64_t M;
     float sar;
-    __device__ __forceinline__ void row(int64_t r) { sar = r < M ? sa[r] : 0.0f; }
+    float swv[4][4][4];  // the lane's 64 column scales, 0 past N
+    // c0: first output column of the lane's (j, g) groups.  The loads are
+    // clamped and unconditional, so they issue back to back without branches.
+    __device__ __forceinline__ EpiScaleI8(const float *sa_, const float *sw, int64_t M_, int64_t N,
+                                          int64_t c0)
+        : sa(sa_), M(M_), sar(0.0f) {
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int g = 0; g < 4; g++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int64_t col = c0 + j * 32 + 8 * g + e;
+                    const float v = sw[col < N ? col : N - 1];
+                    swv[j][g][e] = col < N ? v : 0.0f;
+                }
+    }
+    __device__ __forceinline__ void row(int64_t r) {
+        const float v = sa[r < M ? r : M - 1];
+        sar = r < M ? v : 0.0f;
+    }
     __device__ __forceinline__ float operator()(float a, int j, int g, int e) const {
-        const int64_t col = c0 + j * 32 + 8 * g + e;
-        return (a * sar) * (col < N ? sw[col] : 0.0f);
+        return (a * sar) * swv[j][g][e];
     }
 };
 
@@ -258,7 +306,7 @@ __global__ __launch_bounds__(64) void gemm_i8_fixup_kernel(
     const unsigned t = blockIdx.x >> 2, pid = sp.full + t;
     const TileCoord tc = tile_at(pid, tiles_m, tiles_n, GROUP_M);
     const int64_t m0 = (int64_t)tc.m * BM, n0 = (int64_t)tc.n * BN;
-    EpiScaleI8 sc{sa, sw, M, N, n0 + (wave & 1) * 128 + 4 * (lane >> 5), 0.0f};
+    EpiScaleI8 sc(sa, sw, M, N, n0 + (wave & 1) * 128 + 4 * (lane >> 5));
     split_fixup_epilogue<OUT, EPI, int, S>(spart + (size_t)t * S * kSplitWords, sc, lds8, M, N, m0, n0, wave,
                                            lane, y, (EPI & kEpiAmax) ? partial + pid : nullptr);
 }
@@ -277,8 +325,8 @@ static hipError_t launch_i8_paths(hipStream_t s, const int8_t *qa, const float *
     constexpr bool CAN_SPLIT = OUT != 2;
     // Kernels need more dynamic LDS than the default limit: opt in once.
     static const hipError_t attr = [] {
-        hipError_t e = allow_lds(gemm_i8_kernel<OUT, EPI>, 2 * i8gemm::STAGE);
-        if (e == hipSuccess) e = allow_lds(gemm_i8_dma_kernel<OUT, EPI>, gdma::LDS_BYTES);
+        hipError_t e = allow_lds(gemm_i8_kernel<OUT, EPI>, 2 * i8gemm::STAGE + kI8ScaleBytes);
+        if (e == hipSuccess) e = allow_lds(gemm_i8_dma_kernel<OUT, EPI>, gdma::LDS_BYTES + kI8ScaleBytes);
         if (e == hipSuccess) e = allow_lds(gemm_i8_split_kernel, gdma::LDS_BYTES);
 
         return e;
@@ -288,13 +336,15 @@ static hipError_t launch_i8_paths(hipStream_t s, const int8_t *qa, const float *
     const dim3 block(256);
     const unsigned utm = (unsigned)tm, utn = (unsigned)tn;
     if (K % gdma::BK != 0) {
-        hipLaunchKernelGGL((gemm_i8_kernel<OUT, EPI>), dim3((unsigned)(tm * tn)), block, 2 * i8gemm::STAGE, s, qa,
+        hipLaunchKernelGGL((gemm_i8_kernel<OUT, EPI>), dim3((unsigned)(tm * tn)), block,
+                           2 * i8gemm::STAGE + kI8ScaleBytes, s, qa,
                            sa, qw, sw, M, N, K, y, utm, utn, partial);
         return hipGetLastError();
     }
     const SplitPlan sp = plan_split(tm * tn, (int)(K / gdma::BK), CAN_SPLIT && spart != nullptr && K >= kSplitMinKInt8);
     if (sp.full > 0) {
-        hipLaunchKernelGGL((gemm_i8_dma_kernel<OUT, EPI>), dim3(sp.full), block, gdma::LDS_BYTES, s, qa, sa, qw,
+        hipLaunchKernelGGL((gemm_i8_dma_kernel<OUT, EPI>), dim3(sp.full), block,
+                           gdma::LDS_BYTES + kI8ScaleBytes, s, qa, sa, qw,
                            sw, M, N, K, y, utm, utn, partial);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
