@@ -161,7 +161,8 @@ def test_weight_int8_from_nvfp4_parity(orc, N, K):
 
 def test_weight_int8_from_nvfp4_random_codes(orc):
     # arbitrary codes, every finite E4M3 scale, a tensor scale far from 1, and
-    # an all-zero row
+    # an all-zero row; g = 2^101 takes the kernel's clamped rounding (above
+    # 2^100 it does not assume finite values), the others its magic-number one
     require_gpu()
     say("weight_int8_from_nvfp4 random codes")
     rng = np.random.default_rng(63)
@@ -169,7 +170,7 @@ def test_weight_int8_from_nvfp4_random_codes(orc):
     cw = rng.integers(0, 256, (N, K // 2)).astype(np.uint8)
     sw = rng.integers(0, 0x7F, (N, K // 16)).astype(np.uint8)
     cw[5] = 0
-    for g in (3.0517578e-05, 0.75, 1.7e3):
+    for g in (3.0517578e-05, 0.75, 1.7e3, 2.0 ** 101):
         q_ref, s_ref = orc.w8_from_nvfp4(cw, sw, g)
         qw, swr = empty((N, K), np.int8), empty((N,), np.float32)
         dm.weight_int8_from_nvfp4(dev(cw), dev(sw), dev(np.array([g], np.float32)), qw, swr)
