@@ -56,21 +56,22 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_split_kernel(
 }
 
 // The tail tiles of a split launch with fp32 accumulators (BF16 and NVFP4
-// GEMMs): one wave per 128 x 128 quadrant, the partials added in split
-// order, then the fp32 epilogue.
+// GEMMs): one wave per 32-row slice of a 128 x 128 quadrant (16 per tail
+// tile), the partials added in split order, then the fp32 epilogue.
 template <int OUT, int EPI, int S>
 __global__ __launch_bounds__(64) void gemm_f32_fixup_kernel(
     const float *__restrict__ ga, const float *__restrict__ gw, int64_t M, int64_t N,
     void *__restrict__ y, unsigned tiles_m, unsigned tiles_n, unsigned group_m,
     float *__restrict__ partial, SplitPlan sp, const uint32_t *__restrict__ spart) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const int lane = threadIdx.x, wave = blockIdx.x & 3;
-    const unsigned t = blockIdx.x >> 2, pid = sp.full + t;
+    // workgroup = (tail tile t, quadrant wave, 32-row slice i)
+    const int lane = threadIdx.x, i = blockIdx.x & 3, wave = (blockIdx.x >> 2) & 3;
+    const unsigned t = blockIdx.x >> 4, pid = sp.full + t;
     const TileCoord tc = tile_at(pid, tiles_m, tiles_n, group_m);
     const int64_t m0 = (int64_t)tc.m * 256, n0 = (int64_t)tc.n * 256;
     EpiScaleF32 sc{ga ? *ga : 1.0f, gw ? *gw : 1.0f};
     split_fixup_epilogue<OUT, EPI, float, S>(spart + (size_t)t * S * kSplitWords, sc, lds, M, N, m0, n0, wave,
-                                             lane, y, (EPI & kEpiAmax) ? partial + pid : nullptr);
+                                             i, lane, y, (EPI & kEpiAmax) ? partial + pid : nullptr);
 }
 
 template <class KernelFn>
@@ -83,8 +84,8 @@ template <int OUT, int EPI>
 static hipError_t launch_fixup(hipStream_t s, const float *ga, const float *gw, int64_t M, int64_t N,
                                void *y, unsigned tiles_m, unsigned tiles_n, unsigned group_m,
                                float *partial, const SplitPlan &sp, const uint32_t *spart) {
-    const dim3 fg(4 * sp.tail), fb(64);
-    const size_t fl = EpiBand<OUT == 1 ? 2 : 4>::BYTES;
+    const dim3 fg(16 * sp.tail), fb(64);
+    const size_t fl = (size_t)kFixupRows * EpiBand<OUT == 1 ? 2 : 4>::STRIDE;
 #define DMPQ_F32_FIX(S_)                                                                         \
     case S_:                                                                                     \
         hipLaunchKernelGGL((gemm_f32_fixup_kernel<OUT, EPI, S_>), fg, fb, fl, s, ga, gw, M, N, y, tiles_m, \

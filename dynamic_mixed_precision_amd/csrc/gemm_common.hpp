@@ -156,13 +156,13 @@ __device__ __forceinline__ float gelu_f32(float v) {
     return 0.5f * v * (x >= 0.0f ? e : 2.0f - e);
 }
 
-// Copy one wave's LDS band (kEpiRows x 128 values of ESIZE bytes) to y at
+// Copy one wave's LDS band (ROWS x 128 values of ESIZE bytes) to y at
 // (row0, col0), clipping to M x N.  vec: rows of y are 16-byte aligned.
 // kEpiGelu: each value passes through GELU on its way out.  kEpiAmax (bf16
 // only): the two lanes holding one 16-block finish its Hadamard (stages 1,
 // 2, 4 in-lane, stage 8 across the lane pair, then * 1/4) and the lane's max
 // |value| over valid blocks is returned.
-template <int ESIZE, int EPI = 0>
+template <int ESIZE, int EPI = 0, int ROWS = kEpiRows>
 __device__ __forceinline__ float epi_band_to_global(const uint8_t *band, void *y, int64_t M,
                                                     int64_t N, int64_t row0, int64_t col0,
                                                     int lane, bool vec) {
@@ -174,7 +174,7 @@ __device__ __forceinline__ float epi_band_to_global(const uint8_t *band, void *y
     const int64_t col = col0 + chunk * PER;
     float amax = 0.0f;
 #pragma unroll 4
-    for (int p = 0; p < kEpiRows / B::ROWS_PER_PASS; p++) {
+    for (int p = 0; p < ROWS / B::ROWS_PER_PASS; p++) {
         const int r = p * B::ROWS_PER_PASS + lane / B::LANES_PER_ROW;
         const int64_t row = row0 + r;
         uint4 v = *reinterpret_cast<const uint4 *>(band + r * B::STRIDE + chunk * 16);
@@ -314,20 +314,24 @@ __device__ __forceinline__ void f32_band_epilogue(v16f (&acc)[4][4], uint8_t *ld
     band_epilogue<OUT, EPI>(acc, sc, lds, M, N, m0, n0, wave, wm, wn, lane, y, slot);
 }
 
-// The epilogue of one 128 x 128 quadrant of a split tile, run by a
-// one-wave workgroup straight from the tile's partials (no accumulator
-// array: a register-resident tile plus the loads in flight would spill).
-// For each MFMA block (i, j), the lane's four 16-byte pieces of all S
-// splits are loaded together, added in split order as T (int32: exact;
-// fp32: fixed order), scaled by sc and written to the band; the band then
-// goes out as in band_epilogue.  part: the tile's first split; wave:
-// the quadrant (the wave of the whole-tile kernels whose lanes' layout the
-// partials follow).  The fused amax goes to *slot by an atomic max (the
-// split kernel zeroed it; the maximum does not depend on the order).
+// The epilogue of one 32-row slice i of a 128 x 128 quadrant of a split
+// tile, run by a one-wave workgroup straight from the tile's partials (no
+// accumulator array: a register-resident tile plus the loads in flight would
+// spill).  A tail of T tiles so gets 16 T waves, enough to keep the partial
+// reads in flight on every CU.  For each MFMA block (i, j), the lane's four
+// 16-byte pieces of all S splits are loaded together, added in split order
+// as T (int32: exact; fp32: fixed order), scaled by sc and written to a
+// 32-row band, which then goes out as in band_epilogue.  part: the tile's
+// first split; wave: the quadrant (the wave of the whole-tile kernels whose
+// lanes' layout the partials follow).  The fused amax goes to *slot by an
+// atomic max (the split kernel zeroed it; the maximum does not depend on the
+// order).
+constexpr int kFixupRows = 32;
+
 template <int OUT, int EPI, class T, int S, class Scale>
 __device__ __forceinline__ void split_fixup_epilogue(const uint32_t *part, Scale &sc, uint8_t *lds,
                                                      int64_t M, int64_t N, int64_t m0, int64_t n0,
-                                                     int wave, int lane, void *y, float *slot) {
+                                                     int wave, int i, int lane, void *y, float *slot) {
     constexpr int ES = OUT == 1 ? 2 : 4;
     using Band = EpiBand<ES>;
     constexpr size_t kPieces = kSplitWords / 4;
@@ -336,47 +340,39 @@ __device__ __forceinline__ void split_fixup_epilogue(const uint32_t *part, Scale
     const int lm = lane & 31, lh = lane >> 5;
     uint8_t *band = lds;
     const bool vec = ((N * ES) & 15) == 0;
-    float amax = 0.0f;
+    sc.row(m0 + wm * 128 + i * 32 + lm);
 #pragma unroll
-    for (int h = 0; h < 2; h++) {
+    for (int j = 0; j < 4; j++) {
+        uint4 v[S][4];
 #pragma unroll
-        for (int ii = 0; ii < 2; ii++) {
-            const int i = 2 * h + ii;
-            sc.row(m0 + wm * 128 + i * 32 + lm);
+        for (int s = 0; s < S; s++)
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                uint4 v[S][4];
+            for (int g = 0; g < 4; g++) v[s][g] = p4[s * kPieces + ((i * 4 + j) * 4 + g) * 256 + tid];
 #pragma unroll
-                for (int s = 0; s < S; s++)
+        for (int g = 0; g < 4; g++) {
+            T x[4] = {__builtin_bit_cast(T, v[0][g].x), __builtin_bit_cast(T, v[0][g].y),
+                      __builtin_bit_cast(T, v[0][g].z), __builtin_bit_cast(T, v[0][g].w)};
 #pragma unroll
-                    for (int g = 0; g < 4; g++) v[s][g] = p4[s * kPieces + ((i * 4 + j) * 4 + g) * 256 + tid];
-#pragma unroll
-                for (int g = 0; g < 4; g++) {
-                    T x[4] = {__builtin_bit_cast(T, v[0][g].x), __builtin_bit_cast(T, v[0][g].y),
-                              __builtin_bit_cast(T, v[0][g].z), __builtin_bit_cast(T, v[0][g].w)};
-#pragma unroll
-                    for (int s = 1; s < S; s++) {
-                        x[0] += __builtin_bit_cast(T, v[s][g].x);
-                        x[1] += __builtin_bit_cast(T, v[s][g].y);
-                        x[2] += __builtin_bit_cast(T, v[s][g].z);
-                        x[3] += __builtin_bit_cast(T, v[s][g].w);
-                    }
-                    float v4[4];
-#pragma unroll
-                    for (int e = 0; e < 4; e++) v4[e] = sc((float)x[e], j, g, e);
-                    uint8_t *dst = band + (ii * 32 + lm) * Band::STRIDE + (j * 32 + 8 * g + 4 * lh) * ES;
-                    if constexpr (OUT == 0)
-                        *reinterpret_cast<float4 *>(dst) = make_float4(v4[0], v4[1], v4[2], v4[3]);
-                    else
-                        *reinterpret_cast<uint2 *>(dst) = make_uint2(cvt_pk_bf16(v4[0], v4[1]), cvt_pk_bf16(v4[2], v4[3]));
-                }
-                // bound the loads in flight (one block's, two for few splits)
-                if (S > 4 || (j & 1)) __builtin_amdgcn_sched_barrier(0);
+            for (int s = 1; s < S; s++) {
+                x[0] += __builtin_bit_cast(T, v[s][g].x);
+                x[1] += __builtin_bit_cast(T, v[s][g].y);
+                x[2] += __builtin_bit_cast(T, v[s][g].z);
+                x[3] += __builtin_bit_cast(T, v[s][g].w);
             }
+            float v4[4];
+#pragma unroll
+            for (int e = 0; e < 4; e++) v4[e] = sc((float)x[e], j, g, e);
+            uint8_t *dst = band + lm * Band::STRIDE + (j * 32 + 8 * g + 4 * lh) * ES;
+            if constexpr (OUT == 0)
+                *reinterpret_cast<float4 *>(dst) = make_float4(v4[0], v4[1], v4[2], v4[3]);
+            else
+                *reinterpret_cast<uint2 *>(dst) = make_uint2(cvt_pk_bf16(v4[0], v4[1]), cvt_pk_bf16(v4[2], v4[3]));
         }
-        amax = fmaxf(amax, epi_band_to_global<ES, EPI>(band, y, M, N, m0 + wm * 128 + h * 64,
-                                                       n0 + wn * 128, lane, vec));
+        // bound the loads in flight (one block's, two for few splits)
+        if (S > 4 || (j & 1)) __builtin_amdgcn_sched_barrier(0);
     }
+    float amax = epi_band_to_global<ES, EPI, kFixupRows>(band, y, M, N, m0 + wm * 128 + i * 32,
+                                                         n0 + wn * 128, lane, vec);
     if constexpr ((EPI & kEpiAmax) != 0) {
         // non-negative floats order as their bit patterns
         amax = wave_max(amax);

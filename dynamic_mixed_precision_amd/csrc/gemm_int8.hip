@@ -294,7 +294,8 @@ struct EpiScaleI8 {
 
 // The tail tiles of a split launch: the int32 partials of each tile's split
 // workgroups added in split order (exact), then the same scaled epilogue.
-// One workgroup of one wave per 128 x 128 quadrant (4 per tail tile).
+// One workgroup of one wave per 32-row slice of a 128 x 128 quadrant (16 per
+// tail tile).
 template <int OUT, int EPI, int S>
 __global__ __launch_bounds__(64) void gemm_i8_fixup_kernel(
     const float *__restrict__ sa, const float *__restrict__ sw, int64_t M, int64_t N,
@@ -302,13 +303,14 @@ __global__ __launch_bounds__(64) void gemm_i8_fixup_kernel(
     SplitPlan sp, const uint32_t *__restrict__ spart) {
     using namespace gdma;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds8[];
-    const int lane = threadIdx.x, wave = blockIdx.x & 3;
-    const unsigned t = blockIdx.x >> 2, pid = sp.full + t;
+    // workgroup = (tail tile t, quadrant wave, 32-row slice i)
+    const int lane = threadIdx.x, i = blockIdx.x & 3, wave = (blockIdx.x >> 2) & 3;
+    const unsigned t = blockIdx.x >> 4, pid = sp.full + t;
     const TileCoord tc = tile_at(pid, tiles_m, tiles_n, GROUP_M);
     const int64_t m0 = (int64_t)tc.m * BM, n0 = (int64_t)tc.n * BN;
     EpiScaleI8 sc(sa, sw, M, N, n0 + (wave & 1) * 128 + 4 * (lane >> 5));
     split_fixup_epilogue<OUT, EPI, int, S>(spart + (size_t)t * S * kSplitWords, sc, lds8, M, N, m0, n0, wave,
-                                           lane, y, (EPI & kEpiAmax) ? partial + pid : nullptr);
+                                           i, lane, y, (EPI & kEpiAmax) ? partial + pid : nullptr);
 }
 
 template <class KernelFn>
@@ -355,8 +357,8 @@ static hipError_t launch_i8_paths(hipStream_t s, const int8_t *qa, const float *
                                M, N, K, utm, utn, sp, spart, (EPI & kEpiAmax) ? partial : nullptr);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
-            const dim3 fg(4 * sp.tail), fb(64);
-            const size_t fl = EpiBand<OUT == 1 ? 2 : 4>::BYTES;
+            const dim3 fg(16 * sp.tail), fb(64);
+            const size_t fl = (size_t)kFixupRows * EpiBand<OUT == 1 ? 2 : 4>::STRIDE;
             const uint32_t *cp = spart;
 #define DMPQ_I8_FIX(S_)                                                                          \
     case S_:                                                                                     \
