@@ -27,10 +27,12 @@ before timing; weights are prepared once, outside the timed region.
 
 Prints one JSON line.  value = qGEMM tera-ops per second of the whole step
 (all GEMM ops of the step / step wall time).  Inside the timed region HIP
-events on the launch stream bracket the GEMM calls, which give the dominant
-kernel's per-launch duration (the roofline); the per-kernel table comes from
-as many further steps with events around every call (an event record costs
-several microseconds of GPU time, so the timed region keeps them few).
+events on the launch stream bracket the calls of the GEMM with the most time
+in the warmup steps (the dominant kernel), which give its per-launch duration
+(the roofline); the per-kernel table comes from as many further steps with
+events around every call.  An event record leaves the GPU idle for a few
+microseconds, so the timed region keeps them few and uses events without the
+system-scope fence.
 """
 from __future__ import annotations
 
@@ -68,6 +70,9 @@ def parse():
                    help="on: the GEMMs get the full workspace, so the last partial wave of tiles is "
                         "split along K; off: a workspace with room for the fused-amax maxima only")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--events", choices=["nofence", "torch"], default="nofence",
+                   help="timing events: HIP events without the system-scope fence (default), "
+                        "or default torch.cuda events")
     p.add_argument("--cpu-rows", type=int, default=512,
                    help="rows of the qkv linear the oracle runs for the CPU baseline")
     p.add_argument("--calibrate-mib", type=int, default=0,
@@ -84,24 +89,86 @@ def parse():
     return p.parse_args()
 
 
+class HipTimingEvent:
+    """A HIP event for timing only, created with hipEventDisableSystemFence:
+    recording it skips the system-scope cache writeback and invalidation that
+    a default event performs, which otherwise leaves the GPU idle for several
+    microseconds at every record.  Same record / elapsed_time interface as
+    torch.cuda.Event; recorded on torch's current stream.  Reading a time
+    needs a device synchronization first (the bench synchronizes before it
+    reads any)."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+    _hip = None
+
+    @classmethod
+    def _lib(cls):
+        if cls._hip is None:
+            import ctypes as C
+            # the HIP runtime this process already uses (torch's), not a second copy
+            path = None
+            with open("/proc/self/maps") as f:
+                for line in f:
+                    if "libamdhip64.so" in line:
+                        path = line.split()[-1]
+                        break
+            if path is None:
+                raise RuntimeError("libamdhip64 is not loaded in this process")
+            h = C.CDLL(path)
+            h.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
+            h.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+            h.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+            h.hipEventDestroy.argtypes = [C.c_void_p]
+            cls._hip = h
+        return cls._hip
+
+    def __init__(self, torch):
+        import ctypes as C
+        self.torch = torch
+        self.ev = C.c_void_p()
+        if self._lib().hipEventCreateWithFlags(C.byref(self.ev), self.DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self):
+        if self._lib().hipEventRecord(self.ev, self.torch.cuda.current_stream().cuda_stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, end) -> float:
+        import ctypes as C
+        ms = C.c_float()
+        if self._lib().hipEventElapsedTime(C.byref(ms), self.ev, end.ev) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self.ev:
+            self._hip.hipEventDestroy(self.ev)
+
+
 class KernelTimer:
     """HIP events around library calls on the current stream.  The events are
     created before timing starts (prepare), so a timed call costs only its two
     event records; `only` restricts the events to the named calls (None: every
-    call).  Event records are not free (several us each), so the timed region
-    brackets only the GEMM calls and a separate pass times every call."""
+    call).  Event records are not free, so the timed region brackets only the
+    GEMM calls and a separate pass times every call.  kind "nofence": timing
+    events without the system-scope fence (HipTimingEvent); "torch": default
+    torch.cuda events."""
 
-    def __init__(self, torch):
+    def __init__(self, torch, kind="nofence"):
         self.torch = torch
+        self.kind = kind
         self.rec = {}
         self.on = False
         self.only = None
         self.calls = 0          # calls that would be timed, counted while off
         self.pool = []
 
+    def _event(self):
+        if self.kind == "torch":
+            return self.torch.cuda.Event(enable_timing=True)
+        return HipTimingEvent(self.torch)
+
     def prepare(self, n):
-        ev = self.torch.cuda.Event
-        self.pool = [(ev(enable_timing=True), ev(enable_timing=True)) for _ in range(n)]
+        self.pool = [(self._event(), self._event()) for _ in range(n)]
         self.pool.reverse()
         self.rec = {}
 
@@ -114,8 +181,7 @@ class KernelTimer:
         if self.pool:
             s, e = self.pool.pop()
         else:
-            s = self.torch.cuda.Event(enable_timing=True)
-            e = self.torch.cuda.Event(enable_timing=True)
+            s, e = self._event(), self._event()
         s.record()
         fn(*a, **kw)
         e.record()
@@ -226,7 +292,7 @@ def main():
     torch.cuda.synchronize()
     setup_s = time.time() - t0
 
-    kt = KernelTimer(torch)
+    kt = KernelTimer(torch, args.events)
     pdr_ratio = [None] * n_blocks
     gemm_ops_step = 0
     routes_seen = []
@@ -309,12 +375,21 @@ def main():
         del cx, cd, co
         calib = dict(kernel=CALIB_KERNEL, elements=n, read_bytes=4 * n, write_bytes=2 * n)
 
-    # the timed region brackets the GEMM calls (the dominant-kernel
-    # candidates) with events; every other call runs without them
+    # Warmup brackets the GEMM calls (the dominant-kernel candidates) with
+    # events; the timed region then brackets only the calls of the one with
+    # the most time, since every event record leaves the GPU idle for a few
+    # microseconds.  Every other call runs without events.
     kt.only = GEMM_CALLS
+    kt.on = True
     for _ in range(args.warmup):
-        kt.calls = 0
         step()
+    torch.cuda.synchronize()
+    kt.on = False
+    warm = kt.summary(max(args.warmup, 1))
+    if warm:
+        kt.only = {max(warm, key=lambda n: warm[n]["total_ms"])}
+    kt.calls = 0
+    step()  # counts the calls to bracket per step (one more untimed step)
     kt.prepare(kt.calls * args.steps)
     torch.cuda.synchronize()
     kt.on = True
@@ -409,6 +484,8 @@ def main():
         "act_quant_GBps": round(q_bytes * 1e-9 / (q_ms * 1e-3), 1),
         "kernels": kernels,
         "kernels_note": "per-call HIP events on every call, in as many untimed steps after the timed region",
+        "timing_events": ("HIP events without the system-scope fence" if args.events == "nofence"
+                          else "torch.cuda events"),
         "kernels_by_shape": by_shape,
         "roofline": roofline,
         "setup_s": round(setup_s, 1),
