@@ -277,6 +277,7 @@ def main():
     # per block: S1, S2 at [b, 0:2] and the outlier count at [b, 2] (rows of
     # 32 bytes keep every device pointer 16-byte aligned)
     gsums_host = torch.zeros((n_blocks, 4), dtype=torch.float64).pin_memory()
+    gsums_np = gsums_host.numpy()  # the same pinned memory: numpy indexing costs far less on the host
     gsums = torch.zeros((n_blocks, 4), dtype=torch.float64, device="cuda")
     ws_out = dm.new_workspace(dm.OP_OUTLIER)
     fuse = args.fuse_ffn == "on"
@@ -308,14 +309,13 @@ def main():
                    gsums[b, 2:3], ws_out, _shape=f"{M}x{H}")
         gsums_host.copy_(gsums, non_blocking=True)
         torch.cuda.current_stream().synchronize()
-        routes = [dm.gate_and_route(gsums_host[b, :2].numpy(), alpha, beta, tau)[2]
+        routes = [dm.gate_and_route(gsums_np[b, :2], alpha, beta, tau)[2]
                   for b in range(n_blocks)]
         if pdr is not None:
             for b in range(n_blocks):
-                if dm.pdr_decide(float(gsums_host[b, 2]), M * H, pdr[1]):
+                if dm.pdr_decide(float(gsums_np[b, 2]), M * H, pdr[1]):
                     routes[b] = np.full(len(routes[b]), dm.ROUTE_BF16, np.uint8)
-                pdr_ratio[b] = float(gsums_host[b, 2]) / (M * H)
-        routes_seen.append([r.tolist() for r in routes])
+                pdr_ratio[b] = float(gsums_np[b, 2]) / (M * H)
         ops = 0
         # 2. quantized linears at the routed precision
         for b, blk in enumerate(blocks):
@@ -362,6 +362,7 @@ def main():
                blk["x_out"], blk["delta"], blk["delta_valid"], tsums[b], ws, _shape=f"{M}x{H}")
             blk["delta_valid"] = True
         gemm_ops_step = ops
+        routes_seen.append([r.tolist() for r in routes])  # bookkeeping, off the sync-to-launch path
 
     calib = None
     if args.calibrate_mib > 0:
