@@ -3,10 +3,13 @@
 
 One step is one pass of the whole hot path over a CogVideoX-5B-like batch
 (17776 tokens, hidden 3072, FFN 12288) of four DiT blocks:
-  1. Gamma sums of every block (its input/output at the previous step) and
-     the Purified Delta Refresh outlier count of every block input (kappa=4;
+  1. the Purified Delta Refresh outlier count of every block input (kappa=4;
      the synthetic inputs have a ratio near 0.7%, below rho=1%, so no block is
-     forced to BF16), one device->host copy of the sums, then the host router
+     forced to BF16), one device->host copy of it and of every block's Gamma
+     sums, then the host router.  The Gamma sums S1, S2 of a block's input and
+     output at the previous step are what that step's TDC refresh computed
+     (--gamma standalone adds a dmpq_gamma_sums call per block instead).  The
+     router computes
      E = alpha*Gamma+beta (alpha=1, beta=0, tau=0.2; the synthetic blocks have
      Gamma ~ 0.05, 0.40, 0.05, 0.40, so two blocks route to INT8 and two to
      NVFP4) and the PDR decision;
@@ -62,6 +65,11 @@ def parse():
     p.add_argument("--pdr", default="4,0.01", metavar="KAPPA,RHO",
                    help="Purified Delta Refresh check of every block input ('off' to skip it); "
                         "a block above rho runs its linears as BF16 GEMMs")
+    p.add_argument("--gamma", choices=["refresh", "standalone"], default="refresh",
+                   help="where the router's Gamma sums S1, S2 come from: the previous step's TDC "
+                        "refresh of the block, which computes them over the same tensors "
+                        "(default; the first step finds Gamma missing and routes INT8), or a "
+                        "dmpq_gamma_sums call per block at the step start")
     p.add_argument("--fuse-ffn", choices=["on", "off"], default="off",
                    help="on: ffn_down's input is ffn_up's output, GELU and the next NVFP4 amax are "
                         "fused into ffn_up's GEMM epilogue (needs --out-dtype bf16); off: every "
@@ -273,12 +281,13 @@ def main():
     w8_scratch = torch.empty(big, dtype=torch.int8, device="cuda")
     s8_scratch = torch.empty(max(lin.N for lin in cfg.linears), device="cuda")
     ws = dm.new_workspace(dm.OP_TDC)
-    tsums = torch.zeros((n_blocks, 4), dtype=torch.float64, device="cuda")
-    # per block: S1, S2 at [b, 0:2] and the outlier count at [b, 2] (rows of
-    # 32 bytes keep every device pointer 16-byte aligned)
-    gsums_host = torch.zeros((n_blocks, 4), dtype=torch.float64).pin_memory()
-    gsums_np = gsums_host.numpy()  # the same pinned memory: numpy indexing costs far less on the host
-    gsums = torch.zeros((n_blocks, 4), dtype=torch.float64, device="cuda")
+    # per block, one 64-byte row (every device pointer stays 16-byte aligned):
+    # [0:4] the TDC refresh's S1..S4, [4:6] the standalone Gamma sums S1, S2,
+    # [6] the PDR outlier count.  One device-to-host copy per step.
+    sums = torch.zeros((n_blocks, 8), dtype=torch.float64, device="cuda")
+    sums_host = torch.zeros((n_blocks, 8), dtype=torch.float64).pin_memory()
+    sums_np = sums_host.numpy()  # the same pinned memory: numpy indexing costs far less on the host
+    refreshed = [False] * n_blocks  # the block's refresh sums are from the previous step
     ws_out = dm.new_workspace(dm.OP_OUTLIER)
     fuse = args.fuse_ffn == "on"
     if fuse and out_dtype != dm.OUT_BF16:
@@ -300,22 +309,28 @@ def main():
 
     def step():
         nonlocal gemm_ops_step
-        # 1. Gamma predictor + router: one device->host boundary per step
+        # 1. Gamma predictor + router: one device->host boundary per step.
+        # Gamma's sums are the previous step's (the refresh computed them), or
+        # with --gamma standalone a dmpq_gamma_sums call per block.
         for b, blk in enumerate(blocks):
-            kt("gamma_sums", 4.0 * M * H, dm.gamma_sums, blk["x_in"], blk["x_out"], gsums[b, :2], ws,
-               _shape=f"{M}x{H}")
+            if args.gamma == "standalone":
+                kt("gamma_sums", 4.0 * M * H, dm.gamma_sums, blk["x_in"], blk["x_out"], sums[b, 4:6], ws,
+                   _shape=f"{M}x{H}")
             if pdr is not None:
                 kt("outlier_count", 2.0 * M * H, dm.outlier_count, blk["x_in"].view(M, H), pdr[0],
-                   gsums[b, 2:3], ws_out, _shape=f"{M}x{H}")
-        gsums_host.copy_(gsums, non_blocking=True)
+                   sums[b, 6:7], ws_out, _shape=f"{M}x{H}")
+        sums_host.copy_(sums, non_blocking=True)
         torch.cuda.current_stream().synchronize()
-        routes = [dm.gate_and_route(gsums_np[b, :2], alpha, beta, tau)[2]
-                  for b in range(n_blocks)]
+        if args.gamma == "standalone":
+            routes = [dm.gate_and_route(sums_np[b, 4:6], alpha, beta, tau)[2] for b in range(n_blocks)]
+        else:
+            routes = [dm.gate_and_route(sums_np[b, 0:2] if refreshed[b] else None, alpha, beta, tau)[2]
+                      for b in range(n_blocks)]
         if pdr is not None:
             for b in range(n_blocks):
-                if dm.pdr_decide(float(gsums_np[b, 2]), M * H, pdr[1]):
+                if dm.pdr_decide(float(sums_np[b, 6]), M * H, pdr[1]):
                     routes[b] = np.full(len(routes[b]), dm.ROUTE_BF16, np.uint8)
-                pdr_ratio[b] = float(gsums_np[b, 2]) / (M * H)
+                pdr_ratio[b] = float(sums_np[b, 6]) / (M * H)
         ops = 0
         # 2. quantized linears at the routed precision
         for b, blk in enumerate(blocks):
@@ -359,8 +374,9 @@ def main():
                        L["sw"], L["gw"], ybuf[lin.name], epi, ws_gemm, out_dtype, _shape=gshape)
             # 3. Temporal Delta Cache refresh of the block
             kt("tdc_step_refresh", 8.0 * M * H, dm.tdc_step, dm.TDC_REFRESH, blk["x_in"],
-               blk["x_out"], blk["delta"], blk["delta_valid"], tsums[b], ws, _shape=f"{M}x{H}")
+               blk["x_out"], blk["delta"], blk["delta_valid"], sums[b, 0:4], ws, _shape=f"{M}x{H}")
             blk["delta_valid"] = True
+            refreshed[b] = True
         gemm_ops_step = ops
         routes_seen.append([r.tolist() for r in routes])  # bookkeeping, off the sync-to-launch path
 
@@ -479,6 +495,8 @@ def main():
                                                     "outlier_ratio_per_block": [round(v, 5) for v in pdr_ratio]},
                    "gemm_out": args.out_dtype,
                    "int8_weights": args.int8_weights,
+                   "gamma_sums": ("the previous step's TDC refresh" if args.gamma == "refresh"
+                                  else "dmpq_gamma_sums at the step start"),
                    "ffn_fused": fuse,
                    "tail_split": args.tail_split == "on",
                    "gemm_tera_ops_per_step": round(gemm_ops_step / 1e12, 3)},
