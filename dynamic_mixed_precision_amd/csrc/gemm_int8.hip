@@ -261,7 +261,7 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_split_kernel(
 }
 
 // Output scaling of the INT8 fixup: y = (float(acc) * sA[row]) * sW[col],
-// bit-exact in fp32.  c0: first output column of the lane's (j, g) groups.
+// bit-exact in fp32.
 struct EpiScaleI8 {
     const float *sa;
     int64_t M;
