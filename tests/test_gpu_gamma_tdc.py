@@ -144,3 +144,31 @@ def test_tdc_schedule_lockstep(orc):
         x = workloads.to_bf16_bits(workloads.bf16_bits_to_f32(x) + np.float32(0.01) *
                                    rng.standard_normal((M, H)).astype(np.float32))
     assert 0 < sum(pattern) < len(pattern), pattern
+
+
+@pytest.mark.parametrize("n", [1000, 17776 * 3072])
+def test_refresh_sums_are_gamma_sums(orc, n):
+    """A REFRESH returns S1 = sum |out - in| and S2 = sum |in| over the same
+    tensors as dmpq_gamma_sums, so the next step's router can take Gamma from
+    it (the bench's default).  The two kernels add in different orders: each
+    is within 1e-6 of the oracle, so within 2e-6 of each other, and the oracle
+    itself defines both sums alike."""
+    require_gpu()
+    say(f"refresh sums vs gamma sums n={n}")
+    rng = np.random.default_rng(n + 5)
+    xi = workloads.activations(rng, 1, n, n_out=0).ravel()
+    xo = workloads.perturbed_output(rng, xi.reshape(1, -1), 0.2).ravel()
+    g = _gpu_gamma(xi, xo)
+    s = torch.zeros(4, dtype=torch.float64, device="cuda")
+    dm.tdc_step(dm.TDC_REFRESH, dev(xi), dev(xo), dev(np.zeros(n, np.uint16)), False, s,
+                dm.new_workspace(dm.OP_TDC))
+    torch.cuda.synchronize()
+    r = host(s)[:2]
+    assert np.all(np.abs(r - g) <= 2 * REL * np.abs(g)), (r, g)
+    d_ref = np.zeros(n, np.uint16)
+    assert np.array_equal(orc.tdc_refresh(xi, xo, d_ref, False)[:2], orc.gamma_sums(xi, xo))
+    alpha, beta = np.ones(4), np.zeros(4)
+    gamma = g[0] / g[1]
+    for tau in (0.5 * gamma, 2.0 * gamma):
+        assert np.array_equal(dm.gate_and_route(g, alpha, beta, tau)[2],
+                              dm.gate_and_route(r, alpha, beta, tau)[2])
