@@ -124,6 +124,40 @@ def _ptr(t) -> int | None:
     return t.data_ptr()
 
 
+_OUT_BYTES = {OUT_F32: 4, OUT_BF16: 2, OUT_I32: 4}
+
+
+def _need(t, name: str, nbytes: int, esize: int | None = None) -> None:
+    """The C entry points take bare device pointers, so the sizes they will
+    read and write are checked here: raise ValueError unless tensor ``t`` holds
+    at least ``nbytes`` bytes (and, with ``esize``, has elements of that size)."""
+    if t is None:
+        raise ValueError(f"{name} is missing")
+    if esize is not None and t.element_size() != esize:
+        raise ValueError(f"{name} has {t.element_size()}-byte elements, needs {esize}-byte ones")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name} holds {have} bytes, needs {nbytes}")
+
+
+def _need_out(y, M: int, N: int, out_dtype: int) -> None:
+    if out_dtype in _OUT_BYTES:  # an unknown type is the library's error to report
+        _need(y, "y", M * N * _OUT_BYTES[out_dtype], _OUT_BYTES[out_dtype])
+
+
+def _need_nvfp4(codes, scales, g, rows: int, K: int, what: str) -> None:
+    """An NVFP4 operand of `rows` x K: K/2 code bytes and K/16 scale bytes per
+    row, one fp32 tensor scale."""
+    _need(codes, f"{what} codes", rows * K // 2, 1)
+    _need(scales, f"{what} scales", rows * K // 16, 1)
+    _need(g, f"{what} tensor scale", 4, 4)
+
+
+def _need_k(w, K: int, what: str) -> None:
+    if len(w.shape) != 2 or w.shape[1] != K:
+        raise ValueError(f"{what} has shape {tuple(w.shape)}, needs {K} per row")
+
+
 def last_error() -> str:
     return lib().dmpq_last_error().decode()
 
@@ -143,6 +177,10 @@ def new_workspace(op: int, device="cuda", M: int = 0, K: int = 0):
 
 
 def gamma_sums(x_in, x_out, sums, ws, stream=None) -> None:
+    n = x_in.numel()
+    _need(x_in, "x_in", 2 * n, 2)
+    _need(x_out, "x_out", 2 * n, 2)
+    _need(sums, "sums", 16, 8)
     _check(lib().dmpq_gamma_sums(_stream(stream), _ptr(x_in), _ptr(x_out), x_in.numel(),
                                  _ptr(sums), _ptr(ws), ws.numel()), "dmpq_gamma_sums")
 
@@ -166,28 +204,63 @@ def gate_and_route(sums2, alpha, beta, tau: float):
 
 def hadamard_quant_int8(x, q, s_row, flags: int = 0, stream=None) -> None:
     M, K = x.shape
+    _need(x, "x", 2 * M * K, 2)
+    _need(q, "q", M * K, 1)
+    _need(s_row, "s_row", 4 * M, 4)
     _check(lib().dmpq_hadamard_quant_int8(_stream(stream), _ptr(x), M, K, flags, _ptr(q),
                                           _ptr(s_row)), "dmpq_hadamard_quant_int8")
 
 
 def hadamard_quant_nvfp4(x, codes, scales, g, ws, flags: int = 0, stream=None) -> None:
     M, K = x.shape
+    _need(x, "x", 2 * M * K, 2)
+    _need_nvfp4(codes, scales, g, M, K, "output")
     _check(lib().dmpq_hadamard_quant_nvfp4(_stream(stream), _ptr(x), M, K, flags, _ptr(codes),
                                            _ptr(scales), _ptr(g), _ptr(ws), ws.numel()),
            "dmpq_hadamard_quant_nvfp4")
 
 
-def qgemm_int8(qa, sa, qw, sw, y, out_dtype: int = OUT_F32, stream=None) -> None:
+def _need_int8_gemm(qa, sa, qw, sw, y, out_dtype):
     M, K = qa.shape
     N = qw.shape[0]
+    _need(qa, "qa", M * K, 1)
+    _need(sa, "sa", 4 * M, 4)
+    _need_k(qw, K, "qw")
+    _need(qw, "qw", N * K, 1)
+    _need(sw, "sw", 4 * N, 4)
+    _need_out(y, M, N, out_dtype)
+    return M, N, K
+
+
+def _need_nvfp4_gemm(ca, sa, ga, cw, sw, gw, y, out_dtype):
+    M, K = ca.shape[0], 2 * ca.shape[1]
+    N = cw.shape[0]
+    _need_nvfp4(ca, sa, ga, M, K, "activation")
+    _need_k(cw, K // 2, "cw")
+    _need_nvfp4(cw, sw, gw, N, K, "weight")
+    _need_out(y, M, N, out_dtype)
+    return M, N, K
+
+
+def _need_bf16_gemm(x, w, y, out_dtype):
+    M, K = x.shape
+    N = w.shape[0]
+    _need(x, "x", 2 * M * K, 2)
+    _need_k(w, K, "w")
+    _need(w, "w", 2 * N * K, 2)
+    _need_out(y, M, N, out_dtype)
+    return M, N, K
+
+
+def qgemm_int8(qa, sa, qw, sw, y, out_dtype: int = OUT_F32, stream=None) -> None:
+    M, N, K = _need_int8_gemm(qa, sa, qw, sw, y, out_dtype)
     _check(lib().dmpq_qgemm_int8(_stream(stream), _ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), M, N, K,
                                  out_dtype, _ptr(y)), "dmpq_qgemm_int8")
 
 
 def qgemm_nvfp4(ca, sa, ga, cw, sw, gw, y, out_dtype: int = OUT_F32,
                 variant: int = FP4_BF16_DEQUANT, stream=None) -> None:
-    M, K = ca.shape[0], 2 * ca.shape[1]
-    N = cw.shape[0]
+    M, N, K = _need_nvfp4_gemm(ca, sa, ga, cw, sw, gw, y, out_dtype)
     _check(lib().dmpq_qgemm_nvfp4(_stream(stream), _ptr(ca), _ptr(sa), _ptr(ga), _ptr(cw),
                                   _ptr(sw), _ptr(gw), M, N, K, out_dtype, _ptr(y), variant),
            "dmpq_qgemm_nvfp4")
@@ -208,6 +281,11 @@ def tdc_decide(st: TdcState, eps_sim: float, delta_acc: float) -> bool:
 
 def tdc_step(mode: int, x_in, x_out, delta, delta_valid: bool, sums=None, ws=None,
              stream=None) -> None:
+    n = x_in.numel()
+    for t, name in ((x_in, "x_in"), (x_out, "x_out"), (delta, "delta")):
+        _need(t, name, 2 * n, 2)
+    if mode == TDC_REFRESH:
+        _need(sums, "sums", 32, 8)
     _check(lib().dmpq_tdc_step(_stream(stream), mode, _ptr(x_in), _ptr(x_out), _ptr(delta),
                                x_in.numel(), int(delta_valid), _ptr(sums), _ptr(ws),
                                0 if ws is None else ws.numel()), "dmpq_tdc_step")
@@ -223,6 +301,10 @@ def tdc_commit(st: TdcState, mode: int, sums4=None) -> None:
 def prep_weight(w, cw, sw, gw, qw, sw_row, ws, int8_mode: int = W8_FROM_NVFP4,
                 stream=None) -> None:
     N, K = w.shape
+    _need(w, "w", 2 * N * K, 2)
+    _need_nvfp4(cw, sw, gw, N, K, "weight")
+    _need(qw, "qw", N * K, 1)
+    _need(sw_row, "sw_row", 4 * N, 4)
     _check(lib().dmpq_prep_weight(_stream(stream), _ptr(w), N, K, int8_mode, _ptr(cw), _ptr(sw),
                                   _ptr(gw), _ptr(qw), _ptr(sw_row), _ptr(ws), ws.numel()),
            "dmpq_prep_weight")
@@ -231,6 +313,9 @@ def prep_weight(w, cw, sw, gw, qw, sw_row, ws, int8_mode: int = W8_FROM_NVFP4,
 def weight_int8_from_nvfp4(cw, sw, gw, qw, sw_row, stream=None) -> None:
     """INT8 weight (qw, sw_row) from the NVFP4 weight (cw, sw, gw)."""
     N, K = cw.shape[0], 2 * cw.shape[1]
+    _need_nvfp4(cw, sw, gw, N, K, "weight")
+    _need(qw, "qw", N * K, 1)
+    _need(sw_row, "sw_row", 4 * N, 4)
     _check(lib().dmpq_weight_int8_from_nvfp4(_stream(stream), _ptr(cw), _ptr(sw), _ptr(gw), N, K,
                                              _ptr(qw), _ptr(sw_row)), "dmpq_weight_int8_from_nvfp4")
 
@@ -238,6 +323,8 @@ def weight_int8_from_nvfp4(cw, sw, gw, qw, sw_row, stream=None) -> None:
 def outlier_count(x, kappa: float, count, ws, stream=None) -> None:
     """PDR outlier count of x [M x K] bf16 (as int16 bits) into count (fp64[1])."""
     M, K = x.shape
+    _need(x, "x", 2 * M * K, 2)
+    _need(count, "count", 8, 8)
     _check(lib().dmpq_outlier_count(_stream(stream), _ptr(x), M, K, float(kappa), _ptr(count),
                                     _ptr(ws), ws.numel()), "dmpq_outlier_count")
 
@@ -250,8 +337,7 @@ def pdr_decide(count: float, n: int, rho: float) -> bool:
 
 def gemm_bf16(x, w, y, out_dtype: int = OUT_F32, stream=None) -> None:
     """Full-precision linear y = x w^T over bf16 operands (fp32 accumulation)."""
-    M, K = x.shape
-    N = w.shape[0]
+    M, N, K = _need_bf16_gemm(x, w, y, out_dtype)
     _check(lib().dmpq_gemm_bf16(_stream(stream), _ptr(x), _ptr(w), M, N, K, out_dtype, _ptr(y)),
            "dmpq_gemm_bf16")
 
@@ -264,8 +350,7 @@ def qgemm_int8_ex(qa, sa, qw, sw, y, epilogue: int = 0, ws=None, out_dtype: int 
                   stream=None) -> None:
     """qgemm_int8 with a producer epilogue (EPI_GELU, EPI_NVFP4_AMAX); with an
     OP_GEMM workspace the last partial wave of tiles is split along K."""
-    M, K = qa.shape
-    N = qw.shape[0]
+    M, N, K = _need_int8_gemm(qa, sa, qw, sw, y, out_dtype)
     _check(lib().dmpq_qgemm_int8_ex(_stream(stream), _ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), M, N,
                                     K, out_dtype, _ptr(y), epilogue, *_ws(ws)),
            "dmpq_qgemm_int8_ex")
@@ -275,8 +360,7 @@ def qgemm_nvfp4_ex(ca, sa, ga, cw, sw, gw, y, epilogue: int = 0, ws=None, out_dt
                    stream=None) -> None:
     """qgemm_nvfp4 (BF16-dequant variant) with a producer epilogue and the
     optional tail split."""
-    M, K = ca.shape[0], 2 * ca.shape[1]
-    N = cw.shape[0]
+    M, N, K = _need_nvfp4_gemm(ca, sa, ga, cw, sw, gw, y, out_dtype)
     _check(lib().dmpq_qgemm_nvfp4_ex(_stream(stream), _ptr(ca), _ptr(sa), _ptr(ga), _ptr(cw),
                                      _ptr(sw), _ptr(gw), M, N, K, out_dtype, _ptr(y), epilogue,
                                      *_ws(ws)),
@@ -286,8 +370,7 @@ def qgemm_nvfp4_ex(ca, sa, ga, cw, sw, gw, y, epilogue: int = 0, ws=None, out_dt
 def gemm_bf16_ex(x, w, y, epilogue: int = 0, ws=None, out_dtype: int = OUT_BF16,
                  stream=None) -> None:
     """gemm_bf16 with a producer epilogue and the optional tail split."""
-    M, K = x.shape
-    N = w.shape[0]
+    M, N, K = _need_bf16_gemm(x, w, y, out_dtype)
     _check(lib().dmpq_gemm_bf16_ex(_stream(stream), _ptr(x), _ptr(w), M, N, K, out_dtype, _ptr(y),
                                    epilogue, *_ws(ws)),
            "dmpq_gemm_bf16_ex")

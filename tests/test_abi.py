@@ -104,8 +104,15 @@ def _expect(status, fn, *args, **kw):
     assert dm.last_error()
 
 
-def test_validation_before_launch(monkeypatch):
+def _library_checks_only(monkeypatch):
+    """The fakes carry shapes but no element sizes: skip the binding's own size
+    checks so that each call reaches the library's validation."""
     monkeypatch.setattr(dm, "_stream", lambda s=None: 0)
+    monkeypatch.setattr(dm, "_need", lambda *a, **k: None)
+
+
+def test_validation_before_launch(monkeypatch):
+    _library_checks_only(monkeypatch)
     x = _Fake((4, 24))
     _expect(2, dm.hadamard_quant_int8, x, _Fake((4, 24)), _Fake((4,)))           # K % 16
     _expect(3, dm.hadamard_quant_int8, _Fake((4, 32), addr=0x10008), _Fake((4, 32)), _Fake((4,)))
@@ -137,7 +144,7 @@ def test_validation_before_launch(monkeypatch):
 def test_fused_epilogue_validation(monkeypatch):
     """Producer-epilogue GEMMs and the quantizer's given-amax flag reject
     bad combinations before any launch."""
-    monkeypatch.setattr(dm, "_stream", lambda s=None: 0)
+    _library_checks_only(monkeypatch)
     M, N, K = 300, 48, 64
     qa, sa, qw, sw = _Fake((M, K)), _Fake((M,)), _Fake((N, K)), _Fake((N,))
     y = _Fake((M, N))
@@ -189,3 +196,43 @@ def test_null_pointer_rejected():
     st = L.dmpq_hadamard_quant_int8(None, None, 4, 32, 0, None, None)
     assert st == 1 and "NULL" in dm.last_error()
     assert L.dmpq_tdc_decide(None, None, None) == 1
+
+
+def test_binding_checks_buffer_sizes(monkeypatch):
+    """The library takes bare pointers, so the binding checks that every tensor
+    holds what the call will read or write.  CPU tensors: a call whose sizes
+    pass reaches the device-pointer check instead."""
+    import torch
+    monkeypatch.setattr(dm, "_stream", lambda s=None: 0)
+    M, N, K = 8, 32, 64
+    i8 = lambda *s: torch.zeros(s, dtype=torch.int8)
+    f32 = lambda *s: torch.zeros(s, dtype=torch.float32)
+    bf = lambda *s: torch.zeros(s, dtype=torch.int16)
+    u8 = lambda *s: torch.zeros(s, dtype=torch.uint8)
+
+    def raises(match, fn, *args, **kw):
+        with pytest.raises(ValueError, match=match):
+            fn(*args, **kw)
+
+    qa, sa, qw, sw = i8(M, K), f32(M), i8(N, K), f32(N)
+    raises("GPU tensors", dm.qgemm_int8, qa, sa, qw, sw, f32(M, N))
+    raises("y holds", dm.qgemm_int8, qa, sa, qw, sw, f32(M, N - 1))
+    raises("y has 4-byte", dm.qgemm_int8, qa, sa, qw, sw, f32(M, N), out_dtype=dm.OUT_BF16)
+    raises("qw has shape", dm.qgemm_int8, qa, sa, i8(N, K - 16), sw, f32(M, N))
+    raises("sa holds", dm.qgemm_int8_ex, qa, f32(M - 1), qw, sw, bf(M, N))
+    ca, sca, g = u8(M, K // 2), u8(M, K // 16), f32(1)
+    cw, scw = u8(N, K // 2), u8(N, K // 16)
+    raises("GPU tensors", dm.qgemm_nvfp4, ca, sca, g, cw, scw, g, f32(M, N))
+    raises("weight scales holds", dm.qgemm_nvfp4, ca, sca, g, cw, u8(N, 1), g, f32(M, N))
+    raises("cw has shape", dm.qgemm_nvfp4_ex, ca, sca, g, u8(N, K), scw, g, bf(M, N))
+    raises("tensor scale", dm.qgemm_nvfp4, ca, sca, torch.zeros(0), cw, scw, g, f32(M, N))
+    raises("w has shape", dm.gemm_bf16, bf(M, K), bf(N, K + 16), f32(M, N))
+    raises("x has 1-byte", dm.hadamard_quant_int8, i8(M, K), i8(M, K), f32(M))
+    raises("q holds", dm.hadamard_quant_int8, bf(M, K), i8(M, K - 1), f32(M))
+    raises("output codes holds", dm.hadamard_quant_nvfp4, bf(M, K), u8(M, K // 4), sca, g, u8(16))
+    raises("sums holds", dm.gamma_sums, bf(64), bf(64), torch.zeros(1, dtype=torch.float64), u8(16))
+    raises("delta holds", dm.tdc_step, dm.TDC_SKIP, bf(64), bf(64), bf(63), True)
+    raises("sums is missing", dm.tdc_step, dm.TDC_REFRESH, bf(64), bf(64), bf(64), False)
+    raises("qw holds", dm.weight_int8_from_nvfp4, cw, scw, g, i8(N, K - 1), f32(N))
+    raises("sw_row holds", dm.prep_weight, bf(N, K), cw, scw, g, i8(N, K), f32(N - 1), u8(16))
+    raises("count holds", dm.outlier_count, bf(M, K), 4.0, torch.zeros(0, dtype=torch.float64), u8(16))
