@@ -220,8 +220,8 @@ def main():
         summarize_traffic(*args.summarize_traffic, args.command)
         return
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} requested, but this build runs on one GPU only "
-              "(the hot path is token-parallel; the multi-GPU sharding is design-only)",
+        print(f"bench.py: --gpus {args.gpus} requested, but the benchmark runs on one GPU only "
+              "(the hot path is token-parallel; sharding it over GPUs is not implemented)",
               file=sys.stderr)
         sys.exit(2)
 

@@ -86,7 +86,8 @@ def _run_fp4(args, M, N, ws, out=dm.OUT_F32):
 @pytest.mark.parametrize("M,N,K,sample", [(600, 528, 512, False), (600, 528, 2048, False),
                                           (4352, 4096, 1024, True),
                                           (workloads.M_480P, 3072, 12288, True),
-                                          (workloads.M_480P, 12288, 3072, True)])
+                                          (workloads.M_480P, 12288, 3072, True),
+                                          (workloads.M_480P, 3072, 3072, True)])
 def test_split_nvfp4(orc, M, N, K, sample):
     require_gpu()
     S = _splits(M, N, K // 256)
