@@ -65,6 +65,22 @@ def test_outlier_count_edges(orc):
     spike[:, 3] = [1.0, -2.0, 1e-30, 3e30]
     sb = workloads.to_bf16_bits(spike)
     assert _check_count(orc, sb, 7.95) == 4 and _check_count(orc, sb, 8.0) == 0
+    # the count compares magnitude bits with a per-row threshold: rows with an
+    # infinity or a NaN count nothing (their sum of squares is not finite),
+    # the other rows count as usual; subnormal and near-maximal magnitudes
+    rng = np.random.default_rng(11)
+    sp = workloads.activations(rng, 8, 64)
+    sp[0, 5], sp[1, 0], sp[2, 63], sp[3, 7] = 0x7F80, 0xFF80, 0x7FC0, 0xFFC1
+    sp[4] = rng.integers(0, 0x80, 64).astype(np.uint16) | (rng.integers(0, 2, 64).astype(np.uint16) << 15)
+    sp[4, 9] = 0x0070                                  # a subnormal spike
+    sp[5] = 0x7F7F                                     # the largest finite bf16, every element
+    sp[6, :] = 0x0001
+    sp[6, 3] = 0x0100                                  # the smallest subnormal, one normal spike
+    for kappa in (0.0, 1.0, 3.0, 7.9):
+        c = _check_count(orc, sp, kappa)
+        per_row = [orc.outlier_count(sp[r:r + 1], kappa) for r in range(8)]
+        assert per_row[:4] == [0, 0, 0, 0] and c == sum(per_row)
+    assert _check_count(orc, sp[6:7], 7.9) == 1 and _check_count(orc, sp[5:6], 0.5) == 64
     out = torch.full((1,), 7.0, dtype=torch.float64, device="cuda")
     dm.outlier_count(torch.empty((0, 64), dtype=torch.int16, device="cuda"), 2.0, out,
                      dm.new_workspace(dm.OP_OUTLIER))
