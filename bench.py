@@ -481,6 +481,8 @@ def main():
     roofline = dict(kernel=dom, bound=d["bound"], achieved=d["achieved"], peak=d["peak"],
                     unit=d["unit"], frac=d["frac"], traffic=None, avg_us_per_call=d["avg_us"],
                     timed_in="timed region" if dom in ktimed else "per-kernel pass")
+    if dom == "qgemm_nvfp4":  # exact NVFP4 runs on the fp16 pipe: its share of that peak too
+        roofline["frac_of_fp16_pipe"] = round(d["achieved"] / PEAK_BF16_TFLOPS, 4)
     roofline.update(measured_traffic(dom))
     q_bytes = sum(ksum[n]["work"] for n in ksum if n.startswith("hadamard_quant"))
     q_ms = sum(ksum[n]["total_ms"] for n in ksum if n.startswith("hadamard_quant"))
