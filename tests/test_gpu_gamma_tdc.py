@@ -96,6 +96,40 @@ def test_tdc_refresh_parity(orc, n, dv):
         assert s1[2] == 0 and s1[3] == 0
 
 
+def test_tdc_gamma_1080p_size(orc):
+    """The 1080p-like block input (106306 tokens x 3072 = 327 M elements), the
+    largest configuration: Gamma sums, a refresh with a valid delta, and a skip
+    at full size.  The inputs tile a seeded 8 M-element draw (the same value
+    distribution, at the full size's grid and partial-sum layout; drawing 327 M
+    values takes minutes).  The refresh's delta is compared whole, the skip
+    output, which is elementwise, on a sample of positions."""
+    require_gpu()
+    n = workloads.M_1080P * 3072
+    say(f"gamma + tdc at the 1080p size n={n}")
+    rng = np.random.default_rng(1080)
+    b = 1 << 23
+    xi0 = workloads.activations(rng, 1, b, n_out=0).ravel()
+    xo0 = workloads.perturbed_output(rng, xi0.reshape(1, -1), 0.2).ravel()
+    d0 = workloads.to_bf16_bits(0.25 * rng.standard_normal(b).astype(np.float32))
+    reps = -(-n // b)
+    xi, xo, d_prev = (np.tile(a, reps)[:n] for a in (xi0, xo0, d0))
+    assert _close(_gpu_gamma(xi, xo), orc.gamma_sums(xi, xo))
+    d_ref = d_prev.copy()
+    s0 = orc.tdc_refresh(xi, xo, d_ref, True)
+    xig, dg = dev(xi), dev(d_prev)
+    s = torch.zeros(4, dtype=torch.float64, device="cuda")
+    dm.tdc_step(dm.TDC_REFRESH, xig, dev(xo), dg, True, s, dm.new_workspace(dm.OP_TDC))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(dg, np.uint16), d_ref)
+    assert _close(host(s), s0), (host(s), s0)
+    out = empty((n,), np.uint16)
+    dm.tdc_step(dm.TDC_SKIP, xig, out, dg, True)
+    torch.cuda.synchronize()
+    idx = np.unique(np.concatenate([rng.integers(0, n, 1 << 20), np.arange(n - 64, n)]))
+    got = host(out, np.uint16)[idx]
+    assert np.array_equal(got, orc.tdc_skip(xi[idx], d_ref[idx]))
+
+
 def test_tdc_schedule_lockstep(orc):
     """A short TDC schedule where the GPU computes every device step and the
     oracle recomputes each one from the GPU's own inputs; decisions come from
