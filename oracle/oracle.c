@@ -59,6 +59,12 @@ float orc_e2m1_value(uint8_t code)
 
 uint8_t orc_e2m1_encode(float v)
 {
+    /* E2M1 has no NaN, and the pages say nothing of non-finite inputs.  The
+     * rule taken here: a NaN encodes as +0 whatever its sign bit (CPUs and
+     * GPUs give invalid operations NaNs of different signs, so a rule that
+     * kept the sign would not be portable). */
+    if (isnan(v))
+        return 0;
     uint8_t sign = signbit(v) ? 8 : 0;
     double a = fabs((double)v);
     if (a >= 6.0)
@@ -85,7 +91,11 @@ float orc_e4m3_value(uint8_t code)
 
 uint8_t orc_e4m3_encode(float v)
 {
-    /* block scales are non-negative by construction; callers pass v >= 0 */
+    /* block scales are non-negative by construction; callers pass v >= 0.
+     * A NaN (the ratio Inf/Inf of a block holding an infinity when the
+     * tensor amax is infinite) encodes as 0, a zero scale. */
+    if (isnan(v))
+        return 0;
     double a = (double)v;
     if (a >= 448.0)
         return 0x7E; /* saturate to the largest finite value */
@@ -151,6 +161,19 @@ static int bad_shape(int64_t M, int64_t K)
  * codes.
  * ==================================================================== */
 
+/* A rounded product as an INT8 code: clamped to +-127; a NaN product (a NaN
+ * input, or an infinity times the zero reciprocal of an infinite row amax)
+ * codes 0.  The amax ignores NaNs, so they never change a row's scale; a row
+ * holding an infinity gets scale +inf and all codes 0. */
+static int8_t int8_code(float r)
+{
+    if (isnan(r))
+        return 0;
+    if (r > 127.0f) r = 127.0f;
+    if (r < -127.0f) r = -127.0f;
+    return (int8_t)r;
+}
+
 int orc_quant_int8(const uint16_t *x, int64_t M, int64_t K, int flags,
                    int8_t *q, float *s_row)
 {
@@ -174,12 +197,8 @@ int orc_quant_int8(const uint16_t *x, int64_t M, int64_t K, int flags,
                 continue;
             }
             s_row[m] = a / 127.0f;
-            for (int64_t k = 0; k < K; k++) {
-                float r = rintf(row[k] * inv);
-                if (r > 127.0f) r = 127.0f;
-                if (r < -127.0f) r = -127.0f;
-                q[m * K + k] = (int8_t)r;
-            }
+            for (int64_t k = 0; k < K; k++)
+                q[m * K + k] = int8_code(rintf(row[k] * inv));
         }
         free(row);
     }
@@ -308,12 +327,8 @@ int orc_w8_from_nvfp4(const uint8_t *cw, const uint8_t *sw, const float *gw,
                 continue;
             }
             sw_row[n] = a / 127.0f;
-            for (int64_t k = 0; k < K; k++) {
-                float r = rintf(wd[k] * inv);
-                if (r > 127.0f) r = 127.0f;
-                if (r < -127.0f) r = -127.0f;
-                qw[n * K + k] = (int8_t)r;
-            }
+            for (int64_t k = 0; k < K; k++)
+                qw[n * K + k] = int8_code(rintf(wd[k] * inv));
         }
         free(wd);
     }

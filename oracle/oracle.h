@@ -49,9 +49,9 @@ int orc_max_threads(void);
 uint16_t orc_bf16_round(float f);        /* fp32 -> bf16 bits, RNE; NaN -> 0x7FC0 */
 float    orc_bf16_value(uint16_t b);     /* bf16 bits -> fp32 (exact) */
 float    orc_e2m1_value(uint8_t code);   /* 4-bit code (low nibble) -> value */
-uint8_t  orc_e2m1_encode(float v);       /* finite v -> nearest code, ties to even, saturating at 6 */
+uint8_t  orc_e2m1_encode(float v);       /* v -> nearest code, ties to even, saturating at 6; NaN -> 0 */
 float    orc_e4m3_value(uint8_t code);   /* finite OCP E4M3 (FN) code -> value */
-uint8_t  orc_e4m3_encode(float v);       /* finite v >= 0 -> nearest code, ties to even, saturating at 448 */
+uint8_t  orc_e4m3_encode(float v);       /* v >= 0 -> nearest code, ties to even, saturating at 448; NaN -> 0 */
 
 /* ---- block Hadamard -------------------------------------------------- */
 void orc_fwht16(const float in[16], float out[16]);

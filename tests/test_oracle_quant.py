@@ -274,3 +274,110 @@ def test_int8_row_without_finite_reciprocal(orc):
     assert s[0] == 0 and not q[0].any()
     assert s[1] == 0 and not q[1].any()
     assert s[2] > 0 and q[2, 7] == 127 and np.count_nonzero(q[2]) == 1
+
+
+# ---- non-finite inputs ------------------------------------------------------
+# The pages say nothing of NaN or infinity.  The rule taken (both sides): a
+# NaN encodes as code 0 (E2M1 +0, E4M3 0, INT8 0) and never enters an amax;
+# a row (INT8) or tensor (NVFP4) holding an infinity has an infinite amax,
+# which makes every reciprocal zero, so its scale is +inf and its codes 0.
+# The pins below are consequences that hold for any implementation of that
+# rule and fail for the plausible alternatives (NaN saturating to +-127 or
+# +-6, a NaN amax, a sign-keeping NaN code).
+
+_QNAN, _NQNAN, _SNAN = 0x7FC0, 0xFFC0, 0x7F81    # bf16 NaN patterns
+_PINF, _NINF = 0x7F80, 0xFF80
+
+
+def test_codecs_encode_nan_as_zero(orc):
+    for v in (float("nan"), -float("nan")):
+        assert orc.e2m1_encode(v) == 0
+        assert orc.e4m3_encode(v) == 0
+    assert orc.e2m1_encode(float("inf")) == 7 and orc.e2m1_encode(-float("inf")) == 15
+    assert orc.e4m3_encode(float("inf")) == 0x7E
+
+
+@pytest.mark.parametrize("nan", [_QNAN, _NQNAN, _SNAN])
+def test_int8_nan_element_is_a_zero(orc, nan):
+    """Without the Hadamard a NaN element codes 0 and the rest of its row
+    quantizes as if the NaN were 0 (it never sets the amax)."""
+    rng = np.random.default_rng(11)
+    x = workloads.activations(rng, 6, 64)
+    z = x.copy()
+    x[2, 5] = nan
+    z[2, 5] = 0
+    x[4, 63] = nan
+    z[4, 63] = 0
+    a = orc.quant_int8(x, flags=orc.NO_HADAMARD)
+    b = orc.quant_int8(z, flags=orc.NO_HADAMARD)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
+def test_int8_nan_spreads_over_its_hadamard_block(orc):
+    """With the Hadamard every output of a block depends on every input, so a
+    NaN makes the whole rotated block NaN: the row quantizes as if that block
+    were zero."""
+    rng = np.random.default_rng(12)
+    x = workloads.activations(rng, 4, 96)
+    z = x.copy()
+    x[1, 37] = _QNAN          # block 2 of row 1
+    z[1, 32:48] = 0
+    x[3, 0] = _NINF           # with one infinity per block every output is +-inf...
+    x[3, 1] = _PINF           # ... with two, some are inf - inf = NaN
+    a = orc.quant_int8(x)
+    b = orc.quant_int8(z)
+    assert np.array_equal(a[0][:3], b[0][:3]) and np.array_equal(a[1][:3], b[1][:3])
+    assert np.isinf(a[1][3]) and a[1][3] > 0 and not a[0][3].any()
+
+
+def test_int8_infinite_row(orc):
+    x = np.full((3, 32), 0x3F80, np.uint16)            # 1.0
+    x[1, 9] = _PINF
+    x[2, 31] = _NINF
+    q, s = orc.quant_int8(x, flags=orc.NO_HADAMARD)
+    assert s[0] == np.float32(1) / np.float32(127) and np.all(q[0] == 127)
+    for r in (1, 2):
+        assert s[r] == np.inf and not q[r].any()
+
+
+@pytest.mark.parametrize("flags", [0, 1])
+def test_nvfp4_nan_element_is_a_zero(orc, flags):
+    """A NaN never sets the tensor or block amax and codes +0.  Without the
+    Hadamard only its own code changes; with it, its whole block quantizes as a
+    zero block (scale 0, codes 0)."""
+    rng = np.random.default_rng(13)
+    x = workloads.activations(rng, 8, 64)
+    z = x.copy()
+    x[3, 21] = _NQNAN
+    x[6, 0] = _SNAN
+    if flags:
+        z[3, 21] = z[6, 0] = 0
+    else:
+        z[3, 16:32] = z[6, 0:16] = 0
+    a = orc.quant_nvfp4(x, flags=flags)
+    b = orc.quant_nvfp4(z, flags=flags)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2]
+
+
+@pytest.mark.parametrize("inf", [_PINF, _NINF])
+def test_nvfp4_infinite_tensor(orc, inf):
+    rng = np.random.default_rng(14)
+    x = workloads.activations(rng, 5, 48)
+    x[4, 40] = inf
+    for flags in (0, 1):
+        c, s, g = orc.quant_nvfp4(x, flags=flags)
+        assert g == np.inf and not c.any() and not s.any()
+
+
+def test_w8_from_infinite_tensor_scale(orc):
+    """An NVFP4 weight with an infinite tensor scale: every nonzero code
+    dequantizes to +-inf and every zero code to 0 * inf = NaN, so each row with
+    a nonzero code gets scale +inf; every code is 0."""
+    rng = np.random.default_rng(15)
+    N, K = 4, 32
+    cw = rng.integers(0, 256, (N, K // 2)).astype(np.uint8)
+    cw[3] = 0
+    sw = rng.integers(1, 0x7F, (N, K // 16)).astype(np.uint8)
+    q, s = orc.w8_from_nvfp4(cw, sw, np.float32(np.inf))
+    assert np.all(s[:3] == np.inf) and not q.any()
+    assert s[3] == 0               # all NaN: the amax stays 0, a zero row
