@@ -111,6 +111,17 @@ double rel_ratio(double num, double den) {
 
 }  // namespace
 
+namespace dmpq {
+// For entry points defined in other translation units.
+dmpq_status set_last_error(dmpq_status code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+}  // namespace dmpq
+
 extern "C" {
 
 const char *dmpq_last_error(void) { return g_err; }

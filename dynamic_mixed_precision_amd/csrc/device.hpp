@@ -1,6 +1,6 @@
 // device.hpp -- device helpers for the gfx950 kernels of libdmpq: bf16 bit
-// conversions, the 16-point block Hadamard in registers, E4M3 / E2M1
-// encoders, wave reductions.  Compiled with -ffp-contract=off so every fp32
+// conversions, the 16-point block Hadamard in registers, the E4M3 codec,
+// wave reductions.  Compiled with -ffp-contract=off so every fp32
 // expression below is a sequence of single IEEE round-to-nearest-even ops.
 #pragma once
 
@@ -91,9 +91,11 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
     return (c & 0x80u) ? -mag : mag;
 }
 
-// Non-negative finite v -> nearest E4M3 code, ties to even, saturating to 448.
+// Non-negative v -> nearest E4M3 code, ties to even, saturating to 448; a NaN
+// (Inf/Inf: a block holding an infinity of a tensor whose amax is infinite)
+// encodes as 0, a zero scale.
 __device__ __forceinline__ uint32_t e4m3_encode_nonneg(float v) {
-    if (v >= 448.0f) return 0x7Eu;
+    if (!(v < 448.0f)) return v >= 448.0f ? 0x7Eu : 0u;
     if (v < 0.015625f) {                      // below 2^-6: subnormal grid m * 2^-9
         return (uint32_t)__builtin_rintf(v * 512.0f);  // 0..8 (8 = 2^-6, the first normal)
     }
@@ -101,17 +103,6 @@ __device__ __forceinline__ uint32_t e4m3_encode_nonneg(float v) {
     u += 0x7FFFFu + ((u >> 20) & 1u);         // RNE at mantissa bit 20
     uint32_t code = (u >> 20) - (120u << 3);  // rebias 127 -> 7, keep 3 mantissa bits
     return code > 0x7Eu ? 0x7Eu : code;
-}
-
-// ---- E2M1 (1 sign, 2 exponent bias 1, 1 mantissa): 0 .5 1 1.5 2 3 4 6 -------
-// Nearest magnitude with ties to the even code, saturating at 6: count the
-// decision boundaries at or below |v| (strict at ties that round down).
-__device__ __forceinline__ uint32_t e2m1_encode(float v) {
-    float a = __builtin_fabsf(v);
-    uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                 (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-                 (uint32_t)(a > 5.0f);
-    return c | ((__float_as_uint(v) >> 28) & 8u);
 }
 
 // ---- wave reductions --------------------------------------------------------

@@ -26,6 +26,9 @@ hipError_t launch_hq_int8(hipStream_t s, const uint16_t *x, int64_t M, int64_t K
                           int8_t *q, float *s_row);
 hipError_t launch_hq_nvfp4(hipStream_t s, const uint16_t *x, int64_t M, int64_t K, int flags,
                            uint8_t *codes, uint8_t *scales, float *g, const Workspace &ws);
+// Partial maxima (floats) the first pass of launch_hq_nvfp4 writes without
+// DMPQ_AMAX_GIVEN: one per workgroup, at most 1024 whatever the size.
+int64_t hq_nvfp4_partials(int64_t M, int64_t K);
 // Output tiles of the GEMMs (256 x 256 on every path that takes an epilogue):
 // the number of per-tile maxima a fused-amax GEMM writes.
 inline int64_t gemm_tiles(int64_t M, int64_t N) { return ((M + 255) / 256) * ((N + 255) / 256); }

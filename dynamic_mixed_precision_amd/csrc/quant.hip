@@ -33,8 +33,6 @@ struct Bf16Rows {
         unpack16(a0, a1, v);
         if (!(flags & 1)) fwht16(v);
     }
-    // bf16 rows may hold infinities and NaNs: always the clamped rounding
-    __device__ __forceinline__ bool all_finite() const { return false; }
 };
 
 // Source of a row's 16-blocks: an NVFP4 weight dequantized to
@@ -67,28 +65,22 @@ struct Nvfp4Rows {
             v[2 * i + 1] = (hi * s) * gg;
         }
     }
-    // |E2M1 * E4M3| <= 6 * 480, so every value is finite when |g| <= 2^100
-    __device__ __forceinline__ bool all_finite() const { return __builtin_fabsf(*g) <= 0x1p100f; }
 };
 
-// Codes of one 16-block, q = RNE(v * inv) as bytes, two ways with the same
-// result for finite v.  Clamped: rint, clamp to +-127, convert.  Magic: for
-// |v| <= amax, |fl(v * inv)| < 127.5 (inv = fl(127/amax), two roundings of
-// at most 2^-24 each), so the clamp never acts; adding 1.5 * 2^23 rounds
-// fl(v * inv) to an integer in the low mantissa bits (ties to even, as
-// rint), whose low byte is the two's-complement code.  Two operations per
-// value plus the byte packing, against about five.
-__device__ __forceinline__ uint4 int8_codes_clamped(const float v[16], float inv) {
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int j = 0; j < 16; j++) {
-        float r = __builtin_rintf(v[j] * inv);
-        r = fminf(fmaxf(r, -127.0f), 127.0f);
-        w[j >> 2] |= ((uint32_t)(int)r & 0xFFu) << (8 * (j & 3));
-    }
-    return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
+// Codes of one 16-block, q = RNE(v * inv) as bytes.  For |v| <= amax,
+// |fl(v * inv)| < 127.5 (inv = fl(127/amax), two roundings of at most 2^-24
+// each), so no clamp is needed; adding 1.5 * 2^23 rounds fl(v * inv) to an
+// integer in the low mantissa bits (ties to even, as rint), whose low byte
+// is the two's-complement code.  Every value of a row satisfies the bound,
+// because amax is the row's maximum.  Non-finite values follow the library's
+// rule: a NaN product (a NaN input, or an infinity times the zero reciprocal
+// of a row whose amax is infinite) stays NaN through the add, keeping its
+// payload, and it codes 0 when the payload's low byte is zero.  That holds
+// for every NaN of a row that is not a zero row: bf16 data carries 16 zero
+// low bits, and invalid operations make the default NaN.  (A NaN tensor
+// scale of an NVFP4 weight makes every value of a row NaN, so the row is a
+// zero row, which the caller stores as zeros.)  Two operations per value
+// plus the byte packing.
 __device__ __forceinline__ uint4 int8_codes_magic(const float v[16], float inv) {
     uint32_t t[16];
 #pragma unroll
@@ -152,18 +144,14 @@ __global__ __launch_bounds__(256) void row_quant_int8_kernel(Src src, int64_t M,
     if (zero_row) inv = 0.0f;
     if (lr == 0) s_row[row] = zero_row ? 0.0f : amax / 127.0f;
     int8_t *qr = q + row * K;
-    if (src.all_finite()) {  // uniform across the grid
 #pragma unroll
-        for (int i = 0; i < BPL; i++) {
-            const int b = lr + i * LPR;
-            if (b < nblk) *reinterpret_cast<uint4 *>(qr + 16 * (int64_t)b) = int8_codes_magic(v[i], inv);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < BPL; i++) {
-            const int b = lr + i * LPR;
-            if (b < nblk) *reinterpret_cast<uint4 *>(qr + 16 * (int64_t)b) = int8_codes_clamped(v[i], inv);
-        }
+    for (int i = 0; i < BPL; i++) {
+        const int b = lr + i * LPR;
+        // a zero row stores zeros outright: its values may all be NaNs of any
+        // payload (an NVFP4 weight with a NaN tensor scale)
+        if (b < nblk)
+            *reinterpret_cast<uint4 *>(qr + 16 * (int64_t)b) =
+                zero_row ? make_uint4(0u, 0u, 0u, 0u) : int8_codes_magic(v[i], inv);
     }
 }
 
@@ -453,7 +441,18 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t *__rest
         uint4 a1 = load_nt16(p + 1);
         float v[16];
         unpack16(a0, a1, v);
-        if (!(flags & 1)) fwht16(v);
+        if (!(flags & 1)) {
+            fwht16(v);
+        } else {
+            // NaN codes +0, but the hardware converter saturates it to +-6 by
+            // sign.  A rotated block needs no care: every rotated value sums
+            // all 16 inputs, so a NaN makes the whole block NaN, its amax 0
+            // and its codes the zero-scale zeros.  Unrotated (a test hook),
+            // a NaN sits among finite values and is replaced by +0 here
+            // (the amax ignores NaNs either way).
+#pragma unroll
+            for (int j = 0; j < 16; j++) v[j] = (v[j] == v[j]) ? v[j] : 0.0f;
+        }
         float ab = 0.0f;
 #pragma unroll
         for (int j = 0; j < 16; j++) ab = fmaxf(ab, __builtin_fabsf(v[j]));
@@ -495,6 +494,10 @@ __global__ __launch_bounds__(1024) void amax_fold_kernel(float *__restrict__ par
     }
 }
 
+int64_t hq_nvfp4_partials(int64_t M, int64_t K) {
+    return stride_grid(M * (K / 16), 256 * 4, kAmaxGroups);
+}
+
 hipError_t launch_hq_nvfp4(hipStream_t s, const uint16_t *x, int64_t M, int64_t K, int flags,
                            uint8_t *codes, uint8_t *scales, float *g, const Workspace &ws) {
     const int64_t nblocks = M * (K / 16);
@@ -504,7 +507,7 @@ hipError_t launch_hq_nvfp4(hipStream_t s, const uint16_t *x, int64_t M, int64_t 
         hipLaunchKernelGGL(amax_fold_kernel, dim3(1), dim3(1024), 0, s, partial, gemm_tiles(M, K));
         nparts = 1;
     } else {
-        nparts = stride_grid(nblocks, 256 * 4, kAmaxGroups);
+        nparts = (unsigned)hq_nvfp4_partials(M, K);
         hipLaunchKernelGGL(nvfp4_amax_kernel, dim3(nparts), dim3(256), 0, s, x, nblocks, flags, partial);
     }
     hipError_t e = hipGetLastError();

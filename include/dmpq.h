@@ -27,8 +27,14 @@
  *   - Every device tensor pointer must be 16-byte aligned.  K must be a
  *     positive multiple of 16 (the Hadamard block and the NVFP4 scale group).
  *     M, N >= 0 (0 is an empty no-op); a buffer of zero elements may be NULL.
- *   - Non-finite inputs (NaN, Inf) are outside the contract: results are
- *     unspecified, but every kernel still terminates.
+ *   - Non-finite inputs (the pages say nothing of them; the rule taken
+ *     here): the quantizers encode a NaN as code 0 (INT8 0, E2M1 +0, E4M3
+ *     scale 0) whatever its sign, and a NaN never enters an amax.  An
+ *     infinity makes its row's (INT8) or tensor's (NVFP4) amax infinite, so
+ *     the reciprocal is 0: scale +inf (INT8 s_row, NVFP4 g), every code 0
+ *     and every NVFP4 block scale 0.  The rotation spreads a NaN over its
+ *     16-block.  The reductions (Gamma, TDC sums, outlier count) and GEMMs
+ *     propagate IEEE results.  Every kernel terminates on any input.
  *   - Workspaces (ws) come from dmpq_workspace_bytes().  They carry
  *     per-workgroup partial results between the kernels of one call and need
  *     no initialization.  Calls that may run concurrently (different streams)

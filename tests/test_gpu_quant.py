@@ -160,9 +160,9 @@ def test_weight_int8_from_nvfp4_parity(orc, N, K):
 
 
 def test_weight_int8_from_nvfp4_random_codes(orc):
-    # arbitrary codes, every finite E4M3 scale, a tensor scale far from 1, and
-    # an all-zero row; g = 2^101 takes the kernel's clamped rounding (above
-    # 2^100 it does not assume finite values), the others its magic-number one
+    # arbitrary codes, every finite E4M3 scale, tensor scales far from 1, an
+    # all-zero row, and the non-finite tensor scales (+inf: rows of +-inf and
+    # NaN values; NaN: all-NaN rows)
     require_gpu()
     say("weight_int8_from_nvfp4 random codes")
     rng = np.random.default_rng(63)
@@ -170,7 +170,10 @@ def test_weight_int8_from_nvfp4_random_codes(orc):
     cw = rng.integers(0, 256, (N, K // 2)).astype(np.uint8)
     sw = rng.integers(0, 0x7F, (N, K // 16)).astype(np.uint8)
     cw[5] = 0
-    for g in (3.0517578e-05, 0.75, 1.7e3, 2.0 ** 101):
+    gvals = np.array([3.0517578e-05, 0.75, 1.7e3, 2.0 ** 101, 3e38, np.inf, np.nan], np.float32)
+    # and NaNs whose low payload byte is not zero (quiet and signalling)
+    gvals = np.concatenate([gvals, np.array([0x7FC000A5, 0x7F800001], np.uint32).view(np.float32)])
+    for g in gvals:
         q_ref, s_ref = orc.w8_from_nvfp4(cw, sw, g)
         qw, swr = empty((N, K), np.int8), empty((N,), np.float32)
         dm.weight_int8_from_nvfp4(dev(cw), dev(sw), dev(np.array([g], np.float32)), qw, swr)
@@ -194,3 +197,34 @@ def test_quant_subnormal_inputs(orc):
     xs = workloads.to_bf16_bits(rng.standard_normal((8, 64)).astype(np.float32) * np.float32(1e-39))
     _check_int8(orc, xs)
     _check_nvfp4(orc, xs)
+
+
+def test_quant_non_finite_inputs(orc):
+    """The non-finite rule (a NaN codes 0 and never enters an amax; an infinity
+    makes its row's or tensor's amax infinite, so its scale is +inf and its
+    codes 0), on rows with quiet and signalling NaNs of both signs, single
+    infinities (every rotated output infinite) and pairs of opposite
+    infinities in one block (NaN and infinite outputs), with and without the
+    Hadamard."""
+    require_gpu()
+    say("quant with NaN and infinite inputs")
+    rng = np.random.default_rng(64)
+    M, K = 24, 96
+    x = workloads.activations(rng, M, K)
+    nans = (0x7FC0, 0xFFC0, 0x7F81, 0xFF81, 0x7FFF)
+    for i, r in enumerate(range(0, 10, 2)):
+        x[r, 7 * i + 3] = nans[i]
+    x[11, 40] = 0x7F80
+    x[13, 50] = 0xFF80
+    x[15, 16], x[15, 17] = 0x7F80, 0xFF80
+    x[17, 32:48] = 0x7FC0
+    for flags in (0, dm.NO_HADAMARD):
+        _check_int8(orc, x, flags)
+    # NVFP4's amax is tensor-wide: NaNs alone (finite amax), then an infinity
+    xn = x.copy()
+    xn[11, 40] = xn[13, 50] = xn[15, 16] = xn[15, 17] = 0x3F80
+    for flags in (0, dm.NO_HADAMARD):
+        _check_nvfp4(orc, xn, flags)
+        _check_nvfp4(orc, x, flags)
+    c, s, g = _gpu_nvfp4(x)
+    assert g == np.inf and not c.any() and not s.any()
