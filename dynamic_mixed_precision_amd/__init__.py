@@ -378,6 +378,9 @@ def gemm_bf16_ex(x, w, y, epilogue: int = 0, ws=None, out_dtype: int = OUT_BF16,
 
 def selftest_codec(codec: int, lo: int, hi: int, stats, stream=None) -> None:
     """Per-code (lowest, highest, count) of the fp32 patterns [lo, hi) through
-    a device converter (CODEC_E4M3 or CODEC_E2M1); stats: uint32/int32 tensor."""
+    a device converter (CODEC_E4M3 or CODEC_E2M1); stats: uint32/int32 tensor
+    of 3 words per code (128 codes for E4M3, 16 for E2M1)."""
+    if codec in (CODEC_E4M3, CODEC_E2M1):  # an unknown codec is the library's error to report
+        _need(stats, "stats", 12 * (128 if codec == CODEC_E4M3 else 16), 4)
     _check(lib().dmpq_selftest_codec(_stream(stream), codec, lo, hi, _ptr(stats)),
            "dmpq_selftest_codec")

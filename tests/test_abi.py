@@ -185,7 +185,7 @@ def test_fused_epilogue_validation(monkeypatch):
 
 
 def test_selftest_validation(monkeypatch):
-    monkeypatch.setattr(dm, "_stream", lambda s=None: 0)
+    _library_checks_only(monkeypatch)
     _expect(1, dm.selftest_codec, 2, 0, 16, _Fake((384,)))
     _expect(1, dm.selftest_codec, dm.CODEC_E4M3, 16, 0, _Fake((384,)))
     _expect(1, dm.selftest_codec, dm.CODEC_E2M1, 0, 0x7F800001, _Fake((48,)))
@@ -236,3 +236,6 @@ def test_binding_checks_buffer_sizes(monkeypatch):
     raises("qw holds", dm.weight_int8_from_nvfp4, cw, scw, g, i8(N, K - 1), f32(N))
     raises("sw_row holds", dm.prep_weight, bf(N, K), cw, scw, g, i8(N, K), f32(N - 1), u8(16))
     raises("count holds", dm.outlier_count, bf(M, K), 4.0, torch.zeros(0, dtype=torch.float64), u8(16))
+    raises("stats holds", dm.selftest_codec, dm.CODEC_E4M3, 0, 16, torch.zeros(3 * 128 - 1, dtype=torch.int32))
+    raises("stats holds", dm.selftest_codec, dm.CODEC_E2M1, 0, 16, torch.zeros(3 * 16 - 1, dtype=torch.int32))
+    raises("stats has 1-byte", dm.selftest_codec, dm.CODEC_E2M1, 0, 16, u8(3 * 16 * 4))

@@ -111,3 +111,63 @@ def test_1080p_ffn_down_linear(orc, route):
     M, N, K = wl.M_1080P, 3072, 12288
     say(f"1080p-like ffn_down M={M} N={N} K={K} route={route}")
     _linear_parity(orc, np.random.default_rng(1090 + route), M, N, K, route, _rows(M, 8861))
+
+
+def _tail_tile_rows(M, N, nk, splits_from_k=True):
+    """Rows of the m-tiles that hold tail tiles of a split launch: the logical
+    tile ids full .. tiles-1 in the library's grouped order (8 tile rows per
+    group, down a group's rows before moving right)."""
+    tm, tn = -(-M // 256), -(-N // 256)
+    tiles = tm * tn
+    tail = tiles % 256
+    s = min(256 // tail, nk) if tail else 0
+    if not splits_from_k or tail == 0 or s < 2:
+        return np.zeros(0, np.int64)
+    mt = set()
+    for pid in range(tiles - tail, tiles):
+        g, in_group = divmod(pid, 8 * tn)
+        rows_in_group = min(tm - 8 * g, 8)
+        mt.add(8 * g + in_group % rows_in_group)
+    return np.concatenate([np.arange(256 * t, min(256 * t + 256, M)) for t in sorted(mt)])
+
+
+@pytest.mark.parametrize("route", [0, 1])
+@pytest.mark.parametrize("li", [0, 1, 2, 3])
+def test_1080p_linears_bench_launch(orc, li, route):
+    """Every 1080p-like linear on both routes, launched as the benchmark does:
+    the *_ex GEMMs with the full GEMM workspace (tail split) and bf16 output.
+    The row sample takes every 37th row of the m-tiles that hold split tail
+    tiles, plus every 1499th row and the last 3.  NVFP4 qkv, out and ffn_down
+    and INT8 ffn_down split a 128-tile tail in two (the two-way fixup); INT8
+    below K = 4096 and ffn_up (no tail) run unsplit."""
+    require_gpu()
+    M = wl.M_1080P
+    lin = wl.VIDEO_1080P.linears[li]
+    N, K = lin.N, lin.K
+    nk = K // 128 if route == dm.ROUTE_INT8 else K // 256
+    tail = _tail_tile_rows(M, N, nk, route != dm.ROUTE_INT8 or K >= 4096)
+    rows = np.unique(np.concatenate([tail[::37], np.arange(0, M, 1499), np.arange(M - 3, M)]))
+    say(f"1080p-like {lin.name} M={M} N={N} K={K} route={route} bench launch, "
+        f"{len(tail)} tail-tile rows, {len(rows)} rows checked")
+    rng = np.random.default_rng(1100 + 10 * li + route)
+    x = wl.activations(rng, M, K)
+    p = orc.prep_weight(wl.weight(rng, N, K))
+    ws = dm.new_workspace(dm.OP_GEMM, "cuda", M, N)
+    y = empty((M, N), np.uint16)
+    sel = torch.from_numpy(rows).cuda()
+    if route == dm.ROUTE_INT8:
+        q0, s0 = orc.quant_int8(x)
+        del x
+        dm.qgemm_int8_ex(dev(q0), dev(s0), dev(p["qw"]), dev(p["sw_row"]), y, 0, ws, dm.OUT_BF16)
+        torch.cuda.synchronize()
+        _, y0 = orc.gemm_int8(q0, s0, p["qw"], p["sw_row"], rows=rows)
+        assert np.array_equal(host(y[sel], np.uint16), wl.to_bf16_bits(y0))
+    else:
+        c0, sc0, g0 = orc.quant_nvfp4(x)
+        del x
+        dm.qgemm_nvfp4_ex(dev(c0), dev(sc0), dev(np.array([g0], np.float32)), dev(p["cw"]),
+                          dev(p["sw"]), dev(np.array([p["gw"]], np.float32)), y, 0, ws, dm.OUT_BF16)
+        torch.cuda.synchronize()
+        y0, b0 = orc.gemm_nvfp4(c0, sc0, g0, p["cw"], p["sw"], p["gw"], rows=rows)
+        yb = wl.bf16_bits_to_f32(host(y[sel], np.uint16)).astype(np.float64)
+        assert np.all(np.abs(yb - y0) <= 1e-5 * b0 + 2.0 ** -8 * np.abs(y0))

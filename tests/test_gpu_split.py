@@ -49,12 +49,15 @@ def _gemm_ws(M, N):
 
 @pytest.mark.parametrize("M,N,K,sample", [(600, 528, 4096, False), (600, 528, 1024, False),
                                           (1792, 1536, 4096, False), (4352, 4096, 4096, True),
+                                          (4096, 2048, 4096, False),
                                           (workloads.M_480P, 3072, 12288, True),
                                           (workloads.M_480P, 3072, 3072, True)])
 def test_split_int8(orc, M, N, K, sample):
     """INT8 splits from K = 4096 on; below that the same call runs unsplit."""
     require_gpu()
     S = _splits(M, N, K // 128) if K >= 4096 else 1
+    if (M, N, K) == (4096, 2048, 4096):
+        assert S == 2                  # 128 tiles: the two-way fixup
     say(f"split int8 M={M} N={N} K={K} splits={S}")
     rng = np.random.default_rng(M + N + K)
     qa, sa = orc.quant_int8(workloads.activations(rng, M, K))
