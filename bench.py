@@ -78,6 +78,13 @@ def parse():
                    help="on: the GEMMs get the full workspace, so the last partial wave of tiles is "
                         "split along K; off: a workspace with room for the fused-amax maxima only")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--extras", choices=["on", "off"], default="on",
+                   help="on: after the headline, also measure the other workloads as labelled "
+                        "extra keys (2B-like linears, 1080p-like all-INT8 and all-NVFP4 steps, the "
+                        "42-block x 50-step TDC schedule), the headline kernels with the MALL "
+                        "flushed before every call, and the oracle's 1-thread quantizers")
+    p.add_argument("--extra-steps", type=int, default=3,
+                   help="timed steps of each extra linear workload (after one warmup step)")
     p.add_argument("--events", choices=["nofence", "torch"], default="nofence",
                    help="timing events: HIP events without the system-scope fence (default), "
                         "or default torch.cuda events")
@@ -92,6 +99,9 @@ def parse():
     p.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"),
                    help="(no GPU) turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of "
                         "'bench.py --calibrate-mib N' into per-launch HBM bytes of the GEMMs")
+    p.add_argument("--summarize-counters", nargs="+", metavar="CSV_OR_OUT_MD",
+                   help="(no GPU) OUT_MD then one or more rocprofv3 --pmc counter_collection CSVs of the "
+                        "same bench command: per-kernel MFMA busy share, clock, VALU and LDS figures")
     p.add_argument("--command", default="",
                    help="the command that produced the csv, recorded in the summary")
     return p.parse_args()
@@ -169,6 +179,7 @@ class KernelTimer:
         self.only = None
         self.calls = 0          # calls that would be timed, counted while off
         self.pool = []
+        self.flush = None       # called before each timed call (evicts the MALL)
 
     def _event(self):
         if self.kind == "torch":
@@ -190,6 +201,8 @@ class KernelTimer:
             s, e = self.pool.pop()
         else:
             s, e = self._event(), self._event()
+        if self.flush is not None:
+            self.flush()
         s.record()
         fn(*a, **kw)
         e.record()
@@ -218,6 +231,9 @@ def main():
         return
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic, args.command)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1:], args.command)
         return
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} requested, but the benchmark runs on one GPU only "
@@ -279,6 +295,7 @@ def main():
     ybuf = {lin.name: torch.empty((M, lin.N), dtype=ydt, device="cuda") for lin in cfg.linears}
     big = max(lin.N * lin.K for lin in cfg.linears)
     w8_scratch = torch.empty(big, dtype=torch.int8, device="cuda")
+    skip_out = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
     s8_scratch = torch.empty(max(lin.N for lin in cfg.linears), device="cuda")
     ws = dm.new_workspace(dm.OP_TDC)
     # per block, one 64-byte row (every device pointer stays 16-byte aligned):
@@ -391,6 +408,24 @@ def main():
         torch.cuda.synchronize()
         del cx, cd, co
         calib = dict(kernel=CALIB_KERNEL, elements=n, read_bytes=4 * n, write_bytes=2 * n)
+        # the GEMMs' own load path (global_load_lds DMA into LDS) on a known
+        # size: one 256 x 256 output tile over K = 65536, so every operand byte
+        # is fetched exactly once (no other tile could share it)
+        kc = DMA_CALIB_K
+        y1 = torch.empty((256, 256), dtype=torch.bfloat16, device="cuda")
+        qa1 = torch.ones((256, kc), dtype=torch.int8, device="cuda")
+        s1 = torch.ones(256, device="cuda")
+        for _ in range(3):
+            dm.qgemm_int8(qa1, s1, qa1, s1, y1, dm.OUT_BF16)
+        c1 = torch.full((256, kc // 2), 0x22, dtype=torch.uint8, device="cuda")
+        e1 = torch.full((256, kc // 16), 0x38, dtype=torch.uint8, device="cuda")
+        g1 = torch.ones(1, device="cuda")
+        for _ in range(3):
+            dm.qgemm_nvfp4(c1, e1, g1, c1, e1, g1, y1, dm.OUT_BF16)
+        torch.cuda.synchronize()
+        del y1, qa1, s1, c1, e1, g1
+        calib["dma_gemm_tile"] = {k: dict(kernel=v[0], read_bytes=v[1], write_bytes=v[2])
+                                  for k, v in DMA_CALIB.items()}
 
     # After the warmup steps, one more step brackets the GEMM calls (the
     # dominant-kernel candidates) with events; the timed region then
@@ -440,38 +475,43 @@ def main():
             for b, blk in enumerate(blocks):
                 kt("gamma_sums_standalone", 4.0 * M * H, dm.gamma_sums, blk["x_in"], blk["x_out"],
                    sums[b, 4:6], ws, _shape=f"{M}x{H}")
+        # the TDC skip (a block reusing its cached delta), timed the same way
+        # into a scratch output
+        for _ in range(args.steps):
+            for b, blk in enumerate(blocks):
+                kt("tdc_step_skip_standalone", 6.0 * M * H, dm.tdc_step, dm.TDC_SKIP, blk["x_in"],
+                   skip_out, blk["delta"], True, _shape=f"{M}x{H}")
     torch.cuda.synchronize()
     kt.on = False
     ksum = kt.summary(args.steps)
     kshape = kt.summary(args.steps, by_shape=True)
-    peaks = {"hadamard_quant_int8": ("hbm", HBM_GBPS, "GB/s"),
-             "weight_int8_from_nvfp4": ("hbm", HBM_GBPS, "GB/s"),
-             "outlier_count": ("hbm", HBM_GBPS, "GB/s"),
-             "gemm_bf16": ("mfma", PEAK_BF16_TFLOPS, "TFLOP/s"),
-             "hadamard_quant_nvfp4": ("hbm", HBM_GBPS, "GB/s"),
-             "hadamard_quant_nvfp4_given": ("hbm", HBM_GBPS, "GB/s"),
-             "gamma_sums": ("hbm", HBM_GBPS, "GB/s"),
-             "gamma_sums_standalone": ("hbm", HBM_GBPS, "GB/s"),
-             "tdc_step_refresh": ("hbm", HBM_GBPS, "GB/s"),
-             "qgemm_int8": ("mfma", PEAK_INT8_TOPS, "TOPS"),
-             "qgemm_nvfp4": ("mfma", PEAK_FP4_TFLOPS, "TFLOP/s")}
-    kernels = {}
-    for name, s in ksum.items():
-        bound, peak, unit = peaks[name]
-        scale = 1e-9 if unit == "GB/s" else 1e-12
-        achieved = s["work"] * scale / (s["total_ms"] * 1e-3)
-        kernels[name] = dict(calls_per_step=s["calls_per_step"], avg_us=round(s["avg_us"], 2),
-                             median_us=round(s["median_us"], 2), achieved=round(achieved, 2), unit=unit,
-                             bound=bound, peak=peak, frac=round(achieved / peak, 4))
-        if name == "qgemm_nvfp4":
-            kernels[name]["frac_of_bf16_pipe"] = round(achieved / PEAK_BF16_TFLOPS, 4)
-    by_shape = {}
-    for (name, shape), s in sorted(kshape.items()):
-        bound, peak, unit = peaks[name]
-        achieved = s["work"] * (1e-9 if unit == "GB/s" else 1e-12) / (s["total_ms"] * 1e-3)
-        by_shape[f"{name} {shape}"] = dict(calls_per_step=s["calls_per_step"], median_us=round(s["median_us"], 2),
-                                           achieved=round(achieved, 2), unit=unit,
-                                           frac=round(achieved / peak, 4))
+    kernels, by_shape = kernel_tables(ksum, kshape)
+
+    # ---- the same per-kernel pass with the memory-side cache flushed ---------
+    # (a 1 GiB read-modify-write before every call evicts the 256 MB MALL:
+    # every operand then comes from HBM, the cold-cache figure)
+    cold = None
+    if args.extras == "on":
+        flush = torch.zeros(1 << 28, dtype=torch.int32, device="cuda")
+        kt.flush = lambda: flush.add_(1)
+        cold_steps = min(args.steps, 5)
+        kt.only = None
+        kt.calls = 0
+        kt.on = False
+        step()
+        kt.prepare(kt.calls * cold_steps)
+        torch.cuda.synchronize()
+        kt.on = True
+        for _ in range(cold_steps):
+            step()
+        torch.cuda.synchronize()
+        kt.on = False
+        kt.flush = None
+        del flush
+        ck, cs = kernel_tables(kt.summary(cold_steps), kt.summary(cold_steps, by_shape=True))
+        cold = {"note": ("every call preceded by a 1 GiB read-modify-write that evicts the 256 MB "
+                         "memory-side cache; medians over %d steps" % cold_steps),
+                "kernels": ck, "kernels_by_shape": cs}
     dom = max(ksum, key=lambda n: ksum[n]["total_ms"])
     d = kernels[dom]
     if dom in ktimed:  # the dominant kernel as timed inside the timed region
@@ -526,9 +566,328 @@ def main():
     }
     if calib is not None:
         result["copy_calibration"] = calib
+    if cold is not None:
+        result["kernels_cold"] = cold
+    if args.extras == "on":
+        # free the headline's tensors first: the extra workloads bring their own
+        del blocks, qbuf, ybuf, w8_scratch, skip_out, ws_gemm
+        torch.cuda.empty_cache()
+        result["extras"] = run_extras(args)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_rows)
+        if args.extras == "on":
+            result["cpu_baseline"]["oracle_quant_1thread"] = oracle_quant_1thread()
     print(json.dumps(result), flush=True)
+
+
+PEAKS = {"hadamard_quant_int8": ("hbm", HBM_GBPS, "GB/s"),
+         "weight_int8_from_nvfp4": ("hbm", HBM_GBPS, "GB/s"),
+         "outlier_count": ("hbm", HBM_GBPS, "GB/s"),
+         "gemm_bf16": ("mfma", PEAK_BF16_TFLOPS, "TFLOP/s"),
+         "hadamard_quant_nvfp4": ("hbm", HBM_GBPS, "GB/s"),
+         "hadamard_quant_nvfp4_given": ("hbm", HBM_GBPS, "GB/s"),
+         "gamma_sums": ("hbm", HBM_GBPS, "GB/s"),
+         "gamma_sums_standalone": ("hbm", HBM_GBPS, "GB/s"),
+         "tdc_step_refresh": ("hbm", HBM_GBPS, "GB/s"),
+         "tdc_step_skip": ("hbm", HBM_GBPS, "GB/s"),
+         "tdc_step_skip_standalone": ("hbm", HBM_GBPS, "GB/s"),
+         "qgemm_int8": ("mfma", PEAK_INT8_TOPS, "TOPS"),
+         "qgemm_nvfp4": ("mfma", PEAK_FP4_TFLOPS, "TFLOP/s")}
+
+
+def kernel_tables(ksum: dict, kshape: dict):
+    """Per-kernel and per-(kernel, shape) figures from KernelTimer summaries:
+    achieved rate (algorithmic work / event-timed duration) against the
+    MI355X peak of the kernel's bound."""
+    kernels = {}
+    for name, s in ksum.items():
+        bound, peak, unit = PEAKS[name]
+        scale = 1e-9 if unit == "GB/s" else 1e-12
+        achieved = s["work"] * scale / (s["total_ms"] * 1e-3)
+        kernels[name] = dict(calls_per_step=s["calls_per_step"], avg_us=round(s["avg_us"], 2),
+                             median_us=round(s["median_us"], 2), achieved=round(achieved, 2), unit=unit,
+                             bound=bound, peak=peak, frac=round(achieved / peak, 4))
+        if name == "qgemm_nvfp4":
+            kernels[name]["frac_of_bf16_pipe"] = round(achieved / PEAK_BF16_TFLOPS, 4)
+    by_shape = {}
+    for (name, shape), s in sorted(kshape.items()):
+        bound, peak, unit = PEAKS[name]
+        achieved = s["work"] * (1e-9 if unit == "GB/s" else 1e-12) / (s["total_ms"] * 1e-3)
+        by_shape[f"{name} {shape}"] = dict(calls_per_step=s["calls_per_step"], median_us=round(s["median_us"], 2),
+                                           achieved=round(achieved, 2), unit=unit,
+                                           frac=round(achieved / peak, 4))
+    return kernels, by_shape
+
+
+# ---- the other workloads, measured after the headline ------------------------
+
+def _gemm_call(dm, kt, route, x, qb, L, y, ws_q, ws_gemm, w8, s8, epi=0):
+    """One routed linear as the headline step runs it: Hadamard + quant, the
+    NVFP4 -> INT8 weight conversion into the shared scratch (INT8 route), and
+    the quantized GEMM with the full GEMM workspace, bf16 output."""
+    M, K = x.shape
+    N = L["N"]
+    flops = 2.0 * M * N * K
+    gshape = f"{M}x{N}x{K}"
+    if route == dm.ROUTE_INT8:
+        kt("hadamard_quant_int8", 3.0 * M * K + 4.0 * M, dm.hadamard_quant_int8, x, qb["q"], qb["s"],
+           _shape=f"{M}x{K}")
+        qw = w8[:N * K].view(N, K)
+        sw = s8[:N]
+        kt("weight_int8_from_nvfp4", (0.5 + 1.0 / 16 + 1.0) * N * K + 8.0 * N, dm.weight_int8_from_nvfp4,
+           L["cw"], L["sw"], L["gw"], qw, sw, _shape=f"{N}x{K}")
+        kt("qgemm_int8", flops, dm.qgemm_int8_ex, qb["q"], qb["s"], qw, sw, y, epi, ws_gemm, dm.OUT_BF16,
+           _shape=gshape)
+    else:
+        kt("hadamard_quant_nvfp4", (2.0 + 0.5 + 1.0 / 16) * M * K + 4.0, dm.hadamard_quant_nvfp4, x,
+           qb["c"], qb["sc"], qb["g"], ws_q, _shape=f"{M}x{K}")
+        kt("qgemm_nvfp4", flops, dm.qgemm_nvfp4_ex, qb["c"], qb["sc"], qb["g"], L["cw"], L["sw"], L["gw"], y,
+           epi, ws_gemm, dm.OUT_BF16, _shape=gshape)
+    return flops
+
+
+def _nvfp4_weight(torch, dm, w, ws_prep):
+    N, K = w.shape
+    L = dict(N=N, cw=torch.empty((N, K // 2), dtype=torch.uint8, device="cuda"),
+             sw=torch.empty((N, K // 16), dtype=torch.uint8, device="cuda"),
+             gw=torch.zeros(1, device="cuda"))
+    qw = torch.empty((N, K), dtype=torch.int8, device="cuda")   # prep's INT8 output, not kept
+    swr = torch.empty(N, device="cuda")
+    dm.prep_weight(w, L["cw"], L["sw"], L["gw"], qw, swr, ws_prep)
+    return L
+
+
+def _quant_buffers(torch, M, K):
+    return dict(q=torch.empty((M, K), dtype=torch.int8, device="cuda"), s=torch.empty(M, device="cuda"),
+                c=torch.empty((M, K // 2), dtype=torch.uint8, device="cuda"),
+                sc=torch.empty((M, K // 16), dtype=torch.uint8, device="cuda"),
+                g=torch.zeros(1, device="cuda"))
+
+
+def run_linears_workload(torch, dm, wl, cfg, steps: int, events: str) -> dict:
+    """Every linear of a config on one route per step (all INT8, then all
+    NVFP4), each on its own synthetic input, launched as in the headline
+    step.  Wall time per step without events, then the per-kernel figures
+    from as many steps with events around every call."""
+    M = cfg.M
+    gen = wl.device_generator(cfg.seeds[0])
+    ws_prep = dm.new_workspace(dm.OP_PREP_WEIGHT)
+    lins = []
+    for lin in cfg.linears:
+        x = wl.activations_device(gen, M, lin.K)
+        L = _nvfp4_weight(torch, dm, wl.weight_device(gen, lin.N, lin.K), ws_prep)
+        lins.append(dict(L, x=x, name=lin.name, K=lin.K))
+    qbuf = {K: _quant_buffers(torch, M, K) for K in sorted({lin.K for lin in cfg.linears})}
+    nmax = max(lin.N for lin in cfg.linears)
+    ybuf = torch.empty(M * nmax, dtype=torch.bfloat16, device="cuda")
+    w8 = torch.empty(max(lin.N * lin.K for lin in cfg.linears), dtype=torch.int8, device="cuda")
+    s8 = torch.empty(nmax, device="cuda")
+    ws_q = dm.new_workspace(dm.OP_QUANT_NVFP4)
+    ws_gemm = dm.new_workspace(dm.OP_GEMM, "cuda", M, nmax)
+    kt = KernelTimer(torch, events)
+
+    def step(route):
+        ops = 0.0
+        for L in lins:
+            y = ybuf[:M * L["N"]].view(M, L["N"])
+            ops += _gemm_call(dm, kt, route, L["x"], qbuf[L["K"]], L, y, ws_q, ws_gemm, w8, s8)
+        return ops
+
+    out = {}
+    for route, rname in ((dm.ROUTE_INT8, "all_int8"), (dm.ROUTE_NVFP4, "all_nvfp4")):
+        step(route)                           # warmup
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            ops = step(route)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / steps
+        kt.rec = {}
+        kt.on = True
+        for _ in range(steps):
+            step(route)
+        torch.cuda.synchronize()
+        kt.on = False
+        kernels, by_shape = kernel_tables(kt.summary(steps), kt.summary(steps, by_shape=True))
+        out[rname] = {"ms_per_step": round(1e3 * dt, 3), "gemm_tera_ops_per_step": round(ops / 1e12, 3),
+                      "value_TOPS": round(ops / dt / 1e12, 2), "kernels": kernels,
+                      "kernels_by_shape": by_shape}
+    return out
+
+
+def run_schedule_workload(torch, dm, wl, events: str, T: int = 50, NB: int = 42) -> dict:
+    """The full TDC schedule on a proxy DiT: NB residual blocks
+    x + W2 GELU(W1 x) (hidden 1920 -> 1920 -> 1920, W1 ~ N(0, 1/H),
+    W2 ~ N(0, 0.3^2/H)) at 17776 tokens over T timesteps of a drifting latent
+    z_t = z_{t-1} + 0.02 N(0, 1).  Per block and timestep the library's
+    TdcScheduler decides skip or refresh; a refresh routes both linears by
+    the block's Gamma (INT8 when it is missing) and runs them with the GELU
+    fused into the first GEMM's epilogue; the residual add is torch glue.
+    Thresholds from three always-refresh steps (tau = median Gamma,
+    eps_sim = median d, delta_acc = 2.5 median d).  Runs the schedule three
+    times from the same state: without events (the wall time), with events
+    around every library call (per-kernel time; its decisions must equal the
+    first run's), and with every block refreshed (the no-TDC reference)."""
+    import numpy as np
+
+    from dynamic_mixed_precision_amd.schedule import TdcScheduler
+    cfg = wl.PROXY_DIT
+    M, H = cfg.M, cfg.hidden
+    gen = wl.device_generator(cfg.seeds[0])
+    ws_prep = dm.new_workspace(dm.OP_PREP_WEIGHT)
+    blocks = []
+    for _ in range(NB):
+        w1 = wl.weight_device(gen, H, H)
+        w2 = (wl.weight_device(gen, H, H).float() * 0.3).to(torch.bfloat16)
+        blocks.append((_nvfp4_weight(torch, dm, w1, ws_prep), _nvfp4_weight(torch, dm, w2, ws_prep)))
+    z = [wl.activations_device(gen, M, H)]
+    for _ in range(T - 1):                    # the drifting latents, resident before timing
+        n = torch.randn((M, H), generator=gen, device="cuda", dtype=torch.float32)
+        z.append((z[-1].float() + 0.02 * n).to(torch.bfloat16))
+    del n
+    qb = _quant_buffers(torch, M, H)
+    h = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    act = [torch.empty((M, H), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    w8 = torch.empty(H * H, dtype=torch.int8, device="cuda")
+    s8 = torch.empty(H, device="cuda")
+    ws_q = dm.new_workspace(dm.OP_QUANT_NVFP4)
+    ws_gemm = dm.new_workspace(dm.OP_GEMM, "cuda", M, H)
+    alpha, beta = np.ones(2), np.zeros(2)
+
+    def run(steps, tau, eps, dacc, kt, force_refresh=False):
+        sched = TdcScheduler(NB, M * H, alpha, beta, tau, eps, dacc)
+        log = []
+        ops = 0.0
+        for t in range(steps):
+            sched.begin_step()
+            x = z[t]
+            for i in range(NB):
+                out = act[i % 2]
+                if not force_refresh and sched.decide(i):
+                    b = sched.blocks[i]
+                    kt("tdc_step_skip", 6.0 * M * H, dm.tdc_step, dm.TDC_SKIP, x.view(-1), out.view(-1),
+                       b.delta, True, _shape=f"{M}x{H}")
+                    dm.tdc_commit(b.state, dm.TDC_SKIP)
+                    log.append((t, i, "skip"))
+                else:
+                    r = sched.routes(i)[2]
+                    l1, l2 = blocks[i]
+                    ops += _gemm_call(dm, kt, int(r[0]), x, qb, l1, h, ws_q, ws_gemm, w8, s8, dm.EPI_GELU)
+                    ops += _gemm_call(dm, kt, int(r[1]), h, qb, l2, y, ws_q, ws_gemm, w8, s8)
+                    torch.add(x, y, out=out)
+                    b = sched.blocks[i]
+                    kt("tdc_step_refresh", 8.0 * M * H, dm.tdc_step, dm.TDC_REFRESH, x.view(-1), out.view(-1),
+                       b.delta, bool(b.state.delta_valid), b.sums, sched.ws, _shape=f"{M}x{H}")
+                    b.sums_host.copy_(b.sums, non_blocking=True)
+                    b.pending = True
+                    log.append((t, i, tuple(int(v) for v in r)))
+                x = out
+        sched.begin_step()
+        return sched, log, ops
+
+    off = KernelTimer(torch, events)
+    cal, _, _ = run(3, float("inf"), 0.0, 0.0, off)          # always refresh, routes NVFP4
+    gam = [b.state.gamma for b in cal.blocks]
+    ds = [b.state.d for b in cal.blocks]
+    tau, eps = float(np.median(gam)), float(np.median(ds))
+    dacc = 2.5 * eps
+    del cal
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    _, log, ops = run(T, tau, eps, dacc, off)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kt = KernelTimer(torch, events)
+    kt.on = True
+    _, log_ev, _ = run(T, tau, eps, dacc, kt)
+    torch.cuda.synchronize()
+    kt.on = False
+    kernels, by_shape = kernel_tables(kt.summary(T), kt.summary(T, by_shape=True))
+    lib_ms = sum(v["total_ms"] for v in kt.summary(T).values())
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    _, _, ops_all = run(T, tau, eps, dacc, off, force_refresh=True)
+    torch.cuda.synchronize()
+    wall_all = time.perf_counter() - t0
+    skips = sum(1 for e in log if e[2] == "skip")
+    calls = [r for e in log if e[2] != "skip" for r in e[2]]
+    n8 = sum(1 for r in calls if r == dm.ROUTE_INT8)
+    n4 = sum(1 for r in calls if r == dm.ROUTE_NVFP4)
+    bits = {dm.ROUTE_INT8: 8.0, dm.ROUTE_NVFP4: 4.5}
+    return {
+        "workload": (f"proxy DiT, {NB} blocks x + W2 GELU(W1 x) (hidden {H}), {M} tokens, {T} timesteps of "
+                     "a drifting latent; TDC skip/refresh + Gamma router, GELU fused into W1's GEMM"),
+        "thresholds": {"tau": tau, "eps_sim": eps, "delta_acc": dacc, "alpha": 1.0, "beta": 0.0},
+        "block_steps": NB * T, "skips": skips, "skip_rate": round(skips / (NB * T), 4),
+        "linear_calls": {"INT8": n8, "NVFP4": n4},
+        "avg_activation_bits": round(sum(bits[r] for r in calls) / max(len(calls), 1), 3),
+        "ms_per_timestep": round(1e3 * wall / T, 3),
+        "ms_per_timestep_all_refresh": round(1e3 * wall_all / T, 3),
+        "tdc_speedup": round(wall_all / wall, 3),
+        "gemm_tera_ops": round(ops / 1e12, 3), "gemm_tera_ops_all_refresh": round(ops_all / 1e12, 3),
+        "library_kernel_ms_per_timestep": round(lib_ms / T, 3),
+        "decisions_equal_across_runs": log == log_ev,
+        "kernels": kernels, "kernels_by_shape": by_shape,
+    }
+
+
+def run_extras(args) -> dict:
+    import torch
+
+    import dynamic_mixed_precision_amd as dm
+    import workloads as wl
+    out = {}
+    for key, cfg in (("cogvideox2b_linears", wl.COGVIDEOX_2B), ("video1080p_linears", wl.VIDEO_1080P)):
+        out[key] = dict(workload=f"{cfg.name}: {', '.join(f'{l.name} {l.N}x{l.K}' for l in cfg.linears)}, "
+                                 f"{cfg.M} tokens, each on its own synthetic input; all-INT8 step, "
+                                 "then all-NVFP4 step",
+                        **run_linears_workload(torch, dm, wl, cfg, args.extra_steps, args.events))
+        torch.cuda.empty_cache()
+    out["proxy_dit_tdc_schedule"] = run_schedule_workload(torch, dm, wl, args.events)
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_info() -> dict:
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(),
+            "cpus_available": len(os.sched_getaffinity(0))}
+
+
+def oracle_quant_1thread() -> dict:
+    """The oracle's two quantizers on one host thread: the tiny config
+    (256 x 256) and a 1024-token slice of the 2B-like hidden (1920)."""
+    import numpy as np
+
+    import oracle as orc
+    import workloads as wl
+    before = orc.max_threads()
+    orc.set_threads(1)
+    out = {}
+    try:
+        for name, (M, K) in (("tiny_256x256", (256, 256)), ("2b_hidden_1024x1920", (1024, 1920))):
+            x = wl.activations(np.random.default_rng(M + K), M, K)
+            t = time.perf_counter()
+            orc.quant_int8(x)
+            t8 = time.perf_counter() - t
+            t = time.perf_counter()
+            orc.quant_nvfp4(x)
+            t4 = time.perf_counter() - t
+            out[name] = {"int8_GBps": round((3.0 * M * K + 4 * M) / t8 / 1e9, 4),
+                         "nvfp4_GBps": round((2.5625 * M * K + 4) / t4 / 1e9, 4),
+                         "int8_s": round(t8, 4), "nvfp4_s": round(t4, 4)}
+    finally:
+        orc.set_threads(before)
+    return dict(threads=1, **out)
 
 
 def cpu_baseline(rows: int) -> dict:
@@ -553,7 +912,7 @@ def cpu_baseline(rows: int) -> dict:
     dt = time.perf_counter() - t
     ops = 2 * (2.0 * rows * N * K)
     return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": orc.max_threads(),
-            "kind": "oracle",
+            "kind": "oracle", **cpu_info(),
             "sample": f"{rows} tokens of the qkv linear ({N}x{K}), INT8 and NVFP4 routes, "
                       f"quant + GEMM, {dt:.1f} s"}
 
@@ -576,6 +935,14 @@ GEMM_SOURCES = {"qgemm_nvfp4": ["gemm_nvfp4.hip", "gemm_bf16.hip", "gemm_common.
                 "qgemm_int8": ["gemm_int8.hip", "gemm_dma.hpp", "gemm_common.hpp", "device.hpp",
                                "internal.hpp"]}
 CALIB_KERNEL = "dmpq::tdc_skip_kernel"
+# Known-size calibration of the DMA load path: one 256 x 256 tile over K =
+# DMA_CALIB_K (a one-workgroup launch, so its dispatches are told apart from
+# the step's by their grid of 256 work-items); bytes each operand moves once.
+DMA_CALIB_K = 65536
+DMA_CALIB = {"qgemm_int8": ("dmpq::gemm_i8_dma_kernel<1, *>", 2 * 256 * DMA_CALIB_K + 2 * 256 * 4,
+                            256 * 256 * 2),
+             "qgemm_nvfp4": ("dmpq::gemm_fp4_dma_kernel<1, *>",
+                             2 * 256 * (DMA_CALIB_K // 2 + DMA_CALIB_K // 16) + 8, 256 * 256 * 2)}
 HERE = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_JSON = os.path.join(HERE, "profiles", "traffic_qgemm_cogvideox5b.json")
 
@@ -606,6 +973,18 @@ def gemm_algorithmic_bytes(api: str) -> float:
     return tot / len(cfg.linears)
 
 
+def gemm_operand_bytes(api: str) -> float:
+    """Average compulsory operand bytes (codes + scales of A and W) of one GEMM
+    launch of the step."""
+    import workloads as wl
+    cfg = wl.COGVIDEOX_5B
+    tot = 0.0
+    for lin in cfg.linears:
+        per = (lin.K / 2 + lin.K / 16) if api == "qgemm_nvfp4" else (lin.K + 4)
+        tot += (cfg.M + lin.N) * per
+    return tot / len(cfg.linears)
+
+
 def measured_traffic(api: str) -> dict:
     """traffic = counter-measured HBM bytes per launch (calibrated), or None
     when no measurement exists or the kernel's sources changed since."""
@@ -622,6 +1001,10 @@ def measured_traffic(api: str) -> dict:
         return out
     out["traffic"] = rec["bytes_per_launch"]
     out["traffic_over_algorithmic"] = round(rec["bytes_per_launch"] / out["algorithmic_bytes_per_launch"], 3)
+    if "fetch_factor_used" in rec:
+        out["traffic_note"] = ("FETCH_SIZE and WRITE_SIZE of L2 misses (the memory-side cache serves part "
+                               "of them), scaled by factors %.3g / %.3g measured on a one-tile launch of "
+                               "the same DMA load path" % (rec["fetch_factor_used"], rec["write_factor_used"]))
     return out
 
 
@@ -636,13 +1019,18 @@ def _kernel_re(kernel: str):
     return re.compile(re.escape(kernel).replace(r"\*", r"\d+") + r"\(")
 
 
-def _per_kernel_kib(rows, kernel: str):
-    """Counter value (KiB) of every dispatch of `kernel`, in dispatch order."""
+def _per_kernel_kib(rows, kernel: str, grid=None, not_grid=None):
+    """Counter value (KiB) of every dispatch of `kernel`, in dispatch order;
+    `grid` / `not_grid`: keep only dispatches with / without that many work-items."""
     pat = _kernel_re(kernel)
     sel = {}
     for r in rows:
-        if pat.search(r["Kernel_Name"]):
-            sel[int(r["Dispatch_Id"])] = sel.get(int(r["Dispatch_Id"]), 0.0) + float(r["Counter_Value"])
+        if not pat.search(r["Kernel_Name"]):
+            continue
+        g = int(r.get("Grid_Size", 0) or 0)
+        if (grid is not None and g != grid) or (not_grid is not None and g == not_grid):
+            continue
+        sel[int(r["Dispatch_Id"])] = sel.get(int(r["Dispatch_Id"]), 0.0) + float(r["Counter_Value"])
     return [sel[k] for k in sorted(sel)]
 
 
@@ -660,27 +1048,127 @@ def summarize_traffic(fetch_csv: str, write_csv: str, out_json: str, command: st
         "kernel": CALIB_KERNEL, "elements": n, "read_bytes": 4 * n, "write_bytes": 2 * n,
         "fetch_kib_per_dispatch": cf, "write_kib_per_dispatch": cw,
         "fetch_factor": round(f_read, 5), "write_factor": round(f_write, 5)}}
+    # the DMA load path of each GEMM on its known-size one-tile launch; its
+    # factors (not the streaming kernel's) scale that GEMM's counts
+    dma = {}
+    for api, (kname, rbytes, wbytes) in DMA_CALIB.items():
+        df = _per_kernel_kib(fr, kname, grid=256)
+        dw = _per_kernel_kib(wr, kname, grid=256)
+        if len(df) != 3 or len(dw) != 3:
+            raise SystemExit(f"expected 3 one-tile dispatches of {kname}, got {len(df)}, {len(dw)}")
+        dma[api] = {"kernel": kname, "read_bytes": rbytes, "write_bytes": wbytes,
+                    "fetch_kib_per_dispatch": df, "write_kib_per_dispatch": dw,
+                    "fetch_factor": round(rbytes / (1024.0 * sum(df) / 3), 5),
+                    "write_factor": round(wbytes / (1024.0 * sum(dw) / 3), 5)}
+    rec["calibration_dma"] = dma
     for api, knames in GEMM_KERNELS.items():
-        calls = len(_per_kernel_kib(fr, knames[0]))  # one whole-tile dispatch per call
-        f = [v for k in knames for v in _per_kernel_kib(fr, k)]
-        w = [v for k in knames for v in _per_kernel_kib(wr, k)]
+        # one whole-tile dispatch per call (the one-tile calibration launches excluded)
+        calls = len(_per_kernel_kib(fr, knames[0], not_grid=256))
+        f = [v for k in knames for v in _per_kernel_kib(fr, k, not_grid=256)]
+        w = [v for k in knames for v in _per_kernel_kib(wr, k, not_grid=256)]
         if not calls or len(f) != len(w):
             continue
-        fb = 1024.0 * f_read * sum(f) / calls
-        wb = 1024.0 * f_write * sum(w) / calls
+        ff, fw = dma[api]["fetch_factor"], dma[api]["write_factor"]
+        fb = 1024.0 * ff * sum(f) / calls
+        wb = 1024.0 * fw * sum(w) / calls
         alg = gemm_algorithmic_bytes(api)
         rec[api] = {"kernels": knames, "calls": calls, "dispatches": len(f),
                     "sources_sha256": sources_sha256(api),
+                    "fetch_factor_used": ff, "write_factor_used": fw,
                     "fetch_kib_per_call_raw": round(sum(f) / calls, 1),
                     "write_kib_per_call_raw": round(sum(w) / calls, 1),
                     "fetch_bytes_per_launch": round(fb), "write_bytes_per_launch": round(wb),
                     "bytes_per_launch": round(fb + wb),
                     "algorithmic_bytes_per_launch": round(alg),
-                    "traffic_over_algorithmic": round((fb + wb) / alg, 3)}
+                    "traffic_over_algorithmic": round((fb + wb) / alg, 3),
+                    "fetch_over_operand_bytes": round(fb / gemm_operand_bytes(api), 3)}
     with open(out_json, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
     print(json.dumps(rec, indent=1))
+
+
+def summarize_counters(out_md: str, csvs: list, command: str, n_xcd: int = 8, n_cu: int = 256) -> dict:
+    """Per-kernel counter figures from rocprofv3 --pmc runs of one command
+    (one-workgroup calibration dispatches excluded).  Each dispatch's counters
+    are summed over the chip; GRBM_GUI_ACTIVE counts each XCD's cycles, so
+    cycles = GRBM_GUI_ACTIVE / n_xcd, clock = cycles / duration, and the MFMA
+    busy share = SQ_VALU_MFMA_BUSY_CYCLES / (cycles * CUs * 4 SIMDs)."""
+    import csv
+    import re
+    per = {}   # kernel -> counter -> list of (value, duration_ns) per dispatch
+    ndisp = {}  # kernel -> most dispatches in one file
+    for path in csvs:
+        disp = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if "dmpq" not in r["Kernel_Name"] or int(r.get("Grid_Size", 0) or 0) == 256:
+                    continue
+                key = (int(r["Dispatch_Id"]), r["Counter_Name"])
+                name = re.sub(r"\(.*", "", r["Kernel_Name"]).replace("void ", "")
+                dur = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+                v = disp.get(key, (name, 0.0, dur))
+                disp[key] = (name, v[1] + float(r["Counter_Value"]), dur)
+        seen = {}
+        for (d, counter), (name, val, dur) in disp.items():
+            per.setdefault(name, {}).setdefault(counter, []).append((val, dur))
+            seen.setdefault(name, set()).add(d)
+        for name, ds in seen.items():
+            ndisp[name] = max(ndisp.get(name, 0), len(ds))
+
+    def mean(name, c):
+        xs = per[name].get(c)
+        return None if not xs else sum(v for v, _ in xs) / len(xs)
+
+    res = {}
+    for name, cs in per.items():
+        g = cs.get("GRBM_GUI_ACTIVE")
+        row = {"dispatches": ndisp[name]}
+        if g:
+            cyc = [v / n_xcd for v, _ in g]
+            row["avg_us"] = sum(d for _, d in g) / len(g) / 1e3
+            row["clock_GHz"] = sum(c / d for c, (_, d) in zip(cyc, g)) / len(g)
+            mb = mean(name, "SQ_VALU_MFMA_BUSY_CYCLES")
+            if mb is not None:
+                row["mfma_busy"] = mb / (sum(cyc) / len(cyc) * n_cu * 4)
+        vi, mi = mean(name, "SQ_INSTS_VALU"), mean(name, "SQ_INSTS_MFMA")
+        if vi is not None and mi:
+            row["valu_per_mfma"] = vi / mi
+        wa, wc = mean(name, "SQ_WAIT_INST_ANY"), mean(name, "SQ_WAVE_CYCLES")
+        if wa is not None and wc:
+            row["wait_share"] = wa / wc
+        bc = mean(name, "SQ_LDS_BANK_CONFLICT")
+        if bc is not None:
+            row["lds_bank_conflict_cycles"] = bc
+            la = mean(name, "SQ_ACTIVE_INST_LDS")
+            if la:
+                row["lds_conflict_per_active"] = bc / la
+        res[name] = row
+
+    def fmt(v, f):
+        return "-" if v is None else f.format(v)
+
+    lines = ["# rocprofv3 counters per kernel: bench.py step, CogVideoX-5B-like batch", "",
+             "Commands (each counter set is its own run, from /tmp, repository at $GRAFT_REPO_ROOT):", "",
+             "```", command, "```", "",
+             f"Cycles = GRBM_GUI_ACTIVE / {n_xcd} XCDs; clock = cycles / dispatch duration; MFMA busy = "
+             f"SQ_VALU_MFMA_BUSY_CYCLES / (cycles x {n_cu} CUs x 4 SIMDs); wait share = SQ_WAIT_INST_ANY / "
+             "SQ_WAVE_CYCLES; LDS conflict = SQ_LDS_BANK_CONFLICT cycles per dispatch (and per "
+             "SQ_ACTIVE_INST_LDS cycle).  Durations are those of the counter runs (dispatches serialized).",
+             "", "| kernel | dispatches | avg us | clock GHz | MFMA busy | VALU / MFMA insts | wait share | "
+             "LDS conflict cycles | conflict / LDS active |", "|---|---|---|---|---|---|---|---|---|"]
+    for name in sorted(res, key=lambda n: -res[n].get("avg_us", 0) * res[n]["dispatches"]):
+        r = res[name]
+        lines.append(f"| `{name}` | {r['dispatches']} | {fmt(r.get('avg_us'), '{:.1f}')} | "
+                     f"{fmt(r.get('clock_GHz'), '{:.2f}')} | {fmt(r.get('mfma_busy'), '{:.1%}')} | "
+                     f"{fmt(r.get('valu_per_mfma'), '{:.2f}')} | {fmt(r.get('wait_share'), '{:.1%}')} | "
+                     f"{fmt(r.get('lds_bank_conflict_cycles'), '{:.3g}')} | "
+                     f"{fmt(r.get('lds_conflict_per_active'), '{:.3f}')} |")
+    lines.append("")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+    return res
 
 
 def summarize_stats(stats_csv: str, out_md: str, command: str) -> None:

@@ -66,6 +66,7 @@ def _declare(L):
     f32, f64 = C.c_float, C.c_double
     sig = {
         "orc_max_threads": (C.c_int, []),
+        "orc_set_threads": (None, [C.c_int]),
         "orc_bf16_round": (u16, [f32]),
         "orc_bf16_value": (f32, [u16]),
         "orc_e2m1_value": (f32, [u8]),
@@ -119,6 +120,11 @@ def _u16(x) -> np.ndarray:
 
 def max_threads() -> int:
     return int(lib().orc_max_threads())
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads of the oracle's parallel loops from now on."""
+    lib().orc_set_threads(int(n))
 
 
 # ---- codecs -------------------------------------------------------------

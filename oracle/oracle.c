@@ -21,6 +21,12 @@ int orc_max_threads(void)
     return omp_get_max_threads();
 }
 
+void orc_set_threads(int n)
+{
+    if (n > 0)
+        omp_set_num_threads(n);
+}
+
 /* ======================================================================
  * Codecs.  The pages name the formats only: NVFP4 is a micro-scaling block
  * format whose elements are E2M1 ([gist-it] §4 "Supporto Hardware Nativo";

@@ -44,6 +44,8 @@ extern "C" {
 
 /* OpenMP threads the oracle's parallel loops use (for reporting). */
 int orc_max_threads(void);
+/* Threads for the oracle's later parallel loops (timing runs; n > 0). */
+void orc_set_threads(int n);
 
 /* ---- codecs ---------------------------------------------------------- */
 uint16_t orc_bf16_round(float f);        /* fp32 -> bf16 bits, RNE; NaN -> 0x7FC0 */
