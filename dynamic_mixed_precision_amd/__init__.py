@@ -34,7 +34,8 @@ EXPORTS = ("dmpq_last_error", "dmpq_version", "dmpq_workspace_bytes", "dmpq_gamm
            "dmpq_qgemm_int8", "dmpq_qgemm_nvfp4", "dmpq_tdc_init", "dmpq_tdc_decide",
            "dmpq_tdc_step", "dmpq_tdc_commit", "dmpq_prep_weight", "dmpq_weight_int8_from_nvfp4",
            "dmpq_outlier_count", "dmpq_pdr_decide", "dmpq_gemm_bf16", "dmpq_qgemm_int8_ex",
-           "dmpq_qgemm_nvfp4_ex", "dmpq_gemm_bf16_ex", "dmpq_selftest_codec")
+           "dmpq_qgemm_nvfp4_ex", "dmpq_gemm_bf16_ex", "dmpq_selftest_codec",
+           "dmpq_hadamard_quant_nvfp4_noalloc")
 
 
 class DmpqError(RuntimeError):
@@ -95,6 +96,7 @@ def _declare(L):
                                       C.c_size_t]),
         "dmpq_gemm_bf16_ex": (i32, [vp, vp, vp, i64, i64, i64, i32, vp, i32, vp, C.c_size_t]),
         "dmpq_selftest_codec": (i32, [vp, i32, C.c_uint32, C.c_uint32, vp]),
+        "dmpq_hadamard_quant_nvfp4_noalloc": (i32, [vp, vp, i64, i64, i32, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -218,6 +220,16 @@ def hadamard_quant_nvfp4(x, codes, scales, g, ws, flags: int = 0, stream=None) -
     _check(lib().dmpq_hadamard_quant_nvfp4(_stream(stream), _ptr(x), M, K, flags, _ptr(codes),
                                            _ptr(scales), _ptr(g), _ptr(ws), ws.numel()),
            "dmpq_hadamard_quant_nvfp4")
+
+
+def hadamard_quant_nvfp4_noalloc(x, codes, scales, g, flags: int = 0, stream=None) -> None:
+    """hadamard_quant_nvfp4 without a workspace (the library's static scratch)."""
+    M, K = x.shape
+    _need(x, "x", 2 * M * K, 2)
+    _need_nvfp4(codes, scales, g, M, K, "output")
+    _check(lib().dmpq_hadamard_quant_nvfp4_noalloc(_stream(stream), _ptr(x), M, K, flags,
+                                                   _ptr(codes), _ptr(scales), _ptr(g)),
+           "dmpq_hadamard_quant_nvfp4_noalloc")
 
 
 def _need_int8_gemm(qa, sa, qw, sw, y, out_dtype):

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(PKG, "libdmpq.so")
 BUILD_DIR = os.path.join(ROOT, "_build", "dmpq")
 
 SOURCES = ["api.hip", "quant.hip", "reduce.hip", "gemm_int8.hip", "gemm_nvfp4.hip", "gemm_bf16.hip",
-           "selftest.hip"]
+           "selftest.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 # -ffp-contract=off: every fp32 expression is a sequence of single IEEE RNE

@@ -164,6 +164,23 @@ dmpq_status dmpq_hadamard_quant_nvfp4(hipStream_t stream, const uint16_t *x, int
                                       float *d_g, void *ws, size_t ws_bytes);
 
 /* ---------------------------------------------------------------------------
+ * dmpq_hadamard_quant_nvfp4 without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, kernels and results as
+ * dmpq_hadamard_quant_nvfp4 with flags 0 or DMPQ_NO_HADAMARD; the first
+ * pass's partial maxima go to a static 64 KiB device array instead (one copy
+ * per device, kept until the process ends; it holds the partials of any
+ * tensor size, and a size that would not fit is rejected with
+ * DMPQ_ERR_WORKSPACE).  DMPQ_AMAX_GIVEN is rejected (DMPQ_ERR_UNSUPPORTED):
+ * it reads the producer GEMM's workspace.  Allocates nothing.  Every call on
+ * a device shares that device's array: calls that overlap on one device
+ * (concurrent streams, threads) race and must be ordered by the caller.
+ * ------------------------------------------------------------------------- */
+dmpq_status dmpq_hadamard_quant_nvfp4_noalloc(hipStream_t stream, const uint16_t *x, int64_t M,
+                                              int64_t K, int flags, uint8_t *codes,
+                                              uint8_t *scales, float *d_g);
+
+/* ---------------------------------------------------------------------------
  * INT8 quantized linear ([gist-en] §2.A "Routing"; [gist-zh] §2.A weight
  * handling).  acc[m][n] = sum_k qa[m][k] * qw[n][k] (exact int32), then
  * out_dtype F32: y = (float(acc) * sa[m]) * sw[n]; BF16: RNE of that value;
