@@ -246,8 +246,18 @@ hipError_t launch_w8_from_nvfp4(hipStream_t s, const uint8_t *cw, const uint8_t 
 // outlier ratio is computed in full precision).  An element x of a token row
 // (K channels, raw input, no Hadamard) counts when x^2 * K > kappa^2 * S with
 // S = the row's sum of squares, all in fp64: each square of a bf16 value is
-// exact, and S is added in a fixed order (per lane, then a fixed tree).  The
-// row stays in registers between the sum and the count.  Each workgroup
+// exact, and S is added in a fixed order (per lane, then a fixed tree).
+//
+// The per-element test needs no fp64 work: x^2 * K is exact in fp64 (at most
+// 16 + 15 significant bits) and increasing in |x|, so with R = kappa^2 * S
+// the row's outliers are exactly the elements whose bf16 magnitude bits are
+// at least b*, the least pattern b with v(b)^2 * K > R.  A square root gives
+// a candidate c (the bf16 truncation of sqrt(R / K) through fp32); b* is c,
+// c + 1 or c + 2 (the candidate's relative error, below 2^-23, is far under
+// the bf16 spacing), decided by exact fp64 tests, once per row.  Elements then
+// count by one integer compare.  A row whose R is not finite (an infinity or
+// NaN in it) has no outliers, as in the fp64 test.  The row stays in
+// registers (raw bf16 words) between the sum and the count.  Each workgroup
 // writes its count to partial[blockIdx.x]; finalize_sums adds them.
 // ---------------------------------------------------------------------------
 template <int W>
@@ -255,6 +265,26 @@ __device__ __forceinline__ double group_sum_d(double v) {
 #pragma unroll
     for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, W);
     return v;
+}
+
+// bf16 magnitude pattern b (0 .. 0x7F80) as an fp64 value (exact)
+__device__ __forceinline__ double bf16_mag(uint32_t b) { return (double)__uint_as_float(b << 16); }
+
+// Least bf16 magnitude pattern b with v(b)^2 * K > R, for finite R >= 0
+// (0x7F81, above every finite magnitude and infinity, when none qualifies).
+__device__ __forceinline__ uint32_t outlier_threshold(double R, double dK) {
+    const float tf = (float)__builtin_sqrt(R / dK);
+    uint32_t c = __float_as_uint(tf) >> 16;  // truncation toward zero
+    if (c > 0x7F80u) c = 0x7F80u;
+#pragma unroll
+    for (int d = 0; d < 3; d++) {  // b* is c, c + 1 or c + 2; c + 2 is tested too
+        const uint32_t b = c + d;
+        if (b <= 0x7F80u) {
+            const double v = bf16_mag(b);
+            if (v * v * dK > R) return b;
+        }
+    }
+    return c + 3 <= 0x7F80u ? c + 3 : 0x7F81u;
 }
 
 template <int LPR, int BPL>
@@ -272,7 +302,6 @@ __global__ __launch_bounds__(256) void outlier_count_kernel(const uint16_t *__re
     for (int64_t r0 = (int64_t)blockIdx.x * ROWS; r0 < M; r0 += (int64_t)gridDim.x * ROWS) {
         const int64_t row = r0 + tid / LPR;
         const bool row_ok = row < M;
-        // the row stays in registers as raw bf16 (8 words per 16-block)
         uint4 raw[BPL][2];
         double s = 0.0;
 #pragma unroll
@@ -304,19 +333,18 @@ __global__ __launch_bounds__(256) void outlier_count_kernel(const uint16_t *__re
             s = t;
             __syncthreads();
         }
-        const double rhs = kk * s;
-        // zero padding never counts: 0 > rhs is false for rhs >= 0 (or NaN)
+        const double R = kk * s;
+        // a non-finite R (or a row past M) counts nothing: 0xFFFF is above
+        // every magnitude; zero padding never counts either (threshold >= 1)
+        const uint32_t thr = (row_ok && R <= 1.7976931348623157e308) ? outlier_threshold(R, dK) : 0xFFFFu;
 #pragma unroll
         for (int i = 0; i < BPL; i++) {
-            float v[16];
-            unpack16(raw[i][0], raw[i][1], v);
-            // |x|^2 in fp64 (exact; fp32 would overflow or underflow at bf16's range),
-            // written differently from the sum above so that the compiler does not
-            // keep 16*BPL fp64 squares live across the row reduction
+            const uint32_t w[8] = {raw[i][0].x, raw[i][0].y, raw[i][0].z, raw[i][0].w,
+                                   raw[i][1].x, raw[i][1].y, raw[i][1].z, raw[i][1].w};
 #pragma unroll
-            for (int j = 0; j < 16; j++) {
-                const double a = __builtin_fabs((double)v[j]);
-                cnt += (a * a * dK > rhs) ? 1 : 0;
+            for (int j = 0; j < 8; j++) {
+                cnt += (int)((w[j] & 0x7FFFu) >= thr);
+                cnt += (int)(((w[j] >> 16) & 0x7FFFu) >= thr);
             }
         }
     }
@@ -327,6 +355,10 @@ __global__ __launch_bounds__(256) void outlier_count_kernel(const uint16_t *__re
     if (tid == 0) partial[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
+// One count per workgroup: the workspace holds kMaxSums * kMaxPartials of
+// them, so every row group of a 17776-token input gets its own workgroup.
+constexpr int kOutlierGroups = kMaxSums * kMaxPartials;
+
 hipError_t launch_outlier_count(hipStream_t s, const uint16_t *x, int64_t M, int64_t K,
                                 double kappa, double *count, const Workspace &ws) {
     RowPlan p;
@@ -334,7 +366,7 @@ hipError_t launch_outlier_count(hipStream_t s, const uint16_t *x, int64_t M, int
     const double kk = kappa * kappa;
     const int64_t rows = 256 / p.lpr;
     const int64_t groups64 = (M + rows - 1) / rows;
-    const int groups = (int)(groups64 < kMaxPartials ? groups64 : kMaxPartials);
+    const int groups = (int)(groups64 < kOutlierGroups ? groups64 : kOutlierGroups);
     if (groups > 0) {
         const dim3 grid((unsigned)groups);
         switch (p.lpr * 16 + p.bpl) {

@@ -17,8 +17,6 @@ namespace dmpq {
 
 namespace {
 
-constexpr int kUnroll = 4;
-
 __device__ __forceinline__ uint4 ld16(const uint16_t *p) {
     return load_nt16(p);
 }
@@ -54,18 +52,27 @@ __device__ void block_partials(double (&s)[NS], double *partial) {
 
 // Second stage of every sum: one workgroup adds the per-group partials in a
 // fixed order (thread t takes partials t, t+256, ..., then a fixed tree), so
-// the result does not depend on scheduling.
-template <int NS>
+// the result does not depend on scheduling.  The loop has a fixed trip count
+// (kIter >= nparts / 256) with guarded loads, so every load is issued before
+// the first add waits: this kernel is pure latency, a few microseconds.
+template <int NS, int kIter>
 __global__ __launch_bounds__(256) void finalize_sums_kernel(const double *__restrict__ partial,
                                                             int nparts, double *__restrict__ out) {
     __shared__ double red[NS][4];
     const int tid = threadIdx.x;
+    double v[kIter][NS];
+#pragma unroll
+    for (int k = 0; k < kIter; k++) {
+        const int i = tid + 256 * k;
+#pragma unroll
+        for (int j = 0; j < NS; j++) v[k][j] = i < nparts ? partial[(size_t)i * NS + j] : 0.0;
+    }
     double t[NS];
 #pragma unroll
-    for (int j = 0; j < NS; j++) t[j] = 0.0;
-    for (int i = tid; i < nparts; i += 256) {
+    for (int j = 0; j < NS; j++) {
+        t[j] = 0.0;
 #pragma unroll
-        for (int j = 0; j < NS; j++) t[j] += partial[(size_t)i * NS + j];
+        for (int k = 0; k < kIter; k++) t[j] += v[k][j];
     }
 #pragma unroll
     for (int j = 0; j < NS; j++) t[j] = wave_sum(t[j]);
@@ -77,6 +84,14 @@ __global__ __launch_bounds__(256) void finalize_sums_kernel(const double *__rest
     if (tid < NS) out[tid] = (red[tid][0] + red[tid][1]) + (red[tid][2] + red[tid][3]);
 }
 
+// Grid of the streaming sum kernels: one 16-byte chunk per operand per lane
+// per iteration and at most this many workgroups.  Measured on the 17776 x
+// 3072 tensors (54.6 M elements): two-operand sums stream at 6.0 (MALL
+// flushed) to 6.6 TB/s (hot) this way, against 5.6 to 6.0 with four chunks in
+// flight per lane over 2048 workgroups; the refresh's three reads and one
+// write reach 6.2 TB/s hot.  Fewer workgroups also halve the finalize work.
+constexpr unsigned kSumGroups = 1024;
+
 // ---------------------------------------------------------------------------
 // Gamma sums: S1 = sum |out - in|, S2 = sum |in|.
 // ---------------------------------------------------------------------------
@@ -86,30 +101,7 @@ __global__ __launch_bounds__(256) void gamma_kernel(const uint16_t *__restrict__
     double s[2] = {0.0, 0.0};
     const int64_t nch = n / 8;
     const int64_t stride = (int64_t)gridDim.x * 256;
-    int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    for (; c + (kUnroll - 1) * stride < nch; c += kUnroll * stride) {
-        uint4 a[kUnroll], b[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; u++) {
-            a[u] = ld16(xin + 8 * (c + u * stride));
-            b[u] = ld16(xout + 8 * (c + u * stride));
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; u++) {
-            float va[8], vb[8];
-            to8(a[u], va);
-            to8(b[u], vb);
-            float f1 = 0.0f, f2 = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 8; i++) {
-                f1 += __builtin_fabsf(vb[i] - va[i]);
-                f2 += __builtin_fabsf(va[i]);
-            }
-            s[0] += (double)f1;
-            s[1] += (double)f2;
-        }
-    }
-    for (; c < nch; c += stride) {
+    for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < nch; c += stride) {
         float va[8], vb[8];
         to8(ld16(xin + 8 * c), va);
         to8(ld16(xout + 8 * c), vb);
@@ -134,9 +126,10 @@ __global__ __launch_bounds__(256) void gamma_kernel(const uint16_t *__restrict__
 
 hipError_t launch_gamma(hipStream_t st, const uint16_t *x_in, const uint16_t *x_out, int64_t n,
                         double *sums, const Workspace &ws) {
-    const unsigned g = stride_grid(n / 8, 256 * kUnroll * 2, kMaxPartials);
+    const unsigned g = stride_grid(n / 8, 256, kSumGroups);
     hipLaunchKernelGGL(gamma_kernel, dim3(g), dim3(256), 0, st, x_in, x_out, n, ws.partial);
-    hipLaunchKernelGGL(finalize_sums_kernel<2>, dim3(1), dim3(256), 0, st, ws.partial, (int)g, sums);
+    hipLaunchKernelGGL((finalize_sums_kernel<2, kSumGroups / 256>), dim3(1), dim3(256), 0, st, ws.partial, (int)g,
+                       sums);
     return hipGetLastError();
 }
 
@@ -220,27 +213,10 @@ __global__ __launch_bounds__(256) void tdc_refresh_kernel(const uint16_t *__rest
     double s[4] = {0.0, 0.0, 0.0, 0.0};
     const int64_t nch = n / 8;
     const int64_t stride = (int64_t)gridDim.x * 256;
-    int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-    for (; c + (kUnroll - 1) * stride < nch; c += kUnroll * stride) {
-        uint4 ia[kUnroll], oa[kUnroll], da[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; u++) {
-            ia[u] = ld16(xin + 8 * (c + u * stride));
-            oa[u] = ld16(xout + 8 * (c + u * stride));
-            da[u] = DV ? ld16(delta + 8 * (c + u * stride)) : zero;
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; u++) {
-            uint4 nd;
-            refresh8<DV>(ia[u], oa[u], da[u], s, nd);
-            store_nt16(delta + 8 * (c + u * stride), nd);
-        }
-    }
-    for (; c < nch; c += stride) {
+    for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < nch; c += stride) {
         uint4 nd;
-        refresh8<DV>(ld16(xin + 8 * c), ld16(xout + 8 * c), DV ? ld16(delta + 8 * c) : zero, s,
-                     nd);
+        refresh8<DV>(ld16(xin + 8 * c), ld16(xout + 8 * c), DV ? ld16(delta + 8 * c) : zero, s, nd);
         store_nt16(delta + 8 * c, nd);
     }
     if (blockIdx.x == 0 && threadIdx.x < n - 8 * nch) {
@@ -264,23 +240,38 @@ __global__ __launch_bounds__(256) void tdc_refresh_kernel(const uint16_t *__rest
 hipError_t launch_tdc_refresh(hipStream_t st, const uint16_t *x_in, const uint16_t *x_out,
                               uint16_t *delta, int64_t n, int delta_valid, double *sums,
                               const Workspace &ws) {
-    const unsigned g = stride_grid(n / 8, 256 * kUnroll * 2, kMaxPartials);
+    const unsigned g = stride_grid(n / 8, 256, kSumGroups);
     if (delta_valid)
         hipLaunchKernelGGL(tdc_refresh_kernel<true>, dim3(g), dim3(256), 0, st, x_in, x_out,
                            delta, n, ws.partial);
     else
         hipLaunchKernelGGL(tdc_refresh_kernel<false>, dim3(g), dim3(256), 0, st, x_in, x_out,
                            delta, n, ws.partial);
-    hipLaunchKernelGGL(finalize_sums_kernel<4>, dim3(1), dim3(256), 0, st, ws.partial, (int)g, sums);
+    hipLaunchKernelGGL((finalize_sums_kernel<4, kSumGroups / 256>), dim3(1), dim3(256), 0, st, ws.partial, (int)g,
+                       sums);
     return hipGetLastError();
 }
 
 hipError_t launch_finalize_sums(hipStream_t st, const double *partial, int nparts, int ns,
                                 double *out) {
+    // up to kMaxSums * kMaxPartials / ns partials (the workspace's capacity)
+    if (nparts < 0 || (int64_t)nparts * ns > (int64_t)kMaxSums * kMaxPartials) return hipErrorInvalidValue;
     switch (ns) {
-        case 1: hipLaunchKernelGGL(finalize_sums_kernel<1>, dim3(1), dim3(256), 0, st, partial, nparts, out); break;
-        case 2: hipLaunchKernelGGL(finalize_sums_kernel<2>, dim3(1), dim3(256), 0, st, partial, nparts, out); break;
-        case 4: hipLaunchKernelGGL(finalize_sums_kernel<4>, dim3(1), dim3(256), 0, st, partial, nparts, out); break;
+        case 1:
+            if (nparts <= 1024)
+                hipLaunchKernelGGL((finalize_sums_kernel<1, 4>), dim3(1), dim3(256), 0, st, partial, nparts, out);
+            else
+                hipLaunchKernelGGL((finalize_sums_kernel<1, kMaxSums * kMaxPartials / 256>), dim3(1), dim3(256), 0,
+                                   st, partial, nparts, out);
+            break;
+        case 2:
+            hipLaunchKernelGGL((finalize_sums_kernel<2, kMaxSums * kMaxPartials / 512>), dim3(1), dim3(256), 0, st,
+                               partial, nparts, out);
+            break;
+        case 4:
+            hipLaunchKernelGGL((finalize_sums_kernel<4, kMaxPartials / 256>), dim3(1), dim3(256), 0, st, partial,
+                               nparts, out);
+            break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

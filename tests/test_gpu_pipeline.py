@@ -171,3 +171,34 @@ def test_1080p_linears_bench_launch(orc, li, route):
         y0, b0 = orc.gemm_nvfp4(c0, sc0, g0, p["cw"], p["sw"], p["gw"], rows=rows)
         yb = wl.bf16_bits_to_f32(host(y[sel], np.uint16)).astype(np.float64)
         assert np.all(np.abs(yb - y0) <= 1e-5 * b0 + 2.0 ** -8 * np.abs(y0))
+
+
+@pytest.mark.parametrize("li", [0, 1, 2, 3])
+def test_w4a8_chain_5b(orc, li):
+    """The INT8 route with only the NVFP4 weight kept, as the benchmark runs
+    it: the weight converted to INT8 into a scratch buffer right before the
+    GEMM (dmpq_weight_int8_from_nvfp4), then the _ex GEMM with the full
+    workspace and fp32 output -- bit-exact against the oracle's conversion
+    followed by its INT8 GEMM, on a row sample of the 5B-like shapes."""
+    require_gpu()
+    cfg = wl.COGVIDEOX_5B
+    lin = cfg.linears[li]
+    M, N, K = cfg.M, lin.N, lin.K
+    say(f"W4A8 chain 5B-like {lin.name} M={M} N={N} K={K}")
+    rng = np.random.default_rng(400 + li)
+    x = wl.activations(rng, M, K)
+    w = wl.weight(rng, N, K)
+    p = orc.prep_weight(w)
+    q0, s0 = orc.quant_int8(x)
+    qw0, sw0 = orc.w8_from_nvfp4(p["cw"], p["sw"], p["gw"])
+    rows = _rows(M, 997)
+    _, y0 = orc.gemm_int8(q0, s0, qw0, sw0, rows=rows)
+    qw, swr = empty((N, K), np.int8), empty((N,), np.float32)
+    dm.weight_int8_from_nvfp4(dev(p["cw"]), dev(p["sw"]), dev(np.array([p["gw"]], np.float32)), qw, swr)
+    y = empty((M, N), np.float32)
+    dm.qgemm_int8_ex(dev(q0), dev(s0), qw, swr, y, 0, dm.new_workspace(dm.OP_GEMM, "cuda", M, N),
+                     dm.OUT_F32)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(qw), qw0) and np.array_equal(host(swr).view(np.uint32), sw0.view(np.uint32))
+    sel = torch.from_numpy(rows).cuda()
+    assert np.array_equal(host(y[sel]).view(np.uint32), y0.view(np.uint32))
