@@ -1036,7 +1036,9 @@ def _per_kernel_kib(rows, kernel: str, grid=None, not_grid=None):
 
 def summarize_traffic(fetch_csv: str, write_csv: str, out_json: str, command: str) -> None:
     fr, wr = _counter_rows(fetch_csv, "FETCH_SIZE"), _counter_rows(write_csv, "WRITE_SIZE")
-    cf, cw = _per_kernel_kib(fr, CALIB_KERNEL), _per_kernel_kib(wr, CALIB_KERNEL)
+    # the calibration's three dispatches come before the warmup steps (which
+    # may run the same kernel again)
+    cf, cw = _per_kernel_kib(fr, CALIB_KERNEL)[:3], _per_kernel_kib(wr, CALIB_KERNEL)[:3]
     if len(cf) != 3 or len(cw) != 3:
         raise SystemExit(f"expected 3 calibration dispatches, got {len(cf)}, {len(cw)}")
     # the calibration buffers' size is recorded in the command (--calibrate-mib N)
@@ -1154,7 +1156,9 @@ def summarize_counters(out_md: str, csvs: list, command: str, n_xcd: int = 8, n_
              f"Cycles = GRBM_GUI_ACTIVE / {n_xcd} XCDs; clock = cycles / dispatch duration; MFMA busy = "
              f"SQ_VALU_MFMA_BUSY_CYCLES / (cycles x {n_cu} CUs x 4 SIMDs); wait share = SQ_WAIT_INST_ANY / "
              "SQ_WAVE_CYCLES; LDS conflict = SQ_LDS_BANK_CONFLICT cycles per dispatch (and per "
-             "SQ_ACTIVE_INST_LDS cycle).  Durations are those of the counter runs (dispatches serialized).",
+             "SQ_ACTIVE_INST_LDS cycle).  Durations are those of the counter runs (dispatches serialized); "
+             "for kernels shorter than about 100 us the GRBM window exceeds the dispatch timestamps, so their "
+             "clock column overstates.  SQ_INSTS_VALU counts the MFMA instructions too.",
              "", "| kernel | dispatches | avg us | clock GHz | MFMA busy | VALU / MFMA insts | wait share | "
              "LDS conflict cycles | conflict / LDS active |", "|---|---|---|---|---|---|---|---|---|"]
     for name in sorted(res, key=lambda n: -res[n].get("avg_us", 0) * res[n]["dispatches"]):
