@@ -20,10 +20,13 @@ One step is one pass of the whole hot path over a CogVideoX-5B-like batch
      along K);
      an INT8-routed linear first converts its NVFP4 weight to INT8 into one
      shared scratch buffer (only the 4.5-bit weights are kept);
-     with --fuse-ffn on, ffn_down consumes ffn_up's output instead: the
-     ffn_up GEMM applies GELU in its epilogue and, when ffn_down is routed to
-     NVFP4, also leaves the per-tile Hadamard amax that lets ffn_down's
-     quantizer skip its amax pass (this adds the GELU's work to the step);
+     every linear reads its own synthetic input (the linears alone); with
+     --fuse-ffn on, ffn_down reads GELU of ffn_up's output, as in a DiT FFN:
+     the ffn_up GEMM applies GELU in its epilogue and, when ffn_down is
+     routed to NVFP4, also leaves the per-tile Hadamard amax that lets
+     ffn_down's quantizer skip its amax pass; --fuse-ffn separate runs that
+     FFN with GELU as its own kernel and the two-pass quantizer (both forms
+     are measured as extra keys);
   3. per block, the Temporal Delta Cache refresh (delta, four L1 sums).
 Inputs are synthetic (seeded, drawn on the device) and resident in HBM
 before timing; weights are prepared once, outside the timed region.
@@ -70,10 +73,13 @@ def parse():
                         "refresh of the block, which computes them over the same tensors "
                         "(default; the first step finds Gamma missing and routes INT8), or a "
                         "dmpq_gamma_sums call per block at the step start")
-    p.add_argument("--fuse-ffn", choices=["on", "off"], default="off",
-                   help="on: ffn_down's input is ffn_up's output, GELU and the next NVFP4 amax are "
-                        "fused into ffn_up's GEMM epilogue (needs --out-dtype bf16); off: every "
-                        "linear reads its own synthetic input (the linears alone)")
+    p.add_argument("--fuse-ffn", choices=["on", "separate", "off"], default="off",
+                   help="on: ffn_down's input is GELU(ffn_up's output), with GELU and the next "
+                        "NVFP4 tensor amax fused into ffn_up's GEMM epilogue, so an NVFP4-routed "
+                        "ffn_down quantizes with the given amax and reads its input once (needs "
+                        "--out-dtype bf16); separate: the same FFN with GELU as a separate kernel after "
+                        "ffn_up and ffn_down's two-pass quantizer (the like-for-like unfused form); "
+                        "off (default): every linear reads its own synthetic input (the linears alone)")
     p.add_argument("--tail-split", choices=["on", "off"], default="on",
                    help="on: the GEMMs get the full workspace, so the last partial wave of tiles is "
                         "split along K; off: a workspace with room for the fused-amax maxima only")
@@ -307,11 +313,14 @@ def main():
     refreshed = [False] * n_blocks  # the block's refresh sums are from the previous step
     ws_out = dm.new_workspace(dm.OP_OUTLIER)
     fuse = args.fuse_ffn == "on"
-    if fuse and out_dtype != dm.OUT_BF16:
-        print("bench.py: --fuse-ffn on needs --out-dtype bf16", file=sys.stderr)
+    separate = args.fuse_ffn == "separate"
+    if (fuse or separate) and out_dtype != dm.OUT_BF16:
+        print("bench.py: --fuse-ffn on/separate needs --out-dtype bf16", file=sys.stderr)
         sys.exit(2)
     names = [lin.name for lin in cfg.linears]
     i_up, i_down = names.index("ffn_up"), names.index("ffn_down")
+    gelu_buf = (torch.empty((M, cfg.linears[i_up].N), dtype=torch.bfloat16, device="cuda")
+                if separate else None)
     # the GEMMs' workspace: fused-amax maxima, then the split area of the
     # last partial wave of tiles (sized for the widest output)
     ws_gemm = dm.new_workspace(dm.OP_GEMM if args.tail_split == "on" else dm.OP_GEMM_AMAX, "cuda", M,
@@ -367,6 +376,12 @@ def main():
                     x = ybuf[names[i_up]].view(torch.int16)
                     if route == dm.ROUTE_NVFP4:
                         qflags, qws = dm.AMAX_GIVEN, ws_gemm
+                if separate and li == i_down:
+                    # GELU as its own kernel (torch, exact erf form, bf16 in and out)
+                    yu = ybuf[names[i_up]]
+                    kt("gelu_separate", 4.0 * yu.numel(), torch.ops.aten.gelu.out, yu, approximate="none",
+                       out=gelu_buf, _shape=f"{M}x{yu.shape[1]}")
+                    x = gelu_buf.view(torch.int16)
                 if route == dm.ROUTE_BF16:
                     kt("gemm_bf16", flops, dm.gemm_bf16_ex, x.view(M, lin.K), L["w"], ybuf[lin.name],
                        epi, ws_gemm, out_dtype, _shape=gshape)
@@ -551,7 +566,10 @@ def main():
                    "int8_weights": args.int8_weights,
                    "gamma_sums": ("the previous step's TDC refresh" if args.gamma == "refresh"
                                   else "dmpq_gamma_sums at the step start"),
-                   "ffn_fused": fuse,
+                   "ffn": {"on": "ffn_down reads GELU(ffn_up); GELU and the NVFP4 amax fused into ffn_up's "
+                                 "epilogue",
+                           "separate": "ffn_down reads GELU(ffn_up); GELU as a separate kernel",
+                           "off": "every linear on its own input"}[args.fuse_ffn],
                    "tail_split": args.tail_split == "on",
                    "gemm_tera_ops_per_step": round(gemm_ops_step / 1e12, 3)},
         "act_quant_GBps": round(q_bytes * 1e-9 / (q_ms * 1e-3), 1),
@@ -591,6 +609,7 @@ PEAKS = {"hadamard_quant_int8": ("hbm", HBM_GBPS, "GB/s"),
          "tdc_step_refresh": ("hbm", HBM_GBPS, "GB/s"),
          "tdc_step_skip": ("hbm", HBM_GBPS, "GB/s"),
          "tdc_step_skip_standalone": ("hbm", HBM_GBPS, "GB/s"),
+         "gelu_separate": ("hbm", HBM_GBPS, "GB/s"),
          "qgemm_int8": ("mfma", PEAK_INT8_TOPS, "TOPS"),
          "qgemm_nvfp4": ("mfma", PEAK_FP4_TFLOPS, "TFLOP/s")}
 
@@ -609,6 +628,10 @@ def kernel_tables(ksum: dict, kshape: dict):
                              bound=bound, peak=peak, frac=round(achieved / peak, 4))
         if name == "qgemm_nvfp4":
             kernels[name]["frac_of_bf16_pipe"] = round(achieved / PEAK_BF16_TFLOPS, 4)
+        if name == "hadamard_quant_nvfp4":
+            # the two-pass form moves 2 + 2 + 0.5625 B per element against the
+            # 2.5625 algorithmic ones: its own bound is that share of the peak
+            kernels[name]["frac_of_two_read_bound"] = round(achieved / (peak * 2.5625 / 4.5625), 4)
     by_shape = {}
     for (name, shape), s in sorted(kshape.items()):
         bound, peak, unit = PEAKS[name]
@@ -846,7 +869,30 @@ def run_extras(args) -> dict:
         torch.cuda.empty_cache()
     out["proxy_dit_tdc_schedule"] = run_schedule_workload(torch, dm, wl, args.events)
     torch.cuda.empty_cache()
+    # the step with a real DiT FFN (ffn_down reads GELU(ffn_up)), each form in
+    # a child process (the same command with another --fuse-ffn): GELU and
+    # the NVFP4 amax fused into ffn_up's epilogue, and like-for-like with
+    # GELU as a separate kernel and the two-pass quantizer
+    for mode in ("on", "separate"):
+        out[f"headline_step_ffn_{mode}"] = child_bench(
+            ["--fuse-ffn", mode, "--extras", "off", "--no-cpu-baseline", "--steps", str(min(args.steps, 10)),
+             "--warmup", str(min(args.warmup, 3)), "--events", args.events])
     return out
+
+
+def child_bench(extra_args: list) -> dict:
+    """Run bench.py with extra_args in a child process and keep the figures
+    that compare step forms."""
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), *extra_args], capture_output=True, text=True,
+                       timeout=600)
+    if r.returncode != 0:
+        return {"error": f"exit {r.returncode}: {r.stderr.strip()[-300:]}"}
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    keep = ("hadamard_quant_nvfp4", "hadamard_quant_nvfp4_given", "gelu_separate", "qgemm_nvfp4", "qgemm_int8")
+    return {"args": " ".join(extra_args), "value_TOPS": d["value"], "ms_per_step": d["ms_per_step"],
+            "act_quant_GBps": d["act_quant_GBps"], "ffn": d["config"]["ffn"],
+            "kernels": {k: v for k, v in d["kernels"].items() if k in keep}}
 
 
 def cpu_info() -> dict:
