@@ -869,6 +869,7 @@ def run_extras(args) -> dict:
         torch.cuda.empty_cache()
     out["proxy_dit_tdc_schedule"] = run_schedule_workload(torch, dm, wl, args.events)
     torch.cuda.empty_cache()
+    out["int8_weight_forms_5b"] = run_int8_weight_forms(torch, dm, wl, 5, args.events)
     # the step with a real DiT FFN (ffn_down reads GELU(ffn_up)), each form in
     # a child process (the same command with another --fuse-ffn): GELU and
     # the NVFP4 amax fused into ffn_up's epilogue, and like-for-like with
@@ -877,6 +878,58 @@ def run_extras(args) -> dict:
         out[f"headline_step_ffn_{mode}"] = child_bench(
             ["--fuse-ffn", mode, "--extras", "off", "--no-cpu-baseline", "--steps", str(min(args.steps, 10)),
              "--warmup", str(min(args.warmup, 3)), "--events", args.events])
+    return out
+
+
+def run_int8_weight_forms(torch, dm, wl, reps: int, events: str) -> dict:
+    """The INT8 route's two exact forms of the NVFP4 weight on the 5B-like
+    linears (17776 tokens): the separate conversion into a scratch INT8
+    weight followed by the INT8 GEMM (the headline step's form), and the
+    INT8 GEMM that converts the weight inside its tile load.  Per-call HIP
+    event times over `reps` calls of each, and whether the two outputs agree
+    bit for bit."""
+    cfg = wl.COGVIDEOX_5B
+    M = cfg.M
+    gen = wl.device_generator(cfg.seeds[0] + 100)
+    ws_prep = dm.new_workspace(dm.OP_PREP_WEIGHT)
+    kt = KernelTimer(torch, events)
+    out = {}
+    for lin in cfg.linears:
+        N, K = lin.N, lin.K
+        x = wl.activations_device(gen, M, K)
+        L = _nvfp4_weight(torch, dm, wl.weight_device(gen, N, K), ws_prep)
+        qa = torch.empty((M, K), dtype=torch.int8, device="cuda")
+        sa = torch.empty(M, device="cuda")
+        dm.hadamard_quant_int8(x, qa, sa)
+        qw = torch.empty((N, K), dtype=torch.int8, device="cuda")
+        swr = torch.empty(N, device="cuda")
+        y1 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        y2 = torch.empty_like(y1)
+        ws_gemm = dm.new_workspace(dm.OP_GEMM, "cuda", M, N)
+        ws_w4 = dm.new_workspace(dm.OP_GEMM_W4, "cuda", M, N)
+        conv = (dm.weight_int8_from_nvfp4, L["cw"], L["sw"], L["gw"], qw, swr)
+        gemm = (dm.qgemm_int8_ex, qa, sa, qw, swr, y1, 0, ws_gemm, dm.OUT_BF16)
+        fused = (dm.qgemm_int8_from_nvfp4, qa, sa, L["cw"], L["sw"], L["gw"], y2, ws_w4, 0, dm.OUT_BF16)
+        for f in (conv, gemm, fused):  # warmup
+            f[0](*f[1:])
+        torch.cuda.synchronize()
+        kt.rec = {}
+        kt.on = True
+        for _ in range(reps):
+            kt("convert", 0.0, *conv)
+            kt("int8_gemm", 0.0, *gemm)
+            kt("fused", 0.0, *fused)
+        torch.cuda.synchronize()
+        kt.on = False
+        t = {k: v["avg_us"] for k, v in kt.summary(reps).items()}
+        flops = 2.0 * M * N * K
+        out[f"{lin.name} {M}x{N}x{K}"] = {
+            "convert_us": round(t["convert"], 1), "int8_gemm_us": round(t["int8_gemm"], 1),
+            "convert_then_gemm_us": round(t["convert"] + t["int8_gemm"], 1), "fused_us": round(t["fused"], 1),
+            "fused_TOPS": round(flops / t["fused"] / 1e6, 1),
+            "bit_identical": bool(torch.equal(y1.view(torch.int16), y2.view(torch.int16)))}
+        del x, L, qa, qw, y1, y2, ws_gemm, ws_w4
+        torch.cuda.empty_cache()
     return out
 
 

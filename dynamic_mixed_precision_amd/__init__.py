@@ -28,6 +28,7 @@ TDC_SKIP, TDC_REFRESH = 0, 1
 FP4_BF16_DEQUANT = 0
 FP4_SCALED_MFMA = 1
 OP_GAMMA, OP_QUANT_NVFP4, OP_TDC, OP_PREP_WEIGHT, OP_OUTLIER, OP_GEMM_AMAX, OP_GEMM = 0, 1, 2, 3, 4, 5, 6
+OP_GEMM_W4 = 7
 
 EXPORTS = ("dmpq_last_error", "dmpq_version", "dmpq_workspace_bytes", "dmpq_gamma_sums",
            "dmpq_gate_and_route", "dmpq_hadamard_quant_int8", "dmpq_hadamard_quant_nvfp4",
@@ -35,7 +36,7 @@ EXPORTS = ("dmpq_last_error", "dmpq_version", "dmpq_workspace_bytes", "dmpq_gamm
            "dmpq_tdc_step", "dmpq_tdc_commit", "dmpq_prep_weight", "dmpq_weight_int8_from_nvfp4",
            "dmpq_outlier_count", "dmpq_pdr_decide", "dmpq_gemm_bf16", "dmpq_qgemm_int8_ex",
            "dmpq_qgemm_nvfp4_ex", "dmpq_gemm_bf16_ex", "dmpq_selftest_codec",
-           "dmpq_hadamard_quant_nvfp4_noalloc")
+           "dmpq_hadamard_quant_nvfp4_noalloc", "dmpq_qgemm_int8_from_nvfp4")
 
 
 class DmpqError(RuntimeError):
@@ -97,6 +98,8 @@ def _declare(L):
         "dmpq_gemm_bf16_ex": (i32, [vp, vp, vp, i64, i64, i64, i32, vp, i32, vp, C.c_size_t]),
         "dmpq_selftest_codec": (i32, [vp, i32, C.c_uint32, C.c_uint32, vp]),
         "dmpq_hadamard_quant_nvfp4_noalloc": (i32, [vp, vp, i64, i64, i32, vp, vp, vp]),
+        "dmpq_qgemm_int8_from_nvfp4": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, i32, vp,
+                                             C.c_size_t]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -229,7 +232,7 @@ def hadamard_quant_nvfp4_noalloc(x, codes, scales, g, flags: int = 0, stream=Non
     _need_nvfp4(codes, scales, g, M, K, "output")
     _check(lib().dmpq_hadamard_quant_nvfp4_noalloc(_stream(stream), _ptr(x), M, K, flags,
                                                    _ptr(codes), _ptr(scales), _ptr(g)),
-           "dmpq_hadamard_quant_nvfp4_noalloc")
+           "dmpq_hadamard_quant_nvfp4_noalloc", "dmpq_qgemm_int8_from_nvfp4")
 
 
 def _need_int8_gemm(qa, sa, qw, sw, y, out_dtype):
@@ -330,6 +333,22 @@ def weight_int8_from_nvfp4(cw, sw, gw, qw, sw_row, stream=None) -> None:
     _need(sw_row, "sw_row", 4 * N, 4)
     _check(lib().dmpq_weight_int8_from_nvfp4(_stream(stream), _ptr(cw), _ptr(sw), _ptr(gw), N, K,
                                              _ptr(qw), _ptr(sw_row)), "dmpq_weight_int8_from_nvfp4")
+
+
+def qgemm_int8_from_nvfp4(qa, sa, cw, sw, gw, y, ws, epilogue: int = 0, out_dtype: int = OUT_BF16,
+                          stream=None) -> None:
+    """INT8 linear against the NVFP4 weight (cw, sw, gw), converted inside the
+    GEMM; ws: an OP_GEMM_W4 workspace for (M, N)."""
+    M, K = qa.shape
+    N = cw.shape[0]
+    _need(qa, "qa", M * K, 1)
+    _need(sa, "sa", 4 * M, 4)
+    _need_k(cw, K // 2, "cw")
+    _need_nvfp4(cw, sw, gw, N, K, "weight")
+    _need_out(y, M, N, out_dtype)
+    _check(lib().dmpq_qgemm_int8_from_nvfp4(_stream(stream), _ptr(qa), _ptr(sa), _ptr(cw), _ptr(sw),
+                                            _ptr(gw), M, N, K, out_dtype, _ptr(y), epilogue, *_ws(ws)),
+           "dmpq_qgemm_int8_from_nvfp4")
 
 
 def outlier_count(x, kappa: float, count, ws, stream=None) -> None:

@@ -138,6 +138,9 @@ size_t dmpq_workspace_bytes(int op, int64_t M, int64_t K) {
         case DMPQ_OP_GEMM:
             if (M < 0 || K < 0) return 0;
             return gemm_slot_bytes(M, K) + kSplitAreaBytes;
+        case DMPQ_OP_GEMM_W4:  // the fused-amax slots, then s_row and inv_row of the weight
+            if (M < 0 || K < 0) return 0;
+            return gemm_slot_bytes(M, K) + 2 * sizeof(float) * (size_t)K;
         case DMPQ_OP_GAMMA:
         case DMPQ_OP_QUANT_NVFP4:
         case DMPQ_OP_TDC:
@@ -255,6 +258,34 @@ dmpq_status dmpq_qgemm_int8_ex(hipStream_t stream, const int8_t *qa, const float
     return hip_status(launch_gemm_int8(stream, qa, sa, qw, sw, M, N, K, out_dtype, y, epilogue,
                                        static_cast<float *>(ws), split_area(ws, ws_bytes, M, N)),
                       __func__);
+}
+
+dmpq_status dmpq_qgemm_int8_from_nvfp4(hipStream_t stream, const int8_t *qa, const float *sa,
+                                       const uint8_t *cw, const uint8_t *sw, const float *d_gw,
+                                       int64_t M, int64_t N, int64_t K, int out_dtype, void *y,
+                                       int epilogue, void *ws, size_t ws_bytes) {
+    if (dmpq_status s = check_gemm(__func__, M, N, K)) return s;
+    if (K % 128 != 0)
+        return fail(DMPQ_ERR_UNSUPPORTED, "%s: K = %lld is not a multiple of 128", __func__, (long long)K);
+    REQUIRE_PTR_N(qa, M);
+    REQUIRE_PTR_N(sa, M);
+    REQUIRE_PTR_N(cw, N);
+    REQUIRE_PTR_N(sw, N);
+    REQUIRE_PTR(d_gw);
+    REQUIRE_PTR_N(y, M * N);
+    if (dmpq_status s = check_epilogue(__func__, M, N, out_dtype, 7, epilogue, ws, ws_bytes)) return s;
+    const size_t need = dmpq_workspace_bytes(DMPQ_OP_GEMM_W4, M, N);
+    if (!ws) return fail(DMPQ_ERR_WORKSPACE, "%s: workspace is NULL", __func__);
+    if (ws_bytes < need)
+        return fail(DMPQ_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", __func__, ws_bytes, need);
+    if (M == 0 || N == 0) return ok();
+    float *s_row = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + gemm_slot_bytes(M, N));
+    float *inv_row = s_row + N;
+    hipError_t e = launch_w8_row_scales(stream, cw, sw, d_gw, N, K, s_row, inv_row);
+    if (e == hipSuccess)
+        e = launch_gemm_int8_w4(stream, qa, sa, cw, sw, d_gw, s_row, inv_row, M, N, K, out_dtype, y, epilogue,
+                                static_cast<float *>(ws));
+    return hip_status(e, __func__);
 }
 
 dmpq_status dmpq_qgemm_nvfp4(hipStream_t stream, const uint8_t *ca, const uint8_t *sa,

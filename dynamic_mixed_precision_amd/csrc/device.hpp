@@ -105,6 +105,65 @@ __device__ __forceinline__ uint32_t e4m3_encode_nonneg(float v) {
     return code > 0x7Eu ? 0x7Eu : code;
 }
 
+// ---- NVFP4 -> INT8 weight requantization ----------------------------------
+
+// The 16 values (E2M1 value * E4M3 value) * g of one NVFP4 block in fp32:
+// codes c (8 bytes, element 2i in the low nibble of byte i), block scale s
+// (the decoded E4M3 value), tensor scale g.  The E2M1 values come from the
+// hardware converter (v_cvt_scalef32_pk_f32_fp4 with scale 1.0: exact, low
+// nibble first); E2M1 x E4M3 is exact in fp32, so only the product by g
+// rounds.
+__device__ __forceinline__ void nvfp4_block_values(const uint2 c, float s, float g, float v[16]) {
+    typedef float v2f __attribute__((ext_vector_type(2)));
+    v2f e[8];  // the byte select is an immediate
+    e[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.x, 1.0f, 0);
+    e[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.x, 1.0f, 1);
+    e[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.x, 1.0f, 2);
+    e[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.x, 1.0f, 3);
+    e[4] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.y, 1.0f, 0);
+    e[5] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.y, 1.0f, 1);
+    e[6] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.y, 1.0f, 2);
+    e[7] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.y, 1.0f, 3);
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const float lo = e[i].x, hi = e[i].y;  // scalars first: no element-lvalue casts
+        v[2 * i] = (lo * s) * g;
+        v[2 * i + 1] = (hi * s) * g;
+    }
+}
+
+// Codes of one 16-block, q = RNE(v * inv) as bytes.  For |v| <= amax,
+// |fl(v * inv)| < 127.5 (inv = fl(127/amax), two roundings of at most 2^-24
+// each), so no clamp is needed; adding 1.5 * 2^23 rounds fl(v * inv) to an
+// integer in the low mantissa bits (ties to even, as rint), whose low byte
+// is the two's-complement code.  Every value of a row satisfies the bound,
+// because amax is the row's maximum.  Non-finite values follow the library's
+// rule: a NaN product (a NaN input, or an infinity times the zero reciprocal
+// of a row whose amax is infinite) stays NaN through the add, keeping its
+// payload, and it codes 0 when the payload's low byte is zero.  That holds
+// for every NaN of a row that is not a zero row: bf16 data carries 16 zero
+// low bits, and invalid operations make the default NaN.  (A NaN tensor
+// scale of an NVFP4 weight makes every value of a row NaN, so the row is a
+// zero row, which the caller stores as zeros.)  Two operations per value
+// plus the byte packing.
+__device__ __forceinline__ uint4 int8_codes_magic(const float v[16], float inv) {
+    uint32_t t[16];
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+        const float p = v[j] * inv;
+        t[j] = __float_as_uint(p + 12582912.0f);
+    }
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        // v_perm_b32: selector byte n picks byte n of {hi, lo} (0-3 lo, 4-7 hi)
+        const uint32_t lo = __builtin_amdgcn_perm(t[4 * k + 1], t[4 * k], 0x0c0c0400u);
+        const uint32_t hi = __builtin_amdgcn_perm(t[4 * k + 3], t[4 * k + 2], 0x0c0c0400u);
+        w[k] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // ---- wave reductions --------------------------------------------------------
 
 template <int W>

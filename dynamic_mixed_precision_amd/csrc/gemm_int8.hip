@@ -213,6 +213,137 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// INT8 GEMM against an NVFP4 weight converted in the weight-tile load
+// (gist.science Chinese summary §2.A: weights are kept in NVFP4 and converted
+// when an INT8 GEMM needs them).  The weight tile of each stage is loaded as
+// NVFP4 codes and E4M3 scales (0.5625 bytes per element instead of 1) and
+// requantized to INT8 in registers with the per-row reciprocal of
+// w8_row_scales_kernel, by the same operations in the same order as the
+// separate conversion (nvfp4_block_values, then int8_codes_magic), before it
+// is written to LDS; a row with s_row 0 codes as zeros.  The B operand is
+// therefore the separately converted weight bit for bit, and so is the
+// result.  The main loop is the register-staged one of gemm_i8_kernel
+// (K % 128 == 0 here, rows past M or N load a clamped row whose outputs are
+// never stored, so no masks): the loads of stage kt+1 are in flight during
+// stage kt's MFMAs, and the conversion runs when they are written to LDS.
+// Weight staging: piece p = tid + 256 j (j < 4) is 32 elements of row p / 4 =
+// tid / 4 + 64 j, the 16 code bytes and 2 scale bytes at piece p % 4 of the
+// stage, so a thread's four rows are fixed for the whole K loop.
+// ---------------------------------------------------------------------------
+template <int OUT, int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_i8w4_kernel(
+    const int8_t *__restrict__ A, const float *__restrict__ sa, const uint8_t *__restrict__ cw,
+    const uint8_t *__restrict__ sw, const float *__restrict__ gw, const float *__restrict__ s_row,
+    const float *__restrict__ inv_row, int64_t M, int64_t N, int64_t K, void *__restrict__ y,
+    unsigned tiles_m, unsigned tiles_n, float *__restrict__ partial) {
+    using namespace i8gemm;
+    extern __shared__ __attribute__((aligned(16))) int8_t lds[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const unsigned pid = xcd_order(blockIdx.x, gridDim.x);
+    const TileCoord tc = tile_at(pid, tiles_m, tiles_n, GROUP_M);
+    const int64_t m0 = (int64_t)tc.m * BM, n0 = (int64_t)tc.n * BN;
+
+    v16i acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0;
+
+    constexpr int WP = 4;  // weight pieces per thread per stage
+    const int piece = tid & 3;
+    const uint8_t *wc[WP];
+    const uint16_t *ws2[WP];
+    float inv[WP];
+    bool zrow[WP];
+    const float g = *gw;
+#pragma unroll
+    for (int j = 0; j < WP; j++) {
+        const int64_t r = n0 + (tid >> 2) + 64 * j;
+        const int64_t gn = r < N ? r : N - 1;
+        wc[j] = cw + gn * (K / 2) + piece * 16;
+        ws2[j] = reinterpret_cast<const uint16_t *>(sw + gn * (K / 16) + piece * 2);
+        inv[j] = inv_row[gn];
+        zrow[j] = s_row[gn] == 0.0f;
+    }
+    uint4 ra[LOADS], rc[WP];
+    uint32_t rs[WP];
+    const int nk = (int)(K / BK);
+
+#define DMPQ_I8W4_GLOAD(k0)                                                                  \
+    _Pragma("unroll") for (int j = 0; j < LOADS; j++) {                                      \
+        const int c = tid + 256 * j;                                                         \
+        const int64_t gm = m0 + (c >> 3);                                                    \
+        ra[j] = *reinterpret_cast<const uint4 *>(A + (gm < M ? gm : M - 1) * K + (k0) + (c & 7) * 16); \
+    }                                                                                        \
+    _Pragma("unroll") for (int j = 0; j < WP; j++) {                                         \
+        rc[j] = *reinterpret_cast<const uint4 *>(wc[j] + (k0) / 2);                           \
+        rs[j] = ws2[j][(k0) / 32];                                                           \
+    }
+#define DMPQ_I8W4_SSTORE(buf)                                                                \
+    {                                                                                        \
+        int8_t *base = lds + (buf) * STAGE;                                                  \
+        _Pragma("unroll") for (int j = 0; j < LOADS; j++) {                                  \
+            const int c = tid + 256 * j;                                                     \
+            *reinterpret_cast<uint4 *>(base + (c >> 3) * ROW + (c & 7) * 16) = ra[j];         \
+        }                                                                                    \
+        _Pragma("unroll") for (int j = 0; j < WP; j++) {                                     \
+            float v[16];                                                                     \
+            uint4 q0 = make_uint4(0u, 0u, 0u, 0u), q1 = q0;                                  \
+            nvfp4_block_values(make_uint2(rc[j].x, rc[j].y), e4m3_value(rs[j] & 0xFFu), g, v); \
+            if (!zrow[j]) q0 = int8_codes_magic(v, inv[j]);                                  \
+            nvfp4_block_values(make_uint2(rc[j].z, rc[j].w), e4m3_value(rs[j] >> 8), g, v);  \
+            if (!zrow[j]) q1 = int8_codes_magic(v, inv[j]);                                  \
+            int8_t *dst = base + (BM + (tid >> 2) + 64 * j) * ROW + piece * 32;              \
+            *reinterpret_cast<uint4 *>(dst) = q0;                                            \
+            *reinterpret_cast<uint4 *>(dst + 16) = q1;                                       \
+        }                                                                                    \
+    }
+
+    float *scl = reinterpret_cast<float *>(lds + 2 * STAGE);
+    i8_scale_dma(scl, sa, s_row, M, N, m0, n0, tid);
+    DMPQ_I8W4_GLOAD((int64_t)0)
+    DMPQ_I8W4_SSTORE(0)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the scale DMA has landed
+    __syncthreads();
+
+    for (int kt = 0; kt < nk; kt++) {
+        const int cur = kt & 1;
+        const bool more = kt + 1 < nk;
+        // unconditional (the last stage reloads itself, in bounds): under a
+        // branch the compiler keeps the staged A chunks in scratch memory
+        DMPQ_I8W4_GLOAD((int64_t)(more ? kt + 1 : kt) * BK)
+        const int8_t *As = lds + cur * STAGE + (wm * 128 + (lane & 31)) * ROW + (lane >> 5) * 16;
+        const int8_t *Ws = lds + cur * STAGE + (BM + wn * 128 + (lane & 31)) * ROW + (lane >> 5) * 16;
+#pragma unroll
+        for (int ks = 0; ks < BK; ks += 32) {
+            v4i a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                a[i] = *reinterpret_cast<const v4i *>(As + i * 32 * ROW + ks);
+                b[i] = *reinterpret_cast<const v4i *>(Ws + i * 32 * ROW + ks);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[j], a[i], acc[i][j], 0, 0, 0);
+        }
+        if (more) {
+            DMPQ_I8W4_SSTORE(cur ^ 1)
+        }
+        __syncthreads();
+    }
+#undef DMPQ_I8W4_GLOAD
+#undef DMPQ_I8W4_SSTORE
+
+    DMPQ_I8_EPILOGUE(scl)
+}
+
+// ---------------------------------------------------------------------------
 // Fast path for K % 128 == 0: the DMA-fed main loop of gemm_dma.hpp with i8
 // MFMA (v_mfma_i32_32x32x32_i8), then the scaled epilogue.
 // ---------------------------------------------------------------------------
@@ -373,6 +504,42 @@ static hipError_t launch_i8_paths(hipStream_t s, const int8_t *qa, const float *
         }
     }
     return hipGetLastError();
+}
+
+template <int OUT, int EPI>
+static hipError_t launch_i8w4(hipStream_t s, const int8_t *qa, const float *sa, const uint8_t *cw,
+                              const uint8_t *sw, const float *gw, const float *s_row, const float *inv_row,
+                              int64_t M, int64_t N, int64_t K, void *y, float *partial) {
+    static const hipError_t attr = allow_lds(gemm_i8w4_kernel<OUT, EPI>, 2 * i8gemm::STAGE + kI8ScaleBytes);
+    if (attr != hipSuccess) return attr;
+    const int64_t tm = (M + 255) / 256, tn = (N + 255) / 256;
+    hipLaunchKernelGGL((gemm_i8w4_kernel<OUT, EPI>), dim3((unsigned)(tm * tn)), dim3(256),
+                       2 * i8gemm::STAGE + kI8ScaleBytes, s, qa, sa, cw, sw, gw, s_row, inv_row, M, N, K, y,
+                       (unsigned)tm, (unsigned)tn, partial);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_int8_w4(hipStream_t s, const int8_t *qa, const float *sa, const uint8_t *cw,
+                               const uint8_t *sw, const float *gw, const float *s_row,
+                               const float *inv_row, int64_t M, int64_t N, int64_t K, int out_dtype,
+                               void *y, int epi, float *partial) {
+    if (M == 0 || N == 0) return hipSuccess;
+    if (K % i8gemm::BK != 0) return hipErrorInvalidValue;
+    if (epi == 0) {
+        switch (out_dtype) {
+            case 0: return launch_i8w4<0, 0>(s, qa, sa, cw, sw, gw, s_row, inv_row, M, N, K, y, partial);
+            case 1: return launch_i8w4<1, 0>(s, qa, sa, cw, sw, gw, s_row, inv_row, M, N, K, y, partial);
+            case 2: return launch_i8w4<2, 0>(s, qa, sa, cw, sw, gw, s_row, inv_row, M, N, K, y, partial);
+        }
+        return hipErrorInvalidValue;
+    }
+    if (out_dtype != 1) return hipErrorInvalidValue;
+    switch (epi) {
+        case 1: return launch_i8w4<1, 1>(s, qa, sa, cw, sw, gw, s_row, inv_row, M, N, K, y, partial);
+        case 2: return launch_i8w4<1, 2>(s, qa, sa, cw, sw, gw, s_row, inv_row, M, N, K, y, partial);
+        case 3: return launch_i8w4<1, 3>(s, qa, sa, cw, sw, gw, s_row, inv_row, M, N, K, y, partial);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm_int8(hipStream_t s, const int8_t *qa, const float *sa, const int8_t *qw,

@@ -35,6 +35,11 @@ inline int64_t gemm_tiles(int64_t M, int64_t N) { return ((M + 255) / 256) * ((N
 hipError_t launch_w8_from_nvfp4(hipStream_t s, const uint8_t *cw, const uint8_t *sw,
                                 const float *gw, int64_t N, int64_t K, int8_t *qw,
                                 float *sw_row);
+// Row scales for the INT8 GEMM that converts an NVFP4 weight in its tile
+// load: s_row = amax/127 and inv_row = 127/amax of each row of
+// (E2M1 * E4M3) * gw, both 0 for a row whose reciprocal is not finite.
+hipError_t launch_w8_row_scales(hipStream_t s, const uint8_t *cw, const uint8_t *sw, const float *gw,
+                                int64_t N, int64_t K, float *s_row, float *inv_row);
 bool hq_int8_supported(int64_t K);
 
 hipError_t launch_gamma(hipStream_t s, const uint16_t *x_in, const uint16_t *x_out, int64_t n,
@@ -77,6 +82,14 @@ constexpr int64_t kSplitMinKInt8 = 4096;
 hipError_t launch_gemm_int8(hipStream_t s, const int8_t *qa, const float *sa, const int8_t *qw,
                             const float *sw, int64_t M, int64_t N, int64_t K, int out_dtype,
                             void *y, int epi, float *partial, uint32_t *spart);
+// The INT8 GEMM against an NVFP4 weight (cw, sw, gw) converted to INT8 in
+// the weight-tile load with the row scales of launch_w8_row_scales; the
+// same result as launch_gemm_int8 on the converted weight.  K % 128 == 0;
+// whole tiles only (no split); epi and partial as in launch_gemm_int8.
+hipError_t launch_gemm_int8_w4(hipStream_t s, const int8_t *qa, const float *sa, const uint8_t *cw,
+                               const uint8_t *sw, const float *gw, const float *s_row,
+                               const float *inv_row, int64_t M, int64_t N, int64_t K, int out_dtype,
+                               void *y, int epi, float *partial);
 hipError_t launch_gemm_bf16(hipStream_t s, const uint16_t *x, const uint16_t *w, int64_t M,
                             int64_t N, int64_t K, int out_dtype, void *y, int epi, float *partial,
                             uint32_t *spart);

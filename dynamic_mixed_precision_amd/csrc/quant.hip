@@ -36,68 +36,18 @@ struct Bf16Rows {
 };
 
 // Source of a row's 16-blocks: an NVFP4 weight dequantized to
-// (E2M1 value * E4M3 value) * g in fp32.  The E2M1 values come from the
-// hardware converter (v_cvt_scalef32_pk_f32_fp4 with scale 1.0: exact, low
-// nibble first); the conversion is VALU-bound, and the bit decode it
-// replaces cost about seven operations per element.
+// (E2M1 value * E4M3 value) * g in fp32 (nvfp4_block_values: the hardware
+// E2M1 converter; the conversion is VALU-bound, and the bit decode it
+// replaces cost about seven operations per element).
 struct Nvfp4Rows {
     const uint8_t *codes;
     const uint8_t *scales;
     const float *g;
     __device__ __forceinline__ void load(int64_t row, int64_t K, int b, float v[16]) const {
-        typedef float v2f __attribute__((ext_vector_type(2)));
         const uint2 c = *reinterpret_cast<const uint2 *>(codes + row * (K / 2) + 8 * (int64_t)b);
-        const float s = e4m3_value(scales[row * (K / 16) + b]);
-        const float gg = *g;
-        v2f e[8];  // the byte select is an immediate
-        e[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.x, 1.0f, 0);
-        e[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.x, 1.0f, 1);
-        e[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.x, 1.0f, 2);
-        e[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.x, 1.0f, 3);
-        e[4] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.y, 1.0f, 0);
-        e[5] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.y, 1.0f, 1);
-        e[6] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.y, 1.0f, 2);
-        e[7] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.y, 1.0f, 3);
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const float lo = e[i].x, hi = e[i].y;  // scalars first: no element-lvalue casts
-            v[2 * i] = (lo * s) * gg;
-            v[2 * i + 1] = (hi * s) * gg;
-        }
+        nvfp4_block_values(c, e4m3_value(scales[row * (K / 16) + b]), *g, v);
     }
 };
-
-// Codes of one 16-block, q = RNE(v * inv) as bytes.  For |v| <= amax,
-// |fl(v * inv)| < 127.5 (inv = fl(127/amax), two roundings of at most 2^-24
-// each), so no clamp is needed; adding 1.5 * 2^23 rounds fl(v * inv) to an
-// integer in the low mantissa bits (ties to even, as rint), whose low byte
-// is the two's-complement code.  Every value of a row satisfies the bound,
-// because amax is the row's maximum.  Non-finite values follow the library's
-// rule: a NaN product (a NaN input, or an infinity times the zero reciprocal
-// of a row whose amax is infinite) stays NaN through the add, keeping its
-// payload, and it codes 0 when the payload's low byte is zero.  That holds
-// for every NaN of a row that is not a zero row: bf16 data carries 16 zero
-// low bits, and invalid operations make the default NaN.  (A NaN tensor
-// scale of an NVFP4 weight makes every value of a row NaN, so the row is a
-// zero row, which the caller stores as zeros.)  Two operations per value
-// plus the byte packing.
-__device__ __forceinline__ uint4 int8_codes_magic(const float v[16], float inv) {
-    uint32_t t[16];
-#pragma unroll
-    for (int j = 0; j < 16; j++) {
-        const float p = v[j] * inv;
-        t[j] = __float_as_uint(p + 12582912.0f);
-    }
-    uint32_t w[4];
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-        // v_perm_b32: selector byte n picks byte n of {hi, lo} (0-3 lo, 4-7 hi)
-        const uint32_t lo = __builtin_amdgcn_perm(t[4 * k + 1], t[4 * k], 0x0c0c0400u);
-        const uint32_t hi = __builtin_amdgcn_perm(t[4 * k + 3], t[4 * k + 2], 0x0c0c0400u);
-        w[k] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-    }
-    return make_uint4(w[0], w[1], w[2], w[3]);
-}
 
 template <int LPR, int BPL, class Src>
 __global__ __launch_bounds__(256) void row_quant_int8_kernel(Src src, int64_t M, int64_t K,
@@ -232,6 +182,44 @@ static hipError_t launch_rows(hipStream_t s, const Src &src, int64_t M, int64_t 
 hipError_t launch_hq_int8(hipStream_t s, const uint16_t *x, int64_t M, int64_t K, int flags,
                           int8_t *q, float *s_row) {
     return launch_rows(s, Bf16Rows{x, flags}, M, K, q, s_row);
+}
+
+// Per-row scales of the INT8 weight requantized from an NVFP4 weight, for the
+// INT8 GEMM that converts the weight in its tile load: the same amax and
+// reciprocal as row_quant_int8_kernel<..., Nvfp4Rows> (a maximum does not
+// depend on the order), s = amax/127 and inv = 127/amax; a row whose
+// reciprocal is not finite gets s = 0 and inv = 0 (the GEMM codes it as
+// zeros).  One wave per row.
+__global__ __launch_bounds__(256) void w8_row_scales_kernel(Nvfp4Rows src, int64_t N, int64_t K,
+                                                            float *__restrict__ s_row,
+                                                            float *__restrict__ inv_row) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= N) return;  // the whole wave
+    const int nblk = (int)(K / 16);
+    float amax = 0.0f;
+    for (int b = lane; b < nblk; b += kWave) {
+        float v[16];
+        src.load(row, K, b, v);
+#pragma unroll
+        for (int j = 0; j < 16; j++) amax = fmaxf(amax, __builtin_fabsf(v[j]));
+    }
+    amax = wave_max(amax);
+    float inv = 127.0f / amax;
+    const bool zero_row = !(inv <= FLT_MAX);
+    if (zero_row) inv = 0.0f;
+    if (lane == 0) {
+        s_row[row] = zero_row ? 0.0f : amax / 127.0f;
+        inv_row[row] = inv;
+    }
+}
+
+hipError_t launch_w8_row_scales(hipStream_t s, const uint8_t *cw, const uint8_t *sw, const float *gw,
+                                int64_t N, int64_t K, float *s_row, float *inv_row) {
+    if (N == 0) return hipSuccess;
+    hipLaunchKernelGGL(w8_row_scales_kernel, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s,
+                       Nvfp4Rows{cw, sw, gw}, N, K, s_row, inv_row);
+    return hipGetLastError();
 }
 
 hipError_t launch_w8_from_nvfp4(hipStream_t s, const uint8_t *cw, const uint8_t *sw,

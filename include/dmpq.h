@@ -90,17 +90,19 @@ enum { DMPQ_TDC_SKIP = 0, DMPQ_TDC_REFRESH = 1 };
 enum { DMPQ_FP4_BF16_DEQUANT = 0, DMPQ_FP4_SCALED_MFMA = 1 };
 /* Workspace users. */
 enum { DMPQ_OP_GAMMA = 0, DMPQ_OP_QUANT_NVFP4 = 1, DMPQ_OP_TDC = 2, DMPQ_OP_PREP_WEIGHT = 3,
-       DMPQ_OP_OUTLIER = 4, DMPQ_OP_GEMM_AMAX = 5, DMPQ_OP_GEMM = 6 };
+       DMPQ_OP_OUTLIER = 4, DMPQ_OP_GEMM_AMAX = 5, DMPQ_OP_GEMM = 6, DMPQ_OP_GEMM_W4 = 7 };
 
 /* Message describing the calling thread's last error ("" if none). */
 const char *dmpq_last_error(void);
 /* Library version string. */
 const char *dmpq_version(void);
 /* Bytes of workspace the op needs, 0 for an unknown op.  Most ops need a
- * fixed amount.  Two depend on a GEMM's output shape (pass its M and N as
+ * fixed amount.  Three depend on a GEMM's output shape (pass its M and N as
  * (M, K)): DMPQ_OP_GEMM_AMAX, a fused-amax producer GEMM and the NVFP4
  * quantization of its output; DMPQ_OP_GEMM, the full workspace of the *_ex
- * GEMMs (the same tile maxima first, then 64 MiB for the K split). */
+ * GEMMs (the same tile maxima first, then 64 MiB for the K split);
+ * DMPQ_OP_GEMM_W4, dmpq_qgemm_int8_from_nvfp4 (the tile maxima, then two
+ * floats per weight row). */
 size_t dmpq_workspace_bytes(int op, int64_t M, int64_t K);
 
 /* ---------------------------------------------------------------------------
@@ -279,6 +281,26 @@ dmpq_status dmpq_prep_weight(hipStream_t stream, const uint16_t *w, int64_t N, i
 dmpq_status dmpq_weight_int8_from_nvfp4(hipStream_t stream, const uint8_t *cw, const uint8_t *sw,
                                         const float *d_gw, int64_t N, int64_t K, int8_t *qw,
                                         float *sw_row);
+
+/* ---------------------------------------------------------------------------
+ * INT8 linear against an NVFP4 weight converted inside the GEMM ([gist-zh]
+ * §2.A weight-handling bullet: weights stay in NVFP4 and are converted when
+ * an INT8 GEMM needs them).  No INT8 copy of the weight is written: a first
+ * kernel computes each weight row's scale s_row = amax/127 and reciprocal
+ * 127/amax (the rule of dmpq_weight_int8_from_nvfp4) into ws, and the GEMM
+ * requantizes each weight tile from the NVFP4 codes as it stages the tile.
+ * y equals dmpq_qgemm_int8_ex(qa, sa, qw, sw_row, ...) with (qw, sw_row) from
+ * dmpq_weight_int8_from_nvfp4(cw, sw, d_gw), bit for bit, on every output
+ * type and epilogue.  qa [M x K] int8, sa [M]; cw [N x K/2], sw [N x K/16],
+ * d_gw (device fp32).  K % 128 == 0 (else DMPQ_ERR_UNSUPPORTED).  out_dtype
+ * F32, BF16 or I32; epilogue as dmpq_qgemm_int8_ex (no tail split).  ws:
+ * dmpq_workspace_bytes(DMPQ_OP_GEMM_W4, M, N) bytes, required; calls that
+ * share a workspace must not overlap.
+ * ------------------------------------------------------------------------- */
+dmpq_status dmpq_qgemm_int8_from_nvfp4(hipStream_t stream, const int8_t *qa, const float *sa,
+                                       const uint8_t *cw, const uint8_t *sw, const float *d_gw,
+                                       int64_t M, int64_t N, int64_t K, int out_dtype, void *y,
+                                       int epilogue, void *ws, size_t ws_bytes);
 
 /* ---------------------------------------------------------------------------
  * Purified Delta Refresh ([gist-en] §2.C "Solution"; [gist-it] §2.C;
