@@ -232,7 +232,7 @@ def hadamard_quant_nvfp4_noalloc(x, codes, scales, g, flags: int = 0, stream=Non
     _need_nvfp4(codes, scales, g, M, K, "output")
     _check(lib().dmpq_hadamard_quant_nvfp4_noalloc(_stream(stream), _ptr(x), M, K, flags,
                                                    _ptr(codes), _ptr(scales), _ptr(g)),
-           "dmpq_hadamard_quant_nvfp4_noalloc", "dmpq_qgemm_int8_from_nvfp4")
+           "dmpq_hadamard_quant_nvfp4_noalloc")
 
 
 def _need_int8_gemm(qa, sa, qw, sw, y, out_dtype):

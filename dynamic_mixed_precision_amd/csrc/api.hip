@@ -37,13 +37,14 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // A device pointer must be non-NULL and 16-byte aligned, except that a buffer
 // of zero elements may be NULL (torch hands out NULL for empty tensors).
-#define REQUIRE_PTR_N(p, count)                                                          \
+#define REQUIRE_PTR_NF(fn, p, count)                                                     \
     do {                                                                                 \
         if ((count) > 0 && !(p))                                                         \
-            return fail(DMPQ_ERR_INVALID_ARG, "%s: %s is NULL", __func__, #p);           \
+            return fail(DMPQ_ERR_INVALID_ARG, "%s: %s is NULL", (fn), #p);               \
         if ((p) && !aligned16(p))                                                        \
-            return fail(DMPQ_ERR_MISALIGNED, "%s: %s is not 16-byte aligned", __func__, #p); \
+            return fail(DMPQ_ERR_MISALIGNED, "%s: %s is not 16-byte aligned", (fn), #p); \
     } while (0)
+#define REQUIRE_PTR_N(p, count) REQUIRE_PTR_NF(__func__, p, count)
 #define REQUIRE_PTR(p) REQUIRE_PTR_N(p, 1)
 
 #define REQUIRE_HOST(p)                                                                 \
@@ -119,6 +120,24 @@ dmpq_status set_last_error(dmpq_status code, const char *fmt, ...) {
     vsnprintf(g_err, sizeof g_err, fmt, ap);
     va_end(ap);
     return code;
+}
+
+// The arguments of the NVFP4 quantizer other than its workspace, checked
+// in the name of entry point fn (also before the no-workspace entry point
+// makes any HIP call).
+dmpq_status check_hq_nvfp4_args(const char *fn, const uint16_t *x, int64_t M, int64_t K, int flags,
+                                const uint8_t *codes, const uint8_t *scales, const float *d_g) {
+    if (M < 0) return fail(DMPQ_ERR_BAD_SHAPE, "%s: M = %lld < 0", fn, (long long)M);
+    if (dmpq_status s = check_k(fn, K)) return s;
+    REQUIRE_PTR_NF(fn, x, M);
+    REQUIRE_PTR_NF(fn, codes, M);
+    REQUIRE_PTR_NF(fn, scales, M);
+    REQUIRE_PTR_NF(fn, d_g, 1);
+    if (flags & ~(DMPQ_NO_HADAMARD | DMPQ_AMAX_GIVEN))
+        return fail(DMPQ_ERR_INVALID_ARG, "%s: unknown flags %d", fn, flags);
+    if ((flags & DMPQ_NO_HADAMARD) && (flags & DMPQ_AMAX_GIVEN))
+        return fail(DMPQ_ERR_INVALID_ARG, "%s: DMPQ_AMAX_GIVEN needs the rotation", fn);
+    return DMPQ_OK;
 }
 }  // namespace dmpq
 
@@ -201,16 +220,7 @@ dmpq_status dmpq_hadamard_quant_int8(hipStream_t stream, const uint16_t *x, int6
 dmpq_status dmpq_hadamard_quant_nvfp4(hipStream_t stream, const uint16_t *x, int64_t M,
                                       int64_t K, int flags, uint8_t *codes, uint8_t *scales,
                                       float *d_g, void *ws, size_t ws_bytes) {
-    if (M < 0) return fail(DMPQ_ERR_BAD_SHAPE, "%s: M = %lld < 0", __func__, (long long)M);
-    if (dmpq_status s = check_k(__func__, K)) return s;
-    REQUIRE_PTR_N(x, M);
-    REQUIRE_PTR_N(codes, M);
-    REQUIRE_PTR_N(scales, M);
-    REQUIRE_PTR(d_g);
-    if (flags & ~(DMPQ_NO_HADAMARD | DMPQ_AMAX_GIVEN))
-        return fail(DMPQ_ERR_INVALID_ARG, "%s: unknown flags %d", __func__, flags);
-    if ((flags & DMPQ_NO_HADAMARD) && (flags & DMPQ_AMAX_GIVEN))
-        return fail(DMPQ_ERR_INVALID_ARG, "%s: DMPQ_AMAX_GIVEN needs the rotation", __func__);
+    if (dmpq_status s = check_hq_nvfp4_args(__func__, x, M, K, flags, codes, scales, d_g)) return s;
     if (dmpq_status s = check_ws(__func__, ws, ws_bytes)) return s;
     if ((flags & DMPQ_AMAX_GIVEN) && ws_bytes < dmpq_workspace_bytes(DMPQ_OP_GEMM_AMAX, M, K))
         return fail(DMPQ_ERR_WORKSPACE, "%s: workspace has %zu bytes, the producer's tile maxima need %zu",

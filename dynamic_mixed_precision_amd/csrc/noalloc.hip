@@ -53,6 +53,8 @@ hipError_t scratch_of_current_device(void **out) {
 }  // namespace
 
 dmpq_status set_last_error(dmpq_status code, const char *fmt, ...);  // api.hip
+dmpq_status check_hq_nvfp4_args(const char *fn, const uint16_t *x, int64_t M, int64_t K, int flags,
+                                const uint8_t *codes, const uint8_t *scales, const float *d_g);  // api.hip
 }  // namespace dmpq
 
 using namespace dmpq;
@@ -61,23 +63,23 @@ extern "C" dmpq_status dmpq_hadamard_quant_nvfp4_noalloc(hipStream_t stream, con
                                                          int64_t M, int64_t K, int flags,
                                                          uint8_t *codes, uint8_t *scales,
                                                          float *d_g) {
+    // every argument is checked before the first HIP call
+    if (dmpq_status st = check_hq_nvfp4_args(__func__, x, M, K, flags, codes, scales, d_g)) return st;
     if (flags & DMPQ_AMAX_GIVEN)
         return set_last_error(DMPQ_ERR_UNSUPPORTED,
                               "%s: DMPQ_AMAX_GIVEN reads the producer GEMM's workspace; use "
                               "dmpq_hadamard_quant_nvfp4", __func__);
-    if (M >= 0 && K > 0 && K % 16 == 0) {
-        const size_t need = (size_t)hq_nvfp4_partials(M, K) * sizeof(float);
-        if (need > kScratchBytes)
-            return set_last_error(DMPQ_ERR_WORKSPACE,
-                                  "%s: M = %lld, K = %lld needs %zu bytes of scratch, the static "
-                                  "array holds %zu", __func__, (long long)M, (long long)K, need,
-                                  kScratchBytes);
-    }
+    const size_t need = (size_t)hq_nvfp4_partials(M, K) * sizeof(float);
+    if (need > kScratchBytes)
+        return set_last_error(DMPQ_ERR_WORKSPACE,
+                              "%s: M = %lld, K = %lld needs %zu bytes of scratch, the static "
+                              "array holds %zu", __func__, (long long)M, (long long)K, need,
+                              kScratchBytes);
     void *ws = nullptr;
     const hipError_t e = scratch_of_current_device(&ws);
     if (e != hipSuccess)
         return set_last_error(DMPQ_ERR_HIP, "%s: scratch address: %s", __func__, hipGetErrorString(e));
-    // the checked entry point validates the rest and launches on the scratch
-    // (kWsBytes, the workspace size it requires)
+    // the checked entry point launches on the scratch (kWsBytes, the
+    // workspace size it requires)
     return dmpq_hadamard_quant_nvfp4(stream, x, M, K, flags, codes, scales, d_g, ws, kScratchBytes);
 }

@@ -184,6 +184,29 @@ def test_fused_epilogue_validation(monkeypatch):
             _Fake((big, 1 << 12)), _Fake((1,)), _Fake((small,), numel=small), flags=dm.AMAX_GIVEN)
 
 
+def test_noalloc_and_w4_gemm_validation(monkeypatch):
+    """The no-workspace quantizer and the INT8 GEMM that converts an NVFP4
+    weight reject bad arguments before any launch (and their bindings reach
+    the library's error path)."""
+    _library_checks_only(monkeypatch)
+    _expect(2, dm.hadamard_quant_nvfp4_noalloc, _Fake((4, 24)), _Fake((4, 12)), _Fake((4, 1)), _Fake((1,)))
+    _expect(4, dm.hadamard_quant_nvfp4_noalloc, _Fake((4, 32)), _Fake((4, 16)), _Fake((4, 2)), _Fake((1,)),
+            flags=dm.AMAX_GIVEN)
+    M, N, K = 4, 8, 256
+    qa, sa, cw, sw, gw, y = (_Fake((M, K)), _Fake((M,)), _Fake((N, K // 2)), _Fake((N, K // 16)), _Fake((1,)),
+                             _Fake((M, N)))
+    need = dm.workspace_bytes(dm.OP_GEMM_W4, M, N)
+    assert need >= 8 * N
+    ws = _Fake((need,))
+    # K = 192 is not a multiple of 128
+    _expect(4, dm.qgemm_int8_from_nvfp4, _Fake((M, 192)), sa, _Fake((N, 96)), _Fake((N, 12)), gw, y, ws)
+    _expect(6, dm.qgemm_int8_from_nvfp4, qa, sa, cw, sw, gw, y, None)
+    _expect(6, dm.qgemm_int8_from_nvfp4, qa, sa, cw, sw, gw, y, _Fake((need - 1,)))
+    _expect(3, dm.qgemm_int8_from_nvfp4, qa, sa, cw, sw, gw, y, _Fake((need,), addr=0x10008))
+    _expect(1, dm.qgemm_int8_from_nvfp4, qa, sa, cw, sw, gw, y, ws, epilogue=4)
+    _expect(4, dm.qgemm_int8_from_nvfp4, qa, sa, cw, sw, gw, y, ws, epilogue=dm.EPI_GELU, out_dtype=dm.OUT_F32)
+
+
 def test_selftest_validation(monkeypatch):
     _library_checks_only(monkeypatch)
     _expect(1, dm.selftest_codec, 2, 0, 16, _Fake((384,)))
