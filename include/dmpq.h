@@ -174,7 +174,9 @@ dmpq_status dmpq_hadamard_quant_nvfp4(hipStream_t stream, const uint16_t *x, int
  * per device, kept until the process ends; it holds the partials of any
  * tensor size, and a size that would not fit is rejected with
  * DMPQ_ERR_WORKSPACE).  DMPQ_AMAX_GIVEN is rejected (DMPQ_ERR_UNSUPPORTED):
- * it reads the producer GEMM's workspace.  Allocates nothing.  Every call on
+ * it reads the producer GEMM's workspace.  Every argument is checked before
+ * the first HIP call (the scratch address is looked up once per device, on
+ * the first valid call).  Allocates nothing.  Every call on
  * a device shares that device's array: calls that overlap on one device
  * (concurrent streams, threads) race and must be ordered by the caller.
  * ------------------------------------------------------------------------- */
