@@ -374,72 +374,111 @@ __device__ __forceinline__ v8h dq8(const uint4 c, const v2h s2) {
 }
 
 // ---------------------------------------------------------------------------
-// DMA path (K % 256 == 0).  Raw codes and scales go from global memory
-// straight into LDS with global_load_lds_dwordx4, whole 128-byte rows per
-// stage (8 rows per instruction), and every wave dequantizes the fragments of
-// its own MFMAs from LDS into registers.  Compared with staging dequantized
-// tiles, the load path touches one cache line per 128 bytes instead of one per
-// 32, and LDS holds 4.5 bits per element instead of 16.
+// DMA path (K % 128 == 0).  Raw codes and scales go from global memory
+// straight into LDS with global_load_lds, and every wave dequantizes the
+// fragments of its own MFMAs from LDS into registers.  Compared with staging
+// dequantized tiles, the load path touches whole row segments of 64 or 128
+// bytes, and LDS holds 4.5 bits per element instead of 16.
 //
-// Stage: 256 K elements, per operand 256 rows x 128 code bytes (piece p of a
-// row, 16 bytes = K positions 32p .. 32p+31, stored at slot p ^ ((row >> 1) & 7)
-// so the 32-row fragment reads are conflict-free) and 256 rows x 16 scale
-// bytes; two stages in flight.  K order inside a 64-element chunk c: lane half
-// h holds piece 2c + h and feeds k-step s the positions 8s .. 8s+7 of it (the
-// same order on both operands, so products pair the same elements).
+// A stage is BK = 256 K elements (K % 256 == 0), or 128 (any other
+// K % 128 == 0, e.g. a 1920 hidden).  Per operand: 256 rows x BK/2 code
+// bytes, piece p of a row (16 bytes = K positions 32p .. 32p+31) stored at
+// slot p ^ key(row), key = (row >> 1) & 7 for 128-byte rows and
+// (row >> 2) & 3 for 64-byte rows, so the 32-row fragment reads hit distinct
+// 16-byte slots of each 256-byte bank span; and 256 rows x BK/16 scale bytes,
+// row-major for BK = 256 (one 16-byte DMA per row) and as two dword planes
+// (plane w: dword w of every row) for BK = 128, which the 4-byte DMA can
+// write.  Two stages in flight.  K order inside a 64-element chunk c: lane
+// half h holds piece 2c + h and feeds k-step s the positions 8s .. 8s+7 of it
+// (the same order on both operands, so products pair the same elements).
 // ---------------------------------------------------------------------------
+template <int BK>
+struct Fp4Dma {
+    static_assert(BK == 256 || BK == 128, "stage of 256 or 128 K elements");
+    static constexpr int BM = 256, BN = 256, BKE = BK;
+    static constexpr int CROW = BK / 2, SROW = BK / 16;    // code / scale bytes per row per stage
+    static constexpr int CODES = BM * CROW, SCALES = BM * SROW;
+    static constexpr int STAGE = 2 * CODES + 2 * SCALES;   // A codes, W codes, A scales, W scales
+    static constexpr int LDS_BYTES = 2 * STAGE > 4 * EpiBand<4>::BYTES ? 2 * STAGE : 4 * EpiBand<4>::BYTES;
+    static constexpr int CBLK = CODES / 1024 / 4;          // 1 KB code blocks per wave per operand
+    static constexpr int PIECES = CROW / 16;               // 16-byte pieces per row (8 or 4)
+    static constexpr int RBLK = 1024 / CROW;               // rows per code block (8 or 16)
+    static constexpr int SDMA = BK == 256 ? 1 : 2;         // scale DMA instructions per wave per operand
+    static constexpr int PER = 2 * CBLK + 2 * SDMA;        // DMA instructions per wave per stage (18 or 12)
+    static constexpr int CHUNKS = BK / 64;                 // 64-element chunks per stage
+    static constexpr unsigned GROUP_M = 8;
+    __device__ static __forceinline__ int key(int row) { return BK == 256 ? (row >> 1) & 7 : (row >> 2) & 3; }
+};
 namespace fp4dma {
-constexpr int BM = 256, BN = 256, BKE = 256;
-constexpr int CROW = BKE / 2, SROW = BKE / 16;  // code / scale bytes per row per stage
-constexpr int CODES = BM * CROW, SCALES = BM * SROW;
-constexpr int STAGE = 2 * CODES + 2 * SCALES;   // A codes, W codes, A scales, W scales
-constexpr int LDS_BYTES = 2 * STAGE;
-static_assert(4 * EpiBand<4>::BYTES <= LDS_BYTES, "epilogue bands fit in the stage buffers");
+constexpr int BM = 256, BN = 256;
 constexpr unsigned GROUP_M = 8;
+static_assert(Fp4Dma<256>::LDS_BYTES <= 160 * 1024 && Fp4Dma<128>::LDS_BYTES <= 160 * 1024,
+              "LDS of the NVFP4 DMA kernels");
 }  // namespace fp4dma
 
 // Per-lane state of the DMA kernel.  Fragment rows ra = wm*128 + 32i + lane%32
-// share the swizzle key ((lane%32) >> 1) & 7, so the row block i only adds a
-// constant (an immediate offset) to the lane's base addresses.
+// share the swizzle key of lane%32, so the row block i only adds a constant
+// (an immediate offset) to the lane's base addresses.
+template <int BK>
 struct Fp4DmaLane {
-    const uint8_t *srcA[8], *srcW[8], *srcSA, *srcSW;
+    const uint8_t *srcA[Fp4Dma<BK>::CBLK], *srcW[Fp4Dma<BK>::CBLK], *srcSA, *srcSW;
     int offA, offW, offSA, offSW;  // byte offsets of the lane's first fragment row in a stage
     int wave, hk, sh, sw;
 };
 
-// DMA instruction d (0..17) of a stage: code blocks q = d/2 of A (d even) and
-// W (d odd), then the A and the W scale block.
-__device__ __forceinline__ void fp4dma_one(uint8_t *dst, const Fp4DmaLane &L, int64_t st, int d) {
-    using namespace fp4dma;
+// DMA instruction d (0 .. PER-1) of the stage st: code blocks q = d/2 of A (d
+// even) and W (d odd), then the scales: BK = 256, the A and the W block (16
+// bytes per row); BK = 128, A and W plane 0, then A and W plane 1 (4 bytes
+// per row).
+template <int BK>
+__device__ __forceinline__ void fp4dma_one(uint8_t *dst, const Fp4DmaLane<BK> &L, int64_t st, int d) {
+    using T = Fp4Dma<BK>;
     typedef __attribute__((address_space(3))) void lds_void;
-    if (d < 16) {
+    if (d < 2 * T::CBLK) {
         const int q = d >> 1, b = L.wave + 4 * q;
-        const uint8_t *src = ((d & 1) ? L.srcW[q] : L.srcA[q]) + st * CROW;
-        __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(dst + (d & 1) * CODES + b * 1024), 16, 0, 0);
-    } else {
-        const uint8_t *src = (d == 17 ? L.srcSW : L.srcSA) + st * SROW;
+        const uint8_t *src = ((d & 1) ? L.srcW[q] : L.srcA[q]) + st * T::CROW;
+        __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(dst + (d & 1) * T::CODES + b * 1024), 16, 0, 0);
+    } else if constexpr (BK == 256) {
+        const uint8_t *src = (d == 2 * T::CBLK + 1 ? L.srcSW : L.srcSA) + st * T::SROW;
         __builtin_amdgcn_global_load_lds((const void *)src,
-                                         (lds_void *)(dst + 2 * CODES + (d == 17) * SCALES + L.wave * 1024), 16, 0, 0);
+                                         (lds_void *)(dst + 2 * T::CODES + (d == 2 * T::CBLK + 1) * T::SCALES + L.wave * 1024),
+                                         16, 0, 0);
+    } else {
+        const int e = d - 2 * T::CBLK, op = e & 1, w = e >> 1;
+        const uint8_t *src = (op ? L.srcSW : L.srcSA) + st * T::SROW + 4 * w;
+        __builtin_amdgcn_global_load_lds((const void *)src,
+                                         (lds_void *)(dst + 2 * T::CODES + op * T::SCALES + w * (T::BM * 4) + L.wave * 256),
+                                         4, 0, 0);
     }
 }
 
 // One stage of the DMA kernel: run the stage held in `cur` while the DMA of
-// stage st_next goes into `nxt`, its 18 instructions spread over the MFMAs of
+// stage st_next goes into `nxt`, its PER instructions spread over the MFMAs of
 // the first 64-element chunk (one after every third MFMA) rather than issued
 // in one burst.  The DMA is issued on every stage so that no branch wraps the
 // MFMA code; after the last stage the caller passes a stage nobody reads
 // again.  The two buffers are separate restrict parameters so that, once
 // inlined, the compiler knows the stage's LDS reads cannot alias the DMA in
 // flight and does not wait for it.
+template <int BK>
 __device__ __forceinline__ void fp4dma_stage(const uint8_t *__restrict__ cur, uint8_t *__restrict__ nxt,
-                                             int64_t st_next, const Fp4DmaLane &L,
-                                             v16f (&acc)[4][4]) {
-    using namespace fp4dma;
+                                             int64_t st_next, const Fp4DmaLane<BK> &L, v16f (&acc)[4][4]) {
+    using T = Fp4Dma<BK>;
+    constexpr int CROW = T::CROW, SROW = T::SROW, PER = T::PER;
+    // the lane's scale words: word c holds the four scale bytes of chunk c
     uint4 sA[4], sW[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        sA[i] = *reinterpret_cast<const uint4 *>(cur + L.offSA + i * 32 * SROW);
-        sW[i] = *reinterpret_cast<const uint4 *>(cur + L.offSW + i * 32 * SROW);
+        if constexpr (BK == 256) {
+            sA[i] = *reinterpret_cast<const uint4 *>(cur + L.offSA + i * 32 * SROW);
+            sW[i] = *reinterpret_cast<const uint4 *>(cur + L.offSW + i * 32 * SROW);
+        } else {
+            sA[i].x = *reinterpret_cast<const uint32_t *>(cur + L.offSA + i * 128);
+            sA[i].y = *reinterpret_cast<const uint32_t *>(cur + L.offSA + T::BM * 4 + i * 128);
+            sW[i].x = *reinterpret_cast<const uint32_t *>(cur + L.offSW + i * 128);
+            sW[i].y = *reinterpret_cast<const uint32_t *>(cur + L.offSW + T::BM * 4 + i * 128);
+            sA[i].z = sA[i].w = sW[i].z = sW[i].w = 0u;  // no chunks 2 and 3
+        }
     }
 #define DMPQ_F4D_CODES(dA, dW, c)                                                              \
     {                                                                                          \
@@ -454,14 +493,14 @@ __device__ __forceinline__ void fp4dma_stage(const uint8_t *__restrict__ cur, ui
         fa[i] = dq8<S>(cA[i], scA[i]);                                                         \
         fb[i] = dq8<S>(cW[i], scW[i]);                                                         \
     }
-// 16 MFMAs; with DMA (D0 >= 0) instructions D0, D0+1, ... (below 18) after
+// 16 MFMAs; with DMA (D0 >= 0) instructions D0, D0+1, ... (below PER) after
 // MFMAs 2, 5, 8, 11, 14
 #define DMPQ_F4D_MFMA(fa, fb, D0)                                                              \
     _Pragma("unroll") for (int i = 0; i < 4; i++)                                              \
         _Pragma("unroll") for (int j = 0; j < 4; j++) {                                        \
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0); \
             const int t = 4 * i + j;                                                           \
-            if ((D0) >= 0 && t % 3 == 2 && (D0) + t / 3 < 18) fp4dma_one(nxt, L, st_next, (D0) + t / 3); \
+            if ((D0) >= 0 && t % 3 == 2 && (D0) + t / 3 < PER) fp4dma_one<BK>(nxt, L, st_next, (D0) + t / 3); \
         }
 #define DMPQ_F4D_CHUNK(cA, cW, c, D0)                                                          \
     {                                                                                          \
@@ -486,11 +525,15 @@ __device__ __forceinline__ void fp4dma_stage(const uint8_t *__restrict__ cur, ui
     DMPQ_F4D_CODES(cA0, cW0, 0)
     DMPQ_F4D_CODES(cA1, cW1, 1)
     DMPQ_F4D_CHUNK(cA0, cW0, 0, 0)
-    DMPQ_F4D_CODES(cA0, cW0, 2)
-    DMPQ_F4D_CHUNK(cA1, cW1, 1, -1)
-    DMPQ_F4D_CODES(cA1, cW1, 3)
-    DMPQ_F4D_CHUNK(cA0, cW0, 2, -1)
-    DMPQ_F4D_CHUNK(cA1, cW1, 3, -1)
+    if constexpr (T::CHUNKS == 4) {
+        DMPQ_F4D_CODES(cA0, cW0, 2)
+        DMPQ_F4D_CHUNK(cA1, cW1, 1, -1)
+        DMPQ_F4D_CODES(cA1, cW1, 3)
+        DMPQ_F4D_CHUNK(cA0, cW0, 2, -1)
+        DMPQ_F4D_CHUNK(cA1, cW1, 3, -1)
+    } else {
+        DMPQ_F4D_CHUNK(cA1, cW1, 1, -1)
+    }
 #undef DMPQ_F4D_CODES
 #undef DMPQ_F4D_DQ
 #undef DMPQ_F4D_MFMA
@@ -499,11 +542,12 @@ __device__ __forceinline__ void fp4dma_stage(const uint8_t *__restrict__ cur, ui
 
 // The main loop of the DMA kernel over stages kt0 .. kt1-1 of the tile at
 // (m0, n0); on return the stage buffers are free.
+template <int BK>
 __device__ __forceinline__ void fp4dma_mainloop(const uint8_t *__restrict__ ca, const uint8_t *__restrict__ sa,
                                                 const uint8_t *__restrict__ cw, const uint8_t *__restrict__ sw,
                                                 int64_t M, int64_t N, int64_t K, int64_t m0, int64_t n0,
                                                 int kt0, int kt1, uint8_t *lds, v16f (&acc)[4][4]) {
-    using namespace fp4dma;
+    using T = Fp4Dma<BK>;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -517,18 +561,19 @@ __device__ __forceinline__ void fp4dma_mainloop(const uint8_t *__restrict__ ca, 
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
-    // DMA sources.  Code block b = wave + 4q (q = 0..7) covers tile rows
-    // 8b .. 8b+7, lane l filling slot l % 8 of row 8b + l / 8; scale block
-    // `wave` covers rows 64 wave .. +63, one 16-byte row per lane.  Rows past
-    // M or N load a clamped row; their outputs are never stored.
-    Fp4DmaLane L;
+    // DMA sources.  Code block b = wave + 4q covers tile rows RBLK*b ..
+    // RBLK*b + RBLK-1, lane l filling slot l % PIECES of row
+    // RBLK*b + l / PIECES; the scale DMA of a wave covers rows 64 wave .. +63,
+    // one lane per row.  Rows past M or N load a clamped row; their outputs
+    // are never stored.
+    Fp4DmaLane<BK> L;
     L.wave = wave;
     L.hk = lane >> 5;
     L.sh = 16 * L.hk;
 #pragma unroll
-    for (int q = 0; q < 8; q++) {
-        const int row = 8 * (wave + 4 * q) + (lane >> 3);
-        const int piece = (lane & 7) ^ ((row >> 1) & 7);
+    for (int q = 0; q < T::CBLK; q++) {
+        const int row = T::RBLK * (wave + 4 * q) + lane / T::PIECES;
+        const int piece = (lane % T::PIECES) ^ T::key(row);
         const int64_t gm = m0 + row < M ? m0 + row : M - 1;
         const int64_t gn = n0 + row < N ? n0 + row : N - 1;
         L.srcA[q] = ca + gm * rb + piece * 16;
@@ -541,33 +586,34 @@ __device__ __forceinline__ void fp4dma_mainloop(const uint8_t *__restrict__ ca, 
         L.srcSA = sa + gm * nb;
         L.srcSW = sw + gn * nb;
     }
-    L.offA = (wm * 128 + (lane & 31)) * CROW;
-    L.offW = CODES + (wn * 128 + (lane & 31)) * CROW;
-    L.offSA = 2 * CODES + (wm * 128 + (lane & 31)) * SROW;
-    L.offSW = 2 * CODES + SCALES + (wn * 128 + (lane & 31)) * SROW;
-    L.sw = ((lane & 31) >> 1) & 7;
+    const int ra = wm * 128 + (lane & 31), rw = wn * 128 + (lane & 31);
+    L.offA = ra * T::CROW;
+    L.offW = T::CODES + rw * T::CROW;
+    L.offSA = 2 * T::CODES + ra * (BK == 256 ? T::SROW : 4);
+    L.offSW = 2 * T::CODES + T::SCALES + rw * (BK == 256 ? T::SROW : 4);
+    L.sw = T::key(lane & 31);
 
 #pragma unroll
-    for (int d = 0; d < 18; d++) fp4dma_one(lds, L, kt0, d);
+    for (int d = 0; d < T::PER; d++) fp4dma_one<BK>(lds, L, kt0, d);
     for (int kt = 0; kt < nk; kt++) {
         __builtin_amdgcn_s_waitcnt(0xC07F & ~0xC00F);  // vmcnt(0): this wave's loads of stage kt
         __syncthreads();                               // ... and every other wave's
         // after the last stage the copy goes to a buffer nobody reads again
-        fp4dma_stage(lds + (kt & 1) * STAGE, lds + ((kt & 1) ^ 1) * STAGE, kt0 + (kt + 1 < nk ? kt + 1 : kt), L,
-                     acc);
+        fp4dma_stage<BK>(lds + (kt & 1) * T::STAGE, lds + ((kt & 1) ^ 1) * T::STAGE,
+                         kt0 + (kt + 1 < nk ? kt + 1 : kt), L, acc);
     }
     __builtin_amdgcn_s_waitcnt(0xC07F & ~0xC00F);  // the last copy has landed
     __syncthreads();  // every wave is done reading the stage buffers before they hold bands
 }
 
-template <int OUT, int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_fp4_dma_kernel(
-    const uint8_t *__restrict__ ca, const uint8_t *__restrict__ sa, const float *__restrict__ ga,
-    const uint8_t *__restrict__ cw, const uint8_t *__restrict__ sw, const float *__restrict__ gw,
-    int64_t M, int64_t N, int64_t K, void *__restrict__ y, unsigned tiles_m, unsigned tiles_n,
-    float *__restrict__ partial) {
+template <int OUT, int EPI, int BK>
+__device__ __forceinline__ void fp4dma_tile(const uint8_t *__restrict__ ca, const uint8_t *__restrict__ sa,
+                                            const float *__restrict__ ga, const uint8_t *__restrict__ cw,
+                                            const uint8_t *__restrict__ sw, const float *__restrict__ gw,
+                                            int64_t M, int64_t N, int64_t K, void *__restrict__ y,
+                                            unsigned tiles_m, unsigned tiles_n, float *__restrict__ partial,
+                                            uint8_t *lds) {
     using namespace fp4dma;
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -575,22 +621,61 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_dma_kernel(
     const TileCoord tc = tile_at(pid, tiles_m, tiles_n, GROUP_M);
     const int64_t m0 = (int64_t)tc.m * BM, n0 = (int64_t)tc.n * BN;
     v16f acc[4][4];
-    fp4dma_mainloop(ca, sa, cw, sw, M, N, K, m0, n0, 0, (int)(K / BKE), lds, acc);
+    fp4dma_mainloop<BK>(ca, sa, cw, sw, M, N, K, m0, n0, 0, (int)(K / BK), lds, acc);
     fp4_epilogue<OUT, EPI>(acc, lds, ga, gw, M, N, m0, n0, wave, wm, wn, lane, y, partial, pid);
 }
 
+// The whole-tile kernels, one per stage size (kernels of their own, so that
+// each keeps its name in traces).
+template <int OUT, int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_fp4_dma_kernel(
+    const uint8_t *__restrict__ ca, const uint8_t *__restrict__ sa, const float *__restrict__ ga,
+    const uint8_t *__restrict__ cw, const uint8_t *__restrict__ sw, const float *__restrict__ gw,
+    int64_t M, int64_t N, int64_t K, void *__restrict__ y, unsigned tiles_m, unsigned tiles_n,
+    float *__restrict__ partial) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    fp4dma_tile<OUT, EPI, 256>(ca, sa, ga, cw, sw, gw, M, N, K, y, tiles_m, tiles_n, partial, lds);
+}
+
+template <int OUT, int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_fp4_dma128_kernel(
+    const uint8_t *__restrict__ ca, const uint8_t *__restrict__ sa, const float *__restrict__ ga,
+    const uint8_t *__restrict__ cw, const uint8_t *__restrict__ sw, const float *__restrict__ gw,
+    int64_t M, int64_t N, int64_t K, void *__restrict__ y, unsigned tiles_m, unsigned tiles_n,
+    float *__restrict__ partial) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    fp4dma_tile<OUT, EPI, 128>(ca, sa, ga, cw, sw, gw, M, N, K, y, tiles_m, tiles_n, partial, lds);
+}
+
 // The split workgroups of a SplitPlan launch (see gemm_i8_split_kernel).
+template <int BK>
+__device__ __forceinline__ void fp4dma_split(const uint8_t *__restrict__ ca, const uint8_t *__restrict__ sa,
+                                             const uint8_t *__restrict__ cw, const uint8_t *__restrict__ sw,
+                                             int64_t M, int64_t N, int64_t K, unsigned tiles_m, unsigned tiles_n,
+                                             const SplitPlan &sp, uint32_t *__restrict__ spart,
+                                             float *__restrict__ partial, uint8_t *lds) {
+    using namespace fp4dma;
+    const SplitUnit u = split_unit(sp, tiles_m, tiles_n, GROUP_M);
+    if (partial && u.kt0 == 0 && threadIdx.x == 0) partial[sp.full + blockIdx.x / sp.splits] = 0.0f;
+    v16f acc[4][4];
+    fp4dma_mainloop<BK>(ca, sa, cw, sw, M, N, K, (int64_t)u.tc.m * BM, (int64_t)u.tc.n * BN, u.kt0, u.kt1, lds, acc);
+    store_split_partial(acc, spart + (size_t)blockIdx.x * kSplitWords, threadIdx.x);
+}
+
 __global__ __launch_bounds__(256, 1) void gemm_fp4_split_kernel(
     const uint8_t *__restrict__ ca, const uint8_t *__restrict__ sa, const uint8_t *__restrict__ cw,
     const uint8_t *__restrict__ sw, int64_t M, int64_t N, int64_t K, unsigned tiles_m, unsigned tiles_n,
     SplitPlan sp, uint32_t *__restrict__ spart, float *__restrict__ partial) {
-    using namespace fp4dma;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const SplitUnit u = split_unit(sp, tiles_m, tiles_n, GROUP_M);
-    if (partial && u.kt0 == 0 && threadIdx.x == 0) partial[sp.full + blockIdx.x / sp.splits] = 0.0f;
-    v16f acc[4][4];
-    fp4dma_mainloop(ca, sa, cw, sw, M, N, K, (int64_t)u.tc.m * BM, (int64_t)u.tc.n * BN, u.kt0, u.kt1, lds, acc);
-    store_split_partial(acc, spart + (size_t)blockIdx.x * kSplitWords, threadIdx.x);
+    fp4dma_split<256>(ca, sa, cw, sw, M, N, K, tiles_m, tiles_n, sp, spart, partial, lds);
+}
+
+__global__ __launch_bounds__(256, 1) void gemm_fp4_split128_kernel(
+    const uint8_t *__restrict__ ca, const uint8_t *__restrict__ sa, const uint8_t *__restrict__ cw,
+    const uint8_t *__restrict__ sw, int64_t M, int64_t N, int64_t K, unsigned tiles_m, unsigned tiles_n,
+    SplitPlan sp, uint32_t *__restrict__ spart, float *__restrict__ partial) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    fp4dma_split<128>(ca, sa, cw, sw, M, N, K, tiles_m, tiles_n, sp, spart, partial, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -730,6 +815,31 @@ static hipError_t allow_lds(KernelFn fn, size_t bytes) {
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
+// The DMA path for one stage size: the whole-tile kernel over the full
+// waves, then (with a split plan) the tail's split workgroups and the fixup.
+template <int OUT, int EPI, int BK, class TileFn, class SplitFn>
+static hipError_t launch_fp4_dma(hipStream_t s, TileFn tile_kernel, SplitFn split_kernel, const uint8_t *ca,
+                                 const uint8_t *sa, const float *ga, const uint8_t *cw, const uint8_t *sw,
+                                 const float *gw, int64_t M, int64_t N, int64_t K, void *y, float *partial,
+                                 uint32_t *spart, unsigned utm, unsigned utn) {
+    constexpr size_t lds = Fp4Dma<BK>::LDS_BYTES;
+    const SplitPlan sp = plan_split((int64_t)utm * utn, (int)(K / BK), spart != nullptr);
+    if (sp.full > 0) {
+        hipLaunchKernelGGL(tile_kernel, dim3(sp.full), dim3(256), lds, s, ca, sa, ga, cw, sw, gw, M, N, K, y, utm,
+                           utn, partial);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (sp.splits > 1) {
+        hipLaunchKernelGGL(split_kernel, dim3(sp.tail * sp.splits), dim3(256), lds, s, ca, sa, cw, sw, M, N, K, utm,
+                           utn, sp, spart, (EPI & kEpiAmax) ? partial : nullptr);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_f32_fixup(s, ga, gw, M, N, y, utm, utn, fp4dma::GROUP_M, partial, sp, spart, OUT, EPI);
+    }
+    return hipGetLastError();
+}
+
 template <int OUT, int EPI>
 static hipError_t launch_fp4_paths(hipStream_t s, const uint8_t *ca, const uint8_t *sa,
                                    const float *ga, const uint8_t *cw, const uint8_t *sw,
@@ -739,30 +849,23 @@ static hipError_t launch_fp4_paths(hipStream_t s, const uint8_t *ca, const uint8
     static const hipError_t attr = [] {
         hipError_t e = allow_lds(gemm_fp4_f16_kernel<OUT, EPI>, 2 * STAGE);
         if (e == hipSuccess) e = allow_lds(gemm_fp4_fast_kernel<OUT, EPI>, 2 * STAGE);
-        if (e == hipSuccess) e = allow_lds(gemm_fp4_dma_kernel<OUT, EPI>, fp4dma::LDS_BYTES);
-        if (e == hipSuccess) e = allow_lds(gemm_fp4_split_kernel, fp4dma::LDS_BYTES);
+        if (e == hipSuccess) e = allow_lds(gemm_fp4_dma_kernel<OUT, EPI>, Fp4Dma<256>::LDS_BYTES);
+        if (e == hipSuccess) e = allow_lds(gemm_fp4_split_kernel, Fp4Dma<256>::LDS_BYTES);
+        if (e == hipSuccess) e = allow_lds(gemm_fp4_dma128_kernel<OUT, EPI>, Fp4Dma<128>::LDS_BYTES);
+        if (e == hipSuccess) e = allow_lds(gemm_fp4_split128_kernel, Fp4Dma<128>::LDS_BYTES);
         return e;
     }();
     if (attr != hipSuccess) return attr;
     const int64_t tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
     const dim3 grid((unsigned)(tm * tn)), block(256);
     const unsigned utm = (unsigned)tm, utn = (unsigned)tn;
-    if (K % fp4dma::BKE == 0) {
-        const SplitPlan sp = plan_split(tm * tn, (int)(K / fp4dma::BKE), spart != nullptr);
-        if (sp.full > 0) {
-            hipLaunchKernelGGL((gemm_fp4_dma_kernel<OUT, EPI>), dim3(sp.full), block, fp4dma::LDS_BYTES, s, ca, sa,
-                               ga, cw, sw, gw, M, N, K, y, utm, utn, partial);
-            const hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
-        }
-        if (sp.splits > 1) {
-            hipLaunchKernelGGL(gemm_fp4_split_kernel, dim3(sp.tail * sp.splits), block, fp4dma::LDS_BYTES, s, ca, sa,
-                               cw, sw, M, N, K, utm, utn, sp, spart, (EPI & kEpiAmax) ? partial : nullptr);
-            const hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
-            return launch_f32_fixup(s, ga, gw, M, N, y, utm, utn, fp4dma::GROUP_M, partial, sp, spart, OUT, EPI);
-        }
-    } else if (K % (4 * 16) == 0) {
+    if (K % 256 == 0)
+        return launch_fp4_dma<OUT, EPI, 256>(s, gemm_fp4_dma_kernel<OUT, EPI>, gemm_fp4_split_kernel, ca, sa, ga,
+                                             cw, sw, gw, M, N, K, y, partial, spart, utm, utn);
+    if (K % 128 == 0)
+        return launch_fp4_dma<OUT, EPI, 128>(s, gemm_fp4_dma128_kernel<OUT, EPI>, gemm_fp4_split128_kernel, ca, sa,
+                                             ga, cw, sw, gw, M, N, K, y, partial, spart, utm, utn);
+    if (K % (4 * 16) == 0) {
         hipLaunchKernelGGL((gemm_fp4_fast_kernel<OUT, EPI>), grid, block, 2 * STAGE, s, ca, sa, ga, cw,
                            sw, gw, M, N, K, y, utm, utn, partial);
     } else {
