@@ -1,6 +1,7 @@
 """GPU parity of the tail split along K: the *_ex GEMMs with a full GEMM
 workspace (DMPQ_OP_GEMM) split the tiles beyond the last multiple of 256
-along K and add the parts in a fixed order in a second kernel.
+along K (by stages: 256 K elements, or 128 for an NVFP4 K that is a
+multiple of 128 but not of 256) and add the parts in a fixed order in a second kernel.
 
 INT8: int32 parts add exactly, so the outputs are bit-exact against the
 oracle and bit-identical to the unsplit call.  NVFP4 and BF16: the same
@@ -87,13 +88,16 @@ def _run_fp4(args, M, N, ws, out=dm.OUT_F32):
 
 
 @pytest.mark.parametrize("M,N,K,sample", [(600, 528, 512, False), (600, 528, 2048, False),
+                                          (600, 528, 1920, False), (600, 528, 384, False),
                                           (4352, 4096, 1024, True),
                                           (workloads.M_480P, 3072, 12288, True),
                                           (workloads.M_480P, 12288, 3072, True),
-                                          (workloads.M_480P, 3072, 3072, True)])
+                                          (workloads.M_480P, 3072, 3072, True),
+                                          (workloads.M_480P, 1920, 1920, True)])
 def test_split_nvfp4(orc, M, N, K, sample):
+    # K % 256 == 0 runs 256-element stages, other K % 128 == 0 128-element ones
     require_gpu()
-    S = _splits(M, N, K // 256)
+    S = _splits(M, N, K // 256 if K % 256 == 0 else K // 128)
     say(f"split nvfp4 M={M} N={N} K={K} splits={S}")
     assert S > 1
     rng = np.random.default_rng(2 * M + N + K)
@@ -137,15 +141,14 @@ def test_split_bf16(orc, M, N, K, sample):
     assert np.all(err <= TOL * b0), float((err / np.maximum(b0, 1e-300)).max())
 
 
-@pytest.mark.parametrize("kind", ["int8", "nvfp4", "bf16"])
-def test_split_with_fused_epilogue(orc, kind):
+@pytest.mark.parametrize("kind,K", [("int8", 4096), ("nvfp4", 2048), ("nvfp4", 1920), ("bf16", 208)])
+def test_split_with_fused_epilogue(orc, kind, K):
     """GELU + amax on split tiles: the output equals the unsplit fused call's
     (INT8) or its GELU of the split pre-activation, and the per-tile maxima
     are the tiles' own, so the given-amax quantization matches the two-pass
     one bit for bit."""
     require_gpu()
     M, N = 600, 528
-    K = {"int8": 4096, "nvfp4": 2048, "bf16": 208}[kind]
     say(f"split + fused epilogue {kind} M={M} N={N} K={K}")
     rng = np.random.default_rng(K + 5)
     x = workloads.activations(rng, M, K)

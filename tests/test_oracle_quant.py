@@ -2,10 +2,13 @@
 
 Pinned against: exact round trips of tensors built on the quantization grid
 (scale a power of two for INT8; g = 1 and every block amax = 6 * scale for
-NVFP4), zero and spike special cases, RNE error bounds, row-permutation
+NVFP4), NVFP4 scales and codes at g != 1 against exact rational RNE, zero
+and spike special cases, RNE error bounds, row-permutation
 equivariance, the Hadamard composed from its closed form, and X W^T
 invariance of the rotation.
 """
+from fractions import Fraction
+
 import numpy as np
 import pytest
 
@@ -142,6 +145,73 @@ def test_nvfp4_properties_random(orc):
     err = np.abs(val * S16 - xt)
     clip = np.maximum(np.abs(xt) - 6 * S16, 0)
     assert np.all(err <= 1.0 * S16 * (1 + 1e-6) + clip)
+
+
+def _rne_on_grid(q, grid):
+    """Index of the nearest value of the ascending exact grid to q >= 0 (ties to
+    the even index, values above the top saturate), and whether q lies within
+    a relative 2^-20 of a midpoint (where fp32 evaluation may round either way)."""
+    if q >= grid[-1]:
+        return len(grid) - 1, False
+    hi = next(i for i, v in enumerate(grid) if v >= q)
+    if grid[hi] == q or hi == 0:
+        return hi, False
+    lo = hi - 1
+    mid = (grid[lo] + grid[hi]) / 2
+    near = abs(q - mid) <= q * Fraction(1, 2 ** 20)
+    if q == mid:
+        return (lo if lo % 2 == 0 else hi), near
+    return (lo if q < mid else hi), near
+
+
+def _e4m3_grid():
+    vals = []
+    for c in range(0x7F):  # non-negative finite codes, ascending
+        e, m = c >> 3, c & 7
+        vals.append(Fraction(m, 8) * Fraction(1, 64) if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7))
+    return vals
+
+
+def test_nvfp4_scales_and_codes_against_exact_rationals(orc):
+    """At g != 1, on blocks spanning the E4M3 range: every block scale is the
+    E4M3 RNE of the exact rational 448 * a_b / A and every code the E2M1 RNE
+    of x / (E4M3(...) * A / 2688), except within fp32 rounding distance of a
+    midpoint (the pages fix no evaluation order; those cases are counted)."""
+    rng = np.random.default_rng(31)
+    M, K = 24, 384
+    x = workloads.activations(rng, M, K)
+    c, s, g = orc.quant_nvfp4(x, flags=orc.NO_HADAMARD)
+    xf = bf16_bits_to_f32(x)
+    A = Fraction(float(np.abs(xf).max()))
+    assert g == np.float32(np.float32(float(A)) / np.float32(2688.0)) and g != 1.0
+    e4 = _e4m3_grid()
+    e2 = [Fraction(v, 2) for v in (0, 1, 2, 3, 4, 6, 8, 12)]
+    codes = orc.nibbles(c)
+    skipped = checked = 0
+    for m in range(M):
+        for b in range(K // 16):
+            blk = xf[m, 16 * b:16 * b + 16]
+            ab = Fraction(float(np.abs(blk).max()))
+            want, near = _rne_on_grid(448 * ab / A, e4)
+            if near:
+                skipped += 1
+                continue
+            assert s[m, b] == want, (m, b)
+            S = e4[want] * A / 2688
+            if float(S) < np.finfo(np.float32).tiny:
+                assert not codes[m, 16 * b:16 * b + 16].any()
+                continue
+            for i in range(16):
+                v = Fraction(float(blk[i]))
+                k, near = _rne_on_grid(abs(v) / S, e2)
+                if near:
+                    skipped += 1
+                    continue
+                sign = 8 if np.signbit(blk[i]) else 0
+                assert codes[m, 16 * b + i] == (k | sign), (m, b, i)
+                checked += 1
+    assert len(set(s.ravel().tolist())) > 20          # many scale codes exercised
+    assert checked > 0.95 * M * K and skipped < 0.01 * M * K
 
 
 def test_nvfp4_hadamard_is_block_rotation(orc):
