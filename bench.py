@@ -750,19 +750,26 @@ def run_schedule_workload(torch, dm, wl, events: str, T: int = 50, NB: int = 42)
     eps_sim = median d, delta_acc = 2.5 median d).  Runs the schedule three
     times from the same state: without events (the wall time), with events
     around every library call (per-kernel time; its decisions must equal the
-    first run's), and with every block refreshed (the no-TDC reference)."""
+    first run's), and with every block refreshed (the no-TDC reference).
+    A fourth run uses a fitted router: over CAL always-refresh steps every
+    linear's NVFP4 error against its BF16 output (ErrorProbe) is paired with
+    the Gamma the router saw, alpha_l and beta_l are fitted by least squares
+    (fit_router) and tau is the median predicted error of those samples."""
     import numpy as np
 
+    from dynamic_mixed_precision_amd.calibrate import ErrorProbe, fit_router
     from dynamic_mixed_precision_amd.schedule import TdcScheduler
+    CAL = 6
     cfg = wl.PROXY_DIT
     M, H = cfg.M, cfg.hidden
     gen = wl.device_generator(cfg.seeds[0])
     ws_prep = dm.new_workspace(dm.OP_PREP_WEIGHT)
-    blocks = []
+    blocks, blocks_bf16 = [], []
     for _ in range(NB):
         w1 = wl.weight_device(gen, H, H)
         w2 = (wl.weight_device(gen, H, H).float() * 0.3).to(torch.bfloat16)
         blocks.append((_nvfp4_weight(torch, dm, w1, ws_prep), _nvfp4_weight(torch, dm, w2, ws_prep)))
+        blocks_bf16.append((w1, w2))
     z = [wl.activations_device(gen, M, H)]
     for _ in range(T - 1):                    # the drifting latents, resident before timing
         n = torch.randn((M, H), generator=gen, device="cuda", dtype=torch.float32)
@@ -778,8 +785,8 @@ def run_schedule_workload(torch, dm, wl, events: str, T: int = 50, NB: int = 42)
     ws_gemm = dm.new_workspace(dm.OP_GEMM, "cuda", M, H)
     alpha, beta = np.ones(2), np.zeros(2)
 
-    def run(steps, tau, eps, dacc, kt, force_refresh=False):
-        sched = TdcScheduler(NB, M * H, alpha, beta, tau, eps, dacc)
+    def run(steps, tau, eps, dacc, kt, force_refresh=False, router=(alpha, beta), probe=None):
+        sched = TdcScheduler(NB, M * H, router[0], router[1], tau, eps, dacc)
         log = []
         ops = 0.0
         for t in range(steps):
@@ -794,9 +801,11 @@ def run_schedule_workload(torch, dm, wl, events: str, T: int = 50, NB: int = 42)
                     dm.tdc_commit(b.state, dm.TDC_SKIP)
                     log.append((t, i, "skip"))
                 else:
-                    r = sched.routes(i)[2]
+                    g_seen, _, r = sched.routes(i)
                     l1, l2 = blocks[i]
                     ops += _gemm_call(dm, kt, int(r[0]), x, qb, l1, h, ws_q, ws_gemm, w8, s8, dm.EPI_GELU)
+                    if probe is not None and sched.blocks[i].state.gamma_valid:
+                        probe(g_seen, (x, l1, blocks_bf16[i][0]), (h, l2, blocks_bf16[i][1]))
                     ops += _gemm_call(dm, kt, int(r[1]), h, qb, l2, y, ws_q, ws_gemm, w8, s8)
                     torch.add(x, y, out=out)
                     b = sched.blocks[i]
@@ -833,18 +842,43 @@ def run_schedule_workload(torch, dm, wl, events: str, T: int = 50, NB: int = 42)
     _, _, ops_all = run(T, tau, eps, dacc, off, force_refresh=True)
     torch.cuda.synchronize()
     wall_all = time.perf_counter() - t0
-    skips = sum(1 for e in log if e[2] == "skip")
-    calls = [r for e in log if e[2] != "skip" for r in e[2]]
-    n8 = sum(1 for r in calls if r == dm.ROUTE_INT8)
-    n4 = sum(1 for r in calls if r == dm.ROUTE_NVFP4)
+
+    # fitted router: (Gamma seen, NVFP4 error of each linear) over CAL steps
+    ep = ErrorProbe(M, H, H)
+    samples = []
+
+    def probe(g_seen, *lins):
+        samples.append((g_seen, [ep(xi, wb, L["cw"], L["sw"], L["gw"]) for xi, L, wb in lins]))
+
+    run(CAL, float("inf"), 0.0, 0.0, off, probe=probe)       # always refresh, routes NVFP4
+    gs = np.array([smp[0] for smp in samples])
+    errs = np.array([smp[1] for smp in samples])
+    a_fit, b_fit, rms = fit_router(gs, errs)
+    tau_fit = float(np.median(a_fit[None, :] * gs[:, None] + b_fit[None, :]))
+    del ep
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    _, log_fit, _ = run(T, tau_fit, eps, dacc, off, router=(a_fit, b_fit))
+    torch.cuda.synchronize()
+    wall_fit = time.perf_counter() - t0
+
     bits = {dm.ROUTE_INT8: 8.0, dm.ROUTE_NVFP4: 4.5}
+
+    def mix(lg):
+        calls = [r for e in lg if e[2] != "skip" for r in e[2]]
+        return (sum(1 for e in lg if e[2] == "skip"), sum(1 for r in calls if r == dm.ROUTE_INT8),
+                sum(1 for r in calls if r == dm.ROUTE_NVFP4),
+                round(sum(bits[r] for r in calls) / max(len(calls), 1), 3))
+
+    skips, n8, n4, avg_bits = mix(log)
+    fs, f8, f4, fbits = mix(log_fit)
     return {
         "workload": (f"proxy DiT, {NB} blocks x + W2 GELU(W1 x) (hidden {H}), {M} tokens, {T} timesteps of "
                      "a drifting latent; TDC skip/refresh + Gamma router, GELU fused into W1's GEMM"),
         "thresholds": {"tau": tau, "eps_sim": eps, "delta_acc": dacc, "alpha": 1.0, "beta": 0.0},
         "block_steps": NB * T, "skips": skips, "skip_rate": round(skips / (NB * T), 4),
         "linear_calls": {"INT8": n8, "NVFP4": n4},
-        "avg_activation_bits": round(sum(bits[r] for r in calls) / max(len(calls), 1), 3),
+        "avg_activation_bits": avg_bits,
         "ms_per_timestep": round(1e3 * wall / T, 3),
         "ms_per_timestep_all_refresh": round(1e3 * wall_all / T, 3),
         "tdc_speedup": round(wall_all / wall, 3),
@@ -852,6 +886,17 @@ def run_schedule_workload(torch, dm, wl, events: str, T: int = 50, NB: int = 42)
         "library_kernel_ms_per_timestep": round(lib_ms / T, 3),
         "decisions_equal_across_runs": log == log_ev,
         "kernels": kernels, "kernels_by_shape": by_shape,
+        "router_fitted": {
+            "fit": (f"{CAL} always-refresh steps, {len(samples)} block refreshes with Gamma; E = relative L1 "
+                    "error of each linear's NVFP4 output against its BF16 output (W1 before GELU)"),
+            "alpha": [round(float(v), 5) for v in a_fit], "beta": [round(float(v), 5) for v in b_fit],
+            "rms_residual": [round(float(v), 5) for v in rms],
+            "error_range": [round(float(errs.min()), 5), round(float(errs.max()), 5)],
+            "gamma_range": [round(float(gs.min()), 5), round(float(gs.max()), 5)],
+            "tau": round(tau_fit, 5), "skip_rate": round(fs / (NB * T), 4),
+            "linear_calls": {"INT8": f8, "NVFP4": f4}, "avg_activation_bits": fbits,
+            "ms_per_timestep": round(1e3 * wall_fit / T, 3),
+        },
     }
 
 
