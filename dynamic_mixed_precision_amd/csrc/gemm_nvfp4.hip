@@ -18,9 +18,10 @@
 //
 // Tiling (all paths of variant 0): 256 threads = 2 x 2 waves, workgroup tile
 // 256 x 256, wave tile 128 x 128 = 4 x 4 MFMA 32x32x16 tiles.  Three paths:
-//  * K % 256 == 0 (the DiT shapes): raw codes and scales are copied into LDS
+//  * K % 128 == 0 (the DiT shapes): raw codes and scales are copied into LDS
 //    by DMA and each wave dequantizes its own fragments into registers
-//    (gemm_fp4_dma_kernel);
+//    (gemm_fp4_dma_kernel with 256-element stages when K % 256 == 0,
+//    gemm_fp4_dma128_kernel with 128-element stages otherwise);
 //  * K % 64 == 0: codes are loaded into registers, dequantized once per
 //    workgroup into a double-buffered fp16 LDS tile (gemm_fp4_fast_kernel);
 //  * any K % 16 == 0: as the previous, with the K tail masked
