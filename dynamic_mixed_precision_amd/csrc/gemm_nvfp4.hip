@@ -18,10 +18,10 @@
 //
 // Tiling (all paths of variant 0): 256 threads = 2 x 2 waves, workgroup tile
 // 256 x 256, wave tile 128 x 128 = 4 x 4 MFMA 32x32x16 tiles.  Three paths:
-//  * K % 128 == 0 (the DiT shapes): raw codes and scales are copied into LDS
-//    by DMA and each wave dequantizes its own fragments into registers
-//    (gemm_fp4_dma_kernel with 256-element stages when K % 256 == 0,
-//    gemm_fp4_dma128_kernel with 128-element stages otherwise);
+//  * K % 128 == 0 (the DiT shapes; K >= 384 when K % 256 != 0): raw codes
+//    and scales are copied into LDS by DMA and each wave dequantizes its own
+//    fragments into registers (gemm_fp4_dma_kernel; gemm_fp4_dma_tail_kernel
+//    when K % 256 == 128, whose last stage is a half stage);
 //  * K % 64 == 0: codes are loaded into registers, dequantized once per
 //    workgroup into a double-buffered fp16 LDS tile (gemm_fp4_fast_kernel);
 //  * any K % 16 == 0: as the previous, with the K tail masked
@@ -378,78 +378,65 @@ __device__ __forceinline__ v8h dq8(const uint4 c, const v2h s2) {
 // DMA path (K % 128 == 0).  Raw codes and scales go from global memory
 // straight into LDS with global_load_lds, and every wave dequantizes the
 // fragments of its own MFMAs from LDS into registers.  Compared with staging
-// dequantized tiles, the load path touches whole row segments of 64 or 128
-// bytes, and LDS holds 4.5 bits per element instead of 16.
+// dequantized tiles, the load path touches whole 128-byte row segments, and
+// LDS holds 4.5 bits per element instead of 16.
 //
-// A stage is BK = 256 K elements (K % 256 == 0), or 128 (any other
-// K % 128 == 0, e.g. a 1920 hidden).  Per operand: 256 rows x BK/2 code
-// bytes, piece p of a row (16 bytes = K positions 32p .. 32p+31) stored at
-// slot p ^ key(row), key = (row >> 1) & 7 for 128-byte rows and
-// (row >> 2) & 3 for 64-byte rows, so the 32-row fragment reads hit distinct
-// 16-byte slots of each 256-byte bank span; and 256 rows x BK/16 scale bytes,
-// row-major for BK = 256 (one 16-byte DMA per row) and as two dword planes
-// (plane w: dword w of every row) for BK = 128, which the 4-byte DMA can
-// write.  Two stages in flight.  K order inside a 64-element chunk c: lane
-// half h holds piece 2c + h and feeds k-step s the positions 8s .. 8s+7 of it
-// (the same order on both operands, so products pair the same elements).
+// A stage is 256 K elements.  Per operand: 256 rows x 128 code bytes, piece
+// p of a row (16 bytes = K positions 32p .. 32p+31) stored at slot
+// p ^ ((row >> 1) & 7), so the 32-row fragment reads hit distinct 16-byte
+// slots of each 256-byte bank span; and 256 rows x 16 scale bytes, row-major.
+// Two stages in flight.  K order inside a 64-element chunk c: lane half h
+// holds piece 2c + h and feeds k-step s the positions 8s .. 8s+7 of it (the
+// same order on both operands, so products pair the same elements).
+//
+// When K % 256 == 128 (K >= 384, e.g. a 1920 hidden) the last stage is a
+// half stage of 128 elements (HT), which ends 64 code bytes and 8 scale bytes
+// before a full stage would.  There a lane whose piece lies in the missing
+// half loads the piece 64 bytes earlier (in bounds, never read), and the
+// scale DMA loads the row's 16 bytes from 8 bytes earlier, so the stage's 8
+// scale bytes land in words 2 and 3 of the row's slot; the half stage runs
+// chunks 0 and 1 only.
 // ---------------------------------------------------------------------------
-template <int BK>
-struct Fp4Dma {
-    static_assert(BK == 256 || BK == 128, "stage of 256 or 128 K elements");
-    static constexpr int BM = 256, BN = 256, BKE = BK;
-    static constexpr int CROW = BK / 2, SROW = BK / 16;    // code / scale bytes per row per stage
-    static constexpr int CODES = BM * CROW, SCALES = BM * SROW;
-    static constexpr int STAGE = 2 * CODES + 2 * SCALES;   // A codes, W codes, A scales, W scales
-    static constexpr int LDS_BYTES = 2 * STAGE > 4 * EpiBand<4>::BYTES ? 2 * STAGE : 4 * EpiBand<4>::BYTES;
-    static constexpr int CBLK = CODES / 1024 / 4;          // 1 KB code blocks per wave per operand
-    static constexpr int PIECES = CROW / 16;               // 16-byte pieces per row (8 or 4)
-    static constexpr int RBLK = 1024 / CROW;               // rows per code block (8 or 16)
-    static constexpr int SDMA = BK == 256 ? 1 : 2;         // scale DMA instructions per wave per operand
-    static constexpr int PER = 2 * CBLK + 2 * SDMA;        // DMA instructions per wave per stage (18 or 12)
-    static constexpr int CHUNKS = BK / 64;                 // 64-element chunks per stage
-    static constexpr unsigned GROUP_M = 8;
-    __device__ static __forceinline__ int key(int row) { return BK == 256 ? (row >> 1) & 7 : (row >> 2) & 3; }
-};
 namespace fp4dma {
-constexpr int BM = 256, BN = 256;
+constexpr int BM = 256, BN = 256, BKE = 256;
+constexpr int CROW = BKE / 2, SROW = BKE / 16;   // code / scale bytes per row per stage
+constexpr int CODES = BM * CROW, SCALES = BM * SROW;
+constexpr int STAGE = 2 * CODES + 2 * SCALES;   // A codes, W codes, A scales, W scales
+constexpr int LDS_BYTES = 2 * STAGE > 4 * EpiBand<4>::BYTES ? 2 * STAGE : 4 * EpiBand<4>::BYTES;
+constexpr int CBLK = CODES / 1024 / 4;          // 1 KB code blocks per wave per operand
+constexpr int PER = 2 * CBLK + 2;               // DMA instructions per wave per stage
 constexpr unsigned GROUP_M = 8;
-static_assert(Fp4Dma<256>::LDS_BYTES <= 160 * 1024 && Fp4Dma<128>::LDS_BYTES <= 160 * 1024,
-              "LDS of the NVFP4 DMA kernels");
+static_assert(LDS_BYTES <= 160 * 1024, "LDS of the NVFP4 DMA kernels");
+__device__ __forceinline__ int key(int row) { return (row >> 1) & 7; }
 }  // namespace fp4dma
 
 // Per-lane state of the DMA kernel.  Fragment rows ra = wm*128 + 32i + lane%32
 // share the swizzle key of lane%32, so the row block i only adds a constant
 // (an immediate offset) to the lane's base addresses.
-template <int BK>
 struct Fp4DmaLane {
-    const uint8_t *srcA[Fp4Dma<BK>::CBLK], *srcW[Fp4Dma<BK>::CBLK], *srcSA, *srcSW;
+    const uint8_t *srcA[fp4dma::CBLK], *srcW[fp4dma::CBLK], *srcSA, *srcSW;
     int offA, offW, offSA, offSW;  // byte offsets of the lane's first fragment row in a stage
     int wave, hk, sh, sw;
+    int st_half, tail_shift;       // HT: index of the half stage; the lane's code shift there
 };
 
 // DMA instruction d (0 .. PER-1) of the stage st: code blocks q = d/2 of A (d
-// even) and W (d odd), then the scales: BK = 256, the A and the W block (16
-// bytes per row); BK = 128, A and W plane 0, then A and W plane 1 (4 bytes
-// per row).
-template <int BK>
-__device__ __forceinline__ void fp4dma_one(uint8_t *dst, const Fp4DmaLane<BK> &L, int64_t st, int d) {
-    using T = Fp4Dma<BK>;
+// even) and W (d odd), then the A and the W scale block (16 bytes per row).
+template <bool HT>
+__device__ __forceinline__ void fp4dma_one(uint8_t *dst, const Fp4DmaLane &L, int64_t st, int d) {
+    using namespace fp4dma;
     typedef __attribute__((address_space(3))) void lds_void;
-    if (d < 2 * T::CBLK) {
+    if (d < 2 * CBLK) {
         const int q = d >> 1, b = L.wave + 4 * q;
-        const uint8_t *src = ((d & 1) ? L.srcW[q] : L.srcA[q]) + st * T::CROW;
-        __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(dst + (d & 1) * T::CODES + b * 1024), 16, 0, 0);
-    } else if constexpr (BK == 256) {
-        const uint8_t *src = (d == 2 * T::CBLK + 1 ? L.srcSW : L.srcSA) + st * T::SROW;
-        __builtin_amdgcn_global_load_lds((const void *)src,
-                                         (lds_void *)(dst + 2 * T::CODES + (d == 2 * T::CBLK + 1) * T::SCALES + L.wave * 1024),
-                                         16, 0, 0);
+        const uint8_t *src = ((d & 1) ? L.srcW[q] : L.srcA[q]) + st * CROW;
+        if constexpr (HT) src += st == L.st_half ? L.tail_shift : 0;
+        __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(dst + (d & 1) * CODES + b * 1024), 16, 0, 0);
     } else {
-        const int e = d - 2 * T::CBLK, op = e & 1, w = e >> 1;
-        const uint8_t *src = (op ? L.srcSW : L.srcSA) + st * T::SROW + 4 * w;
+        const bool w = d == 2 * CBLK + 1;
+        const uint8_t *src = (w ? L.srcSW : L.srcSA) + st * SROW;
+        if constexpr (HT) src -= st == L.st_half ? 8 : 0;
         __builtin_amdgcn_global_load_lds((const void *)src,
-                                         (lds_void *)(dst + 2 * T::CODES + op * T::SCALES + w * (T::BM * 4) + L.wave * 256),
-                                         4, 0, 0);
+                                         (lds_void *)(dst + 2 * CODES + w * SCALES + L.wave * 1024), 16, 0, 0);
     }
 }
 
@@ -460,25 +447,23 @@ __device__ __forceinline__ void fp4dma_one(uint8_t *dst, const Fp4DmaLane<BK> &L
 // MFMA code; after the last stage the caller passes a stage nobody reads
 // again.  The two buffers are separate restrict parameters so that, once
 // inlined, the compiler knows the stage's LDS reads cannot alias the DMA in
-// flight and does not wait for it.
-template <int BK>
+// flight and does not wait for it.  HALF: `cur` holds the half stage.
+template <bool HT, bool HALF>
 __device__ __forceinline__ void fp4dma_stage(const uint8_t *__restrict__ cur, uint8_t *__restrict__ nxt,
-                                             int64_t st_next, const Fp4DmaLane<BK> &L, v16f (&acc)[4][4]) {
-    using T = Fp4Dma<BK>;
-    constexpr int CROW = T::CROW, SROW = T::SROW, PER = T::PER;
+                                             int64_t st_next, const Fp4DmaLane &L, v16f (&acc)[4][4]) {
+    using namespace fp4dma;
     // the lane's scale words: word c holds the four scale bytes of chunk c
+    // (the half stage's two chunks sit in words 2 and 3)
     uint4 sA[4], sW[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        if constexpr (BK == 256) {
-            sA[i] = *reinterpret_cast<const uint4 *>(cur + L.offSA + i * 32 * SROW);
-            sW[i] = *reinterpret_cast<const uint4 *>(cur + L.offSW + i * 32 * SROW);
-        } else {
-            sA[i].x = *reinterpret_cast<const uint32_t *>(cur + L.offSA + i * 128);
-            sA[i].y = *reinterpret_cast<const uint32_t *>(cur + L.offSA + T::BM * 4 + i * 128);
-            sW[i].x = *reinterpret_cast<const uint32_t *>(cur + L.offSW + i * 128);
-            sW[i].y = *reinterpret_cast<const uint32_t *>(cur + L.offSW + T::BM * 4 + i * 128);
-            sA[i].z = sA[i].w = sW[i].z = sW[i].w = 0u;  // no chunks 2 and 3
+        sA[i] = *reinterpret_cast<const uint4 *>(cur + L.offSA + i * 32 * SROW);
+        sW[i] = *reinterpret_cast<const uint4 *>(cur + L.offSW + i * 32 * SROW);
+        if constexpr (HALF) {
+            sA[i].x = sA[i].z;
+            sA[i].y = sA[i].w;
+            sW[i].x = sW[i].z;
+            sW[i].y = sW[i].w;
         }
     }
 #define DMPQ_F4D_CODES(dA, dW, c)                                                              \
@@ -501,7 +486,7 @@ __device__ __forceinline__ void fp4dma_stage(const uint8_t *__restrict__ cur, ui
         _Pragma("unroll") for (int j = 0; j < 4; j++) {                                        \
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0); \
             const int t = 4 * i + j;                                                           \
-            if ((D0) >= 0 && t % 3 == 2 && (D0) + t / 3 < PER) fp4dma_one<BK>(nxt, L, st_next, (D0) + t / 3); \
+            if ((D0) >= 0 && t % 3 == 2 && (D0) + t / 3 < PER) fp4dma_one<HT>(nxt, L, st_next, (D0) + t / 3); \
         }
 #define DMPQ_F4D_CHUNK(cA, cW, c, D0)                                                          \
     {                                                                                          \
@@ -526,7 +511,7 @@ __device__ __forceinline__ void fp4dma_stage(const uint8_t *__restrict__ cur, ui
     DMPQ_F4D_CODES(cA0, cW0, 0)
     DMPQ_F4D_CODES(cA1, cW1, 1)
     DMPQ_F4D_CHUNK(cA0, cW0, 0, 0)
-    if constexpr (T::CHUNKS == 4) {
+    if constexpr (!HALF) {
         DMPQ_F4D_CODES(cA0, cW0, 2)
         DMPQ_F4D_CHUNK(cA1, cW1, 1, -1)
         DMPQ_F4D_CODES(cA1, cW1, 3)
@@ -542,13 +527,14 @@ __device__ __forceinline__ void fp4dma_stage(const uint8_t *__restrict__ cur, ui
 }
 
 // The main loop of the DMA kernel over stages kt0 .. kt1-1 of the tile at
-// (m0, n0); on return the stage buffers are free.
-template <int BK>
+// (m0, n0); on return the stage buffers are free.  HT: stage K / 256 is the
+// half stage.
+template <bool HT>
 __device__ __forceinline__ void fp4dma_mainloop(const uint8_t *__restrict__ ca, const uint8_t *__restrict__ sa,
                                                 const uint8_t *__restrict__ cw, const uint8_t *__restrict__ sw,
                                                 int64_t M, int64_t N, int64_t K, int64_t m0, int64_t n0,
                                                 int kt0, int kt1, uint8_t *lds, v16f (&acc)[4][4]) {
-    using T = Fp4Dma<BK>;
+    using namespace fp4dma;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -562,19 +548,18 @@ __device__ __forceinline__ void fp4dma_mainloop(const uint8_t *__restrict__ ca, 
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
-    // DMA sources.  Code block b = wave + 4q covers tile rows RBLK*b ..
-    // RBLK*b + RBLK-1, lane l filling slot l % PIECES of row
-    // RBLK*b + l / PIECES; the scale DMA of a wave covers rows 64 wave .. +63,
-    // one lane per row.  Rows past M or N load a clamped row; their outputs
-    // are never stored.
-    Fp4DmaLane<BK> L;
+    // DMA sources.  Code block b = wave + 4q covers tile rows 8b .. 8b+7,
+    // lane l filling slot l % 8 of row 8b + l / 8; the scale DMA of a wave
+    // covers rows 64 wave .. +63, one lane per row.  Rows past M or N load a
+    // clamped row; their outputs are never stored.
+    Fp4DmaLane L;
     L.wave = wave;
     L.hk = lane >> 5;
     L.sh = 16 * L.hk;
 #pragma unroll
-    for (int q = 0; q < T::CBLK; q++) {
-        const int row = T::RBLK * (wave + 4 * q) + lane / T::PIECES;
-        const int piece = (lane % T::PIECES) ^ T::key(row);
+    for (int q = 0; q < CBLK; q++) {
+        const int row = 8 * (wave + 4 * q) + lane / 8;
+        const int piece = (lane % 8) ^ key(row);
         const int64_t gm = m0 + row < M ? m0 + row : M - 1;
         const int64_t gn = n0 + row < N ? n0 + row : N - 1;
         L.srcA[q] = ca + gm * rb + piece * 16;
@@ -588,26 +573,38 @@ __device__ __forceinline__ void fp4dma_mainloop(const uint8_t *__restrict__ ca, 
         L.srcSW = sw + gn * nb;
     }
     const int ra = wm * 128 + (lane & 31), rw = wn * 128 + (lane & 31);
-    L.offA = ra * T::CROW;
-    L.offW = T::CODES + rw * T::CROW;
-    L.offSA = 2 * T::CODES + ra * (BK == 256 ? T::SROW : 4);
-    L.offSW = 2 * T::CODES + T::SCALES + rw * (BK == 256 ? T::SROW : 4);
-    L.sw = T::key(lane & 31);
+    L.offA = ra * CROW;
+    L.offW = CODES + rw * CROW;
+    L.offSA = 2 * CODES + ra * SROW;
+    L.offSW = 2 * CODES + SCALES + rw * SROW;
+    L.sw = key(lane & 31);
+    // HT: the lane's code piece is the same in every block q (key(8 (wave +
+    // 4q) + lane / 8) does not depend on q); pieces 4 .. 7 lie in the half
+    // stage's missing half
+    L.st_half = (int)(K / 256);
+    L.tail_shift = ((lane % 8) ^ key(8 * wave + lane / 8)) >= 4 ? -64 : 0;
+    const bool half_last = HT && kt1 == L.st_half + 1;
+    const int nfull = nk - (half_last ? 1 : 0);
 
 #pragma unroll
-    for (int d = 0; d < T::PER; d++) fp4dma_one<BK>(lds, L, kt0, d);
-    for (int kt = 0; kt < nk; kt++) {
+    for (int d = 0; d < PER; d++) fp4dma_one<HT>(lds, L, kt0, d);
+    for (int kt = 0; kt < nfull; kt++) {
         __builtin_amdgcn_s_waitcnt(0xC07F & ~0xC00F);  // vmcnt(0): this wave's loads of stage kt
         __syncthreads();                               // ... and every other wave's
         // after the last stage the copy goes to a buffer nobody reads again
-        fp4dma_stage<BK>(lds + (kt & 1) * T::STAGE, lds + ((kt & 1) ^ 1) * T::STAGE,
-                         kt0 + (kt + 1 < nk ? kt + 1 : kt), L, acc);
+        fp4dma_stage<HT, false>(lds + (kt & 1) * STAGE, lds + ((kt & 1) ^ 1) * STAGE,
+                                kt0 + (kt + 1 < nk ? kt + 1 : kt), L, acc);
+    }
+    if (half_last) {
+        __builtin_amdgcn_s_waitcnt(0xC07F & ~0xC00F);
+        __syncthreads();
+        fp4dma_stage<HT, true>(lds + (nfull & 1) * STAGE, lds + ((nfull & 1) ^ 1) * STAGE, kt0 + nfull, L, acc);
     }
     __builtin_amdgcn_s_waitcnt(0xC07F & ~0xC00F);  // the last copy has landed
     __syncthreads();  // every wave is done reading the stage buffers before they hold bands
 }
 
-template <int OUT, int EPI, int BK>
+template <int OUT, int EPI, bool HT>
 __device__ __forceinline__ void fp4dma_tile(const uint8_t *__restrict__ ca, const uint8_t *__restrict__ sa,
                                             const float *__restrict__ ga, const uint8_t *__restrict__ cw,
                                             const uint8_t *__restrict__ sw, const float *__restrict__ gw,
@@ -622,12 +619,12 @@ __device__ __forceinline__ void fp4dma_tile(const uint8_t *__restrict__ ca, cons
     const TileCoord tc = tile_at(pid, tiles_m, tiles_n, GROUP_M);
     const int64_t m0 = (int64_t)tc.m * BM, n0 = (int64_t)tc.n * BN;
     v16f acc[4][4];
-    fp4dma_mainloop<BK>(ca, sa, cw, sw, M, N, K, m0, n0, 0, (int)(K / BK), lds, acc);
+    fp4dma_mainloop<HT>(ca, sa, cw, sw, M, N, K, m0, n0, 0, (int)(K / BKE) + (HT ? 1 : 0), lds, acc);
     fp4_epilogue<OUT, EPI>(acc, lds, ga, gw, M, N, m0, n0, wave, wm, wn, lane, y, partial, pid);
 }
 
-// The whole-tile kernels, one per stage size (kernels of their own, so that
-// each keeps its name in traces).
+// The whole-tile kernels: K % 256 == 0, and with the closing half stage
+// (kernels of their own, so that each keeps its name in traces).
 template <int OUT, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_fp4_dma_kernel(
     const uint8_t *__restrict__ ca, const uint8_t *__restrict__ sa, const float *__restrict__ ga,
@@ -635,21 +632,21 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_dma_kernel(
     int64_t M, int64_t N, int64_t K, void *__restrict__ y, unsigned tiles_m, unsigned tiles_n,
     float *__restrict__ partial) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    fp4dma_tile<OUT, EPI, 256>(ca, sa, ga, cw, sw, gw, M, N, K, y, tiles_m, tiles_n, partial, lds);
+    fp4dma_tile<OUT, EPI, false>(ca, sa, ga, cw, sw, gw, M, N, K, y, tiles_m, tiles_n, partial, lds);
 }
 
 template <int OUT, int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_fp4_dma128_kernel(
+__global__ __launch_bounds__(256, 1) void gemm_fp4_dma_tail_kernel(
     const uint8_t *__restrict__ ca, const uint8_t *__restrict__ sa, const float *__restrict__ ga,
     const uint8_t *__restrict__ cw, const uint8_t *__restrict__ sw, const float *__restrict__ gw,
     int64_t M, int64_t N, int64_t K, void *__restrict__ y, unsigned tiles_m, unsigned tiles_n,
     float *__restrict__ partial) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    fp4dma_tile<OUT, EPI, 128>(ca, sa, ga, cw, sw, gw, M, N, K, y, tiles_m, tiles_n, partial, lds);
+    fp4dma_tile<OUT, EPI, true>(ca, sa, ga, cw, sw, gw, M, N, K, y, tiles_m, tiles_n, partial, lds);
 }
 
 // The split workgroups of a SplitPlan launch (see gemm_i8_split_kernel).
-template <int BK>
+template <bool HT>
 __device__ __forceinline__ void fp4dma_split(const uint8_t *__restrict__ ca, const uint8_t *__restrict__ sa,
                                              const uint8_t *__restrict__ cw, const uint8_t *__restrict__ sw,
                                              int64_t M, int64_t N, int64_t K, unsigned tiles_m, unsigned tiles_n,
@@ -659,7 +656,7 @@ __device__ __forceinline__ void fp4dma_split(const uint8_t *__restrict__ ca, con
     const SplitUnit u = split_unit(sp, tiles_m, tiles_n, GROUP_M);
     if (partial && u.kt0 == 0 && threadIdx.x == 0) partial[sp.full + blockIdx.x / sp.splits] = 0.0f;
     v16f acc[4][4];
-    fp4dma_mainloop<BK>(ca, sa, cw, sw, M, N, K, (int64_t)u.tc.m * BM, (int64_t)u.tc.n * BN, u.kt0, u.kt1, lds, acc);
+    fp4dma_mainloop<HT>(ca, sa, cw, sw, M, N, K, (int64_t)u.tc.m * BM, (int64_t)u.tc.n * BN, u.kt0, u.kt1, lds, acc);
     store_split_partial(acc, spart + (size_t)blockIdx.x * kSplitWords, threadIdx.x);
 }
 
@@ -668,15 +665,15 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_split_kernel(
     const uint8_t *__restrict__ sw, int64_t M, int64_t N, int64_t K, unsigned tiles_m, unsigned tiles_n,
     SplitPlan sp, uint32_t *__restrict__ spart, float *__restrict__ partial) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    fp4dma_split<256>(ca, sa, cw, sw, M, N, K, tiles_m, tiles_n, sp, spart, partial, lds);
+    fp4dma_split<false>(ca, sa, cw, sw, M, N, K, tiles_m, tiles_n, sp, spart, partial, lds);
 }
 
-__global__ __launch_bounds__(256, 1) void gemm_fp4_split128_kernel(
+__global__ __launch_bounds__(256, 1) void gemm_fp4_split_tail_kernel(
     const uint8_t *__restrict__ ca, const uint8_t *__restrict__ sa, const uint8_t *__restrict__ cw,
     const uint8_t *__restrict__ sw, int64_t M, int64_t N, int64_t K, unsigned tiles_m, unsigned tiles_n,
     SplitPlan sp, uint32_t *__restrict__ spart, float *__restrict__ partial) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    fp4dma_split<128>(ca, sa, cw, sw, M, N, K, tiles_m, tiles_n, sp, spart, partial, lds);
+    fp4dma_split<true>(ca, sa, cw, sw, M, N, K, tiles_m, tiles_n, sp, spart, partial, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -816,24 +813,24 @@ static hipError_t allow_lds(KernelFn fn, size_t bytes) {
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-// The DMA path for one stage size: the whole-tile kernel over the full
-// waves, then (with a split plan) the tail's split workgroups and the fixup.
-template <int OUT, int EPI, int BK, class TileFn, class SplitFn>
+// The DMA path: the whole-tile kernel over the full waves, then (with a split
+// plan) the tail's split workgroups and the fixup.  HT: K / 256 full stages
+// and the half stage.
+template <int OUT, int EPI, bool HT, class TileFn, class SplitFn>
 static hipError_t launch_fp4_dma(hipStream_t s, TileFn tile_kernel, SplitFn split_kernel, const uint8_t *ca,
                                  const uint8_t *sa, const float *ga, const uint8_t *cw, const uint8_t *sw,
                                  const float *gw, int64_t M, int64_t N, int64_t K, void *y, float *partial,
                                  uint32_t *spart, unsigned utm, unsigned utn) {
-    constexpr size_t lds = Fp4Dma<BK>::LDS_BYTES;
-    const SplitPlan sp = plan_split((int64_t)utm * utn, (int)(K / BK), spart != nullptr);
+    const SplitPlan sp = plan_split((int64_t)utm * utn, (int)(K / fp4dma::BKE) + (HT ? 1 : 0), spart != nullptr);
     if (sp.full > 0) {
-        hipLaunchKernelGGL(tile_kernel, dim3(sp.full), dim3(256), lds, s, ca, sa, ga, cw, sw, gw, M, N, K, y, utm,
-                           utn, partial);
+        hipLaunchKernelGGL(tile_kernel, dim3(sp.full), dim3(256), fp4dma::LDS_BYTES, s, ca, sa, ga, cw, sw, gw, M,
+                           N, K, y, utm, utn, partial);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (sp.splits > 1) {
-        hipLaunchKernelGGL(split_kernel, dim3(sp.tail * sp.splits), dim3(256), lds, s, ca, sa, cw, sw, M, N, K, utm,
-                           utn, sp, spart, (EPI & kEpiAmax) ? partial : nullptr);
+        hipLaunchKernelGGL(split_kernel, dim3(sp.tail * sp.splits), dim3(256), fp4dma::LDS_BYTES, s, ca, sa, cw, sw,
+                           M, N, K, utm, utn, sp, spart, (EPI & kEpiAmax) ? partial : nullptr);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         return launch_f32_fixup(s, ga, gw, M, N, y, utm, utn, fp4dma::GROUP_M, partial, sp, spart, OUT, EPI);
@@ -850,10 +847,10 @@ static hipError_t launch_fp4_paths(hipStream_t s, const uint8_t *ca, const uint8
     static const hipError_t attr = [] {
         hipError_t e = allow_lds(gemm_fp4_f16_kernel<OUT, EPI>, 2 * STAGE);
         if (e == hipSuccess) e = allow_lds(gemm_fp4_fast_kernel<OUT, EPI>, 2 * STAGE);
-        if (e == hipSuccess) e = allow_lds(gemm_fp4_dma_kernel<OUT, EPI>, Fp4Dma<256>::LDS_BYTES);
-        if (e == hipSuccess) e = allow_lds(gemm_fp4_split_kernel, Fp4Dma<256>::LDS_BYTES);
-        if (e == hipSuccess) e = allow_lds(gemm_fp4_dma128_kernel<OUT, EPI>, Fp4Dma<128>::LDS_BYTES);
-        if (e == hipSuccess) e = allow_lds(gemm_fp4_split128_kernel, Fp4Dma<128>::LDS_BYTES);
+        if (e == hipSuccess) e = allow_lds(gemm_fp4_dma_kernel<OUT, EPI>, fp4dma::LDS_BYTES);
+        if (e == hipSuccess) e = allow_lds(gemm_fp4_split_kernel, fp4dma::LDS_BYTES);
+        if (e == hipSuccess) e = allow_lds(gemm_fp4_dma_tail_kernel<OUT, EPI>, fp4dma::LDS_BYTES);
+        if (e == hipSuccess) e = allow_lds(gemm_fp4_split_tail_kernel, fp4dma::LDS_BYTES);
         return e;
     }();
     if (attr != hipSuccess) return attr;
@@ -861,11 +858,11 @@ static hipError_t launch_fp4_paths(hipStream_t s, const uint8_t *ca, const uint8
     const dim3 grid((unsigned)(tm * tn)), block(256);
     const unsigned utm = (unsigned)tm, utn = (unsigned)tn;
     if (K % 256 == 0)
-        return launch_fp4_dma<OUT, EPI, 256>(s, gemm_fp4_dma_kernel<OUT, EPI>, gemm_fp4_split_kernel, ca, sa, ga,
-                                             cw, sw, gw, M, N, K, y, partial, spart, utm, utn);
-    if (K % 128 == 0)
-        return launch_fp4_dma<OUT, EPI, 128>(s, gemm_fp4_dma128_kernel<OUT, EPI>, gemm_fp4_split128_kernel, ca, sa,
-                                             ga, cw, sw, gw, M, N, K, y, partial, spart, utm, utn);
+        return launch_fp4_dma<OUT, EPI, false>(s, gemm_fp4_dma_kernel<OUT, EPI>, gemm_fp4_split_kernel, ca, sa, ga,
+                                               cw, sw, gw, M, N, K, y, partial, spart, utm, utn);
+    if (K % 128 == 0 && K >= 384)
+        return launch_fp4_dma<OUT, EPI, true>(s, gemm_fp4_dma_tail_kernel<OUT, EPI>, gemm_fp4_split_tail_kernel, ca,
+                                              sa, ga, cw, sw, gw, M, N, K, y, partial, spart, utm, utn);
     if (K % (4 * 16) == 0) {
         hipLaunchKernelGGL((gemm_fp4_fast_kernel<OUT, EPI>), grid, block, 2 * STAGE, s, ca, sa, ga, cw,
                            sw, gw, M, N, K, y, utm, utn, partial);

@@ -115,7 +115,7 @@ def _run(kind, args, M, N, epilogue, ws):
 
 
 # (kind, K): every main loop -- INT8 DMA (K % 128 == 0) and general; NVFP4
-# DMA (256-element stages for K % 256, 128-element for other K % 128), fast
+# DMA (K % 256, and other K % 128 from 384 with a closing half stage), fast
 # (K % 64), 16-bit (K % 16); BF16 with and without tail.
 PATHS = [("int8", 256), ("int8", 208), ("nvfp4", 512), ("nvfp4", 384), ("nvfp4", 320), ("nvfp4", 208),
          ("bf16", 256), ("bf16", 208)]

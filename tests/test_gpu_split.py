@@ -1,7 +1,7 @@
 """GPU parity of the tail split along K: the *_ex GEMMs with a full GEMM
 workspace (DMPQ_OP_GEMM) split the tiles beyond the last multiple of 256
-along K (by stages: 256 K elements, or 128 for an NVFP4 K that is a
-multiple of 128 but not of 256) and add the parts in a fixed order in a second kernel.
+along K (by stages of 256 K elements; an NVFP4 K that is a multiple of
+128 but not of 256 ends with a half stage) and add the parts in a fixed order in a second kernel.
 
 INT8: int32 parts add exactly, so the outputs are bit-exact against the
 oracle and bit-identical to the unsplit call.  NVFP4 and BF16: the same
@@ -95,9 +95,9 @@ def _run_fp4(args, M, N, ws, out=dm.OUT_F32):
                                           (workloads.M_480P, 3072, 3072, True),
                                           (workloads.M_480P, 1920, 1920, True)])
 def test_split_nvfp4(orc, M, N, K, sample):
-    # K % 256 == 0 runs 256-element stages, other K % 128 == 0 128-element ones
+    # K % 256 == 0 runs 256-element stages; other K % 128 == 0 adds a half stage
     require_gpu()
-    S = _splits(M, N, K // 256 if K % 256 == 0 else K // 128)
+    S = _splits(M, N, K // 256 + (1 if K % 256 else 0))
     say(f"split nvfp4 M={M} N={N} K={K} splits={S}")
     assert S > 1
     rng = np.random.default_rng(2 * M + N + K)
