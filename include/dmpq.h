@@ -357,9 +357,9 @@ dmpq_status dmpq_gemm_bf16(hipStream_t stream, const uint16_t *x, const uint16_t
  * each tile's parts in a fixed order before the epilogue.  INT8 results are
  * unchanged; NVFP4 and BF16 results differ from the unsplit ones only in the
  * fp32 summation order (deterministic, within the same tolerance).  Applies
- * on the DMA paths (INT8 K % 128 == 0 and K >= 4096, NVFP4 K % 128 == 0,
- * every BF16 K) and not to the INT8 I32 output.  Calls that share a
- * workspace must not overlap.
+ * on the DMA paths (INT8 K % 128 == 0 and K >= 4096, NVFP4 K % 128 == 0
+ * and K >= 256, every BF16 K) and not to the INT8 I32 output.  Calls that
+ * share a workspace must not overlap.
  * epilogue 0 with ws NULL is the plain call.
  * ------------------------------------------------------------------------- */
 dmpq_status dmpq_qgemm_int8_ex(hipStream_t stream, const int8_t *qa, const float *sa,
