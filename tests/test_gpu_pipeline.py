@@ -5,7 +5,8 @@
 NVFP4, INT8; the Gamma sums, routes, activation quantization (every row) and
 the GEMM (row sample) of each block's linears match the oracle.
 2B-like (17776 tokens, hidden 1920): every linear (QKV 5760 x 1920, out
-1920 x 1920, FFN up 7680 x 1920, FFN down 1920 x 7680) on both routes.
+1920 x 1920, FFN up 7680 x 1920, FFN down 1920 x 7680) on both routes, with
+the plain entry points and as the benchmark launches them.
 1080p-like (106306 tokens): the FFN-up (12288 x 3072) and FFN-down
 (3072 x 12288) linears on both routes.
 """
@@ -131,25 +132,22 @@ def _tail_tile_rows(M, N, nk, splits_from_k=True):
     return np.concatenate([np.arange(256 * t, min(256 * t + 256, M)) for t in sorted(mt)])
 
 
-@pytest.mark.parametrize("route", [0, 1])
-@pytest.mark.parametrize("li", [0, 1, 2, 3])
-def test_1080p_linears_bench_launch(orc, li, route):
-    """Every 1080p-like linear on both routes, launched as the benchmark does:
-    the *_ex GEMMs with the full GEMM workspace (tail split) and bf16 output.
-    The row sample takes every 37th row of the m-tiles that hold split tail
-    tiles, plus every 1499th row and the last 3.  NVFP4 qkv, out and ffn_down
-    and INT8 ffn_down split a 128-tile tail in two (the two-way fixup); INT8
-    below K = 4096 and ffn_up (no tail) run unsplit."""
-    require_gpu()
-    M = wl.M_1080P
-    lin = wl.VIDEO_1080P.linears[li]
+def _bench_launch_parity(orc, cfg, li, route, seed, every):
+    """One linear of cfg launched as the benchmark does: the *_ex GEMMs with
+    the full GEMM workspace (tail split) and bf16 output.  The row sample
+    takes every 37th row of the m-tiles that hold split tail tiles, plus every
+    `every`-th row and the last 3."""
+    M = cfg.M
+    lin = cfg.linears[li]
     N, K = lin.N, lin.K
-    nk = K // 128 if route == dm.ROUTE_INT8 else K // 256
+    # stages of the split plan: INT8 128 K elements; NVFP4 256, plus the
+    # closing half stage when K % 256 == 128
+    nk = K // 128 if route == dm.ROUTE_INT8 else K // 256 + (1 if K % 256 else 0)
     tail = _tail_tile_rows(M, N, nk, route != dm.ROUTE_INT8 or K >= 4096)
-    rows = np.unique(np.concatenate([tail[::37], np.arange(0, M, 1499), np.arange(M - 3, M)]))
-    say(f"1080p-like {lin.name} M={M} N={N} K={K} route={route} bench launch, "
+    rows = np.unique(np.concatenate([tail[::37], np.arange(0, M, every), np.arange(M - 3, M)]))
+    say(f"{cfg.name} {lin.name} M={M} N={N} K={K} route={route} bench launch, "
         f"{len(tail)} tail-tile rows, {len(rows)} rows checked")
-    rng = np.random.default_rng(1100 + 10 * li + route)
+    rng = np.random.default_rng(seed)
     x = wl.activations(rng, M, K)
     p = orc.prep_weight(wl.weight(rng, N, K))
     ws = dm.new_workspace(dm.OP_GEMM, "cuda", M, N)
@@ -171,6 +169,28 @@ def test_1080p_linears_bench_launch(orc, li, route):
         y0, b0 = orc.gemm_nvfp4(c0, sc0, g0, p["cw"], p["sw"], p["gw"], rows=rows)
         yb = wl.bf16_bits_to_f32(host(y[sel], np.uint16)).astype(np.float64)
         assert np.all(np.abs(yb - y0) <= 1e-5 * b0 + 2.0 ** -8 * np.abs(y0))
+
+
+@pytest.mark.parametrize("route", [0, 1])
+@pytest.mark.parametrize("li", [0, 1, 2, 3])
+def test_1080p_linears_bench_launch(orc, li, route):
+    """Every 1080p-like linear on both routes, launched as the benchmark does.
+    NVFP4 qkv, out and ffn_down and INT8 ffn_down split a 128-tile tail in
+    two (the two-way fixup); INT8 below K = 4096 and ffn_up (no tail) run
+    unsplit."""
+    require_gpu()
+    _bench_launch_parity(orc, wl.VIDEO_1080P, li, route, 1100 + 10 * li + route, 1499)
+
+
+@pytest.mark.parametrize("route", [0, 1])
+@pytest.mark.parametrize("li", [0, 1, 2, 3])
+def test_2b_linears_bench_launch(orc, li, route):
+    """Every 2B-like linear on both routes, launched as the benchmark does.
+    The NVFP4 K = 1920 linears run 256-element stages and the closing half
+    stage, their tails split 3 or 4 ways; INT8 splits only ffn_down
+    (K = 7680)."""
+    require_gpu()
+    _bench_launch_parity(orc, wl.COGVIDEOX_2B, li, route, 1300 + 10 * li + route, 997)
 
 
 @pytest.mark.parametrize("li", [0, 1, 2, 3])
