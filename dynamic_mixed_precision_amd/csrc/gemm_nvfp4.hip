@@ -18,10 +18,11 @@
 //
 // Tiling (all paths of variant 0): 256 threads = 2 x 2 waves, workgroup tile
 // 256 x 256, wave tile 128 x 128 = 4 x 4 MFMA 32x32x16 tiles.  Three paths:
-//  * K % 128 == 0 (the DiT shapes; K >= 384 when K % 256 != 0): raw codes
-//    and scales are copied into LDS by DMA and each wave dequantizes its own
-//    fragments into registers (gemm_fp4_dma_kernel; gemm_fp4_dma_tail_kernel
-//    when K % 256 == 128, whose last stage is a half stage);
+//  * K % 128 == 0 (the DiT shapes; K >= 384 when K % 256 != 0; operands
+//    below 4 GiB): raw codes and scales are copied into LDS by DMA and each
+//    wave dequantizes its own fragments into registers (gemm_fp4_dma_kernel;
+//    gemm_fp4_dma_tail_kernel when K % 256 == 128, whose last stage is a half
+//    stage);
 //  * K % 64 == 0: codes are loaded into registers, dequantized once per
 //    workgroup into a double-buffered fp16 LDS tile (gemm_fp4_fast_kernel);
 //  * any K % 16 == 0: as the previous, with the K tail masked
@@ -414,9 +415,13 @@ __device__ __forceinline__ int key(int row) { return (row >> 1) & 7; }
 // share the swizzle key of lane%32, so the row block i only adds a constant
 // (an immediate offset) to the lane's base addresses.
 struct Fp4DmaLane {
-    const uint8_t *srcA[fp4dma::CBLK], *srcW[fp4dma::CBLK], *srcSA, *srcSW;
+    // DMA sources: the operand bases (uniform) and the lane's byte offsets
+    // into them (32-bit: every operand is below 2 GiB), so that an address is
+    // a scalar base plus a fixed vector offset
+    const uint8_t *ca, *cw, *sa, *sw;
+    uint32_t goffA[fp4dma::CBLK], goffW[fp4dma::CBLK], goffSA, goffSW;
     int offA, offW, offSA, offSW;  // byte offsets of the lane's first fragment row in a stage
-    int wave, hk, sh, sw;
+    int wave, hk, sh, swz;         // wave index (uniform), K half, scale shift, swizzle key
     int st_half, tail_shift;       // HT: index of the half stage; the lane's code shift there
 };
 
@@ -428,16 +433,32 @@ __device__ __forceinline__ void fp4dma_one(uint8_t *dst, const Fp4DmaLane &L, in
     typedef __attribute__((address_space(3))) void lds_void;
     if (d < 2 * CBLK) {
         const int q = d >> 1, b = L.wave + 4 * q;
-        const uint8_t *src = ((d & 1) ? L.srcW[q] : L.srcA[q]) + st * CROW;
-        if constexpr (HT) src += st == L.st_half ? L.tail_shift : 0;
-        __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(dst + (d & 1) * CODES + b * 1024), 16, 0, 0);
+        // base stays opaque here (and the offsets, through fp4dma_launder), so
+        // that the address is a scalar base plus a 32-bit vector offset, with
+        // no per-DMA 64-bit vector add
+        const uint8_t *base = ((d & 1) ? L.cw : L.ca) + st * CROW;
+        asm("" : "+s"(base));
+        uint32_t off = (d & 1) ? L.goffW[q] : L.goffA[q];
+        if constexpr (HT) off += st == L.st_half ? L.tail_shift : 0;
+        __builtin_amdgcn_global_load_lds((const void *)(base + off), (lds_void *)(dst + (d & 1) * CODES + b * 1024),
+                                         16, 0, 0);
     } else {
         const bool w = d == 2 * CBLK + 1;
-        const uint8_t *src = (w ? L.srcSW : L.srcSA) + st * SROW;
-        if constexpr (HT) src -= st == L.st_half ? 8 : 0;
-        __builtin_amdgcn_global_load_lds((const void *)src,
+        const uint8_t *base = (w ? L.sw : L.sa) + st * SROW;
+        if constexpr (HT) base -= st == L.st_half ? 8 : 0;
+        asm("" : "+s"(base));
+        __builtin_amdgcn_global_load_lds((const void *)(base + (w ? L.goffSW : L.goffSA)),
                                          (lds_void *)(dst + 2 * CODES + w * SCALES + L.wave * 1024), 16, 0, 0);
     }
+}
+
+// Makes the lane's DMA offsets opaque values that change (in place, with no
+// instruction) every stage, so that the compiler cannot hoist their 64-bit
+// extension out of the main loop and must address by scalar base + offset.
+__device__ __forceinline__ void fp4dma_launder(Fp4DmaLane &L) {
+#pragma unroll
+    for (int q = 0; q < fp4dma::CBLK; q++) asm("" : "+v"(L.goffA[q]), "+v"(L.goffW[q]));
+    asm("" : "+v"(L.goffSA), "+v"(L.goffSW));
 }
 
 // One stage of the DMA kernel: run the stage held in `cur` while the DMA of
@@ -468,7 +489,7 @@ __device__ __forceinline__ void fp4dma_stage(const uint8_t *__restrict__ cur, ui
     }
 #define DMPQ_F4D_CODES(dA, dW, c)                                                              \
     {                                                                                          \
-        const int slot = ((2 * (c) + L.hk) ^ L.sw) * 16;                                       \
+        const int slot = ((2 * (c) + L.hk) ^ L.swz) * 16;                                      \
         _Pragma("unroll") for (int i = 0; i < 4; i++) {                                        \
             dA[i] = *reinterpret_cast<const uint4 *>(cur + L.offA + slot + i * 32 * CROW);     \
             dW[i] = *reinterpret_cast<const uint4 *>(cur + L.offW + slot + i * 32 * CROW);     \
@@ -536,7 +557,7 @@ __device__ __forceinline__ void fp4dma_mainloop(const uint8_t *__restrict__ ca, 
                                                 int kt0, int kt1, uint8_t *lds, v16f (&acc)[4][4]) {
     using namespace fp4dma;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t nb = K / 16, rb = K / 2;
     const int nk = kt1 - kt0;
@@ -553,6 +574,10 @@ __device__ __forceinline__ void fp4dma_mainloop(const uint8_t *__restrict__ ca, 
     // covers rows 64 wave .. +63, one lane per row.  Rows past M or N load a
     // clamped row; their outputs are never stored.
     Fp4DmaLane L;
+    L.ca = ca;
+    L.cw = cw;
+    L.sa = sa;
+    L.sw = sw;
     L.wave = wave;
     L.hk = lane >> 5;
     L.sh = 16 * L.hk;
@@ -562,22 +587,22 @@ __device__ __forceinline__ void fp4dma_mainloop(const uint8_t *__restrict__ ca, 
         const int piece = (lane % 8) ^ key(row);
         const int64_t gm = m0 + row < M ? m0 + row : M - 1;
         const int64_t gn = n0 + row < N ? n0 + row : N - 1;
-        L.srcA[q] = ca + gm * rb + piece * 16;
-        L.srcW[q] = cw + gn * rb + piece * 16;
+        L.goffA[q] = (uint32_t)(gm * rb + piece * 16);
+        L.goffW[q] = (uint32_t)(gn * rb + piece * 16);
     }
     {
         const int row = 64 * wave + lane;
         const int64_t gm = m0 + row < M ? m0 + row : M - 1;
         const int64_t gn = n0 + row < N ? n0 + row : N - 1;
-        L.srcSA = sa + gm * nb;
-        L.srcSW = sw + gn * nb;
+        L.goffSA = (uint32_t)(gm * nb);
+        L.goffSW = (uint32_t)(gn * nb);
     }
     const int ra = wm * 128 + (lane & 31), rw = wn * 128 + (lane & 31);
     L.offA = ra * CROW;
     L.offW = CODES + rw * CROW;
     L.offSA = 2 * CODES + ra * SROW;
     L.offSW = 2 * CODES + SCALES + rw * SROW;
-    L.sw = key(lane & 31);
+    L.swz = key(lane & 31);
     // HT: the lane's code piece is the same in every block q (key(8 (wave +
     // 4q) + lane / 8) does not depend on q); pieces 4 .. 7 lie in the half
     // stage's missing half
@@ -591,6 +616,7 @@ __device__ __forceinline__ void fp4dma_mainloop(const uint8_t *__restrict__ ca, 
     for (int kt = 0; kt < nfull; kt++) {
         __builtin_amdgcn_s_waitcnt(0xC07F & ~0xC00F);  // vmcnt(0): this wave's loads of stage kt
         __syncthreads();                               // ... and every other wave's
+        fp4dma_launder(L);
         // after the last stage the copy goes to a buffer nobody reads again
         fp4dma_stage<HT, false>(lds + (kt & 1) * STAGE, lds + ((kt & 1) ^ 1) * STAGE,
                                 kt0 + (kt + 1 < nk ? kt + 1 : kt), L, acc);
@@ -857,10 +883,12 @@ static hipError_t launch_fp4_paths(hipStream_t s, const uint8_t *ca, const uint8
     const int64_t tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
     const dim3 grid((unsigned)(tm * tn)), block(256);
     const unsigned utm = (unsigned)tm, utn = (unsigned)tn;
-    if (K % 256 == 0)
+    // the DMA kernels address operands by 32-bit byte offsets
+    const bool off32 = M * (K / 2) <= (int64_t)UINT32_MAX && N * (K / 2) <= (int64_t)UINT32_MAX;
+    if (off32 && K % 256 == 0)
         return launch_fp4_dma<OUT, EPI, false>(s, gemm_fp4_dma_kernel<OUT, EPI>, gemm_fp4_split_kernel, ca, sa, ga,
                                                cw, sw, gw, M, N, K, y, partial, spart, utm, utn);
-    if (K % 128 == 0 && K >= 384)
+    if (off32 && K % 128 == 0 && K >= 384)
         return launch_fp4_dma<OUT, EPI, true>(s, gemm_fp4_dma_tail_kernel<OUT, EPI>, gemm_fp4_split_tail_kernel, ca,
                                               sa, ga, cw, sw, gw, M, N, K, y, partial, spart, utm, utn);
     if (K % (4 * 16) == 0) {
