@@ -237,6 +237,8 @@ static dmpq_status check_gemm(const char *fn, int64_t M, int64_t N, int64_t K) {
         return fail(DMPQ_ERR_UNSUPPORTED, "%s: M or N too large", fn);
     const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
     if (tiles > (int64_t)UINT32_MAX) return fail(DMPQ_ERR_UNSUPPORTED, "%s: too many tiles", fn);
+    if (K > kMaxGemmK)
+        return fail(DMPQ_ERR_UNSUPPORTED, "%s: K = %lld exceeds %lld", fn, (long long)K, (long long)kMaxGemmK);
     return check_k(fn, K);
 }
 

@@ -22,8 +22,13 @@
 // l % 32 of an A-subtile and 4 consecutive output columns per register group.
 //
 // K tail (TAIL = true): when K bytes are not a multiple of 128, the last stage
-// is partial.  Its chunks past K are loaded from the row start (in bounds) and
-// the fragments of its k-steps past K are zeroed in both operands.
+// is partial.  Its chunks past K are loaded from the stage's first chunk (in
+// bounds) and the fragments of its k-steps past K are zeroed in both operands.
+//
+// Addressing: a DMA source is a scalar base (the operand's tile rows plus the
+// stage offset) plus the lane's 32-bit byte offset within those 256 rows
+// (K <= 2^22 keeps it below 2^32), so the instruction takes the scalar-base
+// form and the loop does no 64-bit vector address arithmetic.
 #pragma once
 
 #include "device.hpp"
@@ -67,13 +72,15 @@ __device__ __forceinline__ int swz128(int row, int kc) { return kc ^ ((row >> 1)
 // (expcnt and lgkmcnt left free)
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-// Per-lane state: DMA sources (row start + the lane's chunk) and fragment rows.
+// Per-lane state: DMA sources (the tile's scalar bases and the lane's byte
+// offsets from them: its row and chunk) and fragment rows.
 struct DmaLane {
-    const uint8_t *srcA[gdma::BLOCKS], *srcW[gdma::BLOCKS];
+    const uint8_t *A, *W;                           // first rows of the A and W tiles
+    uint32_t goA[gdma::BLOCKS], goW[gdma::BLOCKS];  // the lane's DMA byte offsets
     int kc[gdma::BLOCKS];  // the lane's 16-byte chunk of its DMA rows
     int offA, offW;        // byte offset of the lane's first fragment row (A; W incl. the A tile)
     int sw, hk;            // swizzle key of the lane's rows, K half
-    int wave;
+    int wave;              // wave index (uniform)
 };
 
 // Fragments of k-step s (32 bytes of each row) of the stage in `buf`.  Rows
@@ -100,20 +107,22 @@ __device__ __forceinline__ void dma_frags(const uint8_t *buf, const DmaLane &L, 
 
 // One DMA instruction of a stage at byte offset k0 of every row: the q-th
 // 1 KB block of operand op (0 = A, 1 = W).  TAIL: a chunk past the row's
-// Kb bytes is loaded from the row start instead (its values are never used).
+// Kb bytes is loaded from the stage's first chunk instead (in bounds: a stage
+// holds at least 32 valid bytes; its values are never used).  The empty asm
+// statement keeps the scalar base opaque, so that the compiler cannot fold
+// the stage offset into a per-lane 64-bit address.
 template <bool TAIL>
 __device__ __forceinline__ void dma_one(uint8_t *dst, const DmaLane &L, int64_t k0, int64_t Kb,
                                         int q, int op) {
     using namespace gdma;
     typedef __attribute__((address_space(3))) void lds_void;
     const int b = L.wave + 4 * q;
-    const uint8_t *src = (op ? L.srcW[q] : L.srcA[q]);
-    if (TAIL) {
-        src = k0 + 16 * L.kc[q] < Kb ? src + k0 : src - 16 * L.kc[q];
-    } else {
-        src += k0;
-    }
-    __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(dst + op * TILE + b * 1024), 16, 0, 0);
+    const uint8_t *base = (op ? L.W : L.A) + k0;
+    asm("" : "+s"(base));
+    uint32_t off = op ? L.goW[q] : L.goA[q];
+    if (TAIL && !(k0 + 16 * L.kc[q] < Kb)) off -= (uint32_t)(16 * L.kc[q]);
+    __builtin_amdgcn_global_load_lds((const void *)(base + off), (lds_void *)(dst + op * TILE + b * 1024), 16, 0,
+                                     0);
 }
 
 template <bool TAIL>
@@ -212,7 +221,7 @@ __device__ __forceinline__ void dma_gemm_mainloop(const uint8_t *__restrict__ A,
                                                   typename Op::acc_t (&acc)[4][4]) {
     using namespace gdma;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
     for (int i = 0; i < 4; i++)
@@ -222,8 +231,11 @@ __device__ __forceinline__ void dma_gemm_mainloop(const uint8_t *__restrict__ A,
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0;
 
     // Per-lane source offsets of this wave's load blocks: block b = wave + 4q
-    // covers tile rows 8b .. 8b+7; lane l fills row 8b + l/8, slot l%8.
+    // covers tile rows 8b .. 8b+7; lane l fills row 8b + l/8, slot l%8.  Rows
+    // past M or N load a clamped row (at or after the tile's first row).
     DmaLane L;
+    L.A = A + m0 * ld;
+    L.W = W + n0 * ld;
     L.wave = wave;
     L.hk = lane >> 5;
 #pragma unroll
@@ -234,8 +246,8 @@ __device__ __forceinline__ void dma_gemm_mainloop(const uint8_t *__restrict__ A,
         const int64_t gm = m0 + row < M ? m0 + row : M - 1;
         const int64_t gn = n0 + row < N ? n0 + row : N - 1;
         L.kc[q] = kc;
-        L.srcA[q] = A + gm * ld + kc * 16;
-        L.srcW[q] = W + gn * ld + kc * 16;
+        L.goA[q] = (uint32_t)((gm - m0) * ld + kc * 16);
+        L.goW[q] = (uint32_t)((gn - n0) * ld + kc * 16);
     }
     L.offA = (wm * 128 + (lane & 31)) * BK;
     L.offW = TILE + (wn * 128 + (lane & 31)) * BK;
@@ -260,6 +272,11 @@ __device__ __forceinline__ void dma_gemm_mainloop(const uint8_t *__restrict__ A,
     dma_frags<TAIL>(lds, L, 0, dma_valid(Kb, 0), a0, b0);
     dma_frags<TAIL>(lds, L, 1, dma_valid(Kb, 0), a1, b1);
     for (int kt = 0; kt < nk; kt++) {
+        // the offsets become opaque values that change (in place, with no
+        // instruction) every stage, so their 64-bit extension stays in the
+        // loop and each DMA keeps the scalar-base form
+#pragma unroll
+        for (int q = 0; q < BLOCKS; q++) asm("" : "+v"(L.goA[q]), "+v"(L.goW[q]));
         uint8_t *cur = lds + (kt & 1) * STAGE;
         uint8_t *nxt = lds + ((kt & 1) ^ 1) * STAGE;
         // second half into nxt: stage kt+1 (kt = 0 repeats the prologue's

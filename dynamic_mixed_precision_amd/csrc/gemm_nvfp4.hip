@@ -18,11 +18,10 @@
 //
 // Tiling (all paths of variant 0): 256 threads = 2 x 2 waves, workgroup tile
 // 256 x 256, wave tile 128 x 128 = 4 x 4 MFMA 32x32x16 tiles.  Three paths:
-//  * K % 128 == 0 (the DiT shapes; K >= 384 when K % 256 != 0; operands
-//    below 4 GiB): raw codes and scales are copied into LDS by DMA and each
-//    wave dequantizes its own fragments into registers (gemm_fp4_dma_kernel;
-//    gemm_fp4_dma_tail_kernel when K % 256 == 128, whose last stage is a half
-//    stage);
+//  * K % 128 == 0 (the DiT shapes; K >= 384 when K % 256 != 0): raw codes
+//    and scales are copied into LDS by DMA and each wave dequantizes its own
+//    fragments into registers (gemm_fp4_dma_kernel; gemm_fp4_dma_tail_kernel
+//    when K % 256 == 128, whose last stage is a half stage);
 //  * K % 64 == 0: codes are loaded into registers, dequantized once per
 //    workgroup into a double-buffered fp16 LDS tile (gemm_fp4_fast_kernel);
 //  * any K % 16 == 0: as the previous, with the K tail masked
@@ -415,9 +414,9 @@ __device__ __forceinline__ int key(int row) { return (row >> 1) & 7; }
 // share the swizzle key of lane%32, so the row block i only adds a constant
 // (an immediate offset) to the lane's base addresses.
 struct Fp4DmaLane {
-    // DMA sources: the operand bases (uniform) and the lane's byte offsets
-    // into them (32-bit: every operand is below 2 GiB), so that an address is
-    // a scalar base plus a fixed vector offset
+    // DMA sources: the tile's first rows of each operand (uniform) and the
+    // lane's byte offsets from them (32-bit: 256 rows of K / 2 bytes, K <=
+    // 2^22), so that an address is a scalar base plus a vector offset
     const uint8_t *ca, *cw, *sa, *sw;
     uint32_t goffA[fp4dma::CBLK], goffW[fp4dma::CBLK], goffSA, goffSW;
     int offA, offW, offSA, offSW;  // byte offsets of the lane's first fragment row in a stage
@@ -574,10 +573,10 @@ __device__ __forceinline__ void fp4dma_mainloop(const uint8_t *__restrict__ ca, 
     // covers rows 64 wave .. +63, one lane per row.  Rows past M or N load a
     // clamped row; their outputs are never stored.
     Fp4DmaLane L;
-    L.ca = ca;
-    L.cw = cw;
-    L.sa = sa;
-    L.sw = sw;
+    L.ca = ca + m0 * rb;
+    L.cw = cw + n0 * rb;
+    L.sa = sa + m0 * nb;
+    L.sw = sw + n0 * nb;
     L.wave = wave;
     L.hk = lane >> 5;
     L.sh = 16 * L.hk;
@@ -587,15 +586,15 @@ __device__ __forceinline__ void fp4dma_mainloop(const uint8_t *__restrict__ ca, 
         const int piece = (lane % 8) ^ key(row);
         const int64_t gm = m0 + row < M ? m0 + row : M - 1;
         const int64_t gn = n0 + row < N ? n0 + row : N - 1;
-        L.goffA[q] = (uint32_t)(gm * rb + piece * 16);
-        L.goffW[q] = (uint32_t)(gn * rb + piece * 16);
+        L.goffA[q] = (uint32_t)((gm - m0) * rb + piece * 16);
+        L.goffW[q] = (uint32_t)((gn - n0) * rb + piece * 16);
     }
     {
         const int row = 64 * wave + lane;
         const int64_t gm = m0 + row < M ? m0 + row : M - 1;
         const int64_t gn = n0 + row < N ? n0 + row : N - 1;
-        L.goffSA = (uint32_t)(gm * nb);
-        L.goffSW = (uint32_t)(gn * nb);
+        L.goffSA = (uint32_t)((gm - m0) * nb);
+        L.goffSW = (uint32_t)((gn - n0) * nb);
     }
     const int ra = wm * 128 + (lane & 31), rw = wn * 128 + (lane & 31);
     L.offA = ra * CROW;
@@ -883,12 +882,10 @@ static hipError_t launch_fp4_paths(hipStream_t s, const uint8_t *ca, const uint8
     const int64_t tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
     const dim3 grid((unsigned)(tm * tn)), block(256);
     const unsigned utm = (unsigned)tm, utn = (unsigned)tn;
-    // the DMA kernels address operands by 32-bit byte offsets
-    const bool off32 = M * (K / 2) <= (int64_t)UINT32_MAX && N * (K / 2) <= (int64_t)UINT32_MAX;
-    if (off32 && K % 256 == 0)
+    if (K % 256 == 0)
         return launch_fp4_dma<OUT, EPI, false>(s, gemm_fp4_dma_kernel<OUT, EPI>, gemm_fp4_split_kernel, ca, sa, ga,
                                                cw, sw, gw, M, N, K, y, partial, spart, utm, utn);
-    if (off32 && K % 128 == 0 && K >= 384)
+    if (K % 128 == 0 && K >= 384)
         return launch_fp4_dma<OUT, EPI, true>(s, gemm_fp4_dma_tail_kernel<OUT, EPI>, gemm_fp4_split_tail_kernel, ca,
                                               sa, ga, cw, sw, gw, M, N, K, y, partial, spart, utm, utn);
     if (K % (4 * 16) == 0) {

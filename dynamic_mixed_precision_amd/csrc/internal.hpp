@@ -75,6 +75,9 @@ constexpr size_t kSplitAreaBytes = kMaxSplitUnits * kSplitWords * 4;
 // traffic (measured on the 17776-token shapes), so only longer K pay.  The
 // NVFP4 and BF16 tails are split at every K.
 constexpr int64_t kSplitMinKInt8 = 4096;
+// Largest K of the GEMM entry points: the DMA kernels address 256 rows of an
+// operand (at most 2 bytes per element) from a scalar base by 32-bit offsets.
+constexpr int64_t kMaxGemmK = int64_t(1) << 22;
 
 // epi: bit 0 GELU, bit 1 fused NVFP4 amax of the output into partial[tile]
 // (bf16 output only); the GEMM tile is 256 x 256 on every path.  spart: the

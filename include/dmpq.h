@@ -25,7 +25,9 @@
  *     weights W are [N x K] (row = output channel, K contiguous); Y = X W^T
  *     is [M x N].
  *   - Every device tensor pointer must be 16-byte aligned.  K must be a
- *     positive multiple of 16 (the Hadamard block and the NVFP4 scale group).
+ *     positive multiple of 16 (the Hadamard block and the NVFP4 scale group);
+ *     the GEMM entry points take K <= 4194304 (2^22; DMPQ_ERR_UNSUPPORTED
+ *     beyond).
  *     M, N >= 0 (0 is an empty no-op); a buffer of zero elements may be NULL.
  *   - Non-finite inputs (the pages say nothing of them; the rule taken
  *     here): the quantizers encode a NaN as code 0 (INT8 0, E2M1 +0, E4M3

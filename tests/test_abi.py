@@ -207,6 +207,21 @@ def test_noalloc_and_w4_gemm_validation(monkeypatch):
     _expect(4, dm.qgemm_int8_from_nvfp4, qa, sa, cw, sw, gw, y, ws, epilogue=dm.EPI_GELU, out_dtype=dm.OUT_F32)
 
 
+def test_gemm_k_limit(monkeypatch):
+    """Every GEMM entry point rejects K above 2^22 before any launch (the DMA
+    kernels address 256 operand rows by 32-bit offsets)."""
+    _library_checks_only(monkeypatch)
+    M, N, K = 2, 4, (1 << 22) + 128
+    y = _Fake((M, N))
+    _expect(4, dm.qgemm_int8, _Fake((M, K)), _Fake((M,)), _Fake((N, K)), _Fake((N,)), y)
+    _expect(4, dm.qgemm_nvfp4, _Fake((M, K // 2)), _Fake((M, K // 16)), _Fake((1,)), _Fake((N, K // 2)),
+            _Fake((N, K // 16)), _Fake((1,)), y)
+    _expect(4, dm.gemm_bf16, _Fake((M, K)), _Fake((N, K)), y)
+    ws = _Fake((dm.workspace_bytes(dm.OP_GEMM_W4, M, N),))
+    _expect(4, dm.qgemm_int8_from_nvfp4, _Fake((M, K)), _Fake((M,)), _Fake((N, K // 2)), _Fake((N, K // 16)),
+            _Fake((1,)), y, ws)
+
+
 def test_selftest_validation(monkeypatch):
     _library_checks_only(monkeypatch)
     _expect(1, dm.selftest_codec, 2, 0, 16, _Fake((384,)))
