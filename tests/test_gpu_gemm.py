@@ -102,9 +102,12 @@ def test_int8_gemm_extremes(orc):
     _check_int8(orc, qa, sa, qw, sw)
 
 
+# K % 256 == 128 from 384 closes with a half stage (384, 640, 1152, 1920, 2432);
+# K = 128 takes the K % 64 kernel
 @pytest.mark.parametrize("M,N,K", [(1, 1, 16), (256, 256, 256), (200, 136, 80), (129, 257, 384),
                                    (64, 96, 1920), (33, 40, 12288), (300, 130, 48), (1, 1, 256),
-                                   (129, 257, 512), (513, 300, 768)])
+                                   (129, 257, 512), (513, 300, 768), (257, 130, 640), (70, 520, 1152),
+                                   (300, 300, 2432), (129, 70, 128)])
 def test_nvfp4_gemm_parity(orc, M, N, K):
     require_gpu()
     say(f"qgemm_nvfp4 M={M} N={N} K={K}")
@@ -125,12 +128,12 @@ def test_nvfp4_gemm_random_codes(orc):
     sw = rng.integers(0, 0x7F, (N, K // 16)).astype(np.uint8)
     _check_nvfp4(orc, ca, sa, 0.75, cw, sw, 1.5e-3)
     _check_nvfp4(orc, ca, sa, 0.0, cw, sw, 1.0)
-    K = 512
-    ca = rng.integers(0, 256, (M, K // 2)).astype(np.uint8)
-    cw = rng.integers(0, 256, (N, K // 2)).astype(np.uint8)
-    sa = rng.integers(0, 0x7F, (M, K // 16)).astype(np.uint8)
-    sw = rng.integers(0, 0x7F, (N, K // 16)).astype(np.uint8)
-    _check_nvfp4(orc, ca, sa, 0.75, cw, sw, 1.5e-3)
+    for K in (512, 640):  # 256-element stages; and two with the closing half stage
+        ca = rng.integers(0, 256, (M, K // 2)).astype(np.uint8)
+        cw = rng.integers(0, 256, (N, K // 2)).astype(np.uint8)
+        sa = rng.integers(0, 0x7F, (M, K // 16)).astype(np.uint8)
+        sw = rng.integers(0, 0x7F, (N, K // 16)).astype(np.uint8)
+        _check_nvfp4(orc, ca, sa, 0.75, cw, sw, 1.5e-3)
 
 
 def test_gemm_empty():
