@@ -188,7 +188,9 @@ dmpq_status dmpq_hadamard_quant_nvfp4_noalloc(hipStream_t stream, const uint16_t
 
 /* ---------------------------------------------------------------------------
  * INT8 quantized linear ([gist-en] §2.A "Routing"; [gist-zh] §2.A weight
- * handling).  acc[m][n] = sum_k qa[m][k] * qw[n][k] (exact int32), then
+ * handling).  acc[m][n] = sum_k qa[m][k] * qw[n][k] (exact int32: codes in
+ * [-127, 127] keep |acc| < 2^31 for any K <= 133144; beyond that the int32
+ * sum wraps if the products do not cancel), then
  * out_dtype F32: y = (float(acc) * sa[m]) * sw[n]; BF16: RNE of that value;
  * I32: the accumulator.  qa [M x K] int8 with per-row scales sa [M];
  * qw [N x K] int8 with per-output-channel scales sw [N]; y [M x N].

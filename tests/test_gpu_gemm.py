@@ -136,6 +136,25 @@ def test_nvfp4_gemm_random_codes(orc):
         _check_nvfp4(orc, ca, sa, 0.75, cw, sw, 1.5e-3)
 
 
+def test_gemm_max_k(orc):
+    """K = 2^22, the largest K the GEMM entry points take (the DMA kernels
+    address 256 rows from a scalar base by 32-bit offsets): INT8, NVFP4 and
+    BF16 against the oracle on a few rows and columns."""
+    require_gpu()
+    M, N, K = 3, 5, 1 << 22
+    say(f"GEMMs at the largest K: M={M} N={N} K={K}")
+    rng = np.random.default_rng(22)
+    (qa, sa), (ca, sca, ga), p = _quantized_pair(orc, rng, M, N, K)
+    _check_int8(orc, qa, sa, p["qw"], p["sw_row"])
+    _check_nvfp4(orc, ca, sca, ga, p["cw"], p["sw"], p["gw"], variants=(dm.FP4_BF16_DEQUANT,))
+    x, w = workloads.activations(rng, M, K), workloads.weight(rng, N, K)
+    y0, b0 = orc.gemm_bf16(x, w)
+    y = empty((M, N), np.float32)
+    dm.gemm_bf16(dev(x), dev(w), y)
+    torch.cuda.synchronize()
+    assert np.all(np.abs(host(y).astype(np.float64) - y0) <= TOL * b0)
+
+
 def test_gemm_empty():
     require_gpu()
     say("qgemm empty shapes")
