@@ -49,16 +49,17 @@ struct Nvfp4Rows {
     }
 };
 
+// One row group (256 / LPR rows) of the row quantizer; red: 4 floats of LDS.
+// Every thread of the workgroup calls it with the same group.
 template <int LPR, int BPL, class Src>
-__global__ __launch_bounds__(256) void row_quant_int8_kernel(Src src, int64_t M, int64_t K,
-                                                             int8_t *__restrict__ q,
-                                                             float *__restrict__ s_row) {
+__device__ __forceinline__ void row_quant_int8_group(const Src &src, int64_t M, int64_t K,
+                                                     int8_t *__restrict__ q, float *__restrict__ s_row,
+                                                     int64_t group, float *red) {
     static_assert(LPR >= 16 && LPR <= 256 && 256 % LPR == 0, "lanes per row");
     constexpr int ROWS = 256 / LPR;
-    __shared__ float red[4];
     const int tid = threadIdx.x;
     const int lr = tid % LPR;
-    const int64_t row = (int64_t)blockIdx.x * ROWS + tid / LPR;
+    const int64_t row = group * ROWS + tid / LPR;
     const int nblk = (int)(K / 16);
     const bool row_ok = row < M;
 
@@ -103,6 +104,33 @@ __global__ __launch_bounds__(256) void row_quant_int8_kernel(Src src, int64_t M,
             *reinterpret_cast<uint4 *>(qr + 16 * (int64_t)b) =
                 zero_row ? make_uint4(0u, 0u, 0u, 0u) : int8_codes_magic(v[i], inv);
     }
+}
+
+template <int LPR, int BPL, class Src>
+__global__ __launch_bounds__(256) void row_quant_int8_kernel(Src src, int64_t M, int64_t K,
+                                                             int8_t *__restrict__ q,
+                                                             float *__restrict__ s_row) {
+    __shared__ float red[4];
+    row_quant_int8_group<LPR, BPL>(src, M, K, q, s_row, blockIdx.x, red);
+}
+
+// The INT8 route's two row quantizations in one launch: workgroups
+// 0 .. wgroups-1 convert the NVFP4 weight rows, the rest quantize the
+// activation rows.  Both run the same row plan (they share K).  The weight
+// rows go first: that conversion moves few bytes and is bound by latency,
+// which the activation rows' stream then covers.
+template <int LPR, int BPL>
+__global__ __launch_bounds__(256) void row_quant_int8_w8_kernel(Nvfp4Rows wsrc, int64_t N,
+                                                                int8_t *__restrict__ qw,
+                                                                float *__restrict__ sw_row,
+                                                                int64_t wgroups, Bf16Rows xsrc,
+                                                                int64_t M, int8_t *__restrict__ q,
+                                                                float *__restrict__ s_row, int64_t K) {
+    __shared__ float red[4];
+    if ((int64_t)blockIdx.x < wgroups)
+        row_quant_int8_group<LPR, BPL>(wsrc, N, K, qw, sw_row, blockIdx.x, red);
+    else
+        row_quant_int8_group<LPR, BPL>(xsrc, M, K, q, s_row, blockIdx.x - wgroups, red);
 }
 
 // Pick lanes-per-row and blocks-per-lane for a row of nblk 16-blocks: the
@@ -228,6 +256,44 @@ hipError_t launch_w8_from_nvfp4(hipStream_t s, const uint8_t *cw, const uint8_t 
     return launch_rows(s, Nvfp4Rows{cw, sw, gw}, N, K, qw, sw_row);
 }
 
+template <int LPR>
+static hipError_t launch_w8_pair_lpr(hipStream_t s, int bpl, const Nvfp4Rows &w, int64_t N, int8_t *qw,
+                                     float *sw_row, const Bf16Rows &x, int64_t M, int8_t *q,
+                                     float *s_row, int64_t K) {
+    const int64_t rows = 256 / LPR;
+    const int64_t wg = (N + rows - 1) / rows, xg = (M + rows - 1) / rows;
+    const dim3 grid((unsigned)(wg + xg));
+    switch (bpl) {
+#define DMPQ_BPL(B)                                                                            \
+    case B:                                                                                    \
+        hipLaunchKernelGGL((row_quant_int8_w8_kernel<LPR, B>), grid, dim3(256), 0, s, w, N, qw, \
+                           sw_row, wg, x, M, q, s_row, K);                                     \
+        break;
+        DMPQ_BPL(1) DMPQ_BPL(2) DMPQ_BPL(3) DMPQ_BPL(4) DMPQ_BPL(6) DMPQ_BPL(8)
+#undef DMPQ_BPL
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_hq_int8_w8(hipStream_t s, const uint16_t *x, int64_t M, int64_t K, int flags,
+                             int8_t *q, float *s_row, const uint8_t *cw, const uint8_t *sw,
+                             const float *gw, int64_t N, int8_t *qw, float *sw_row) {
+    RowPlan p;
+    if (!plan_rows(K, &p)) return hipErrorInvalidValue;
+    if (M == 0 && N == 0) return hipSuccess;
+    const Nvfp4Rows w{cw, sw, gw};
+    const Bf16Rows xr{x, flags};
+    switch (p.lpr) {
+        case 16: return launch_w8_pair_lpr<16>(s, p.bpl, w, N, qw, sw_row, xr, M, q, s_row, K);
+        case 32: return launch_w8_pair_lpr<32>(s, p.bpl, w, N, qw, sw_row, xr, M, q, s_row, K);
+        case 64: return launch_w8_pair_lpr<64>(s, p.bpl, w, N, qw, sw_row, xr, M, q, s_row, K);
+        case 128: return launch_w8_pair_lpr<128>(s, p.bpl, w, N, qw, sw_row, xr, M, q, s_row, K);
+        case 256: return launch_w8_pair_lpr<256>(s, p.bpl, w, N, qw, sw_row, xr, M, q, s_row, K);
+    }
+    return hipErrorInvalidValue;
+}
+
 // ---------------------------------------------------------------------------
 // Outlier count of the Purified Delta Refresh check (gist.science summaries,
 // §2.C: before a refresh writes the cached delta, a block input with a high
@@ -304,8 +370,10 @@ __global__ __launch_bounds__(256) void outlier_count_kernel(const uint16_t *__re
             }
             float v[16];
             unpack16(raw[i][0], raw[i][1], v);
+            // one fused multiply-add: the square of a bf16 value is exact in
+            // fp64, so fma(v, v, s) rounds exactly as s + v * v
 #pragma unroll
-            for (int j = 0; j < 16; j++) s += (double)v[j] * (double)v[j];
+            for (int j = 0; j < 16; j++) s = __builtin_fma((double)v[j], (double)v[j], s);
         }
         if constexpr (LPR <= kWave) {
             s = group_sum_d<LPR>(s);
@@ -325,20 +393,21 @@ __global__ __launch_bounds__(256) void outlier_count_kernel(const uint16_t *__re
         // a non-finite R (or a row past M) counts nothing: 0xFFFF is above
         // every magnitude; zero padding never counts either (threshold >= 1)
         const uint32_t thr = (row_ok && R <= 1.7976931348623157e308) ? outlier_threshold(R, dK) : 0xFFFFu;
+        // the wave's count per element slot: a ballot of the compare and a
+        // scalar population count, so the sum across lanes is free
 #pragma unroll
         for (int i = 0; i < BPL; i++) {
             const uint32_t w[8] = {raw[i][0].x, raw[i][0].y, raw[i][0].z, raw[i][0].w,
                                    raw[i][1].x, raw[i][1].y, raw[i][1].z, raw[i][1].w};
 #pragma unroll
             for (int j = 0; j < 8; j++) {
-                cnt += (int)((w[j] & 0x7FFFu) >= thr);
-                cnt += (int)(((w[j] >> 16) & 0x7FFFu) >= thr);
+                cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64((w[j] & 0x7FFFu) >= thr));
+                cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(((w[j] >> 16) & 0x7FFFu) >= thr));
             }
         }
     }
-    double tot = (double)cnt;
-    tot = wave_sum(tot);
-    if ((tid & (kWave - 1)) == 0) red[tid / kWave] = tot;
+    // cnt is the wave's count (the same in every lane)
+    if ((tid & (kWave - 1)) == 0) red[tid / kWave] = (double)cnt;
     __syncthreads();
     if (tid == 0) partial[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
 }
