@@ -61,10 +61,12 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--out-dtype", choices=["bf16", "f32"], default="bf16",
                    help="GEMM output type (bf16 feeds the next layer; f32 is the parity contract)")
-    p.add_argument("--int8-weights", choices=["convert", "stored"], default="convert",
+    p.add_argument("--int8-weights", choices=["convert", "convert-separate", "stored"], default="convert",
                    help="convert: only NVFP4 weights are kept and an INT8-routed linear converts its "
                         "weight into one scratch buffer right before its GEMM (the method's weight "
-                        "handling); stored: use INT8 weights prepared offline")
+                        "handling), in the same launch as its activation quantization; "
+                        "convert-separate: the same conversion as a launch of its own; stored: use "
+                        "INT8 weights prepared offline")
     p.add_argument("--pdr", default="4,0.01", metavar="KAPPA,RHO",
                    help="Purified Delta Refresh check of every block input ('off' to skip it); "
                         "a block above rho runs its linears as BF16 GEMMs")
@@ -386,13 +388,21 @@ def main():
                     kt("gemm_bf16", flops, dm.gemm_bf16_ex, x.view(M, lin.K), L["w"], ybuf[lin.name],
                        epi, ws_gemm, out_dtype, _shape=gshape)
                 elif route == dm.ROUTE_INT8:
-                    kt("hadamard_quant_int8", 3.0 * M * lin.K + 4.0 * M,
-                       dm.hadamard_quant_int8, x, qb["q"], qb["s"], _shape=f"{M}x{lin.K}")
                     qw, swr = L["qw"], L["swr"]
+                    w8_bytes = (0.5 + 1.0 / 16 + 1.0) * lin.N * lin.K + 8.0 * lin.N
                     if args.int8_weights == "convert":
                         qw = w8_scratch[:lin.N * lin.K].view(lin.N, lin.K)
                         swr = s8_scratch[:lin.N]
-                        kt("weight_int8_from_nvfp4", (0.5 + 1.0 / 16 + 1.0) * lin.N * lin.K + 8.0 * lin.N,
+                        kt("hadamard_quant_int8_w8", 3.0 * M * lin.K + 4.0 * M + w8_bytes,
+                           dm.hadamard_quant_int8_w8, x, qb["q"], qb["s"], L["cw"], L["sw"], L["gw"], qw, swr,
+                           _shape=f"{M}x{lin.K}+{lin.N}x{lin.K}")
+                    else:
+                        kt("hadamard_quant_int8", 3.0 * M * lin.K + 4.0 * M,
+                           dm.hadamard_quant_int8, x, qb["q"], qb["s"], _shape=f"{M}x{lin.K}")
+                    if args.int8_weights == "convert-separate":
+                        qw = w8_scratch[:lin.N * lin.K].view(lin.N, lin.K)
+                        swr = s8_scratch[:lin.N]
+                        kt("weight_int8_from_nvfp4", w8_bytes,
                            dm.weight_int8_from_nvfp4, L["cw"], L["sw"], L["gw"], qw, swr,
                            _shape=f"{lin.N}x{lin.K}")
                     kt("qgemm_int8", flops, dm.qgemm_int8_ex, qb["q"], qb["s"], qw, swr,
@@ -599,6 +609,7 @@ def main():
 
 
 PEAKS = {"hadamard_quant_int8": ("hbm", HBM_GBPS, "GB/s"),
+         "hadamard_quant_int8_w8": ("hbm", HBM_GBPS, "GB/s"),
          "weight_int8_from_nvfp4": ("hbm", HBM_GBPS, "GB/s"),
          "outlier_count": ("hbm", HBM_GBPS, "GB/s"),
          "gemm_bf16": ("mfma", PEAK_BF16_TFLOPS, "TFLOP/s"),
@@ -645,20 +656,20 @@ def kernel_tables(ksum: dict, kshape: dict):
 # ---- the other workloads, measured after the headline ------------------------
 
 def _gemm_call(dm, kt, route, x, qb, L, y, ws_q, ws_gemm, w8, s8, epi=0):
-    """One routed linear as the headline step runs it: Hadamard + quant, the
-    NVFP4 -> INT8 weight conversion into the shared scratch (INT8 route), and
-    the quantized GEMM with the full GEMM workspace, bf16 output."""
+    """One routed linear as the headline step runs it: Hadamard + quant and,
+    on the INT8 route in the same launch, the NVFP4 -> INT8 weight conversion
+    into the shared scratch; then the quantized GEMM with the full GEMM
+    workspace, bf16 output."""
     M, K = x.shape
     N = L["N"]
     flops = 2.0 * M * N * K
     gshape = f"{M}x{N}x{K}"
     if route == dm.ROUTE_INT8:
-        kt("hadamard_quant_int8", 3.0 * M * K + 4.0 * M, dm.hadamard_quant_int8, x, qb["q"], qb["s"],
-           _shape=f"{M}x{K}")
         qw = w8[:N * K].view(N, K)
         sw = s8[:N]
-        kt("weight_int8_from_nvfp4", (0.5 + 1.0 / 16 + 1.0) * N * K + 8.0 * N, dm.weight_int8_from_nvfp4,
-           L["cw"], L["sw"], L["gw"], qw, sw, _shape=f"{N}x{K}")
+        kt("hadamard_quant_int8_w8", 3.0 * M * K + 4.0 * M + (0.5 + 1.0 / 16 + 1.0) * N * K + 8.0 * N,
+           dm.hadamard_quant_int8_w8, x, qb["q"], qb["s"], L["cw"], L["sw"], L["gw"], qw, sw,
+           _shape=f"{M}x{K}+{N}x{K}")
         kt("qgemm_int8", flops, dm.qgemm_int8_ex, qb["q"], qb["s"], qw, sw, y, epi, ws_gemm, dm.OUT_BF16,
            _shape=gshape)
     else:
@@ -953,15 +964,19 @@ def run_int8_weight_forms(torch, dm, wl, reps: int, events: str) -> dict:
         ws_gemm = dm.new_workspace(dm.OP_GEMM, "cuda", M, N)
         ws_w4 = dm.new_workspace(dm.OP_GEMM_W4, "cuda", M, N)
         conv = (dm.weight_int8_from_nvfp4, L["cw"], L["sw"], L["gw"], qw, swr)
+        quant = (dm.hadamard_quant_int8, x, qa, sa)
+        quant_w8 = (dm.hadamard_quant_int8_w8, x, qa, sa, L["cw"], L["sw"], L["gw"], qw, swr)
         gemm = (dm.qgemm_int8_ex, qa, sa, qw, swr, y1, 0, ws_gemm, dm.OUT_BF16)
         fused = (dm.qgemm_int8_from_nvfp4, qa, sa, L["cw"], L["sw"], L["gw"], y2, ws_w4, 0, dm.OUT_BF16)
-        for f in (conv, gemm, fused):  # warmup
+        for f in (conv, gemm, fused, quant, quant_w8):  # warmup
             f[0](*f[1:])
         torch.cuda.synchronize()
         kt.rec = {}
         kt.on = True
         for _ in range(reps):
+            kt("quant", 0.0, *quant)
             kt("convert", 0.0, *conv)
+            kt("quant_w8", 0.0, *quant_w8)
             kt("int8_gemm", 0.0, *gemm)
             kt("fused", 0.0, *fused)
         torch.cuda.synchronize()
@@ -969,6 +984,7 @@ def run_int8_weight_forms(torch, dm, wl, reps: int, events: str) -> dict:
         t = {k: v["avg_us"] for k, v in kt.summary(reps).items()}
         flops = 2.0 * M * N * K
         out[f"{lin.name} {M}x{N}x{K}"] = {
+            "act_quant_us": round(t["quant"], 1), "act_quant_and_convert_one_launch_us": round(t["quant_w8"], 1),
             "convert_us": round(t["convert"], 1), "int8_gemm_us": round(t["int8_gemm"], 1),
             "convert_then_gemm_us": round(t["convert"] + t["int8_gemm"], 1), "fused_us": round(t["fused"], 1),
             "fused_TOPS": round(flops / t["fused"] / 1e6, 1),

@@ -36,7 +36,8 @@ EXPORTS = ("dmpq_last_error", "dmpq_version", "dmpq_workspace_bytes", "dmpq_gamm
            "dmpq_tdc_step", "dmpq_tdc_commit", "dmpq_prep_weight", "dmpq_weight_int8_from_nvfp4",
            "dmpq_outlier_count", "dmpq_pdr_decide", "dmpq_gemm_bf16", "dmpq_qgemm_int8_ex",
            "dmpq_qgemm_nvfp4_ex", "dmpq_gemm_bf16_ex", "dmpq_selftest_codec",
-           "dmpq_hadamard_quant_nvfp4_noalloc", "dmpq_qgemm_int8_from_nvfp4")
+           "dmpq_hadamard_quant_nvfp4_noalloc", "dmpq_qgemm_int8_from_nvfp4",
+           "dmpq_hadamard_quant_int8_w8")
 
 
 class DmpqError(RuntimeError):
@@ -89,6 +90,7 @@ def _declare(L):
         "dmpq_tdc_commit": (i32, [C.POINTER(TdcState), i32, pd]),
         "dmpq_prep_weight": (i32, [vp, vp, i64, i64, i32, vp, vp, vp, vp, vp, vp, C.c_size_t]),
         "dmpq_weight_int8_from_nvfp4": (i32, [vp, vp, vp, vp, i64, i64, vp, vp]),
+        "dmpq_hadamard_quant_int8_w8": (i32, [vp, vp, i64, i64, i32, vp, vp, vp, vp, vp, i64, vp, vp]),
         "dmpq_outlier_count": (i32, [vp, vp, i64, i64, f64, vp, vp, C.c_size_t]),
         "dmpq_pdr_decide": (i32, [f64, i64, f64, C.POINTER(C.c_int)]),
         "dmpq_gemm_bf16": (i32, [vp, vp, vp, i64, i64, i64, i32, vp]),
@@ -333,6 +335,23 @@ def weight_int8_from_nvfp4(cw, sw, gw, qw, sw_row, stream=None) -> None:
     _need(sw_row, "sw_row", 4 * N, 4)
     _check(lib().dmpq_weight_int8_from_nvfp4(_stream(stream), _ptr(cw), _ptr(sw), _ptr(gw), N, K,
                                              _ptr(qw), _ptr(sw_row)), "dmpq_weight_int8_from_nvfp4")
+
+
+def hadamard_quant_int8_w8(x, q, s_row, cw, sw, gw, qw, sw_row, flags: int = 0, stream=None) -> None:
+    """hadamard_quant_int8(x, q, s_row) and weight_int8_from_nvfp4(cw, sw, gw,
+    qw, sw_row) in one launch (x and the weight share K)."""
+    M, K = x.shape
+    N = cw.shape[0]
+    _need(x, "x", 2 * M * K, 2)
+    _need(q, "q", M * K, 1)
+    _need(s_row, "s_row", 4 * M, 4)
+    _need_k(cw, K // 2, "cw")
+    _need_nvfp4(cw, sw, gw, N, K, "weight")
+    _need(qw, "qw", N * K, 1)
+    _need(sw_row, "sw_row", 4 * N, 4)
+    _check(lib().dmpq_hadamard_quant_int8_w8(_stream(stream), _ptr(x), M, K, flags, _ptr(q), _ptr(s_row),
+                                             _ptr(cw), _ptr(sw), _ptr(gw), N, _ptr(qw), _ptr(sw_row)),
+           "dmpq_hadamard_quant_int8_w8")
 
 
 def qgemm_int8_from_nvfp4(qa, sa, cw, sw, gw, y, ws, epilogue: int = 0, out_dtype: int = OUT_BF16,

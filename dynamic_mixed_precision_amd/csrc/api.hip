@@ -442,6 +442,28 @@ dmpq_status dmpq_weight_int8_from_nvfp4(hipStream_t stream, const uint8_t *cw, c
     return hip_status(launch_w8_from_nvfp4(stream, cw, sw, d_gw, N, K, qw, sw_row), __func__);
 }
 
+dmpq_status dmpq_hadamard_quant_int8_w8(hipStream_t stream, const uint16_t *x, int64_t M,
+                                        int64_t K, int flags, int8_t *q, float *s_row,
+                                        const uint8_t *cw, const uint8_t *sw, const float *d_gw,
+                                        int64_t N, int8_t *qw, float *sw_row) {
+    if (M < 0) return fail(DMPQ_ERR_BAD_SHAPE, "%s: M = %lld < 0", __func__, (long long)M);
+    if (N < 0) return fail(DMPQ_ERR_BAD_SHAPE, "%s: N = %lld < 0", __func__, (long long)N);
+    if (dmpq_status s = check_k(__func__, K)) return s;
+    REQUIRE_PTR_N(x, M);
+    REQUIRE_PTR_N(q, M);
+    REQUIRE_PTR_N(s_row, M);
+    REQUIRE_PTR_N(cw, N);
+    REQUIRE_PTR_N(sw, N);
+    REQUIRE_PTR(d_gw);
+    REQUIRE_PTR_N(qw, N);
+    REQUIRE_PTR_N(sw_row, N);
+    if (flags & ~DMPQ_NO_HADAMARD) return fail(DMPQ_ERR_INVALID_ARG, "%s: unknown flags %d", __func__, flags);
+    if (!hq_int8_supported(K))
+        return fail(DMPQ_ERR_UNSUPPORTED, "%s: K = %lld exceeds 32768", __func__, (long long)K);
+    return hip_status(launch_hq_int8_w8(stream, x, M, K, flags, q, s_row, cw, sw, d_gw, N, qw, sw_row),
+                      __func__);
+}
+
 dmpq_status dmpq_outlier_count(hipStream_t stream, const uint16_t *x, int64_t M, int64_t K,
                                double kappa, double *d_count, void *ws, size_t ws_bytes) {
     if (M < 0) return fail(DMPQ_ERR_BAD_SHAPE, "%s: M = %lld < 0", __func__, (long long)M);

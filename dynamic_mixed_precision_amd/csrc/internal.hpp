@@ -35,6 +35,10 @@ inline int64_t gemm_tiles(int64_t M, int64_t N) { return ((M + 255) / 256) * ((N
 hipError_t launch_w8_from_nvfp4(hipStream_t s, const uint8_t *cw, const uint8_t *sw,
                                 const float *gw, int64_t N, int64_t K, int8_t *qw,
                                 float *sw_row);
+// launch_hq_int8 and launch_w8_from_nvfp4 (same K) in one launch
+hipError_t launch_hq_int8_w8(hipStream_t s, const uint16_t *x, int64_t M, int64_t K, int flags,
+                             int8_t *q, float *s_row, const uint8_t *cw, const uint8_t *sw,
+                             const float *gw, int64_t N, int8_t *qw, float *sw_row);
 // Row scales for the INT8 GEMM that converts an NVFP4 weight in its tile
 // load: s_row = amax/127 and inv_row = 127/amax of each row of
 // (E2M1 * E4M3) * gw, both 0 for a row whose reciprocal is not finite.

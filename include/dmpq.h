@@ -289,6 +289,21 @@ dmpq_status dmpq_weight_int8_from_nvfp4(hipStream_t stream, const uint8_t *cw, c
                                         float *sw_row);
 
 /* ---------------------------------------------------------------------------
+ * The two row quantizations of an INT8-routed linear in one launch: the
+ * activation quantization of dmpq_hadamard_quant_int8 (x, M, K, flags -> q,
+ * s_row) and the weight conversion of dmpq_weight_int8_from_nvfp4 (cw, sw,
+ * d_gw, N, K -> qw, sw_row), for the same K ([gist-en] §2.A "Routing": INT8
+ * activations per token; [gist-zh] §2.A weight-handling bullet: the NVFP4
+ * weight converted when an INT8 GEMM needs it).  Outputs are bit-identical
+ * to the two separate calls; M or N may be 0 (that half is skipped).
+ * Argument rules and errors as the two calls; no workspace.
+ * ------------------------------------------------------------------------- */
+dmpq_status dmpq_hadamard_quant_int8_w8(hipStream_t stream, const uint16_t *x, int64_t M,
+                                        int64_t K, int flags, int8_t *q, float *s_row,
+                                        const uint8_t *cw, const uint8_t *sw, const float *d_gw,
+                                        int64_t N, int8_t *qw, float *sw_row);
+
+/* ---------------------------------------------------------------------------
  * INT8 linear against an NVFP4 weight converted inside the GEMM ([gist-zh]
  * §2.A weight-handling bullet: weights stay in NVFP4 and are converted when
  * an INT8 GEMM needs them).  No INT8 copy of the weight is written: a first

@@ -139,6 +139,17 @@ def test_validation_before_launch(monkeypatch):
             _Fake((8, 65536)), _Fake((8,)))
     _expect(3, dm.weight_int8_from_nvfp4, _Fake((8, 16)), _Fake((8, 2)), _Fake((1,), addr=0x10004),
             _Fake((8, 32)), _Fake((8,)))
+    # the one-launch INT8 route: activation and weight rules together
+    xw = (_Fake((4, 32)), _Fake((4, 32)), _Fake((4,)))
+    ww = (_Fake((8, 16)), _Fake((8, 2)), _Fake((1,)), _Fake((8, 32)), _Fake((8,)))
+    _expect(2, dm.hadamard_quant_int8_w8, _Fake((4, 24)), _Fake((4, 24)), _Fake((4,)), _Fake((8, 12)),
+            _Fake((8, 1)), _Fake((1,)), _Fake((8, 24)), _Fake((8,)))
+    _expect(1, dm.hadamard_quant_int8_w8, *xw, *ww, flags=6)
+    _expect(3, dm.hadamard_quant_int8_w8, *xw, _Fake((8, 16)), _Fake((8, 2)), _Fake((1,), addr=0x10004),
+            _Fake((8, 32)), _Fake((8,)))
+    _expect(3, dm.hadamard_quant_int8_w8, _Fake((4, 32), addr=0x10008), _Fake((4, 32)), _Fake((4,)), *ww)
+    _expect(4, dm.hadamard_quant_int8_w8, _Fake((4, 65536)), _Fake((4, 65536)), _Fake((4,)),
+            _Fake((8, 32768)), _Fake((8, 4096)), _Fake((1,)), _Fake((8, 65536)), _Fake((8,)))
 
 
 def test_fused_epilogue_validation(monkeypatch):
@@ -272,6 +283,11 @@ def test_binding_checks_buffer_sizes(monkeypatch):
     raises("delta holds", dm.tdc_step, dm.TDC_SKIP, bf(64), bf(64), bf(63), True)
     raises("sums is missing", dm.tdc_step, dm.TDC_REFRESH, bf(64), bf(64), bf(64), False)
     raises("qw holds", dm.weight_int8_from_nvfp4, cw, scw, g, i8(N, K - 1), f32(N))
+    raises("qw holds", dm.hadamard_quant_int8_w8, bf(M, K), i8(M, K), f32(M), cw, scw, g, i8(N, K - 1), f32(N))
+    raises("s_row holds", dm.hadamard_quant_int8_w8, bf(M, K), i8(M, K), f32(M - 1), cw, scw, g, i8(N, K),
+           f32(N))
+    raises("cw has shape", dm.hadamard_quant_int8_w8, bf(M, K), i8(M, K), f32(M), u8(N, K), scw, g, i8(N, K),
+           f32(N))
     raises("sw_row holds", dm.prep_weight, bf(N, K), cw, scw, g, i8(N, K), f32(N - 1), u8(16))
     raises("count holds", dm.outlier_count, bf(M, K), 4.0, torch.zeros(0, dtype=torch.float64), u8(16))
     raises("stats holds", dm.selftest_codec, dm.CODEC_E4M3, 0, 16, torch.zeros(3 * 128 - 1, dtype=torch.int32))

@@ -183,6 +183,59 @@ def test_weight_int8_from_nvfp4_random_codes(orc):
         assert np.all(host(qw)[5] == 0) and host(swr)[5] == 0
 
 
+def _int8_w8_call(x, cw, sw, g, flags=0):
+    M, K = x.shape
+    N = cw.shape[0]
+    q, s = empty((M, K), np.int8), empty((M,), np.float32)
+    qw, swr = empty((N, K), np.int8), empty((N,), np.float32)
+    dm.hadamard_quant_int8_w8(dev(x).view(M, K), q, s, dev(cw).view(N, K // 2), dev(sw).view(N, K // 16),
+                              dev(np.array([g], np.float32)), qw, swr, flags=flags)
+    torch.cuda.synchronize()
+    return host(q), host(s), host(qw), host(swr)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 16), (37, 33, 96), (300, 200, 3072), (19, 70, 12288),
+                                   (0, 33, 96), (37, 0, 96), (17776, 9216, 3072), (17776, 3072, 12288)])
+def test_int8_w8_one_launch_parity(orc, M, N, K):
+    # the INT8 route's activation quantization and weight conversion in one
+    # launch: each output bit-exact against the oracle (the 5B-like qkv and
+    # ffn_down shapes included)
+    require_gpu()
+    say(f"hadamard_quant_int8_w8 M={M} N={N} K={K}")
+    rng = np.random.default_rng(5 * M + 3 * N + K)
+    x = workloads.activations(rng, M, K)
+    ref = orc.prep_weight(workloads.weight(rng, N, K))
+    flag_set = (0, dm.NO_HADAMARD) if M * K <= 1 << 20 else (0,)
+    for flags in flag_set:
+        q, s, qw, swr = _int8_w8_call(x, ref["cw"], ref["sw"], ref["gw"], flags)
+        q0, s0 = orc.quant_int8(x, flags)
+        assert np.array_equal(s.view(np.uint32), s0.view(np.uint32))
+        assert np.array_equal(q, q0)
+        assert np.array_equal(qw, ref["qw"])
+        assert np.array_equal(swr.view(np.uint32), ref["sw_row"].view(np.uint32))
+
+
+def test_int8_w8_one_launch_weight_rules(orc):
+    # arbitrary codes and scales, an all-zero weight row, and tensor scales
+    # that are tiny, huge, infinite and NaN: the weight half follows the
+    # conversion's rules exactly, beside a ragged activation half
+    require_gpu()
+    say("hadamard_quant_int8_w8 weight rules")
+    rng = np.random.default_rng(64)
+    M, N, K = 45, 130, 2080
+    x = workloads.activations(rng, M, K)
+    cw = rng.integers(0, 256, (N, K // 2)).astype(np.uint8)
+    sw = rng.integers(0, 0x7F, (N, K // 16)).astype(np.uint8)
+    cw[5] = 0
+    q0, s0 = orc.quant_int8(x, 0)
+    for g in np.array([3.0517578e-05, 1.7e3, 2.0 ** 101, np.inf, np.nan], np.float32):
+        q, s, qw, swr = _int8_w8_call(x, cw, sw, g)
+        qw0, swr0 = orc.w8_from_nvfp4(cw, sw, g)
+        assert np.array_equal(qw, qw0)
+        assert np.array_equal(swr.view(np.uint32), swr0.view(np.uint32))
+        assert np.array_equal(q, q0) and np.array_equal(s.view(np.uint32), s0.view(np.uint32))
+
+
 def test_quant_subnormal_inputs(orc):
     # bf16 subnormals (below 2^-126) must be kept, not flushed, through the
     # Hadamard and both quantizers
