@@ -1,5 +1,7 @@
 """GPU parity of the routed hot path on the CogVideoX-like configurations.
 
+Tiny (256 tokens x 256): Gamma, route, both linears on every row, TDC.
+
 5B-like (17776 tokens, hidden 3072): four synthetic blocks with Gamma about
 0.05, 0.40, 0.05, 0.40 route (alpha = 1, beta = 0, tau = 0.2) to NVFP4, INT8,
 NVFP4, INT8; the Gamma sums, routes, activation quantization (every row) and
@@ -53,6 +55,72 @@ def _linear_parity(orc, rng, M, N, K, route, rows):
         assert np.array_equal(host(c), c0) and np.array_equal(host(sc), sc0) and float(host(g)[0]) == g0
         y0, b0 = orc.gemm_nvfp4(c0, sc0, g0, p["cw"], p["sw"], p["gw"], rows=rows)
         assert np.all(np.abs(host(y[sel]).astype(np.float64) - y0) <= 1e-5 * b0)
+
+
+def test_tiny_config_end_to_end(orc):
+    """The tiny configuration (256 tokens x 256, four outlier channels x50,
+    a 256 x 256 N(0, 1/256) weight): Gamma of a random residual block and the
+    route; both quantized linears on every output row, the INT8 one through
+    the one-launch quantizer with the weight conversion; a TDC refresh of the
+    block and a skip from its cached delta."""
+    require_gpu()
+    say("tiny config end to end")
+    cfg = wl.TINY
+    M, K = cfg.M, cfg.hidden
+    N = cfg.linears[0].N
+    rng = np.random.default_rng(cfg.seeds[0])
+    x = wl.activations(rng, M, K)
+    assert wl.n_outlier_channels(K) == 4
+    x_out = wl.residual_block_output(rng, x, K)
+    w = wl.weight(rng, N, K)
+    ws = dm.new_workspace(dm.OP_QUANT_NVFP4)
+    s = torch.zeros(2, dtype=torch.float64, device="cuda")
+    dm.gamma_sums(dev(x), dev(x_out), s, ws)
+    torch.cuda.synchronize()
+    s0 = orc.gamma_sums(x, x_out)
+    assert np.all(np.abs(host(s) - s0) <= 1e-6 * s0)
+    gam = s0[0] / s0[1]
+    for tau in (0.5 * gam, 2.0 * gam):   # one threshold per route
+        r = dm.gate_and_route(host(s), [1.0], [0.0], tau)[2]
+        assert np.array_equal(r, orc.route(s0, [1.0], [0.0], tau)[2])
+    p = orc.prep_weight(w)
+    # INT8 route: activations and the NVFP4 -> INT8 weight in one launch
+    q, sa = empty((M, K), np.int8), empty((M,), np.float32)
+    qw, swr = empty((N, K), np.int8), empty((N,), np.float32)
+    dm.hadamard_quant_int8_w8(dev(x), q, sa, dev(p["cw"]), dev(p["sw"]), dev(np.array([p["gw"]], np.float32)),
+                              qw, swr)
+    y8 = empty((M, N), np.float32)
+    dm.qgemm_int8(q, sa, qw, swr, y8)
+    # NVFP4 route
+    c, sc, g = empty((M, K // 2), np.uint8), empty((M, K // 16), np.uint8), torch.zeros(1, device="cuda")
+    dm.hadamard_quant_nvfp4(dev(x), c, sc, g, ws)
+    y4 = empty((M, N), np.float32)
+    dm.qgemm_nvfp4(c, sc, g, dev(p["cw"]), dev(p["sw"]), dev(np.array([p["gw"]], np.float32)), y4)
+    torch.cuda.synchronize()
+    q0, s0a = orc.quant_int8(x)
+    assert np.array_equal(host(q), q0) and np.array_equal(host(sa).view(np.uint32), s0a.view(np.uint32))
+    assert np.array_equal(host(qw), p["qw"]) and np.array_equal(host(swr).view(np.uint32),
+                                                                p["sw_row"].view(np.uint32))
+    _, y80 = orc.gemm_int8(q0, s0a, p["qw"], p["sw_row"])
+    assert np.array_equal(host(y8).view(np.uint32), y80.view(np.uint32))
+    c0, sc0, g0 = orc.quant_nvfp4(x)
+    assert np.array_equal(host(c), c0) and np.array_equal(host(sc), sc0) and float(host(g)[0]) == g0
+    y40, b0 = orc.gemm_nvfp4(c0, sc0, g0, p["cw"], p["sw"], p["gw"])
+    assert np.all(np.abs(host(y4).astype(np.float64) - y40) <= 1e-5 * b0)
+    # TDC: refresh caches delta = out - in, then a skip rebuilds out from it
+    delta = torch.zeros(M * K, dtype=torch.int16, device="cuda")
+    sums = torch.zeros(4, dtype=torch.float64, device="cuda")
+    dm.tdc_step(dm.TDC_REFRESH, dev(x).view(-1), dev(x_out).view(-1), delta, False, sums,
+                dm.new_workspace(dm.OP_TDC))
+    out = torch.empty(M * K, dtype=torch.int16, device="cuda")
+    torch.cuda.synchronize()
+    d0 = np.zeros(M * K, np.uint16)
+    t0 = orc.tdc_refresh(x.ravel(), x_out.ravel(), d0, False)
+    assert np.array_equal(host(delta, np.uint16), d0)
+    assert np.all(np.abs(host(sums)[:2] - t0[:2]) <= 1e-6 * np.abs(t0[:2]))
+    dm.tdc_step(dm.TDC_SKIP, dev(x).view(-1), out, delta, True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out, np.uint16), orc.tdc_skip(x.ravel(), d0))
 
 
 def test_cogvideox5b_routing_and_linears(orc):
