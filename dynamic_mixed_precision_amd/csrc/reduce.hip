@@ -84,13 +84,17 @@ __global__ __launch_bounds__(256) void finalize_sums_kernel(const double *__rest
     if (tid < NS) out[tid] = (red[tid][0] + red[tid][1]) + (red[tid][2] + red[tid][3]);
 }
 
-// Grid of the streaming sum kernels: one 16-byte chunk per operand per lane
-// per iteration and at most this many workgroups.  Measured on the 17776 x
-// 3072 tensors (54.6 M elements): two-operand sums stream at 6.0 (MALL
-// flushed) to 6.6 TB/s (hot) this way, against 5.6 to 6.0 with four chunks in
-// flight per lane over 2048 workgroups; the refresh's three reads and one
-// write reach 6.2 TB/s hot.  Fewer workgroups also halve the finalize work.
-constexpr unsigned kSumGroups = 1024;
+// Grids of the streaming kernels.  Each lane takes two 16-byte chunks per
+// operand per iteration (chunks c and c + stride, all loads issued before
+// any use), over few long-lived workgroups: 512 for Gamma, 256 (one per CU)
+// for the TDC refresh and skip.  Same-box A/B against one chunk per lane
+// over 1024 (Gamma, refresh) or up to 8192 (skip) workgroups, sums and
+// outputs unchanged: refresh 71.5 against 76.9 us at 17776 x 3072 and 412
+// against 486 us at 106306 x 3072; skip 54.3 against 54.7 and 316 against
+// 392 us; Gamma 35.5 against 35.9 and 188 against 194 us.  Fewer
+// workgroups also shrink the finalize work.
+constexpr unsigned kGammaGroups = 512;
+constexpr unsigned kTdcGroups = 256;
 
 // ---------------------------------------------------------------------------
 // Gamma sums: S1 = sum |out - in|, S2 = sum |in|.
@@ -101,10 +105,10 @@ __global__ __launch_bounds__(256) void gamma_kernel(const uint16_t *__restrict__
     double s[2] = {0.0, 0.0};
     const int64_t nch = n / 8;
     const int64_t stride = (int64_t)gridDim.x * 256;
-    for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < nch; c += stride) {
+    auto add8 = [&](const uint4 &ra, const uint4 &rb) {
         float va[8], vb[8];
-        to8(ld16(xin + 8 * c), va);
-        to8(ld16(xout + 8 * c), vb);
+        to8(ra, va);
+        to8(rb, vb);
         float f1 = 0.0f, f2 = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; i++) {
@@ -113,7 +117,15 @@ __global__ __launch_bounds__(256) void gamma_kernel(const uint16_t *__restrict__
         }
         s[0] += (double)f1;
         s[1] += (double)f2;
+    };
+    int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    for (; c + stride < nch; c += 2 * stride) {
+        const uint4 a0 = ld16(xin + 8 * c), b0 = ld16(xout + 8 * c);
+        const uint4 a1 = ld16(xin + 8 * (c + stride)), b1 = ld16(xout + 8 * (c + stride));
+        add8(a0, b0);
+        add8(a1, b1);
     }
+    if (c < nch) add8(ld16(xin + 8 * c), ld16(xout + 8 * c));
     if (blockIdx.x == 0 && threadIdx.x < n - 8 * nch) {  // ragged tail, < 8 elements
         const int64_t i = 8 * nch + threadIdx.x;
         const float a = __uint_as_float((uint32_t)xin[i] << 16);
@@ -126,9 +138,9 @@ __global__ __launch_bounds__(256) void gamma_kernel(const uint16_t *__restrict__
 
 hipError_t launch_gamma(hipStream_t st, const uint16_t *x_in, const uint16_t *x_out, int64_t n,
                         double *sums, const Workspace &ws) {
-    const unsigned g = stride_grid(n / 8, 256, kSumGroups);
+    const unsigned g = stride_grid(n / 8, 512, kGammaGroups);
     hipLaunchKernelGGL(gamma_kernel, dim3(g), dim3(256), 0, st, x_in, x_out, n, ws.partial);
-    hipLaunchKernelGGL((finalize_sums_kernel<2, kSumGroups / 256>), dim3(1), dim3(256), 0, st, ws.partial, (int)g,
+    hipLaunchKernelGGL((finalize_sums_kernel<2, kGammaGroups / 256>), dim3(1), dim3(256), 0, st, ws.partial, (int)g,
                        sums);
     return hipGetLastError();
 }
@@ -141,17 +153,25 @@ __global__ __launch_bounds__(256) void tdc_skip_kernel(const uint16_t *__restric
                                                        int64_t n, uint16_t *__restrict__ xout) {
     const int64_t nch = n / 8;
     const int64_t stride = (int64_t)gridDim.x * 256;
-    for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < nch; c += stride) {
+    auto skip8 = [&](int64_t ci, const uint4 &ra, const uint4 &rd) {
         float a[8], d[8];
-        to8(ld16(xin + 8 * c), a);
-        to8(ld16(delta + 8 * c), d);
+        to8(ra, a);
+        to8(rd, d);
         uint4 o;
         o.x = cvt_pk_bf16(a[0] + d[0], a[1] + d[1]);
         o.y = cvt_pk_bf16(a[2] + d[2], a[3] + d[3]);
         o.z = cvt_pk_bf16(a[4] + d[4], a[5] + d[5]);
         o.w = cvt_pk_bf16(a[6] + d[6], a[7] + d[7]);
-        store_nt16(xout + 8 * c, o);
+        store_nt16(xout + 8 * ci, o);
+    };
+    int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    for (; c + stride < nch; c += 2 * stride) {
+        const uint4 a0 = ld16(xin + 8 * c), d0 = ld16(delta + 8 * c);
+        const uint4 a1 = ld16(xin + 8 * (c + stride)), d1 = ld16(delta + 8 * (c + stride));
+        skip8(c, a0, d0);
+        skip8(c + stride, a1, d1);
     }
+    if (c < nch) skip8(c, ld16(xin + 8 * c), ld16(delta + 8 * c));
     if (blockIdx.x == 0 && threadIdx.x < n - 8 * nch) {
         const int64_t i = 8 * nch + threadIdx.x;
         const float a = __uint_as_float((uint32_t)xin[i] << 16);
@@ -162,7 +182,7 @@ __global__ __launch_bounds__(256) void tdc_skip_kernel(const uint16_t *__restric
 
 hipError_t launch_tdc_skip(hipStream_t st, const uint16_t *x_in, const uint16_t *delta,
                            int64_t n, uint16_t *x_out) {
-    const unsigned g = stride_grid(n / 8, 256 * 4, 8192);
+    const unsigned g = stride_grid(n / 8, 512, kTdcGroups);
     hipLaunchKernelGGL(tdc_skip_kernel, dim3(g), dim3(256), 0, st, x_in, delta, n, x_out);
     return hipGetLastError();
 }
@@ -214,7 +234,18 @@ __global__ __launch_bounds__(256) void tdc_refresh_kernel(const uint16_t *__rest
     const int64_t nch = n / 8;
     const int64_t stride = (int64_t)gridDim.x * 256;
     const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-    for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < nch; c += stride) {
+    int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    for (; c + stride < nch; c += 2 * stride) {
+        const int64_t c1 = c + stride;
+        const uint4 i0 = ld16(xin + 8 * c), o0 = ld16(xout + 8 * c), d0 = DV ? ld16(delta + 8 * c) : zero;
+        const uint4 i1 = ld16(xin + 8 * c1), o1 = ld16(xout + 8 * c1), d1 = DV ? ld16(delta + 8 * c1) : zero;
+        uint4 nd0, nd1;
+        refresh8<DV>(i0, o0, d0, s, nd0);
+        store_nt16(delta + 8 * c, nd0);
+        refresh8<DV>(i1, o1, d1, s, nd1);
+        store_nt16(delta + 8 * c1, nd1);
+    }
+    if (c < nch) {
         uint4 nd;
         refresh8<DV>(ld16(xin + 8 * c), ld16(xout + 8 * c), DV ? ld16(delta + 8 * c) : zero, s, nd);
         store_nt16(delta + 8 * c, nd);
@@ -240,14 +271,14 @@ __global__ __launch_bounds__(256) void tdc_refresh_kernel(const uint16_t *__rest
 hipError_t launch_tdc_refresh(hipStream_t st, const uint16_t *x_in, const uint16_t *x_out,
                               uint16_t *delta, int64_t n, int delta_valid, double *sums,
                               const Workspace &ws) {
-    const unsigned g = stride_grid(n / 8, 256, kSumGroups);
+    const unsigned g = stride_grid(n / 8, 512, kTdcGroups);
     if (delta_valid)
         hipLaunchKernelGGL(tdc_refresh_kernel<true>, dim3(g), dim3(256), 0, st, x_in, x_out,
                            delta, n, ws.partial);
     else
         hipLaunchKernelGGL(tdc_refresh_kernel<false>, dim3(g), dim3(256), 0, st, x_in, x_out,
                            delta, n, ws.partial);
-    hipLaunchKernelGGL((finalize_sums_kernel<4, kSumGroups / 256>), dim3(1), dim3(256), 0, st, ws.partial, (int)g,
+    hipLaunchKernelGGL((finalize_sums_kernel<4, kTdcGroups / 256>), dim3(1), dim3(256), 0, st, ws.partial, (int)g,
                        sums);
     return hipGetLastError();
 }
