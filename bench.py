@@ -93,6 +93,9 @@ def parse():
                         "flushed before every call, and the oracle's 1-thread quantizers")
     p.add_argument("--extra-steps", type=int, default=3,
                    help="timed steps of each extra linear workload (after one warmup step)")
+    p.add_argument("--host-sync", choices=["spin", "block"], default="spin",
+                   help="the step's one wait for the device (the Gamma/PDR sums): poll an event "
+                        "(spin) or a blocking stream synchronize (block)")
     p.add_argument("--events", choices=["nofence", "torch"], default="nofence",
                    help="timing events: HIP events without the system-scope fence (default), "
                         "or default torch.cuda events")
@@ -254,6 +257,7 @@ def main():
 
     import dynamic_mixed_precision_amd as dm
     import workloads as wl
+    from dynamic_mixed_precision_amd.schedule import spin_sync
 
     dm.lib()
     if not torch.cuda.is_available():
@@ -331,6 +335,7 @@ def main():
     setup_s = time.time() - t0
 
     kt = KernelTimer(torch, args.events)
+    host_t = {"wait": 0.0}  # host seconds spent in the per-step wait
     pdr_ratio = [None] * n_blocks
     gemm_ops_step = 0
     routes_seen = []
@@ -348,7 +353,12 @@ def main():
                 kt("outlier_count", 2.0 * M * H, dm.outlier_count, blk["x_in"].view(M, H), pdr[0],
                    sums[b, 6:7], ws_out, _shape=f"{M}x{H}")
         sums_host.copy_(sums, non_blocking=True)
-        torch.cuda.current_stream().synchronize()
+        t_wait = time.perf_counter()
+        if args.host_sync == "spin":
+            spin_sync()
+        else:
+            torch.cuda.current_stream().synchronize()
+        host_t["wait"] += time.perf_counter() - t_wait
         if args.gamma == "standalone":
             routes = [dm.gate_and_route(sums_np[b, 4:6], alpha, beta, tau)[2] for b in range(n_blocks)]
         else:
@@ -474,11 +484,16 @@ def main():
     kt.prepare(kt.calls * args.steps)
     torch.cuda.synchronize()
     kt.on = True
+    host_t["wait"] = 0.0
     t_start = time.perf_counter()
     for _ in range(args.steps):
         step()
+    t_issued = time.perf_counter()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
+    host_timing = {"sync": args.host_sync,
+                   "wait_ms_per_step": round(1e3 * host_t["wait"] / args.steps, 3),
+                   "enqueue_ms_per_step": round(1e3 * (t_issued - t_start - host_t["wait"]) / args.steps, 3)}
     kt.on = False
     ms_per_step = 1e3 * elapsed / args.steps
     value = gemm_ops_step / (elapsed / args.steps) / 1e12
@@ -586,6 +601,7 @@ def main():
         "kernels": kernels,
         "kernels_note": ("per-call HIP events on every call, in as many untimed steps after the timed "
                          "region; gamma_sums_standalone is timed beside those steps, not in them"),
+        "host": host_timing,
         "timing_events": ("HIP events without the system-scope fence" if args.events == "nofence"
                           else "torch.cuda events"),
         "kernels_by_shape": by_shape,

@@ -31,6 +31,18 @@ from . import (OP_OUTLIER, OP_TDC, ROUTE_BF16, TDC_REFRESH, TDC_SKIP, gate_and_r
                tdc_step)
 
 
+def spin_sync(stream=None) -> None:
+    """Wait until the stream's work so far is done by polling an event.  A
+    blocking synchronize sleeps until the completion interrupt wakes the
+    thread, which on a busy host can leave the GPU idle for a millisecond or
+    more at the one host boundary per timestep; polling reacts within
+    microseconds (it keeps one core busy for the wait)."""
+    ev = torch.cuda.Event()
+    ev.record(stream)
+    while not ev.query():
+        pass
+
+
 @dataclass
 class BlockCache:
     state: object
@@ -66,7 +78,7 @@ class TdcScheduler:
         """The one host boundary per timestep: commit last step's refreshes."""
         if not any(b.pending for b in self.blocks):
             return
-        torch.cuda.current_stream().synchronize()
+        spin_sync()
         for b in self.blocks:
             if b.pending:
                 s = b.sums_host.numpy().copy()
