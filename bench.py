@@ -1148,7 +1148,7 @@ GEMM_SOURCES = {"qgemm_nvfp4": ["gemm_nvfp4.hip", "gemm_bf16.hip", "gemm_common.
                                 "internal.hpp"],
                 "qgemm_int8": ["gemm_int8.hip", "gemm_dma.hpp", "gemm_common.hpp", "device.hpp",
                                "internal.hpp"]}
-CALIB_KERNEL = "dmpq::tdc_skip_kernel"
+CALIB_KERNEL = "dmpq::tdc_skip_kernel<2>"  # the skip kernel at the calibration size (64 M chunks)
 # Known-size calibration of the DMA load path: one 256 x 256 tile over K =
 # DMA_CALIB_K (a one-workgroup launch, so its dispatches are told apart from
 # the step's by their grid of 256 work-items); bytes each operand moves once.
