@@ -339,7 +339,7 @@ def main():
     setup_s = time.time() - t0
 
     kt = KernelTimer(torch, args.events)
-    host_t = {"wait": 0.0}  # host seconds spent in the per-step wait
+    host_t = {"wait": 0.0, "decide": 0.0}  # host seconds in the per-step wait and the decisions after it
     pdr_ratio = [None] * n_blocks
     gemm_ops_step = 0
     routes_seen = []
@@ -362,7 +362,8 @@ def main():
             spin_sync()
         else:
             torch.cuda.current_stream().synchronize()
-        host_t["wait"] += time.perf_counter() - t_wait
+        t_decide = time.perf_counter()
+        host_t["wait"] += t_decide - t_wait
         if args.gamma == "standalone":
             routes = [dm.gate_and_route(sums_np[b, 4:6], alpha, beta, tau)[2] for b in range(n_blocks)]
         else:
@@ -373,6 +374,7 @@ def main():
                 if dm.pdr_decide(float(sums_np[b, 6]), M * H, pdr[1]):
                     routes[b] = np.full(len(routes[b]), dm.ROUTE_BF16, np.uint8)
                 pdr_ratio[b] = float(sums_np[b, 6]) / (M * H)
+        host_t["decide"] += time.perf_counter() - t_decide
         if args.graph == "on" and not kt.on:
             # the issue below, captured once per routing (after one eager
             # pass, which does the library's one-time set-up) and replayed
@@ -516,7 +518,7 @@ def main():
     kt.prepare(kt.calls * args.steps)
     torch.cuda.synchronize()
     kt.on = args.graph == "off"
-    host_t["wait"] = 0.0
+    host_t["wait"] = host_t["decide"] = 0.0
     t_start = time.perf_counter()
     for _ in range(args.steps):
         step()
@@ -525,7 +527,8 @@ def main():
     elapsed = time.perf_counter() - t_start
     host_timing = {"sync": args.host_sync,
                    "wait_ms_per_step": round(1e3 * host_t["wait"] / args.steps, 3),
-                   "enqueue_ms_per_step": round(1e3 * (t_issued - t_start - host_t["wait"]) / args.steps, 3)}
+                   "enqueue_ms_per_step": round(1e3 * (t_issued - t_start - host_t["wait"]) / args.steps, 3),
+                   "decide_ms_per_step": round(1e3 * host_t["decide"] / args.steps, 3)}
     kt.on = False
     ms_per_step = 1e3 * elapsed / args.steps
     value = gemm_ops_step / (elapsed / args.steps) / 1e12
