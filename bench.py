@@ -1373,7 +1373,7 @@ def summarize_counters(out_md: str, csvs: list, command: str, n_xcd: int = 8, n_
         return "-" if v is None else f.format(v)
 
     lines = ["# rocprofv3 counters per kernel: bench.py step, CogVideoX-5B-like batch", "",
-             "Commands (each counter set is its own run, from /tmp, repository at $GRAFT_REPO_ROOT):", "",
+             "Commands (each counter set is its own run, from /tmp, $REPO is the repository root):", "",
              "```", command, "```", "",
              f"Cycles = GRBM_GUI_ACTIVE / {n_xcd} XCDs; clock = cycles / dispatch duration; MFMA busy = "
              f"SQ_VALU_MFMA_BUSY_CYCLES / (cycles x {n_cu} CUs x 4 SIMDs); wait share = SQ_WAIT_INST_ANY / "
@@ -1404,7 +1404,7 @@ def summarize_stats(stats_csv: str, out_md: str, command: str) -> None:
         rows = list(csv.DictReader(f))
     lines = ["# rocprofv3 kernel stats: bench.py step, CogVideoX-5B-like batch "
              "(17776 tokens, 4 blocks x 4 linears, 2 INT8 + 2 NVFP4 blocks)", "",
-             "Command (run from /tmp, repository at $GRAFT_REPO_ROOT):", "", "```", command, "```", "",
+             "Command (run from /tmp, $REPO is the repository root):", "", "```", command, "```", "",
              "| kernel | calls | avg us | min us | max us | share of GPU time |",
              "|---|---|---|---|---|---|"]
     for r in rows:
