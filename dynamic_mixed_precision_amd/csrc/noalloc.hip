@@ -17,7 +17,7 @@ namespace dmpq {
 
 // The array has the size of the caller workspace the checked entry point
 // takes (64 KiB); the first pass writes one float per workgroup and its grid
-// is capped at 1024 workgroups (hq_nvfp4_partials), so it holds the partials
+// is capped at 512 workgroups (hq_nvfp4_partials), so it holds the partials
 // of any tensor.  Every call on a device shares that device's copy, which
 // keeps the last call's contents: the first pass writes every partial the
 // second reads, so nothing needs clearing, but calls that overlap on one

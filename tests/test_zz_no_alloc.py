@@ -30,7 +30,7 @@ def _run(fn, x, flags, *ws):
 def test_noalloc_matches_workspace_call(orc, flags):
     require_gpu()
     ws = dm.new_workspace(dm.OP_QUANT_NVFP4)
-    # the larger call first (1024 first-pass partials), then a smaller one
+    # the larger call first (512 first-pass partials, the cap), then a smaller one
     # whose tensor amax is lower, so stale partials would show in g
     for (M, K), seed, scale in (((4096, 3072), 70, 50.0), ((37, 208), 71, 1.0)):
         say(f"noalloc nvfp4 quant M={M} K={K} flags={flags}")
